@@ -1,0 +1,332 @@
+"""Benchmark of the W8A8 rollout linear on one MI355X.
+
+Default workload: one 7B-shaped decoder layer's quantized linears at decode
+size, INT8, M = 256 tokens: QKV 4608x3584, O 3584x3584, gate and up
+18944x3584, down 3584x18944 (N x K), with per-token activation quantization in
+front of each (gate and up share one): 4 quantizations + 5 GEMMs per step.
+A "step" is one such layer pass over one batch; successive steps walk through
+distinct copies of the layer's weights (more bytes than the 256 MB Infinity
+Cache), like a decode pass walks a model's layers.
+
+The timed region is one replay of a HIP graph holding the K steps, between
+device synchronizations. Events recorded as graph nodes bracket the dominant
+GEMM of every step, which gives its average kernel duration for the roofline
+object. Inputs are seeded synthetic tensors generated on the device.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W8A8 linear TOPS & HBM GB/s vs roofline; decode-layer µs at 7B/32B shapes"
+HBM_PEAK_GBS = 8000.0
+MFMA8_PEAK_TOPS = 5000.0  # dense INT8 / FP8 MFMA
+
+WORKLOADS = {
+    "7b_decode_int8": dict(M=256, qt="int8", chain="7b", sets=4, kind="outliers"),
+    "7b_decode_fp8": dict(M=256, qt="fp8", chain="7b", sets=4, kind="outliers"),
+    "32b_decode_int8": dict(M=512, qt="int8", chain="32b", sets=2, kind="normal"),
+    "32b_decode_fp8": dict(M=512, qt="fp8", chain="32b", sets=2, kind="normal"),
+    "32b_prefill_int8": dict(M=4096, qt="int8", chain="32b_prefill", sets=2, kind="heavy"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def chain_spec(name):
+    from w8a8_gemm_rl_amd import inputs as I
+
+    if name == "7b":
+        return I.CHAIN_7B, I.LINEARS_7B, I.W_SIGMA_7B
+    if name == "32b":
+        return I.CHAIN_32B, I.LINEARS_32B, I.W_SIGMA_32B
+    if name == "32b_prefill":
+        return I.CHAIN_32B_PREFILL, I.LINEARS_32B, I.W_SIGMA_32B
+    raise ValueError(name)
+
+
+def linear_bytes(M, N, K):
+    """Algorithmic bytes of one GEMM: weight codes, activation codes, scales, bf16 out."""
+    return N * K + M * K + 4 * (M + N) + 2 * M * N
+
+
+def quant_bytes(M, K):
+    return 3 * M * K + 4 * M
+
+
+class Layer:
+    """One set of quantized weights for the chain, plus the ops of one step."""
+
+    def __init__(self, chain, shapes, M, qt, sigma, seed, dev, x0, bufs, ws, s):
+        import torch
+
+        from w8a8_gemm_rl_amd import binding as B
+
+        self.B = B
+        self.qt = qt
+        self.ops = []
+        self.W = {}
+        g = torch.Generator(device=dev)
+        for i, L in enumerate(chain):
+            N, K = shapes[L["name"]]
+            g.manual_seed(seed + i)
+            Wf = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * sigma
+            self.W[L["name"]] = B.quantize_weights_uaq(Wf, s, qt)
+            del Wf
+        self.x0, self.bufs, self.ws, self.s = x0, bufs, ws, s
+        self.chain, self.M = chain, M
+
+    def run(self, dom=None, ev=None, per_linear=None):
+        """Enqueue one layer step. ev = (start, end) events around GEMM `dom`;
+        per_linear = {name: (start, end)} events around every GEMM."""
+        B, bufs = self.B, self.bufs
+        done = {}
+        for L in self.chain:
+            src = self.x0 if L["src"] == "x0" else bufs["y_" + L["src"]]
+            key = (L["src"], L["cols"])
+            if L["cols"] is not None:
+                src = src[:, L["cols"][0]:L["cols"][1]]
+            if key not in done:
+                xq, sx = bufs["q_" + L["name"]]
+                B.quantize_act_per_token(src, self.s, self.qt, Xq=xq, scale_x=sx)
+                done[key] = (xq, sx)
+            xq, sx = done[key]
+            Wq, sw = self.W[L["name"]]
+            e = per_linear.get(L["name"]) if per_linear else (ev if L["name"] == dom else None)
+            if e:
+                e[0].record()
+            B.w8a8_gemm(xq, sx, Wq, sw, self.qt, out="bf16", Y=bufs["y_" + L["name"]], ws=self.ws)
+            if e:
+                e[1].record()
+
+
+def cpu_baseline(chain, shapes, M, qt, sigma, kind, s):
+    """Time the CPU oracle on one layer step of the same workload (host cores)."""
+    import numpy as np
+
+    import oracle as O
+    from w8a8_gemm_rl_amd import inputs as I
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    log("cpu baseline: preparing oracle weights ...")
+    layers = []
+    for i, L in enumerate(chain):
+        N, K = shapes[L["name"]]
+        W = I.weights(N, K, sigma, seed=I.matrix_seed(9, i))
+        q = O.quantize_weights_uaq(W, s, qt)
+        del W
+        layers.append(dict(L, Wq=q["Wq"], scale_w=q["scale_w"], act_mult=s))
+    K0 = shapes[chain[0]["name"]][1]
+    x0 = I.activations(M, K0, seed=I.matrix_seed(9, 99), kind=kind)
+    log("cpu baseline: timing one oracle layer step ...")
+    t0 = time.perf_counter()
+    O.decode_chain(x0, layers, qt)
+    dt = time.perf_counter() - t0
+    return dt, threads
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="7b_decode_int8", choices=sorted(WORKLOADS))
+    ap.add_argument("--m", type=int, default=None, help="override the token count M")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}, "
+            f"WORLD_SIZE {world}); the path has no multi-GPU mode")
+        sys.exit(2)
+
+    import torch
+
+    from w8a8_gemm_rl_amd import binding as B
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a HIP device")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+
+    wl = dict(WORKLOADS[args.workload])
+    if args.m is not None:
+        wl["M"] = args.m
+    M, qt, s = wl["M"], wl["qt"], 1.5
+    chain, shapes, sigma = chain_spec(wl["chain"])
+    K0 = shapes[chain[0]["name"]][1]
+
+    # ---- buffers: activations, per-linear codes and outputs, one workspace
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    x = torch.randn((M, K0), generator=g, device=dev)
+    if wl["kind"] == "outliers":
+        n_out = int(round(0.01 * K0))
+        ch = torch.randperm(K0, generator=g, device=dev)[:n_out]
+        x[:, ch] *= 20.0
+    elif wl["kind"] == "heavy":
+        x = x * torch.exp(torch.randn((1, K0), generator=g, device=dev))
+    x0 = x.to(torch.bfloat16)
+    bufs = {}
+    need = 0
+    for L in chain:
+        N, K = shapes[L["name"]]
+        bufs["y_" + L["name"]] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        bufs["q_" + L["name"]] = (torch.empty((M, K), dtype=B.code_dtype(qt), device=dev),
+                                  torch.empty(M, dtype=torch.float32, device=dev))
+        need = max(need, B.workspace_size("qr_w8a8_gemm", M, N, K, qt))
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+
+    log(f"bench: {args.workload} M={M} qt={qt}: building {wl['sets']} weight sets ...")
+    layers = [Layer(chain, shapes, M, qt, sigma, 1000 * (j + 1), dev, x0, bufs, ws, s)
+              for j in range(wl["sets"])]
+    torch.cuda.synchronize()
+
+    # ---- per-step algorithmic work
+    gemm_bytes = {L["name"]: linear_bytes(M, *shapes[L["name"]]) for L in chain}
+    ops_step = sum(2 * M * shapes[L["name"]][0] * shapes[L["name"]][1] for L in chain)
+    quant_keys, qbytes = set(), 0
+    for L in chain:
+        k = (L["src"], L["cols"])
+        if k not in quant_keys:
+            quant_keys.add(k)
+            qbytes += quant_bytes(M, shapes[L["name"]][1])
+    bytes_step = sum(gemm_bytes.values()) + qbytes
+    dom = max(chain, key=lambda L: (gemm_bytes[L["name"]], -chain.index(L)))["name"]
+    Nd, Kd = shapes[dom]
+    dom_ops = 2 * M * Nd * Kd
+    dom_intensity = dom_ops / gemm_bytes[dom]
+    dom_bound = "hbm" if dom_intensity < MFMA8_PEAK_TOPS / HBM_PEAK_GBS * 1000 else "mfma"
+
+    # ---- warmup (eager)
+    log(f"bench: warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        layers[i % len(layers)].run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True, external=True),
+            torch.cuda.Event(enable_timing=True, external=True)) for _ in range(K)]
+    mode = "eager" if args.eager else "hip_graph"
+    if not args.eager:
+        log(f"bench: capturing {K} steps into one HIP graph")
+        graph = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(graph, stream=st):
+                for i in range(K):
+                    layers[i % len(layers)].run(dom=dom, ev=evs[i])
+        torch.cuda.synchronize()
+
+    log(f"bench: timing {K} steps ({mode})")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if args.eager:
+        for i in range(K):
+            layers[i % len(layers)].run(dom=dom, ev=evs[i])
+    else:
+        graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec_step = (t1 - t0) / K
+    dom_ms = [a.elapsed_time(b) for a, b in evs]
+    dom_us = 1000.0 * sum(dom_ms) / len(dom_ms)
+
+    # ---- per-linear breakdown (eager, events around every GEMM; not timed)
+    per = {L["name"]: [] for L in chain}
+    reps = min(20, K)
+    for i in range(reps):
+        e = {L["name"]: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for L in chain}
+        layers[i % len(layers)].run(per_linear=e)
+        torch.cuda.synchronize()
+        for n, (a, b) in e.items():
+            per[n].append(a.elapsed_time(b) * 1000.0)
+    linears = {}
+    for L in chain:
+        n = L["name"]
+        N_, K_ = shapes[n]
+        us = sorted(per[n])[len(per[n]) // 2]
+        linears[n] = dict(N=N_, K=K_, us=round(us, 2),
+                          gbs=round(gemm_bytes[n] / us / 1e3, 1),
+                          tops=round(2 * M * N_ * K_ / us / 1e6, 1),
+                          plan=list(B.gemm_plan(M, N_, K_, qt)))
+
+    achieved = gemm_bytes[dom] / (dom_us * 1e-6) / 1e9 if dom_bound == "hbm" else dom_ops / (dom_us * 1e-6) / 1e12
+    peak = HBM_PEAK_GBS if dom_bound == "hbm" else MFMA8_PEAK_TOPS
+    roofline = {
+        "bound": dom_bound,
+        "achieved": round(achieved, 1),
+        "peak": peak,
+        "unit": "GB/s" if dom_bound == "hbm" else "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None,
+        "kernel": f"{dom} GEMM {Nd}x{Kd} M={M} ({B.tile_name(B.gemm_plan(M, Nd, Kd, qt)[0])}, "
+                  f"splitk {B.gemm_plan(M, Nd, Kd, qt)[1]})",
+        "kernel_us": round(dom_us, 2),
+        "alg_bytes_per_launch": gemm_bytes[dom],
+        "alg_ops_per_launch": dom_ops,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        dt, threads = cpu_baseline(chain, shapes, M, qt, sigma, wl["kind"], s)
+        cpu = {"value": round(bytes_step / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"one {args.workload} layer step (M={M}, all {len(chain)} linears and "
+                         f"their per-token quantizations) by the numpy oracle: {dt:.2f} s",
+               "seconds": round(dt, 3), "host_cpus": os.cpu_count()}
+
+    out = {
+        "metric": METRIC,
+        "value": round(bytes_step / sec_step / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": qt,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: one decoder layer's W8A8 linears, M={M} tokens, "
+                        + ", ".join(f"{L['name']} {shapes[L['name']][0]}x{shapes[L['name']][1]}"
+                                    for L in chain)
+                        + f"; {len(quant_keys)} per-token quantizations + {len(chain)} GEMMs",
+            "M": M, "qtype": qt, "uaq_s": s, "weight_sets": len(layers), "timing": mode,
+            "parallelism": "none (1 GPU)",
+        },
+        "layer_us": round(sec_step * 1e6, 2),
+        "tops": round(ops_step / sec_step / 1e12, 1),
+        "alg_bytes_per_step": bytes_step,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "linears": linears,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

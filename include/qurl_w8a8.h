@@ -1,0 +1,208 @@
+/*
+ * qurl_w8a8.h -- C ABI of the MI355X (gfx950) W8A8 quantized linear used by a
+ * quantized RL rollout actor ("QuRL: Efficient Reinforcement Learning with
+ * Quantized Rollout").
+ *
+ * Sources, cited by page and section:
+ *   [Notes/Framework]  paper-notes page, "Method > Overall framework": the old
+ *                      actor theta_old is quantized to theta_hat_old for every
+ *                      rollout.
+ *   [Notes/UAQ]        same page, "Method > Key designs > UAQ": W X = (W/s)(sX),
+ *                      s > 1 applied to W column-wise and to the activation
+ *                      row-wise, mergeable into the preceding norm.
+ *   [Notes/System]     same page, "Method > System integration": UAQ is a
+ *                      one-time weight preprocessing; rollout runs on INT8/FP8
+ *                      matrix-multiplication kernels.
+ *   [Notes/Training]   same page, "Loss / training strategy": channel-wise
+ *                      weight quantization, token-wise activation
+ *                      quantization, INT8 or FP8, s = 1.5.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Layout     Row-major. Weights W / codes Wq are [N, K] (torch.nn.Linear
+ *            out x in, K contiguous); activations X / codes Xq are [M, K];
+ *            outputs Y are [M, N]. Leading dimensions (ld*) count elements.
+ * Pointers   All array pointers are DEVICE pointers (memory of the current
+ *            HIP device), 16-byte aligned. Codes Xq and Wq are dense
+ *            (leading dimension K).
+ * Dtypes     bf16 is passed as its 16-bit pattern (uint16); INT8 codes are
+ *            int8; FP8 codes are OCP E4M3FN bytes (bias 7, max 448, no inf);
+ *            scales and master weights are IEEE fp32.
+ * Shapes     M, N >= 0 (0 makes the call a successful no-op); K >= 0 with
+ *            K % 16 == 0; INT8 needs K <= 133144 so that K*127^2 < 2^31.
+ *            ldx % 8 == 0, ldw % 4 == 0, ldy % 8 == 0 (bf16) or % 4 (raw).
+ * Ownership  The caller allocates and owns every buffer, including the
+ *            workspace. The library never allocates, frees or synchronizes.
+ * Streams    `stream` is a hipStream_t passed as void* (NULL = the null
+ *            stream). Every call only enqueues work on it and returns.
+ * Errors     Arguments are validated on the host before anything is
+ *            enqueued: a non-QR_OK status means nothing was launched.
+ *            qr_last_error() returns a thread-local message for the last
+ *            failure. Device faults surface at the caller's next
+ *            synchronization, as for any asynchronous HIP work.
+ * Finiteness Inputs must be finite; NaN/Inf inputs give unspecified codes.
+ * Threads    Calls are reentrant; concurrent calls on different streams must
+ *            not share a workspace.
+ */
+#ifndef QURL_W8A8_H
+#define QURL_W8A8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Quantized code type. */
+enum { QR_INT8 = 0, QR_FP8_E4M3FN = 1 };
+
+/* Output mode of qr_w8a8_gemm. */
+enum {
+  QR_OUT_BF16 = 0, /* dequantized bf16 Y */
+  QR_OUT_RAW = 1   /* raw accumulators: int32 (INT8) or fp32 (FP8) */
+};
+
+/* Status codes. */
+enum {
+  QR_OK = 0,
+  QR_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum, bad s */
+  QR_ERR_UNSUPPORTED = -2, /* valid but not handled: K % 16, alignment, K too large */
+  QR_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small */
+  QR_ERR_HIP = -4,         /* a HIP call failed (message has the HIP error) */
+  QR_ERR_NO_DEVICE = -5    /* no HIP device is visible */
+};
+
+/*
+ * qr_quantize_weights_uaq -- theta_old -> theta_hat_old with UAQ
+ *   [Notes/UAQ], [Notes/Framework], [Notes/Training], [Notes/System].
+ *
+ * For every output channel n (row of W):
+ *   W'[n,k]    = fl32(W[n,k] / s)                 (UAQ: the stored weight is W/s)
+ *   a_n        = max_k |W'[n,k]|
+ *   scale_w[n] = fl32(a_n / Q)                    Q = 127 (INT8) or 448 (FP8)
+ *   INT8: Wq   = clamp(round_half_even(fl32(W' / scale_w[n])), -127, 127)
+ *   FP8:  Wq   = E4M3FN_round_half_even(clamp(fl32(W' / scale_w[n]), -448, 448))
+ *   a_n == 0 gives scale_w[n] = 0 and all-zero codes.
+ * s = 1.5 is the pages' value; pass s = 1 to re-quantize weights that were
+ * already divided by s (the per-RL-step refresh).
+ *
+ *   W        [N, ldw] fp32 master weights (read).
+ *   s        UAQ factor, finite and > 0.
+ *   qt       QR_INT8 or QR_FP8_E4M3FN.
+ *   Wq       [N, K] codes (written).
+ *   scale_w  [N] fp32 per-channel scales (written).
+ *   W_scaled optional [N, ldw] fp32 output of W' (NULL to skip). It may equal
+ *            W to reparameterize in place (the one-time preprocessing).
+ *   gamma    optional [K] fp32 gain of the norm that feeds this linear; if
+ *            non-NULL it is multiplied by s in place (gamma' = fl32(gamma*s)),
+ *            which folds the activation-side s into the norm. Do this once,
+ *            at the one-time reparameterization, and only for one of the
+ *            linears that share the norm.
+ *   beta     optional [K] fp32 LayerNorm bias, multiplied by s like gamma.
+ */
+int qr_quantize_weights_uaq(const float* W, int64_t N, int64_t K, int64_t ldw, float s, int qt,
+                            void* Wq, float* scale_w, float* W_scaled, float* gamma, float* beta,
+                            void* stream);
+
+/*
+ * qr_quantize_act_per_token -- token-wise absmax quantization [Notes/Training].
+ *
+ * For every token m (row of X), with x = X[m,:] widened exactly to fp32:
+ *   a_m        = max_k |x_k|,  t_m = fl32(a_m / Q)
+ *   codes      as for the weights, from fl32(x_k / t_m)
+ *   scale_x[m] = fl32(t_m * act_mult)
+ * act_mult carries the UAQ factor onto the activation side of a linear whose
+ * input does not come from a norm that absorbed s ([Notes/UAQ]): pass s there
+ * and 1 for norm-fed linears. (With absmax quantization the codes of s*x equal
+ * those of x, so s only multiplies the scale.)
+ *
+ *   X        [M, ldx] bf16 bit patterns (read).
+ *   act_mult finite, > 0.
+ *   Xq       [M, K] codes (written); scale_x [M] fp32 (written).
+ */
+int qr_quantize_act_per_token(const void* X, int64_t M, int64_t K, int64_t ldx, float act_mult,
+                              int qt, void* Xq, float* scale_x, void* stream);
+
+/*
+ * qr_w8a8_gemm -- quantized product and dequantization epilogue
+ *   [Notes/System] (INT8/FP8 matmul), [Notes/Training].
+ *
+ *   acc[m,n] = sum_k Xq[m,k] * Wq[n,k]
+ *              INT8: exact int32.  FP8: products of E4M3FN values summed in
+ *              fp32 (order unspecified; deterministic for a given shape).
+ *   out = QR_OUT_BF16: Y[m,n] = bf16_rne(fl32(fl32(fl32(acc) * scale_x[m]) * scale_w[n]))
+ *   out = QR_OUT_RAW : Y[m,n] = acc (int32 or fp32), for parity checks.
+ *
+ *   Y        [M, ldy] bf16, int32 or fp32 (written).
+ *   workspace    device scratch of at least qr_workspace_size("qr_w8a8_gemm",
+ *                M, N, K, qt) bytes, 256-byte aligned; may be NULL when that
+ *                size is 0 (no K split for this shape). Layout, shared by
+ *                every call that takes a workspace: the first 16 KiB hold
+ *                split-K arrival counters and must be zero before the first
+ *                call (allocate the workspace zeroed); every call leaves
+ *                them zero and stores nothing else there, so one workspace
+ *                can serve any sequence of calls on one stream. Calls that
+ *                overlap in time (different streams) must not share it.
+ */
+int qr_w8a8_gemm(const void* Xq, const float* scale_x, const void* Wq, const float* scale_w,
+                 int64_t M, int64_t N, int64_t K, int qt, int out, void* Y, int64_t ldy,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qr_linear_fused -- the per-linear call of a rollout engine:
+ *   qr_quantize_act_per_token followed by qr_w8a8_gemm(out = QR_OUT_BF16),
+ *   with the activation codes and scales kept in the workspace.
+ *
+ *   X        [M, ldx] bf16 (read); Y [M, ldy] bf16 (written).
+ *   workspace    at least qr_workspace_size("qr_linear_fused", M, N, K, qt)
+ *                bytes (never 0 when M, N > 0), 256-byte aligned, with the
+ *                same 16 KiB zeroed counter prefix as for qr_w8a8_gemm; the
+ *                activation codes and scales are stored after it.
+ */
+int qr_linear_fused(const void* X, int64_t ldx, float act_mult, const void* Wq, const float* scale_w,
+                    int64_t M, int64_t N, int64_t K, int qt, void* Y, int64_t ldy,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qr_workspace_size -- bytes of workspace needed by `fn` ("qr_w8a8_gemm" or
+ * "qr_linear_fused") for this shape; 0 if none. Pure host function: it
+ * depends only on its arguments (and on qr_set_plan_override). Returns
+ * (size_t)-1 for an unknown fn or invalid sizes.
+ */
+size_t qr_workspace_size(const char* fn, int64_t M, int64_t N, int64_t K, int qt);
+
+/*
+ * qr_gemm_plan -- report the kernel plan qr_w8a8_gemm uses for a shape:
+ *   *tile    index of the tile configuration (see qr_tile_name),
+ *   *splitk  number of K splits (1 = none).
+ * Pure host function; returns QR_OK or QR_ERR_INVALID_ARG.
+ */
+int qr_gemm_plan(int64_t M, int64_t N, int64_t K, int qt, int* tile, int* splitk);
+
+/* Name of tile configuration `tile` (static string) or NULL if out of range. */
+const char* qr_tile_name(int tile);
+
+/* Number of tile configurations. */
+int qr_num_tiles(void);
+
+/*
+ * qr_set_plan_override -- tuning hook: force tile configuration `tile` and
+ * `splitk` splits for every later qr_w8a8_gemm / qr_linear_fused /
+ * qr_workspace_size call in the process (tile < 0 restores automatic
+ * planning). Not thread-safe; meant for benchmarks and tests.
+ * Returns QR_OK or QR_ERR_INVALID_ARG.
+ */
+int qr_set_plan_override(int tile, int splitk);
+
+/* Thread-local message describing the last non-QR_OK status ("" if none). */
+const char* qr_last_error(void);
+
+/* Library version string. */
+const char* qr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QURL_W8A8_H */

@@ -77,6 +77,8 @@ def e4m3fn_decode(codes):
     return sign * mag
 
 
+_CHUNK = 1 << 18
+
 # The 127 finite non-negative values, codes 0x00..0x7E, increasing.
 _POS_CODES = np.arange(0x7F, dtype=np.uint8)
 _POS_VALUES = e4m3fn_decode(_POS_CODES)
@@ -96,6 +98,12 @@ def e4m3fn_encode(x):
     x = np.ascontiguousarray(x, dtype=np.float32)
     if not np.all(np.isfinite(x)):
         raise ValueError("e4m3fn_encode: non-finite input")
+    if x.size > _CHUNK:  # same result, processed in cache-sized pieces
+        flat = x.reshape(-1)
+        out = np.empty(flat.shape, np.uint8)
+        for i in range(0, flat.size, _CHUNK):
+            out[i:i + _CHUNK] = e4m3fn_encode(flat[i:i + _CHUNK])
+        return out.reshape(x.shape)
     ax = np.abs(x.astype(np.float64))
     if np.any(ax > E4M3FN_MAX):
         raise ValueError("e4m3fn_encode: |x| > 448 (saturate first)")

@@ -1,0 +1,154 @@
+"""CPU checks of the C-ABI library: it loads, exports what the header declares,
+and rejects bad arguments on the host before touching a device.
+
+No compute entry point is run here with valid arguments (there is no GPU);
+every call below fails argument validation, which happens before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qurl_w8a8.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from w8a8_gemm_rl_amd import binding
+    binding.lib()
+    return binding
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(qr_\w+)\s*\(", txt)))
+
+
+def test_header_declarations_are_exported(B):
+    names = _declared()
+    assert len(names) >= 4
+    L = B.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(B.EXPORTS) == names
+
+
+def test_exported_dynamic_symbols(B):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in _declared():
+        assert n in syms, n
+
+
+def test_version_and_tiles(B):
+    assert "gfx950" in B.version()
+    n = B.num_tiles()
+    assert n >= 4
+    names = [B.tile_name(i) for i in range(n)]
+    assert all(names) and len(set(names)) == n
+    assert B.tile_name(n) is None and B.tile_name(-1) is None
+
+
+NULL = None
+I8, F8 = 0, 1
+
+
+def _L(B):
+    return B.lib()
+
+
+def test_weight_quant_validation(B):
+    L = _L(B)
+    fake = ctypes.c_void_p(256)
+    # bad qtype
+    assert L.qr_quantize_weights_uaq(fake, 4, 16, 16, 1.5, 7, fake, fake, NULL, NULL, NULL, NULL) == -1
+    assert "qtype" in L.qr_last_error().decode()
+    # negative sizes
+    assert L.qr_quantize_weights_uaq(fake, -1, 16, 16, 1.5, I8, fake, fake, NULL, NULL, NULL, NULL) == -1
+    # s must be finite and positive
+    for s in (0.0, -1.5, float("nan"), float("inf")):
+        assert L.qr_quantize_weights_uaq(fake, 4, 16, 16, s, I8, fake, fake, NULL, NULL, NULL, NULL) == -1
+    # K not a multiple of 16
+    assert L.qr_quantize_weights_uaq(fake, 4, 24, 24, 1.5, I8, fake, fake, NULL, NULL, NULL, NULL) == -2
+    # INT8 accumulator bound
+    assert L.qr_quantize_weights_uaq(fake, 4, 133152, 133152, 1.5, I8, fake, fake, NULL, NULL, NULL, NULL) == -2
+    # null pointers
+    assert L.qr_quantize_weights_uaq(NULL, 4, 16, 16, 1.5, I8, fake, fake, NULL, NULL, NULL, NULL) == -1
+    assert L.qr_quantize_weights_uaq(fake, 4, 16, 16, 1.5, I8, fake, NULL, NULL, NULL, NULL, NULL) == -1
+    # ldw < K
+    assert L.qr_quantize_weights_uaq(fake, 4, 16, 8, 1.5, I8, fake, fake, NULL, NULL, NULL, NULL) == -1
+    # misaligned
+    assert L.qr_quantize_weights_uaq(ctypes.c_void_p(258), 4, 16, 16, 1.5, I8, fake, fake, NULL, NULL, NULL, NULL) == -2
+
+
+def test_act_quant_validation(B):
+    L = _L(B)
+    fake = ctypes.c_void_p(256)
+    assert L.qr_quantize_act_per_token(fake, 4, 32, 32, 0.0, I8, fake, fake, NULL) == -1
+    assert L.qr_quantize_act_per_token(fake, 4, 32, 16, 1.0, I8, fake, fake, NULL) == -1
+    assert L.qr_quantize_act_per_token(fake, 4, 32, 36, 1.0, I8, fake, fake, NULL) == -2  # ldx % 8
+    assert L.qr_quantize_act_per_token(fake, 4, 40, 40, 1.0, F8, fake, fake, NULL) == -2  # K % 16
+    assert L.qr_quantize_act_per_token(NULL, 4, 32, 32, 1.0, F8, fake, fake, NULL) == -1
+    assert L.qr_quantize_act_per_token(fake, 4, 32, 32, 1.0, 2, fake, fake, NULL) == -1
+
+
+def test_gemm_validation(B):
+    L = _L(B)
+    f = ctypes.c_void_p(256)
+    args = lambda **kw: [kw.get(k, v) for k, v in [
+        ("Xq", f), ("sx", f), ("Wq", f), ("sw", f), ("M", 4), ("N", 32), ("K", 64), ("qt", I8),
+        ("out", 0), ("Y", f), ("ldy", 32), ("ws", NULL), ("wsb", 0), ("st", NULL)]]
+    g = L.qr_w8a8_gemm
+    assert g(*args(out=5)) == -1
+    assert g(*args(ldy=16)) == -1
+    assert g(*args(Y=NULL)) == -1
+    assert g(*args(sw=NULL)) == -1
+    assert g(*args(K=72)) == -2
+    assert g(*args(ldy=36)) == -2
+    assert g(*args(Wq=ctypes.c_void_p(264))) == -2
+    # raw output needs no scales but still a Y
+    assert g(*args(out=1, Y=NULL)) == -1
+    # a shape that splits K needs a workspace
+    need = L.qr_workspace_size(b"qr_w8a8_gemm", 16, 512, 4096, I8)
+    assert need > 0
+    assert g(*args(M=16, N=512, K=4096, ldy=512)) == -3
+    assert "workspace" in L.qr_last_error().decode()
+    assert g(*args(M=16, N=512, K=4096, ldy=512, ws=ctypes.c_void_p(512), wsb=need - 1)) == -3
+    assert g(*args(M=16, N=512, K=4096, ldy=512, ws=ctypes.c_void_p(300), wsb=need)) == -3
+
+
+def test_linear_fused_validation(B):
+    L = _L(B)
+    f = ctypes.c_void_p(256)
+    fn = L.qr_linear_fused
+    # X, ldx, act_mult, Wq, sw, M, N, K, qt, Y, ldy, ws, wsb, stream
+    assert fn(f, 64, 1.0, f, f, 4, 32, 64, I8, f, 32, NULL, 0, NULL) == -3  # needs Xq space
+    assert fn(f, 64, -1.0, f, f, 4, 32, 64, I8, f, 32, NULL, 0, NULL) == -1
+    assert fn(f, 60, 1.0, f, f, 4, 32, 64, I8, f, 32, NULL, 0, NULL) == -1
+    assert fn(NULL, 64, 1.0, f, f, 4, 32, 64, I8, f, 32, NULL, 0, NULL) == -1
+
+
+def test_workspace_size_and_plan_are_pure(B):
+    L = _L(B)
+    assert L.qr_workspace_size(b"qr_w8a8_gemm", 0, 512, 512, I8) == 0
+    assert L.qr_workspace_size(b"nope", 4, 512, 512, I8) == ctypes.c_size_t(-1).value
+    assert L.qr_workspace_size(b"qr_w8a8_gemm", 4, 512, 500, I8) == ctypes.c_size_t(-1).value
+    a = L.qr_workspace_size(b"qr_linear_fused", 256, 3584, 3584, I8)
+    b = L.qr_workspace_size(b"qr_w8a8_gemm", 256, 3584, 3584, I8)
+    assert a >= b + 256 * 3584 + 256 * 4 and a % 256 == 0
+    t, s = B.gemm_plan(256, 3584, 3584, "int8")
+    assert 0 <= t < B.num_tiles() and s >= 1
+    # big grids need no split
+    assert B.gemm_plan(4096, 27648, 5120, "int8")[1] == 1
+    # override hook round-trips
+    B.set_plan_override(0, 3)
+    assert B.gemm_plan(256, 3584, 3584, "fp8") == (0, 3)
+    B.set_plan_override(-1)
+    assert B.gemm_plan(256, 3584, 3584, "int8") == (t, s)
+    with pytest.raises(B.QRError):
+        B.set_plan_override(999, 1)

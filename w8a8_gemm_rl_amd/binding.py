@@ -1,0 +1,248 @@
+"""Thin ctypes binding over libqurl_w8a8.so (C ABI in include/qurl_w8a8.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's kernels. If
+the shared library is missing this module raises -- there is no fallback.
+
+Function names mirror the C entry points without the ``qr_`` prefix.
+"""
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqurl_w8a8.so")
+
+QT = {"int8": 0, "fp8": 1}
+OUT = {"bf16": 0, "raw": 1}
+STATUS = {
+    0: "QR_OK", -1: "QR_ERR_INVALID_ARG", -2: "QR_ERR_UNSUPPORTED", -3: "QR_ERR_WORKSPACE",
+    -4: "QR_ERR_HIP", -5: "QR_ERR_NO_DEVICE",
+}
+# Every function include/qurl_w8a8.h declares.
+EXPORTS = [
+    "qr_quantize_weights_uaq", "qr_quantize_act_per_token", "qr_w8a8_gemm", "qr_linear_fused",
+    "qr_workspace_size", "qr_gemm_plan", "qr_tile_name", "qr_num_tiles", "qr_set_plan_override",
+    "qr_last_error", "qr_version",
+]
+
+
+class QRError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+_i64, _f32, _vp, _int, _sz = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_SIGS = {
+    "qr_quantize_weights_uaq": (_int, [_vp, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "qr_quantize_act_per_token": (_int, [_vp, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp]),
+    "qr_w8a8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _sz, _vp]),
+    "qr_linear_fused": (_int, [_vp, _i64, _f32, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _sz, _vp]),
+    "qr_workspace_size": (_sz, [ctypes.c_char_p, _i64, _i64, _i64, _int]),
+    "qr_gemm_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
+    "qr_tile_name": (ctypes.c_char_p, [_int]),
+    "qr_num_tiles": (_int, []),
+    "qr_set_plan_override": (_int, [_int, _int]),
+    "qr_last_error": (ctypes.c_char_p, []),
+    "qr_version": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """Load (once) and return the shared library; raise if it is not built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is not built: run `python -m w8a8_gemm_rl_amd.build`")
+                L = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in _SIGS.items():
+                    f = getattr(L, name)
+                    f.restype = res
+                    f.argtypes = args
+                _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        msg = lib().qr_last_error().decode(errors="replace")
+        raise QRError(fn, status, msg)
+
+
+def _qt(qt):
+    if qt not in QT:
+        raise ValueError(f"qt must be one of {list(QT)}, got {qt!r}")
+    return QT[qt]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on a HIP device")
+
+
+def _rows(t, name):
+    """Leading dimension of a 2-D tensor whose rows are contiguous."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+    return t.stride(0)
+
+
+def code_dtype(qt):
+    return torch.int8 if qt == "int8" else torch.float8_e4m3fn
+
+
+# ----------------------------------------------------------------------------
+# Workspace: one zero-initialised buffer per device, grown on demand. The
+# library leaves it in a reusable state after every call.
+# ----------------------------------------------------------------------------
+_ws = {}
+
+
+def workspace(nbytes, device):
+    dev = torch.device(device)
+    key = dev.index if dev.index is not None else torch.cuda.current_device()
+    buf = _ws.get(key)
+    if nbytes == 0:
+        return None, 0
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _ws[key] = buf
+    return buf, buf.numel()
+
+
+# ----------------------------------------------------------------------------
+# Entry points
+# ----------------------------------------------------------------------------
+
+def version():
+    return lib().qr_version().decode()
+
+
+def num_tiles():
+    return lib().qr_num_tiles()
+
+
+def tile_name(i):
+    r = lib().qr_tile_name(i)
+    return None if r is None else r.decode()
+
+
+def set_plan_override(tile=-1, splitk=0):
+    _check("qr_set_plan_override", lib().qr_set_plan_override(tile, splitk))
+
+
+def gemm_plan(M, N, K, qt):
+    t, s = ctypes.c_int(), ctypes.c_int()
+    _check("qr_gemm_plan", lib().qr_gemm_plan(M, N, K, _qt(qt), ctypes.byref(t), ctypes.byref(s)))
+    return t.value, s.value
+
+
+def workspace_size(fn, M, N, K, qt):
+    r = lib().qr_workspace_size(fn.encode(), M, N, K, _qt(qt))
+    if r == ctypes.c_size_t(-1).value:
+        raise QRError("qr_workspace_size", -1, lib().qr_last_error().decode())
+    return r
+
+
+def quantize_weights_uaq(W, s, qt, Wq=None, scale_w=None, W_scaled=None, gamma=None, beta=None):
+    """W [N, K] fp32 (rows contiguous) -> (Wq [N, K], scale_w [N]) on W's device."""
+    _need_cuda(W, Wq, scale_w, W_scaled, gamma, beta)
+    if W.dtype != torch.float32:
+        raise ValueError("W must be float32")
+    N, K = W.shape
+    ldw = _rows(W, "W")
+    if Wq is None:
+        Wq = torch.empty((N, K), dtype=code_dtype(qt), device=W.device)
+    if scale_w is None:
+        scale_w = torch.empty(N, dtype=torch.float32, device=W.device)
+    if W_scaled is not None and (W_scaled.shape != W.shape or _rows(W_scaled, "W_scaled") != ldw):
+        raise ValueError("W_scaled must have W's shape and row stride")
+    with torch.cuda.device(W.device):
+        st = lib().qr_quantize_weights_uaq(_ptr(W), N, K, ldw, float(s), _qt(qt), _ptr(Wq),
+                                           _ptr(scale_w), _ptr(W_scaled), _ptr(gamma), _ptr(beta),
+                                           _stream(W.device))
+    _check("qr_quantize_weights_uaq", st)
+    return Wq, scale_w
+
+
+def quantize_act_per_token(X, act_mult, qt, Xq=None, scale_x=None):
+    """X [M, K] bf16 (rows contiguous, any row stride) -> (Xq [M, K], scale_x [M])."""
+    _need_cuda(X, Xq, scale_x)
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bfloat16")
+    M, K = X.shape
+    ldx = _rows(X, "X")
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=code_dtype(qt), device=X.device)
+    if scale_x is None:
+        scale_x = torch.empty(M, dtype=torch.float32, device=X.device)
+    with torch.cuda.device(X.device):
+        st = lib().qr_quantize_act_per_token(_ptr(X), M, K, ldx, float(act_mult), _qt(qt), _ptr(Xq),
+                                             _ptr(scale_x), _stream(X.device))
+    _check("qr_quantize_act_per_token", st)
+    return Xq, scale_x
+
+
+def w8a8_gemm(Xq, scale_x, Wq, scale_w, qt, out="bf16", Y=None, ws=None):
+    """Y = dequant(Xq @ Wq^T): bf16 [M, N], or raw int32 / fp32 accumulators."""
+    _need_cuda(Xq, scale_x, Wq, scale_w, Y)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K:
+        raise ValueError("Xq and Wq disagree on K")
+    if Y is None:
+        dt = torch.bfloat16 if out == "bf16" else (torch.int32 if qt == "int8" else torch.float32)
+        Y = torch.empty((M, N), dtype=dt, device=Xq.device)
+    ldy = _rows(Y, "Y")
+    need = workspace_size("qr_w8a8_gemm", M, N, K, qt)
+    if ws is None:
+        ws, wsb = workspace(need, Xq.device)
+    else:
+        wsb = ws.numel() * ws.element_size()
+    with torch.cuda.device(Xq.device):
+        st = lib().qr_w8a8_gemm(_ptr(Xq), _ptr(scale_x), _ptr(Wq), _ptr(scale_w), M, N, K, _qt(qt),
+                                OUT[out], _ptr(Y), ldy, _ptr(ws), wsb, _stream(Xq.device))
+    _check("qr_w8a8_gemm", st)
+    return Y
+
+
+def linear_fused(X, act_mult, Wq, scale_w, qt, Y=None, ws=None):
+    """One rollout linear: per-token quantization of bf16 X, W8A8 product, bf16 Y."""
+    _need_cuda(X, Wq, scale_w, Y)
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bfloat16")
+    M, K = X.shape
+    N = Wq.shape[0]
+    ldx = _rows(X, "X")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    ldy = _rows(Y, "Y")
+    need = workspace_size("qr_linear_fused", M, N, K, qt)
+    if ws is None:
+        ws, wsb = workspace(need, X.device)
+    else:
+        wsb = ws.numel() * ws.element_size()
+    with torch.cuda.device(X.device):
+        st = lib().qr_linear_fused(_ptr(X), ldx, float(act_mult), _ptr(Wq), _ptr(scale_w), M, N, K,
+                                   _qt(qt), _ptr(Y), ldy, _ptr(ws), wsb, _stream(X.device))
+    _check("qr_linear_fused", st)
+    return Y

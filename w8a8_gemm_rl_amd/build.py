@@ -1,0 +1,71 @@
+"""Build libqurl_w8a8.so for gfx950 in-tree with hipcc.
+
+Usage: python -m w8a8_gemm_rl_amd.build   (or __graft_entry__.build()).
+
+Each HIP source is compiled to an object in ``_build/`` (in parallel), then the
+objects are linked into ``w8a8_gemm_rl_amd/libqurl_w8a8.so``. The library is
+rebuilt from scratch on every call. Flags: correctly rounded fp32 division and
+IEEE denormals are hipcc's defaults and must stay so (the quantized codes
+depend on them); packed-fp32 instruction selection is switched off.
+"""
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libqurl_w8a8.so")
+SOURCES = ["quant_kernels.hip", "gemm_kernels.hip", "qr_api.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+CFLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Wno-unused-function",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+    "-I", CSRC,
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return out
+
+
+def build(verbose=True, jobs=None):
+    os.makedirs(BUILD, exist_ok=True)
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+
+    def compile_one(i):
+        src = os.path.join(CSRC, SOURCES[i])
+        return _run([HIPCC, *CFLAGS, "-c", src, "-o", objs[i]])
+
+    jobs = jobs or min(len(SOURCES), 8)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        outs = list(ex.map(compile_one, range(len(SOURCES))))
+    tmp = LIB + ".tmp"
+    outs.append(_run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
+    os.replace(tmp, LIB)
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

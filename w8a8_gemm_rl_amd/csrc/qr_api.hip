@@ -1,0 +1,308 @@
+// C ABI of the W8A8 linear (declared and documented in include/qurl_w8a8.h).
+//
+// Every entry point validates its arguments on the host first and returns an
+// error before anything is enqueued; then it enqueues its kernels on the
+// caller's stream and returns without synchronizing.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "qr_internal.h"
+#include "qurl_w8a8.h"
+
+namespace {
+
+thread_local std::string g_err;
+int g_force_tile = -1;
+int g_force_splitk = 0;
+
+constexpr int64_t kMaxKInt8 = 133144;  // K * 127^2 < 2^31
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int kCUs = 256;  // MI355X compute units: the plan targets this chip
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return QR_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  const int code =
+      (e == hipErrorNoDevice || e == hipErrorInvalidDevice) ? QR_ERR_NO_DEVICE : QR_ERR_HIP;
+  return fail(code, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool valid_qt(int qt) { return qt == QR_INT8 || qt == QR_FP8_E4M3FN; }
+
+// Shape checks common to every call. Returns QR_OK or an error (g_err set).
+int check_shape(const char* fn, int64_t M, int64_t N, int64_t K, int qt) {
+  if (!valid_qt(qt)) return fail(QR_ERR_INVALID_ARG, "%s: unknown qtype %d", fn, qt);
+  if (M < 0 || N < 0 || K < 0)
+    return fail(QR_ERR_INVALID_ARG, "%s: negative size (M=%lld N=%lld K=%lld)", fn, (long long)M,
+                (long long)N, (long long)K);
+  if (M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return fail(QR_ERR_UNSUPPORTED, "%s: size >= 2^31", fn);
+  if (K % 16 != 0) return fail(QR_ERR_UNSUPPORTED, "%s: K=%lld is not a multiple of 16", fn, (long long)K);
+  if (qt == QR_INT8 && K > kMaxKInt8)
+    return fail(QR_ERR_UNSUPPORTED, "%s: K=%lld > %lld would overflow the int32 accumulator", fn,
+                (long long)K, (long long)kMaxKInt8);
+  return QR_OK;
+}
+
+}  // namespace
+
+namespace qr {
+
+GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int force_splitk) {
+  (void)qt;
+  GemmPlan p{};
+  int tile;
+  if (force_tile >= 0) {
+    tile = force_tile;
+  } else if (M <= 16) {
+    tile = 0;
+  } else if (M <= 32) {
+    tile = 1;
+  } else if (M <= 64) {
+    tile = 2;
+  } else if (M <= 128) {
+    tile = 3;
+  } else if (M <= 256) {
+    tile = 4;
+  } else {
+    tile = 5;
+  }
+  const TileDesc& d = tile_desc(tile);
+  p.tile = tile;
+  p.tiles_n = (N + d.BN - 1) / d.BN;
+  p.tiles_m = (M + d.BM - 1) / d.BM;
+  p.nks = (K + d.BK - 1) / d.BK;
+  const int64_t tiles = p.tiles_n * p.tiles_m;
+  int64_t s = 1;
+  if (force_splitk > 0) {
+    s = force_splitk;
+  } else if (tiles > 0 && tiles < kCUs) {
+    // Split K until about two blocks per CU, keeping >= 4 K steps per split.
+    s = (2 * kCUs + tiles - 1) / tiles;
+    const int64_t smax = p.nks / 4;
+    if (s > smax) s = smax;
+    if (s > 32) s = 32;
+    if (s < 1) s = 1;
+  }
+  if (p.nks > 0 && s > p.nks) s = p.nks;
+  if (tiles > kMaxSplitTiles) s = 1;  // one counter per tile must fit the counter region
+  if (s < 1) s = 1;
+  p.splitk = (int)s;
+  if (p.splitk > 1 && tiles > 0)
+    p.part_bytes = align256((size_t)p.splitk * (size_t)tiles * d.BN * d.BM * 4);
+  return p;
+}
+
+}  // namespace qr
+
+extern "C" {
+
+const char* qr_last_error(void) { return g_err.c_str(); }
+
+const char* qr_version(void) { return "qurl_w8a8 0.1.0 (gfx950)"; }
+
+int qr_num_tiles(void) { return qr::num_tiles(); }
+
+const char* qr_tile_name(int tile) {
+  if (tile < 0 || tile >= qr::num_tiles()) return nullptr;
+  return qr::tile_desc(tile).name;
+}
+
+int qr_set_plan_override(int tile, int splitk) {
+  if (tile >= qr::num_tiles() || splitk < 0 || splitk > 1024)
+    return fail(QR_ERR_INVALID_ARG, "qr_set_plan_override: tile %d / splitk %d out of range", tile,
+                splitk);
+  g_force_tile = tile < 0 ? -1 : tile;
+  g_force_splitk = tile < 0 ? 0 : splitk;
+  return ok();
+}
+
+int qr_gemm_plan(int64_t M, int64_t N, int64_t K, int qt, int* tile, int* splitk) {
+  int st = check_shape("qr_gemm_plan", M, N, K, qt);
+  if (st != QR_OK) return st;
+  if (!tile || !splitk) return fail(QR_ERR_INVALID_ARG, "qr_gemm_plan: null output pointer");
+  const qr::GemmPlan p = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk);
+  *tile = p.tile;
+  *splitk = p.splitk;
+  return ok();
+}
+
+size_t qr_workspace_size(const char* fn, int64_t M, int64_t N, int64_t K, int qt) {
+  if (!fn) return (size_t)-1;
+  if (check_shape("qr_workspace_size", M, N, K, qt) != QR_OK) return (size_t)-1;
+  const qr::GemmPlan p = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk);
+  const size_t gemm = (M == 0 || N == 0) ? 0 : p.ws_bytes();
+  if (std::strcmp(fn, "qr_w8a8_gemm") == 0) return gemm;
+  if (std::strcmp(fn, "qr_linear_fused") == 0) {
+    if (M == 0 || N == 0) return 0;
+    return qr::kCounterBytes + p.part_bytes + align256((size_t)M * (size_t)K) +
+           align256((size_t)M * 4);
+  }
+  return (size_t)-1;
+}
+
+int qr_quantize_weights_uaq(const float* W, int64_t N, int64_t K, int64_t ldw, float s, int qt,
+                            void* Wq, float* scale_w, float* W_scaled, float* gamma, float* beta,
+                            void* stream) {
+  const char* fn = "qr_quantize_weights_uaq";
+  int st = check_shape(fn, 0, N, K, qt);
+  if (st != QR_OK) return st;
+  if (!std::isfinite(s) || !(s > 0.0f)) return fail(QR_ERR_INVALID_ARG, "%s: s must be finite and > 0", fn);
+  if (ldw < K) return fail(QR_ERR_INVALID_ARG, "%s: ldw=%lld < K=%lld", fn, (long long)ldw, (long long)K);
+  if (N > 0 && K > 0 && (!W || !Wq)) return fail(QR_ERR_INVALID_ARG, "%s: null W or Wq", fn);
+  if (N > 0 && !scale_w) return fail(QR_ERR_INVALID_ARG, "%s: null scale_w", fn);
+  if (ldw % 4 != 0) return fail(QR_ERR_UNSUPPORTED, "%s: ldw must be a multiple of 4", fn);
+  if (!aligned(W, 16) || !aligned(Wq, 16) || !aligned(W_scaled, 16) || !aligned(scale_w, 4) ||
+      !aligned(gamma, 4) || !aligned(beta, 4))
+    return fail(QR_ERR_UNSUPPORTED, "%s: misaligned pointer (16 bytes for W, Wq, W_scaled)", fn);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  if (gamma || beta) {
+    st = hip_status(qr::launch_fold_norm(gamma, beta, K, s, hs), fn);
+    if (st != QR_OK) return st;
+  }
+  if (N == 0) return ok();
+  return hip_status(qr::launch_weight_quant(W, N, K, ldw, s, qt, Wq, scale_w, W_scaled, hs), fn);
+}
+
+int qr_quantize_act_per_token(const void* X, int64_t M, int64_t K, int64_t ldx, float act_mult,
+                              int qt, void* Xq, float* scale_x, void* stream) {
+  const char* fn = "qr_quantize_act_per_token";
+  int st = check_shape(fn, M, 0, K, qt);
+  if (st != QR_OK) return st;
+  if (!std::isfinite(act_mult) || !(act_mult > 0.0f))
+    return fail(QR_ERR_INVALID_ARG, "%s: act_mult must be finite and > 0", fn);
+  if (ldx < K) return fail(QR_ERR_INVALID_ARG, "%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
+  if (M > 0 && K > 0 && (!X || !Xq)) return fail(QR_ERR_INVALID_ARG, "%s: null X or Xq", fn);
+  if (M > 0 && !scale_x) return fail(QR_ERR_INVALID_ARG, "%s: null scale_x", fn);
+  if (ldx % 8 != 0) return fail(QR_ERR_UNSUPPORTED, "%s: ldx must be a multiple of 8", fn);
+  if (!aligned(X, 16) || !aligned(Xq, 16) || !aligned(scale_x, 4))
+    return fail(QR_ERR_UNSUPPORTED, "%s: misaligned pointer (16 bytes for X, Xq)", fn);
+  if (M == 0) return ok();
+  (void)hipGetLastError();
+  return hip_status(qr::launch_act_quant(X, M, K, ldx, act_mult, qt, Xq, scale_x,
+                                         static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+namespace {
+
+int check_gemm_io(const char* fn, int64_t M, int64_t N, int64_t K, int out, bool need_sx,
+                  const void* sx, const void* Wq, const void* sw, void* Y, int64_t ldy) {
+  if (out != QR_OUT_BF16 && out != QR_OUT_RAW)
+    return fail(QR_ERR_INVALID_ARG, "%s: unknown output mode %d", fn, out);
+  if (ldy < N) return fail(QR_ERR_INVALID_ARG, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if (M > 0 && N > 0) {
+    if (!Y) return fail(QR_ERR_INVALID_ARG, "%s: null Y", fn);
+    if (K > 0 && !Wq) return fail(QR_ERR_INVALID_ARG, "%s: null Wq", fn);
+    if (out == QR_OUT_BF16 && ((need_sx && !sx) || !sw))
+      return fail(QR_ERR_INVALID_ARG, "%s: null scales", fn);
+  }
+  if (ldy % (out == QR_OUT_BF16 ? 8 : 4) != 0)
+    return fail(QR_ERR_UNSUPPORTED, "%s: ldy must be a multiple of %d", fn, out == QR_OUT_BF16 ? 8 : 4);
+  if (!aligned(Wq, 16) || !aligned(Y, 16) || !aligned(sx, 4) || !aligned(sw, 16))
+    return fail(QR_ERR_UNSUPPORTED, "%s: misaligned pointer (16 bytes for Wq, Y, scale_w)", fn);
+  return QR_OK;
+}
+
+int check_ws(const char* fn, void* ws, size_t bytes, size_t need) {
+  if (need == 0) return QR_OK;
+  if (!ws) return fail(QR_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got NULL", fn, need);
+  if (!aligned(ws, 256)) return fail(QR_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  if (bytes < need)
+    return fail(QR_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", fn, need, bytes);
+  return QR_OK;
+}
+
+int run_gemm(const char* fn, const qr::GemmPlan& plan, const void* Xq, const float* sx,
+             const void* Wq, const float* sw, int64_t M, int64_t N, int64_t K, int qt, int out,
+             void* Y, int64_t ldy, void* gemm_ws, hipStream_t hs) {
+  qr::GemmArgs a;
+  a.Xq = static_cast<const uint8_t*>(Xq);
+  a.sx = sx;
+  a.Wq = static_cast<const uint8_t*>(Wq);
+  a.sw = sw;
+  a.M = M; a.N = N; a.K = K;
+  a.Y = Y; a.ldy = ldy;
+  a.out_raw = out == QR_OUT_RAW;
+  // gemm_ws is the start of the workspace: counters first, then partials.
+  a.counters = plan.splitk > 1 ? static_cast<int*>(gemm_ws) : nullptr;
+  a.part = plan.splitk > 1 ? static_cast<char*>(gemm_ws) + qr::kCounterBytes : nullptr;
+  return hip_status(qr::launch_gemm(plan, qt, a, hs), fn);
+}
+
+}  // namespace
+
+int qr_w8a8_gemm(const void* Xq, const float* scale_x, const void* Wq, const float* scale_w,
+                 int64_t M, int64_t N, int64_t K, int qt, int out, void* Y, int64_t ldy,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "qr_w8a8_gemm";
+  int st = check_shape(fn, M, N, K, qt);
+  if (st != QR_OK) return st;
+  st = check_gemm_io(fn, M, N, K, out, true, scale_x, Wq, scale_w, Y, ldy);
+  if (st != QR_OK) return st;
+  if (M > 0 && N > 0 && K > 0 && !Xq) return fail(QR_ERR_INVALID_ARG, "%s: null Xq", fn);
+  if (!aligned(Xq, 16)) return fail(QR_ERR_UNSUPPORTED, "%s: misaligned Xq", fn);
+  if (M == 0 || N == 0) return ok();
+  const qr::GemmPlan plan = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk);
+  st = check_ws(fn, workspace, workspace_bytes, plan.ws_bytes());
+  if (st != QR_OK) return st;
+  (void)hipGetLastError();
+  return run_gemm(fn, plan, Xq, scale_x, Wq, scale_w, M, N, K, qt, out, Y, ldy, workspace,
+                  static_cast<hipStream_t>(stream));
+}
+
+int qr_linear_fused(const void* X, int64_t ldx, float act_mult, const void* Wq, const float* scale_w,
+                    int64_t M, int64_t N, int64_t K, int qt, void* Y, int64_t ldy, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const char* fn = "qr_linear_fused";
+  int st = check_shape(fn, M, N, K, qt);
+  if (st != QR_OK) return st;
+  if (!std::isfinite(act_mult) || !(act_mult > 0.0f))
+    return fail(QR_ERR_INVALID_ARG, "%s: act_mult must be finite and > 0", fn);
+  if (ldx < K) return fail(QR_ERR_INVALID_ARG, "%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
+  st = check_gemm_io(fn, M, N, K, QR_OUT_BF16, false, nullptr, Wq, scale_w, Y, ldy);
+  if (st != QR_OK) return st;
+  if (M > 0 && N > 0 && K > 0 && !X) return fail(QR_ERR_INVALID_ARG, "%s: null X", fn);
+  if (ldx % 8 != 0) return fail(QR_ERR_UNSUPPORTED, "%s: ldx must be a multiple of 8", fn);
+  if (!aligned(X, 16)) return fail(QR_ERR_UNSUPPORTED, "%s: misaligned X", fn);
+  if (M == 0 || N == 0) return ok();
+  const qr::GemmPlan plan = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk);
+  const size_t xq_bytes = align256((size_t)M * (size_t)K);
+  const size_t sx_bytes = align256((size_t)M * 4);
+  const size_t head = qr::kCounterBytes + plan.part_bytes;
+  st = check_ws(fn, workspace, workspace_bytes, head + xq_bytes + sx_bytes);
+  if (st != QR_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  void* gws = ws;
+  void* xq = ws + head;
+  float* sx = reinterpret_cast<float*>(ws + head + xq_bytes);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  st = hip_status(qr::launch_act_quant(X, M, K, ldx, act_mult, qt, xq, sx, hs), fn);
+  if (st != QR_OK) return st;
+  return run_gemm(fn, plan, xq, sx, Wq, scale_w, M, N, K, qt, QR_OUT_BF16, Y, ldy, gws, hs);
+}
+
+}  // extern "C"

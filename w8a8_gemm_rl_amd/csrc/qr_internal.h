@@ -1,0 +1,67 @@
+// Internal interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qr {
+
+hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int64_t ldx, float act_mult,
+                            int qt, void* Xq, float* scale_x, hipStream_t st);
+hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, int64_t ldw, float s, int qt,
+                               void* Wq, float* scale_w, float* Wsc, hipStream_t st);
+hipError_t launch_fold_norm(float* gamma, float* beta, int64_t K, float s, hipStream_t st);
+
+// Static description of one GEMM tile configuration.
+struct TileDesc {
+  const char* name;
+  int T;   // MFMA tile edge (16 or 32)
+  int BN;  // macro-tile extent along N (weight rows)
+  int BM;  // macro-tile extent along M (tokens)
+  int BK;  // bytes of K per pipeline stage
+  int NT;  // threads per block
+};
+
+int num_tiles();
+const TileDesc& tile_desc(int tile);
+
+// Workspace layout shared by every call that takes one:
+//   [0, kCounterBytes)   split-K arrival counters, one int per macro tile.
+//                        Zero between calls: the caller zeroes the workspace
+//                        once, and the block that consumes a counter resets
+//                        it. Nothing else is ever stored here, so any
+//                        sequence of calls may share one workspace.
+//   [kCounterBytes, ...) split-K partial sums, then (qr_linear_fused) the
+//                        activation codes and scales.
+constexpr size_t kCounterBytes = 16384;
+constexpr int64_t kMaxSplitTiles = (int64_t)(kCounterBytes / 4);
+
+// A launch plan for one product shape.
+struct GemmPlan {
+  int tile;
+  int splitk;
+  int64_t tiles_n, tiles_m, nks;
+  size_t part_bytes;  // split-K partial sums (0 without split)
+  // Workspace qr_w8a8_gemm needs: none without split-K.
+  size_t ws_bytes() const { return splitk > 1 ? kCounterBytes + part_bytes : 0; }
+};
+
+GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int force_splitk);
+
+struct GemmArgs {
+  const uint8_t* Xq;
+  const float* sx;
+  const uint8_t* Wq;
+  const float* sw;
+  int64_t M, N, K;
+  void* Y;
+  int64_t ldy;
+  int out_raw;
+  void* part;
+  int* counters;
+};
+
+hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStream_t st);
+
+}  // namespace qr

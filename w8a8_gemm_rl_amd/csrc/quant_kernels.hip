@@ -1,0 +1,244 @@
+// Absmax row quantizers for gfx950: per-token activations (bf16 in) and
+// per-output-channel weights after the UAQ division (fp32 in).
+//
+// Both are HBM-bound streaming kernels: each row is read once with 16-byte
+// loads (kept in registers when it fits), its absmax is reduced across the
+// wavefront with lane shuffles (and across the four waves of a 256-thread
+// block through LDS when one block owns a row), and the codes are written
+// with coalesced 4- or 8-byte stores. Rows longer than the register budget
+// are read twice (the second read is served by L2).
+//
+// Quantization: QuRL paper notes, "Loss / training strategy" (channel-wise
+// weights, token-wise activations, INT8 or FP8); UAQ division by s:
+// "Method > Key designs > UAQ".
+#include "qr_device.h"
+#include "qr_internal.h"
+
+namespace qr {
+namespace {
+
+__device__ __forceinline__ float absmax8_bf16(const uint4 v) {
+  float m = fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x)));
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))));
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
+  return m;
+}
+
+template <int QT>
+__device__ __forceinline__ uint2 codes8_bf16(const uint4 v, float t) {
+  uint2 o;
+  o.x = quant_code<QT>(bf16_lo(v.x), t) | (quant_code<QT>(bf16_hi(v.x), t) << 8) |
+        (quant_code<QT>(bf16_lo(v.y), t) << 16) | (quant_code<QT>(bf16_hi(v.y), t) << 24);
+  o.y = quant_code<QT>(bf16_lo(v.z), t) | (quant_code<QT>(bf16_hi(v.z), t) << 8) |
+        (quant_code<QT>(bf16_lo(v.w), t) << 16) | (quant_code<QT>(bf16_hi(v.w), t) << 24);
+  return o;
+}
+
+// Block-wide max when one 256-thread block owns a row (TPR == 256), or a
+// wave-wide max when each wave owns a row (TPR == 64).
+template <int TPR>
+__device__ __forceinline__ float row_max(float v, float* red) {
+  v = wave_max(v);
+  if constexpr (TPR == 256) {
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  }
+  return v;
+}
+
+// One row per TPR threads; 256 threads per block. MAXC 16-byte chunks per
+// thread are kept in registers (row length <= MAXC * TPR * 8 elements).
+template <int QT, int TPR, int MAXC>
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ X, int64_t M,
+                                                        int64_t K, int64_t ldx, float act_mult,
+                                                        uint8_t* __restrict__ Xq,
+                                                        float* __restrict__ scale_x) {
+  constexpr int RPB = 256 / TPR;
+  __shared__ float red[4];
+  const int lt = threadIdx.x % TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const bool valid = row < M;
+  const int64_t nch = K >> 3;
+  const uint4* xr = reinterpret_cast<const uint4*>(X + (valid ? row : 0) * ldx);
+  const bool fits = nch <= (int64_t)MAXC * TPR;
+
+  uint4 r[MAXC];
+  float amax = 0.0f;
+  if (valid) {
+    if (fits) {
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int64_t c = lt + (int64_t)i * TPR;
+        if (c < nch) {
+          r[i] = xr[c];
+          amax = fmaxf(amax, absmax8_bf16(r[i]));
+        }
+      }
+    } else {
+      for (int64_t c = lt; c < nch; c += TPR) amax = fmaxf(amax, absmax8_bf16(xr[c]));
+    }
+  }
+  amax = row_max<TPR>(amax, red);
+  if (!valid) return;
+
+  const float t = amax / qmax<QT>();
+  if (lt == 0) scale_x[row] = t * act_mult;
+  uint2* qr_ = reinterpret_cast<uint2*>(Xq + row * K);
+  if (t == 0.0f) {
+    for (int64_t c = lt; c < nch; c += TPR) qr_[c] = make_uint2(0u, 0u);
+    return;
+  }
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int64_t c = lt + (int64_t)i * TPR;
+      if (c < nch) qr_[c] = codes8_bf16<QT>(r[i], t);
+    }
+  } else {
+    for (int64_t c = lt; c < nch; c += TPR) qr_[c] = codes8_bf16<QT>(xr[c], t);
+  }
+}
+
+// Weights: W' = fl32(W / s) per element, then per-row absmax quantization of
+// W'. Optionally stores W' (may alias W: every element is read by the thread
+// that overwrites it, before it does).
+template <int QT, int TPR, int MAXC>
+__global__ __launch_bounds__(256) void weight_quant_kernel(const float* W, int64_t N, int64_t K,
+                                                           int64_t ldw, float s,
+                                                           uint8_t* __restrict__ Wq,
+                                                           float* __restrict__ scale_w,
+                                                           float* Wsc) {
+  constexpr int RPB = 256 / TPR;
+  __shared__ float red[4];
+  const int lt = threadIdx.x % TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const bool valid = row < N;
+  const int64_t nch = K >> 2;
+  const float4* wr = reinterpret_cast<const float4*>(W + (valid ? row : 0) * ldw);
+  const bool fits = nch <= (int64_t)MAXC * TPR;
+
+  float4 r[MAXC];
+  float amax = 0.0f;
+  if (valid) {
+    if (fits) {
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int64_t c = lt + (int64_t)i * TPR;
+        if (c < nch) {
+          float4 v = wr[c];
+          v.x = v.x / s; v.y = v.y / s; v.z = v.z / s; v.w = v.w / s;
+          r[i] = v;
+          amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+      }
+    } else {
+      for (int64_t c = lt; c < nch; c += TPR) {
+        const float4 v = wr[c];
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x / s), fabsf(v.y / s)),
+                                 fmaxf(fabsf(v.z / s), fabsf(v.w / s))));
+      }
+    }
+  }
+  amax = row_max<TPR>(amax, red);
+  if (!valid) return;
+
+  const float t = amax / qmax<QT>();
+  if (lt == 0) scale_w[row] = t;
+  uint32_t* qr_ = reinterpret_cast<uint32_t*>(Wq + row * K);
+  float4* sr = Wsc ? reinterpret_cast<float4*>(Wsc + row * ldw) : nullptr;
+  auto emit = [&](int64_t c, float4 v) {
+    if (sr) sr[c] = v;
+    uint32_t q = 0u;
+    if (t != 0.0f)
+      q = quant_code<QT>(v.x, t) | (quant_code<QT>(v.y, t) << 8) |
+          (quant_code<QT>(v.z, t) << 16) | (quant_code<QT>(v.w, t) << 24);
+    qr_[c] = q;
+  };
+  if (fits) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int64_t c = lt + (int64_t)i * TPR;
+      if (c < nch) emit(c, r[i]);
+    }
+  } else {
+    for (int64_t c = lt; c < nch; c += TPR) {
+      float4 v = wr[c];
+      v.x = v.x / s; v.y = v.y / s; v.z = v.z / s; v.w = v.w / s;
+      emit(c, v);
+    }
+  }
+}
+
+// gamma' = fl32(gamma * s), beta' = fl32(beta * s): the activation-side s of
+// UAQ folded into the norm that produces the linear's input.
+__global__ __launch_bounds__(256) void fold_norm_kernel(float* gamma, float* beta, int64_t K,
+                                                         float s) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= K) return;
+  if (gamma) gamma[i] = gamma[i] * s;
+  if (beta) beta[i] = beta[i] * s;
+}
+
+inline unsigned grid_for(int64_t rows, int rpb) { return (unsigned)((rows + rpb - 1) / rpb); }
+
+}  // namespace
+
+hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int64_t ldx, float act_mult,
+                            int qt, void* Xq, float* scale_x, hipStream_t st) {
+  if (M == 0) return hipSuccess;
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  uint8_t* q = static_cast<uint8_t*>(Xq);
+  if (K <= 2048) {
+    const unsigned g = grid_for(M, 4);
+    if (qt == kQInt8)
+      hipLaunchKernelGGL((act_quant_kernel<kQInt8, 64, 4>), dim3(g), dim3(256), 0, st, x, M, K,
+                         ldx, act_mult, q, scale_x);
+    else
+      hipLaunchKernelGGL((act_quant_kernel<kQFp8, 64, 4>), dim3(g), dim3(256), 0, st, x, M, K,
+                         ldx, act_mult, q, scale_x);
+  } else {
+    const unsigned g = grid_for(M, 1);
+    if (qt == kQInt8)
+      hipLaunchKernelGGL((act_quant_kernel<kQInt8, 256, 16>), dim3(g), dim3(256), 0, st, x, M, K,
+                         ldx, act_mult, q, scale_x);
+    else
+      hipLaunchKernelGGL((act_quant_kernel<kQFp8, 256, 16>), dim3(g), dim3(256), 0, st, x, M, K,
+                         ldx, act_mult, q, scale_x);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, int64_t ldw, float s, int qt,
+                               void* Wq, float* scale_w, float* Wsc, hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  uint8_t* q = static_cast<uint8_t*>(Wq);
+  if (K <= 1024) {
+    const unsigned g = grid_for(N, 4);
+    if (qt == kQInt8)
+      hipLaunchKernelGGL((weight_quant_kernel<kQInt8, 64, 4>), dim3(g), dim3(256), 0, st, W, N,
+                         K, ldw, s, q, scale_w, Wsc);
+    else
+      hipLaunchKernelGGL((weight_quant_kernel<kQFp8, 64, 4>), dim3(g), dim3(256), 0, st, W, N, K,
+                         ldw, s, q, scale_w, Wsc);
+  } else {
+    const unsigned g = grid_for(N, 1);
+    if (qt == kQInt8)
+      hipLaunchKernelGGL((weight_quant_kernel<kQInt8, 256, 32>), dim3(g), dim3(256), 0, st, W, N,
+                         K, ldw, s, q, scale_w, Wsc);
+    else
+      hipLaunchKernelGGL((weight_quant_kernel<kQFp8, 256, 32>), dim3(g), dim3(256), 0, st, W, N,
+                         K, ldw, s, q, scale_w, Wsc);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fold_norm(float* gamma, float* beta, int64_t K, float s, hipStream_t st) {
+  if (K == 0 || (!gamma && !beta)) return hipSuccess;
+  hipLaunchKernelGGL(fold_norm_kernel, dim3(grid_for(K, 256)), dim3(256), 0, st, gamma, beta, K, s);
+  return hipGetLastError();
+}
+
+}  // namespace qr

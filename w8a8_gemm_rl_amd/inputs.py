@@ -64,6 +64,15 @@ CHAIN_32B = [
     dict(name="down", src="up", cols=None),
 ]
 
+# 32B prefill: the same chain shape as the 7B layer with 32B linears (QKV fused).
+CHAIN_32B_PREFILL = [
+    dict(name="qkv", src="x0", cols=None),
+    dict(name="o", src="qkv", cols=(0, 5120)),
+    dict(name="gate", src="o", cols=None),
+    dict(name="up", src="o", cols=None),
+    dict(name="down", src="up", cols=None),
+]
+
 DW_SIGMA = 1e-7  # update size, paper notes "Key designs > UAQ" (~1e-7)
 
 
