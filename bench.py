@@ -8,10 +8,13 @@ A "step" is one such layer pass over one batch; successive steps walk through
 distinct copies of the layer's weights (more bytes than the 256 MB Infinity
 Cache), like a decode pass walks a model's layers.
 
-The timed region is one replay of a HIP graph holding the K steps, between
-device synchronizations. Events recorded as graph nodes bracket the dominant
-GEMM of every step, which gives its average kernel duration for the roofline
-object. Inputs are seeded synthetic tensors generated on the device.
+The timed region is K steps between device synchronizations. Each step
+replays a HIP graph of the ops before the dominant GEMM, launches that GEMM
+directly between two stream events (its average duration feeds the roofline
+object), and replays a graph of the ops after it. Inputs are seeded synthetic
+tensors generated on the device. The roofline "traffic" (HBM bytes per
+launch) comes from the committed rocprofv3 counter summary in
+profiles/hbm_traffic.md and is null when the GEMM sources changed since.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -74,7 +77,6 @@ class Layer:
 
         self.B = B
         self.qt = qt
-        self.ops = []
         self.W = {}
         g = torch.Generator(device=dev)
         for i, L in enumerate(chain):
@@ -86,28 +88,126 @@ class Layer:
         self.x0, self.bufs, self.ws, self.s = x0, bufs, ws, s
         self.chain, self.M = chain, M
 
-    def run(self, dom=None, ev=None, per_linear=None):
-        """Enqueue one layer step. ev = (start, end) events around GEMM `dom`;
-        per_linear = {name: (start, end)} events around every GEMM."""
+    def ops(self):
+        """The step as a list of (kind, name, thunk): per-token quantizations
+        (one per distinct input) and GEMMs, in chain order."""
         B, bufs = self.B, self.bufs
-        done = {}
+        out, done = [], {}
         for L in self.chain:
-            src = self.x0 if L["src"] == "x0" else bufs["y_" + L["src"]]
             key = (L["src"], L["cols"])
-            if L["cols"] is not None:
-                src = src[:, L["cols"][0]:L["cols"][1]]
             if key not in done:
                 xq, sx = bufs["q_" + L["name"]]
-                B.quantize_act_per_token(src, self.s, self.qt, Xq=xq, scale_x=sx)
                 done[key] = (xq, sx)
+
+                def q(L=L, xq=xq, sx=sx):
+                    src = self.x0 if L["src"] == "x0" else bufs["y_" + L["src"]]
+                    if L["cols"] is not None:
+                        src = src[:, L["cols"][0]:L["cols"][1]]
+                    B.quantize_act_per_token(src, self.s, self.qt, Xq=xq, scale_x=sx)
+
+                out.append(("quant", L["name"], q))
             xq, sx = done[key]
             Wq, sw = self.W[L["name"]]
-            e = per_linear.get(L["name"]) if per_linear else (ev if L["name"] == dom else None)
+
+            def gm(L=L, xq=xq, sx=sx, Wq=Wq, sw=sw):
+                B.w8a8_gemm(xq, sx, Wq, sw, self.qt, out="bf16", Y=bufs["y_" + L["name"]], ws=self.ws)
+
+            out.append(("gemm", L["name"], gm))
+        return out
+
+    def run(self, per_linear=None):
+        """Enqueue one layer step; per_linear = {name: (start, end)} events around each GEMM."""
+        for kind, name, f in self.ops():
+            e = per_linear.get(name) if (per_linear and kind == "gemm") else None
             if e:
                 e[0].record()
-            B.w8a8_gemm(xq, sx, Wq, sw, self.qt, out="bf16", Y=bufs["y_" + L["name"]], ws=self.ws)
+            f()
             if e:
                 e[1].record()
+
+    def capture_split(self, dom):
+        """Graphs of the ops before and after GEMM `dom`, and `dom` itself as an
+        eager callable (so stream events can bracket exactly that kernel)."""
+        import torch
+
+        ops = self.ops()
+        k = next(i for i, (kind, n, _) in enumerate(ops) if kind == "gemm" and n == dom)
+        parts = [ops[:k], ops[k + 1:]]
+        graphs = []
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        for part in parts:
+            if not part:
+                graphs.append(None)
+                continue
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(st):
+                with torch.cuda.graph(g, stream=st):
+                    for _, _, f in part:
+                        f()
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs[0], ops[k][2], graphs[1]
+
+
+def gemm_source_sha256():
+    """Hash of the sources that define the GEMM kernels and their plans."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w8a8_gemm_rl_amd", "csrc")
+    for f in ("gemm_kernels.hip", "qr_api.hip", "qr_internal.h", "qr_device.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+
+
+def committed_traffic(key):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary, or None if there is none for `key` or the GEMM sources changed
+    since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha = gemm_source_sha256()
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 4 and cells[0] == key:
+                if cells[1] != sha[:16]:
+                    return None
+                return int(cells[2])
+    return None
+
+
+def summarize_rocprof(paths, grid):
+    """Print the figures used from rocprofv3 CSV outputs (kernel trace, or a
+    --pmc counter collection) for dispatches of the given grid size."""
+    import csv
+    import statistics
+
+    for path in paths:
+        rows = list(csv.DictReader(open(path)))
+        if rows and "Counter_Name" in rows[0]:
+            by = {}
+            for r in rows:
+                if int(r["Grid_Size"]) == grid and "gemm_kernel" in r["Kernel_Name"]:
+                    by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            for c, v in by.items():
+                print(f"{path}: {c} per dispatch (grid {grid}): mean {statistics.mean(v):.1f} KiB, "
+                      f"n={len(v)}")
+            if not by:
+                for r in rows:
+                    print(f"{path}: {r['Kernel_Name'][:50]} grid {r['Grid_Size']} "
+                          f"{r['Counter_Name']} {float(r['Counter_Value']):.1f}")
+        else:
+            ds = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in rows
+                  if int(r["Grid_Size_X"]) == grid and "gemm_kernel" in r["Kernel_Name"]]
+            if ds:
+                print(f"{path}: gemm dispatches of grid {grid}: n={len(ds)} mean {statistics.mean(ds):.2f} us "
+                      f"median {statistics.median(ds):.2f} us min {min(ds):.2f} us")
 
 
 def cpu_baseline(chain, shapes, M, qt, sigma, kind, s):
@@ -133,11 +233,16 @@ def cpu_baseline(chain, shapes, M, qt, sigma, kind, s):
         layers.append(dict(L, Wq=q["Wq"], scale_w=q["scale_w"], act_mult=s))
     K0 = shapes[chain[0]["name"]][1]
     x0 = I.activations(M, K0, seed=I.matrix_seed(9, 99), kind=kind)
-    log("cpu baseline: timing one oracle layer step ...")
+    log("cpu baseline: timing oracle layer steps (about 10 s) ...")
     t0 = time.perf_counter()
-    O.decode_chain(x0, layers, qt)
-    dt = time.perf_counter() - t0
-    return dt, threads
+    steps = 0
+    while True:
+        O.decode_chain(x0, layers, qt)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or steps >= 30:
+            break
+    return dt / steps, steps, threads
 
 
 def main():
@@ -149,7 +254,21 @@ def main():
     ap.add_argument("--m", type=int, default=None, help="override the token count M")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--summarize-rocprof", nargs="+", metavar="CSV",
+                    help="print the figures used from rocprofv3 CSV files (with --grid) and exit")
+    ap.add_argument("--grid", type=int, default=0, help="grid size (threads) of the dispatches to summarize")
+    ap.add_argument("--source-sha", action="store_true", help="print the GEMM source hash and exit")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times (for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
     args = ap.parse_args()
+
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.grid)
+        return
+    if args.source_sha:
+        print(gemm_source_sha256()[:16])
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -166,6 +285,15 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
+        return
     B.lib()
 
     wl = dict(WORKLOADS[args.workload])
@@ -224,28 +352,29 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True, external=True),
-            torch.cuda.Event(enable_timing=True, external=True)) for _ in range(K)]
-    mode = "eager" if args.eager else "hip_graph"
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    mode = "eager" if args.eager else "hip_graph_split"
     if not args.eager:
-        log(f"bench: capturing {K} steps into one HIP graph")
-        graph = torch.cuda.CUDAGraph()
-        st = torch.cuda.Stream()
-        st.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(st):
-            with torch.cuda.graph(graph, stream=st):
-                for i in range(K):
-                    layers[i % len(layers)].run(dom=dom, ev=evs[i])
-        torch.cuda.synchronize()
+        log("bench: capturing per-layer graphs (ops before / after the dominant GEMM)")
+        split = [L.capture_split(dom) for L in layers]
 
     log(f"bench: timing {K} steps ({mode})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if args.eager:
         for i in range(K):
-            layers[i % len(layers)].run(dom=dom, ev=evs[i])
+            layers[i % len(layers)].run(per_linear={dom: evs[i]})
     else:
-        graph.replay()
+        for i in range(K):
+            pre, mid, post = split[i % len(split)]
+            if pre is not None:
+                pre.replay()
+            evs[i][0].record()
+            mid()
+            evs[i][1].record()
+            if post is not None:
+                post.replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec_step = (t1 - t0) / K
@@ -272,6 +401,9 @@ def main():
                           tops=round(2 * M * N_ * K_ / us / 1e6, 1),
                           plan=list(B.gemm_plan(M, N_, K_, qt)))
 
+    dom_plan = B.gemm_plan(M, Nd, Kd, qt)
+    traffic_key = f"{args.workload}:{dom}:M{M}:N{Nd}:K{Kd}:tile{dom_plan[0]}:split{dom_plan[1]}"
+    traffic = committed_traffic(traffic_key)
     achieved = gemm_bytes[dom] / (dom_us * 1e-6) / 1e9 if dom_bound == "hbm" else dom_ops / (dom_us * 1e-6) / 1e12
     peak = HBM_PEAK_GBS if dom_bound == "hbm" else MFMA8_PEAK_TOPS
     roofline = {
@@ -280,9 +412,9 @@ def main():
         "peak": peak,
         "unit": "GB/s" if dom_bound == "hbm" else "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        "traffic": None,
-        "kernel": f"{dom} GEMM {Nd}x{Kd} M={M} ({B.tile_name(B.gemm_plan(M, Nd, Kd, qt)[0])}, "
-                  f"splitk {B.gemm_plan(M, Nd, Kd, qt)[1]})",
+        "traffic": traffic,
+        "traffic_key": traffic_key,
+        "kernel": f"{dom} GEMM {Nd}x{Kd} M={M} ({B.tile_name(dom_plan[0])}, splitk {dom_plan[1]})",
         "kernel_us": round(dom_us, 2),
         "alg_bytes_per_launch": gemm_bytes[dom],
         "alg_ops_per_launch": dom_ops,
@@ -290,12 +422,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        dt, threads = cpu_baseline(chain, shapes, M, qt, sigma, wl["kind"], s)
+        dt, nsteps, threads = cpu_baseline(chain, shapes, M, qt, sigma, wl["kind"], s)
         cpu = {"value": round(bytes_step / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"one {args.workload} layer step (M={M}, all {len(chain)} linears and "
-                         f"their per-token quantizations) by the numpy oracle: {dt:.2f} s",
-               "seconds": round(dt, 3), "host_cpus": os.cpu_count()}
+               "sample": f"{nsteps} {args.workload} layer steps (M={M}, all {len(chain)} linears and "
+                         f"their per-token quantizations, exact accumulation) by the numpy oracle, "
+                         f"{dt:.3f} s per step",
+               "seconds_per_step": round(dt, 4), "host_cpus": os.cpu_count()}
 
     out = {
         "metric": METRIC,

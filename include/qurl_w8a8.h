@@ -23,14 +23,16 @@
  *            out x in, K contiguous); activations X / codes Xq are [M, K];
  *            outputs Y are [M, N]. Leading dimensions (ld*) count elements.
  * Pointers   All array pointers are DEVICE pointers (memory of the current
- *            HIP device), 16-byte aligned. Codes Xq and Wq are dense
- *            (leading dimension K).
+ *            HIP device). Matrices are 16-byte aligned, scale vectors 4-byte
+ *            aligned. Codes Xq and Wq are dense (leading dimension K).
  * Dtypes     bf16 is passed as its 16-bit pattern (uint16); INT8 codes are
  *            int8; FP8 codes are OCP E4M3FN bytes (bias 7, max 448, no inf);
  *            scales and master weights are IEEE fp32.
  * Shapes     M, N >= 0 (0 makes the call a successful no-op); K >= 0 with
- *            K % 16 == 0; INT8 needs K <= 133144 so that K*127^2 < 2^31.
- *            ldx % 8 == 0, ldw % 4 == 0, ldy % 8 == 0 (bf16) or % 4 (raw).
+ *            K % 16 == 0; INT8 needs K <= 133144 so that K*127^2 < 2^31;
+ *            the GEMM needs N*K and M*K below 2^31 (code matrices < 2 GiB).
+ *            ldx % 8 == 0, ldw % 4 == 0, any ldy >= N (ldy % 4 == 0 lets the
+ *            epilogue store four outputs at a time).
  * Ownership  The caller allocates and owns every buffer, including the
  *            workspace. The library never allocates, frees or synchronizes.
  * Streams    `stream` is a hipStream_t passed as void* (NULL = the null
@@ -129,21 +131,21 @@ int qr_quantize_act_per_token(const void* X, int64_t M, int64_t K, int64_t ldx, 
  *   [Notes/System] (INT8/FP8 matmul), [Notes/Training].
  *
  *   acc[m,n] = sum_k Xq[m,k] * Wq[n,k]
- *              INT8: exact int32.  FP8: products of E4M3FN values summed in
- *              fp32 (order unspecified; deterministic for a given shape).
+ *              INT8: exact int32.  FP8: sums of E4M3FN products formed by
+ *              the gfx950 MFMA unit, which adds the products of a group of
+ *              k at reduced precision (bits far below the group's largest
+ *              product are dropped) and accumulates groups in fp32; the
+ *              result is deterministic for a given shape and plan.
  *   out = QR_OUT_BF16: Y[m,n] = bf16_rne(fl32(fl32(fl32(acc) * scale_x[m]) * scale_w[n]))
  *   out = QR_OUT_RAW : Y[m,n] = acc (int32 or fp32), for parity checks.
  *
  *   Y        [M, ldy] bf16, int32 or fp32 (written).
  *   workspace    device scratch of at least qr_workspace_size("qr_w8a8_gemm",
  *                M, N, K, qt) bytes, 256-byte aligned; may be NULL when that
- *                size is 0 (no K split for this shape). Layout, shared by
- *                every call that takes a workspace: the first 16 KiB hold
- *                split-K arrival counters and must be zero before the first
- *                call (allocate the workspace zeroed); every call leaves
- *                them zero and stores nothing else there, so one workspace
- *                can serve any sequence of calls on one stream. Calls that
- *                overlap in time (different streams) must not share it.
+ *                size is 0 (no K split for this shape). It holds the split-K
+ *                partial sums; its contents on entry do not matter and are
+ *                undefined on return. Calls that may run at the same time
+ *                (different streams) must not share it.
  */
 int qr_w8a8_gemm(const void* Xq, const float* scale_x, const void* Wq, const float* scale_w,
                  int64_t M, int64_t N, int64_t K, int qt, int out, void* Y, int64_t ldy,
@@ -156,9 +158,8 @@ int qr_w8a8_gemm(const void* Xq, const float* scale_x, const void* Wq, const flo
  *
  *   X        [M, ldx] bf16 (read); Y [M, ldy] bf16 (written).
  *   workspace    at least qr_workspace_size("qr_linear_fused", M, N, K, qt)
- *                bytes (never 0 when M, N > 0), 256-byte aligned, with the
- *                same 16 KiB zeroed counter prefix as for qr_w8a8_gemm; the
- *                activation codes and scales are stored after it.
+ *                bytes (never 0 when M, N > 0), 256-byte aligned scratch:
+ *                split-K partial sums, then the activation codes and scales.
  */
 int qr_linear_fused(const void* X, int64_t ldx, float act_mult, const void* Wq, const float* scale_w,
                     int64_t M, int64_t N, int64_t K, int qt, void* Y, int64_t ldy,

@@ -47,8 +47,16 @@ def assert_bf16_close(y_bits, ref_bits, rel=1e-2, what=""):
 
 
 def fp8_acc_bound(Xq, Wq):
-    """Worst-case fp32 summation error of any order: (K-1) 2^-24 sum_k |x_k w_k|."""
+    """Bound on the device's FP8 accumulators against the exact sums.
+
+    The gfx950 FP8 MFMA (every form: 16x16x32 fp8, 16x16x128 / 32x32x64
+    f8f6f4) adds the products of a group of k at reduced precision: bits far
+    below the group's largest product are dropped (measured: 448 plus seven
+    2^-9 terms in one group returns 448; on random data the error stayed below
+    2^-16.5 of sum_k |x_k w_k|). Allowed here: 2^-12 of sum |x w| for that, plus
+    the worst-case fp32 summation error of any order, (K-1) 2^-24 sum |x w|.
+    """
     dx = np.abs(F.e4m3fn_decode(Xq))
     dw = np.abs(F.e4m3fn_decode(Wq))
     K = Xq.shape[1]
-    return max(K - 1, 1) * 2.0 ** -24 * (dx @ dw.T)
+    return (2.0 ** -12 + max(K - 1, 1) * 2.0 ** -24) * (dx @ dw.T)

@@ -109,7 +109,7 @@ def test_gemm_validation(B):
     assert g(*args(Y=NULL)) == -1
     assert g(*args(sw=NULL)) == -1
     assert g(*args(K=72)) == -2
-    assert g(*args(ldy=36)) == -2
+    assert g(*args(Y=ctypes.c_void_p(264))) == -2
     assert g(*args(Wq=ctypes.c_void_p(264))) == -2
     # raw output needs no scales but still a Y
     assert g(*args(out=1, Y=NULL)) == -1

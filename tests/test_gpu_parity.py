@@ -2,7 +2,8 @@
 
 Bar: bit-exact quantized codes, scales, W/s and int32 accumulators (and, since
 the accumulators and the epilogue order agree, bit-exact INT8 bf16 outputs);
-FP8 accumulators within the fp32 summation bound and FP8 bf16 outputs within
+FP8 accumulators within the bound of the MFMA accumulation (gpu_helpers.fp8_acc_bound)
+and FP8 bf16 outputs within
 the relative tolerance 1e-2 (tests/gpu_helpers.assert_bf16_close).
 Inputs come from the seeded generators in w8a8_gemm_rl_amd.inputs.
 """
@@ -164,10 +165,10 @@ def test_gemm_auto_plan(qt, M, N, K):
 
 
 @pytest.mark.parametrize("qt", QTS)
-@pytest.mark.parametrize("tile", range(8))
+@pytest.mark.parametrize("tile", range(11))
 @pytest.mark.parametrize("splitk", [1, 3])
 def test_gemm_every_tile_and_split(qt, tile, splitk):
-    assert B.num_tiles() == 8
+    assert B.num_tiles() == 11
     M, N, K = 70, 300, 1152  # ragged in M and N for every tile, 9 K steps of 128
     xq, sx, wq, sw = _codes_pair(M, N, K, qt, seed=tile * 10 + splitk)
     B.set_plan_override(tile, splitk)

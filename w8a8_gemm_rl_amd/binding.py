@@ -101,8 +101,10 @@ def _need_cuda(*ts):
 
 def _rows(t, name):
     """Leading dimension of a 2-D tensor whose rows are contiguous."""
-    if t.dim() != 2 or t.stride(1) != 1:
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
         raise ValueError(f"{name} must be 2-D with contiguous rows")
+    if t.shape[0] <= 1:  # the row stride of a single row is arbitrary
+        return max(t.shape[1], 1)
     return t.stride(0)
 
 
@@ -111,8 +113,8 @@ def code_dtype(qt):
 
 
 # ----------------------------------------------------------------------------
-# Workspace: one zero-initialised buffer per device, grown on demand. The
-# library leaves it in a reusable state after every call.
+# Workspace: one scratch buffer per device, grown on demand, shared by calls
+# made on that device (they are stream-ordered on the current stream).
 # ----------------------------------------------------------------------------
 _ws = {}
 
@@ -124,7 +126,7 @@ def workspace(nbytes, device):
     if nbytes == 0:
         return None, 0
     if buf is None or buf.numel() < nbytes:
-        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
         _ws[key] = buf
     return buf, buf.numel()
 

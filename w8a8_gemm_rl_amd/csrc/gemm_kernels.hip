@@ -7,26 +7,32 @@
 // Design (MI355X / CDNA4):
 //  * Both operands are K-contiguous ("TN"). Weights feed the MFMA A operand
 //    (rows i = output channels n), activations feed the B operand (columns
-//    j = tokens m). INT8 uses v_mfma_i32_{16x16x64,32x32x32}_i8 (exact int32
-//    accumulation); FP8 E4M3FN uses v_mfma_scale_f32_{16x16x128,32x32x64}
-//    _f8f6f4 with unit block scales (E8M0 127 = 2^0), fp32 accumulation.
-//  * A block owns a BN x BM macro tile and a contiguous range of K. Tiles of
-//    both operands are staged through LDS, double-buffered, with an XOR
-//    swizzle of 16-byte chunks so that the 16-byte fragment reads of the
-//    MFMA operands are bank-conflict free. One barrier per K step.
+//    j = tokens m). INT8 uses v_mfma_i32_32x32x32_i8 (full rate on gfx950;
+//    the 16x16x64 form runs at half rate and is used only for 16-token
+//    tiles), exact int32 accumulation. FP8 E4M3FN uses
+//    v_mfma_scale_f32_{16x16x128,32x32x64}_f8f6f4 with unit block scales
+//    (E8M0 127 = 2^0), accumulating in fp32.
+//  * A block owns a BN x BM macro tile and a contiguous range of K. Both
+//    operand tiles go global -> registers -> LDS. Global loads run two K
+//    steps ahead of the MFMAs (two register stages), LDS is double-buffered,
+//    and one barrier separates K steps. 16-byte LDS chunks are XOR-swizzled
+//    by row so the 16-byte fragment reads of the MFMA operands are free of
+//    bank conflicts.
 //  * Each lane feeds the MFMA a contiguous 16- or 32-byte run of K for its row.
 //    The K order inside one instruction is the same for A and B, so any lane
 //    placement of K gives the same dot product.
-//  * Decode-sized M is bound by streaming the weights from HBM; when there are
-//    too few macro tiles to cover 256 CUs, K is split across blocks. Partial
-//    sums go to a workspace; the last block of a tile to arrive (an atomic
-//    counter) adds them in split order, which keeps FP8 results
-//    deterministic, and resets the counter for the next call.
-//  * Block indices are remapped so that consecutive logical tiles (same weight
-//    tile, neighbouring token tiles and K splits) land on the same XCD and
-//    share its L2.
+//  * Split K (when there are too few macro tiles for 256 CUs): each block
+//    stores its partial sums to the workspace with plain stores; a second
+//    kernel adds the splits in order and applies the epilogue. No
+//    cross-block synchronization inside a kernel (agent-scope fences flush
+//    and invalidate L2 on this chip), and FP8 sums are deterministic.
+//  * Block indices are remapped so that consecutive logical tiles (same
+//    weight tile, neighbouring token tiles and K splits) run on the same XCD
+//    and share its L2 (blocks are dealt to the 8 XCDs round-robin).
 //  * Epilogue: y = bf16_rne(fl32(fl32(fl32(acc) * sx[m]) * sw[n])), or the raw
 //    accumulators.
+#include <type_traits>
+
 #include "qr_device.h"
 #include "qr_internal.h"
 
@@ -80,25 +86,33 @@ struct Mfma<kQFp8, 32> {
   }
 };
 
+// Word 3 of a raw buffer resource on gfx9 parts: 32-bit data format, no
+// swizzle; with stride 0 the bound check is offset < num_records.
+constexpr int kBufWord3 = 0x00020000;
+
 struct KParams {
   const uint8_t* Xq;
   const float* sx;
   const uint8_t* Wq;
   const float* sw;
   int64_t M, N, K;
-  void* Y;
-  int64_t ldy;
-  int out_raw;
+  void* Y;       // output, or the split-K partial buffer [splitk][M][N]
+  int64_t ldy;   // leading dimension of Y (N for partials)
+  int out_raw;   // 1: store raw accumulators (always for partials)
+  int vec;       // ldy % 4 == 0: four consecutive outputs may be stored as one vector
   int splitk;
   int tiles_n, tiles_m, nks;
-  void* part;
-  int* counters;
 };
 
+// XOR swizzle of the 16-byte chunk index inside an LDS row. The LDS serves
+// a 128-bit read for 16 lanes at a time (256 bytes, 64 banks), and the MFMA
+// fragment reads put 16 consecutive rows at the same logical chunk: with
+// 128-byte rows, rows r and r+1 differ in their bank half, and (r >> 1) & 7
+// spreads the 8 row pairs over the 8 chunk slots (measured: no conflicts).
 template <int BK>
 __device__ __forceinline__ int swz(int row) {
-  if constexpr (BK == 128) return row & 7;
-  else return (row >> 1) & 3;
+  if constexpr (BK == 128) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
 }
 
 // fl32(acc) * sx * sw -> bf16 bits
@@ -116,22 +130,22 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_kernel(const KParams p) 
   constexpr int NT = 64 * WN * WM;
   constexpr int WTN = BN / WN, WTM = BM / WM;
   constexpr int FN = WTN / T, FM = WTM / T;
-  constexpr int CPR = BK / 16;  // 16-byte chunks per LDS row
+  constexpr int CPR = BK / 16;      // 16-byte chunks per LDS row
+  constexpr int RSTEP = NT / CPR;   // rows between one thread's consecutive chunks
   constexpr int CA = BN * CPR, CB = BM * CPR;
   constexpr int LA = (CA + NT - 1) / NT, LBn = (CB + NT - 1) / NT;
   constexpr int NACC = MF::NACC;
   constexpr int KI = MF::KI, LB = MF::LB;
+  constexpr int NKK = BK / KI;
   constexpr int STAGE = (BN + BM) * BK;
   static_assert(BK == 64 || BK == 128, "BK");
+  static_assert(NT % CPR == 0 && RSTEP % 16 == 0, "load rows keep one swizzle");
   static_assert(WTN % T == 0 && WTM % T == 0, "wave tile");
   static_assert(BK % KI == 0, "BK vs MFMA depth");
-  static_assert((FN * FM * NACC) % 4 == 0, "partials in 16-byte groups");
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-  __shared__ int s_last;
 
-  // ---- logical tile of this block (XCD-aware: consecutive logical indices
-  // on one XCD; blocks are dispatched to the 8 XCDs round-robin).
+  // ---- logical tile of this block (XCD-aware, see the file comment)
   const int G = gridDim.x;
   int b = blockIdx.x;
   const int G8 = G & ~7;
@@ -149,8 +163,6 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_kernel(const KParams p) 
   const int wn = wid % WN, wm = wid / WN;
 
   const int64_t N = p.N, M = p.M, K = p.K;
-  const uint8_t* __restrict__ Wq = p.Wq;
-  const uint8_t* __restrict__ Xq = p.Xq;
 
   acc_t acc[FN][FM];
 #pragma unroll
@@ -158,82 +170,108 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_kernel(const KParams p) 
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = acc_t{};
 
-  uint4 ra[LA], rb[LBn];
+  // ---- per-thread load addressing, computed once. Thread tid moves chunk
+  // c_ld of rows r_ld + i * RSTEP with buffer loads: a 32-bit per-thread
+  // offset plus the K advance as a scalar offset. Reads outside the buffer
+  // return zero: rows past N (or M) and chunks past K on a ragged last step
+  // point at offset 2^31, beyond any code matrix (each is under 2 GiB).
+  const int c_ld = tid % CPR;
+  const int r_ld = tid / CPR;
+  const bool ktail = (K % BK) != 0;
+  constexpr uint32_t kOOB = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t rsw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.Wq, (short)0, (int)(uint32_t)(N * K), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rsx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.Xq, (short)0, (int)(uint32_t)(M * K), kBufWord3);
+  uint32_t oa[LA], ob[LBn];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int64_t row = (int64_t)tn * BN + r_ld + i * RSTEP;
+    oa[i] = row < N ? (uint32_t)(row * K + c_ld * 16) : kOOB;
+  }
+#pragma unroll
+  for (int i = 0; i < LBn; ++i) {
+    const int64_t row = (int64_t)tm * BM + r_ld + i * RSTEP;
+    ob[i] = row < M ? (uint32_t)(row * K + c_ld * 16) : kOOB;
+  }
+  // LDS write offset of chunk 0 (chunk i adds i * RSTEP rows, same swizzle)
+  const int wofs = r_ld * BK + ((c_ld ^ swz<BK>(r_ld)) << 4);
 
-  auto gload = [&](int ks) {
-    const int64_t kb = (int64_t)ks * BK;
+  // LDS read offsets of the MFMA fragments: lane row lr of a fragment, whose
+  // base row is a multiple of 16, so the swizzle depends on lr only.
+  const int lr = lane % T;
+  const int lg = (lane / T) * (LB / 16);
+  const int sl = swz<BK>(lr);
+  const int rbaseA = (wn * WTN + lr) * BK;
+  const int rbaseB = BN * BK + (wm * WTM + lr) * BK;
+  int xo0[NKK], xo1[NKK];
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int q = tid + i * NT;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (CA % NT == 0 || q < CA) {
-        const int r = q / CPR, c = q % CPR;
-        const int64_t gn = (int64_t)tn * BN + r;
-        const int64_t kk = kb + c * 16;
-        if (gn < N && kk < K) v = *reinterpret_cast<const uint4*>(Wq + gn * K + kk);
-      }
-      ra[i] = v;
-    }
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int c0 = kk * (KI / 16) + lg;
+    xo0[kk] = (c0 ^ sl) << 4;
+    xo1[kk] = ((c0 + 1) ^ sl) << 4;
+  }
+
+  uint4 ra[2][LA], rb[2][LBn];
+
+  auto ld16 = [&](__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) -> uint4 {
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+  };
+  auto gload = [&](int ks, uint4* da, uint4* db) {
+    const int kb = ks * BK;  // scalar offset
+    if (!ktail || ks + 1 < p.nks) {
 #pragma unroll
-    for (int i = 0; i < LBn; ++i) {
-      const int q = tid + i * NT;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (CB % NT == 0 || q < CB) {
-        const int r = q / CPR, c = q % CPR;
-        const int64_t gm = (int64_t)tm * BM + r;
-        const int64_t kk = kb + c * 16;
-        if (gm < M && kk < K) v = *reinterpret_cast<const uint4*>(Xq + gm * K + kk);
-      }
-      rb[i] = v;
+      for (int i = 0; i < LA; ++i)
+        if (CA % NT == 0 || tid + i * NT < CA) da[i] = ld16(rsw, oa[i], kb);
+#pragma unroll
+      for (int i = 0; i < LBn; ++i)
+        if (CB % NT == 0 || tid + i * NT < CB) db[i] = ld16(rsx, ob[i], kb);
+    } else {
+      const bool kin = kb + c_ld * 16 < K;  // ragged last step
+#pragma unroll
+      for (int i = 0; i < LA; ++i)
+        if (CA % NT == 0 || tid + i * NT < CA) da[i] = ld16(rsw, kin ? oa[i] : kOOB, kb);
+#pragma unroll
+      for (int i = 0; i < LBn; ++i)
+        if (CB % NT == 0 || tid + i * NT < CB) db[i] = ld16(rsx, kin ? ob[i] : kOOB, kb);
     }
   };
 
-  auto sstore = [&](int buf) {
-    uint8_t* A = smem + buf * STAGE;
-    uint8_t* B = A + BN * BK;
+  auto sstore = [&](int buf, const uint4* da, const uint4* db) {
+    uint8_t* A = smem + buf * STAGE + wofs;
+    uint8_t* B = smem + buf * STAGE + BN * BK + wofs;
 #pragma unroll
-    for (int i = 0; i < LA; ++i) {
-      const int q = tid + i * NT;
-      if (CA % NT == 0 || q < CA) {
-        const int r = q / CPR, c = q % CPR;
-        *reinterpret_cast<uint4*>(A + r * BK + ((c ^ swz<BK>(r)) << 4)) = ra[i];
-      }
-    }
+    for (int i = 0; i < LA; ++i)
+      if (CA % NT == 0 || tid + i * NT < CA)
+        *reinterpret_cast<uint4*>(A + i * RSTEP * BK) = da[i];
 #pragma unroll
-    for (int i = 0; i < LBn; ++i) {
-      const int q = tid + i * NT;
-      if (CB % NT == 0 || q < CB) {
-        const int r = q / CPR, c = q % CPR;
-        *reinterpret_cast<uint4*>(B + r * BK + ((c ^ swz<BK>(r)) << 4)) = rb[i];
-      }
-    }
+    for (int i = 0; i < LBn; ++i)
+      if (CB % NT == 0 || tid + i * NT < CB)
+        *reinterpret_cast<uint4*>(B + i * RSTEP * BK) = db[i];
   };
 
-  auto lds_op = [&](const uint8_t* base, int row, int chunk0) -> op_t {
-    const uint4 u0 = *reinterpret_cast<const uint4*>(base + row * BK + ((chunk0 ^ swz<BK>(row)) << 4));
+  auto lds_op = [&](const uint8_t* base, int kk) -> op_t {
+    const uint4 u0 = *reinterpret_cast<const uint4*>(base + xo0[kk]);
     if constexpr (LB == 16) {
       return op_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w};
     } else {
-      const int c1 = chunk0 + 1;
-      const uint4 u1 = *reinterpret_cast<const uint4*>(base + row * BK + ((c1 ^ swz<BK>(row)) << 4));
+      const uint4 u1 = *reinterpret_cast<const uint4*>(base + xo1[kk]);
       return op_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
                   (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
     }
   };
 
   auto compute = [&](int buf) {
-    const uint8_t* A = smem + buf * STAGE;
-    const uint8_t* B = A + BN * BK;
-    const int lr = lane % T;
-    const int lg = (lane / T) * (LB / 16);
+    const uint8_t* A = smem + buf * STAGE + rbaseA;
+    const uint8_t* B = smem + buf * STAGE + rbaseB;
 #pragma unroll
-    for (int kk = 0; kk < BK / KI; ++kk) {
-      const int c0 = kk * (KI / 16) + lg;
+    for (int kk = 0; kk < NKK; ++kk) {
       op_t a[FN], bb[FM];
 #pragma unroll
-      for (int i = 0; i < FN; ++i) a[i] = lds_op(A, wn * WTN + i * T + lr, c0);
+      for (int i = 0; i < FN; ++i) a[i] = lds_op(A + i * T * BK, kk);
 #pragma unroll
-      for (int j = 0; j < FM; ++j) bb[j] = lds_op(B, wm * WTM + j * T + lr, c0);
+      for (int j = 0; j < FM; ++j) bb[j] = lds_op(B + j * T * BK, kk);
 #pragma unroll
       for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -241,153 +279,181 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_kernel(const KParams p) 
     }
   };
 
+  // ---- main loop: data of K step j lives in register stage j & 1. Step it
+  // first writes step it+1 (loaded two steps earlier) to the other LDS
+  // buffer, refills those registers with the loads of step it+3, and then
+  // runs the MFMAs of step it, so the loads are in flight while the matrix
+  // cores work. The loop is unrolled by two so every register stage index is
+  // a compile-time constant (a runtime index moves the stages to scratch).
   const int nk = ks1 - ks0;
+  auto step = [&](int it, auto stage_c) {
+    constexpr int s1 = decltype(stage_c)::value;  // == (it + 1) & 1
+    if (it + 1 < nk) sstore(s1, ra[s1], rb[s1]);
+    if (it + 3 < nk) gload(ks0 + it + 3, ra[s1], rb[s1]);
+    compute(s1 ^ 1);
+    __syncthreads();
+  };
   if (nk > 0) {
-    gload(ks0);
-    sstore(0);
+    gload(ks0, ra[0], rb[0]);
+    if (nk > 1) gload(ks0 + 1, ra[1], rb[1]);
+    sstore(0, ra[0], rb[0]);
+    if (nk > 2) gload(ks0 + 2, ra[0], rb[0]);
     __syncthreads();
-    for (int it = 0; it < nk; ++it) {
-      if (it + 1 < nk) gload(ks0 + it + 1);
-      compute(it & 1);
-      if (it + 1 < nk) sstore((it + 1) & 1);
-      __syncthreads();
+    for (int it = 0; it < nk; it += 2) {
+      step(it, std::integral_constant<int, 1>{});
+      if (it + 1 < nk) step(it + 1, std::integral_constant<int, 0>{});
     }
-  }
-
-  // ---- split-K: publish partials, the last block of the tile reduces them.
-  if (p.splitk > 1) {
-    constexpr int NG = FN * FM * NACC / 4;
-    const int64_t ntiles = (int64_t)p.tiles_n * p.tiles_m;
-    const int64_t tile = (int64_t)tn * p.tiles_m + tm;
-    uint4* part = reinterpret_cast<uint4*>(p.part);
-    {
-      uint4* mine = part + ((int64_t)z * ntiles + tile) * (NG * NT);
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j)
-#pragma unroll
-          for (int r = 0; r < NACC; r += 4) {
-            const int g = (i * FM + j) * (NACC / 4) + r / 4;
-            uint4 v;
-            v.x = __builtin_bit_cast(uint32_t, acc[i][j][r + 0]);
-            v.y = __builtin_bit_cast(uint32_t, acc[i][j][r + 1]);
-            v.z = __builtin_bit_cast(uint32_t, acc[i][j][r + 2]);
-            v.w = __builtin_bit_cast(uint32_t, acc[i][j][r + 3]);
-            mine[g * NT + tid] = v;
-          }
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const int prev = atomicAdd(p.counters + tile, 1);
-      s_last = (prev == p.splitk - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int j = 0; j < FM; ++j)
-#pragma unroll
-        for (int r = 0; r < NACC; r += 4) {
-          const int g = (i * FM + j) * (NACC / 4) + r / 4;
-          acc_t& A = acc[i][j];
-          if constexpr (QT == kQInt8) {
-            int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-            for (int zz = 0; zz < p.splitk; ++zz) {
-              if (zz == z) {
-                s0 += A[r]; s1 += A[r + 1]; s2 += A[r + 2]; s3 += A[r + 3];
-              } else {
-                const uint4 v = part[((int64_t)zz * ntiles + tile) * (NG * NT) + g * NT + tid];
-                s0 += (int)v.x; s1 += (int)v.y; s2 += (int)v.z; s3 += (int)v.w;
-              }
-            }
-            A[r] = s0; A[r + 1] = s1; A[r + 2] = s2; A[r + 3] = s3;
-          } else {
-            float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-            for (int zz = 0; zz < p.splitk; ++zz) {
-              float v0, v1, v2, v3;
-              if (zz == z) {
-                v0 = A[r]; v1 = A[r + 1]; v2 = A[r + 2]; v3 = A[r + 3];
-              } else {
-                const uint4 v = part[((int64_t)zz * ntiles + tile) * (NG * NT) + g * NT + tid];
-                v0 = __uint_as_float(v.x); v1 = __uint_as_float(v.y);
-                v2 = __uint_as_float(v.z); v3 = __uint_as_float(v.w);
-              }
-              s0 += v0; s1 += v1; s2 += v2; s3 += v3;
-            }
-            A[r] = s0; A[r + 1] = s1; A[r + 2] = s2; A[r + 3] = s3;
-          }
-        }
-    if (tid == 0) p.counters[tile] = 0;
   }
 
   // ---- epilogue. Lane layout of an MFMA result: for T = 16 register r of
   // lane l is (i = 4*(l/16) + r, j = l%16); for T = 32 it is
   // (i = 8*(r/4) + 4*(l/32) + r%4, j = l%32). Four consecutive registers are
-  // four consecutive output channels n of one token m.
+  // four consecutive output channels n of one token m. All scale loads are
+  // issued together (buffer loads, zero outside the vectors), then the
+  // outputs are converted and stored.
+  const bool split = p.splitk > 1;
+  const bool raw = split || p.out_raw;
+  constexpr int NG = NACC / 4;  // groups of four registers per fragment
+  const int jj = lane % T;
+  int64_t mrow[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) mrow[j] = (int64_t)tm * BM + wm * WTM + j * T + jj;
+  auto ncol = [&](int i, int g) -> int64_t {
+    const int ii = (T == 16) ? 4 * (lane / 16) : 8 * g + 4 * (lane / 32);
+    return (int64_t)tn * BN + wn * WTN + i * T + ii;
+  };
+  float sxv[FM];
+  float swv[FN][NG][4];
+  if (!raw) {
+    const __amdgpu_buffer_rsrc_t rsx_ = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.sx, (short)0, (int)(uint32_t)(M * 4), kBufWord3);
+    const __amdgpu_buffer_rsrc_t rsw_ = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.sw, (short)0, (int)(uint32_t)(N * 4), kBufWord3);
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+      sxv[j] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+          rsx_, mrow[j] < M ? (int)(mrow[j] * 4) : (int)kOOB, 0, 0));
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int64_t n0 = ncol(i, g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          swv[i][g][e] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+              rsw_, n0 + e < N ? (int)((n0 + e) * 4) : (int)kOOB, 0, 0));
+      }
+  }
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int j = 0; j < FM; ++j)
 #pragma unroll
-      for (int r = 0; r < NACC; r += 4) {
-        const int ii = (T == 16) ? 4 * (lane / 16) : 8 * (r / 4) + 4 * (lane / 32);
-        const int jj = lane % T;
-        const int64_t n0 = (int64_t)tn * BN + wn * WTN + i * T + ii;
-        const int64_t m = (int64_t)tm * BM + wm * WTM + j * T + jj;
+      for (int g = 0; g < NG; ++g) {
+        const int r = 4 * g;
+        const int64_t n0 = ncol(i, g);
+        const int64_t m = mrow[j];
         if (m >= M || n0 >= N) continue;
-        const acc_t& A = acc[i][j];
-        float a4[4];
+        const bool full4 = p.vec && n0 + 3 < N;
+        if (raw) {
+          // int32 or fp32 words, 16 bytes when four outputs fit
+          uint32_t w[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a4[e] = (float)A[r + e];
-        if (p.out_raw) {
-          if constexpr (QT == kQInt8) {
-            int32_t* y = static_cast<int32_t*>(p.Y) + m * p.ldy + n0;
-            if (n0 + 3 < N) {
-              *reinterpret_cast<int4*>(y) = make_int4(A[r], A[r + 1], A[r + 2], A[r + 3]);
-            } else {
-              for (int e = 0; e < 4 && n0 + e < N; ++e) y[e] = A[r + e];
-            }
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (QT == kQInt8) w[e] = (uint32_t)acc[i][j][r + e];
+            else w[e] = __float_as_uint(acc[i][j][r + e]);
+          }
+          uint32_t* y = static_cast<uint32_t*>(p.Y) + (split ? (int64_t)z * M * N : 0) + m * p.ldy + n0;
+          if (full4) {
+            *reinterpret_cast<uint4*>(y) = make_uint4(w[0], w[1], w[2], w[3]);
           } else {
-            float* y = static_cast<float*>(p.Y) + m * p.ldy + n0;
-            if (n0 + 3 < N) {
-              *reinterpret_cast<float4*>(y) = make_float4(a4[0], a4[1], a4[2], a4[3]);
-            } else {
-              for (int e = 0; e < 4 && n0 + e < N; ++e) y[e] = a4[e];
-            }
+            for (int e = 0; e < 4 && n0 + e < N; ++e) y[e] = w[e];
           }
         } else {
-          const float sxm = p.sx[m];
+          uint32_t bb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bb[e] = epi_bf16((float)acc[i][j][r + e], sxv[j], swv[i][g][e]);
           uint16_t* y = static_cast<uint16_t*>(p.Y) + m * p.ldy + n0;
-          if (n0 + 3 < N) {
-            const float4 sw4 = *reinterpret_cast<const float4*>(p.sw + n0);
-            const uint32_t b0 = epi_bf16(a4[0], sxm, sw4.x), b1 = epi_bf16(a4[1], sxm, sw4.y);
-            const uint32_t b2 = epi_bf16(a4[2], sxm, sw4.z), b3 = epi_bf16(a4[3], sxm, sw4.w);
-            *reinterpret_cast<uint2*>(y) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+          if (full4) {
+            *reinterpret_cast<uint2*>(y) = make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
           } else {
-            for (int e = 0; e < 4 && n0 + e < N; ++e)
-              y[e] = (uint16_t)epi_bf16(a4[e], sxm, p.sw[n0 + e]);
+            for (int e = 0; e < 4 && n0 + e < N; ++e) y[e] = (uint16_t)bb[e];
           }
         }
       }
 }
 
+// Split-K second pass: Y[m, n] = epilogue(sum_{z = 0..S-1} part[z][m][n]),
+// summed in split order. One thread per four consecutive n of one m.
+template <int QT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __restrict__ part, int S,
+                                                            int64_t M, int64_t N,
+                                                            const float* __restrict__ sx,
+                                                            const float* __restrict__ sw, void* Y,
+                                                            int64_t ldy, int out_raw, int vec) {
+  const int64_t nq = (N + 3) / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * nq) return;
+  const int64_t m = idx / nq;
+  const int64_t n0 = (idx % nq) * 4;
+  const int cnt = (int)((N - n0) < 4 ? (N - n0) : 4);
+  const bool v4 = (N % 4 == 0);
+  int32_t si[4] = {0, 0, 0, 0};
+  float sf[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int zz = 0; zz < S; ++zz) {
+    const uint32_t* src = part + (int64_t)zz * M * N + m * N + n0;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (v4) {
+      const uint4 u = *reinterpret_cast<const uint4*>(src);
+      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    } else {
+      for (int e = 0; e < cnt; ++e) w[e] = src[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (QT == kQInt8) si[e] += (int32_t)w[e];
+      else sf[e] += __uint_as_float(w[e]);
+    }
+  }
+  const bool full4 = vec && cnt == 4;
+  if (out_raw) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (QT == kQInt8) ? (uint32_t)si[e] : __float_as_uint(sf[e]);
+    uint32_t* y = static_cast<uint32_t*>(Y) + m * ldy + n0;
+    if (full4) *reinterpret_cast<uint4*>(y) = make_uint4(w[0], w[1], w[2], w[3]);
+    else for (int e = 0; e < cnt; ++e) y[e] = w[e];
+  } else {
+    const float sxm = sx[m];
+    uint32_t bb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = (QT == kQInt8) ? (float)si[e] : sf[e];
+      bb[e] = e < cnt ? epi_bf16(a, sxm, sw[n0 + e]) : 0u;
+    }
+    uint16_t* y = static_cast<uint16_t*>(Y) + m * ldy + n0;
+    if (full4) *reinterpret_cast<uint2*>(y) = make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
+    else for (int e = 0; e < cnt; ++e) y[e] = (uint16_t)bb[e];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tile table. Order matters: the planner and the tuning hook refer to tiles
-// by index.
+// by index. (T, BN, BM, BK, WN, WM): MFMA edge, macro tile over N and M,
+// K bytes per stage, waves along N and M.
 // ---------------------------------------------------------------------------
-#define QR_TILES(X)                                  \
-  X(16, 64, 16, 128, 4, 1)  /* 0: M <= 16 streaming  */ \
-  X(16, 128, 32, 128, 4, 1) /* 1: M <= 32            */ \
-  X(16, 128, 64, 128, 2, 2) /* 2: M <= 64            */ \
-  X(32, 128, 128, 128, 2, 2) /* 3: M <= 128          */ \
-  X(32, 128, 256, 128, 2, 2) /* 4: decode M = 256    */ \
-  X(32, 256, 128, 128, 2, 2) /* 5: large M           */ \
-  X(32, 256, 256, 128, 2, 2) /* 6: large M           */ \
-  X(32, 64, 256, 128, 1, 4) /* 7: decode M = 256, narrow */
+#define QR_TILES(X)                                          \
+  X(16, 64, 16, 128, 4, 1)   /* 0: M <= 16, weight streaming */ \
+  X(16, 32, 16, 128, 2, 1)   /* 1: M <= 16, narrow          */ \
+  X(32, 128, 32, 128, 4, 1)  /* 2: M <= 32                  */ \
+  X(32, 64, 64, 128, 2, 2)   /* 3: M <= 64                  */ \
+  X(32, 128, 64, 128, 2, 2)  /* 4: M <= 64, wide            */ \
+  X(32, 64, 128, 128, 2, 2)  /* 5: M <= 128                 */ \
+  X(32, 128, 128, 128, 2, 2) /* 6: M <= 128, wide           */ \
+  X(32, 64, 256, 128, 1, 4)  /* 7: M = 256 decode           */ \
+  X(32, 128, 256, 128, 2, 2) /* 8: M = 256 decode, wide     */ \
+  X(32, 256, 128, 128, 2, 2) /* 9: large M                  */ \
+  X(32, 256, 256, 128, 2, 4) /* 10: large M, 8 waves        */
 
 #define QR_DESC(T, BN, BM, BK, WN, WM) \
   {"t" #T "_n" #BN "_m" #BM "_k" #BK "_w" #WN "x" #WM, T, BN, BM, BK, 64 * WN * WM},
@@ -411,21 +477,37 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   KParams kp;
   kp.Xq = a.Xq; kp.sx = a.sx; kp.Wq = a.Wq; kp.sw = a.sw;
   kp.M = a.M; kp.N = a.N; kp.K = a.K;
-  kp.Y = a.Y; kp.ldy = a.ldy; kp.out_raw = a.out_raw;
   kp.splitk = plan.splitk;
   kp.tiles_n = (int)plan.tiles_n; kp.tiles_m = (int)plan.tiles_m; kp.nks = (int)plan.nks;
-  kp.part = a.part; kp.counters = a.counters;
+  if (plan.splitk > 1) {
+    kp.Y = a.part; kp.ldy = a.N; kp.out_raw = 1; kp.vec = (a.N % 4) == 0;
+  } else {
+    kp.Y = a.Y; kp.ldy = a.ldy; kp.out_raw = a.out_raw; kp.vec = (a.ldy % 4) == 0;
+  }
   const unsigned grid = (unsigned)(plan.tiles_n * plan.tiles_m * plan.splitk);
+  hipError_t e = hipErrorInvalidValue;
   int idx = 0;
 #define QR_CASE(T, BN, BM, BK, WN, WM)                                               \
   if (plan.tile == idx) {                                                             \
-    return qt == kQInt8 ? launch_one<kQInt8, T, BN, BM, BK, WN, WM>(kp, grid, st)    \
-                        : launch_one<kQFp8, T, BN, BM, BK, WN, WM>(kp, grid, st);    \
+    e = qt == kQInt8 ? launch_one<kQInt8, T, BN, BM, BK, WN, WM>(kp, grid, st)       \
+                     : launch_one<kQFp8, T, BN, BM, BK, WN, WM>(kp, grid, st);       \
   }                                                                                   \
   ++idx;
   QR_TILES(QR_CASE)
 #undef QR_CASE
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || plan.splitk <= 1) return e;
+  const int64_t work = a.M * ((a.N + 3) / 4);
+  const unsigned rgrid = (unsigned)((work + 255) / 256);
+  const int vec = (a.ldy % 4) == 0;
+  if (qt == kQInt8)
+    hipLaunchKernelGGL(splitk_reduce_kernel<kQInt8>, dim3(rgrid), dim3(256), 0, st,
+                       static_cast<const uint32_t*>(a.part), plan.splitk, a.M, a.N, a.sx, a.sw,
+                       a.Y, a.ldy, a.out_raw, vec);
+  else
+    hipLaunchKernelGGL(splitk_reduce_kernel<kQFp8>, dim3(rgrid), dim3(256), 0, st,
+                       static_cast<const uint32_t*>(a.part), plan.splitk, a.M, a.N, a.sx, a.sw,
+                       a.Y, a.ldy, a.out_raw, vec);
+  return hipGetLastError();
 }
 
 }  // namespace qr

@@ -20,6 +20,7 @@ int g_force_splitk = 0;
 
 constexpr int64_t kMaxKInt8 = 133144;  // K * 127^2 < 2^31
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxCodeBytes = (int64_t)1 << 31;  // GEMM: 32-bit buffer offsets, 2^31 = out of range
 constexpr int kCUs = 256;  // MI355X compute units: the plan targets this chip
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -72,21 +73,28 @@ namespace qr {
 GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int force_splitk) {
   (void)qt;
   GemmPlan p{};
+  // Tile by token count (indices into the tile table, measured on MI355X):
+  // narrow 16-token tiles stream the weights for single-token decode; 32- to
+  // 128-token tiles for small batches; 64x64 (narrow layers) or 128x64 tiles
+  // for 256-token decode; 256x256 tiles with 8 waves for large token counts
+  // on wide layers.
   int tile;
   if (force_tile >= 0) {
     tile = force_tile;
   } else if (M <= 16) {
-    tile = 0;
-  } else if (M <= 32) {
     tile = 1;
-  } else if (M <= 64) {
+  } else if (M <= 32) {
     tile = 2;
-  } else if (M <= 128) {
+  } else if (M <= 64) {
     tile = 3;
-  } else if (M <= 256) {
-    tile = 4;
-  } else {
+  } else if (M <= 128) {
     tile = 5;
+  } else if (M <= 256) {
+    tile = N <= 8192 ? 3 : 4;
+  } else if (M <= 1024) {
+    tile = N >= 16384 ? 10 : 4;
+  } else {
+    tile = 10;
   }
   const TileDesc& d = tile_desc(tile);
   p.tile = tile;
@@ -94,23 +102,27 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
   p.tiles_m = (M + d.BM - 1) / d.BM;
   p.nks = (K + d.BK - 1) / d.BK;
   const int64_t tiles = p.tiles_n * p.tiles_m;
+  const int64_t target = (M <= 16 ? 4 : 2) * kCUs;  // blocks wanted in flight
   int64_t s = 1;
   if (force_splitk > 0) {
     s = force_splitk;
-  } else if (tiles > 0 && tiles < kCUs) {
-    // Split K until about two blocks per CU, keeping >= 4 K steps per split.
-    s = (2 * kCUs + tiles - 1) / tiles;
-    const int64_t smax = p.nks / 4;
-    if (s > smax) s = smax;
+  } else if (tiles > 0 && tiles < target) {
+    // Split K towards the target block count while the partial sums (4*M*N
+    // bytes per split) stay within a quarter of the weight bytes and every
+    // split keeps at least four K steps.
+    s = (target + tiles - 1) / tiles;
+    const int64_t by_bytes = K / (16 * (M > 0 ? M : 1));
+    const int64_t by_steps = p.nks / 4;
+    if (s > by_bytes) s = by_bytes;
+    if (s > by_steps) s = by_steps;
     if (s > 32) s = 32;
     if (s < 1) s = 1;
   }
   if (p.nks > 0 && s > p.nks) s = p.nks;
-  if (tiles > kMaxSplitTiles) s = 1;  // one counter per tile must fit the counter region
   if (s < 1) s = 1;
   p.splitk = (int)s;
   if (p.splitk > 1 && tiles > 0)
-    p.part_bytes = align256((size_t)p.splitk * (size_t)tiles * d.BN * d.BM * 4);
+    p.part_bytes = align256((size_t)p.splitk * (size_t)M * (size_t)N * 4);
   return p;
 }
 
@@ -156,8 +168,7 @@ size_t qr_workspace_size(const char* fn, int64_t M, int64_t N, int64_t K, int qt
   if (std::strcmp(fn, "qr_w8a8_gemm") == 0) return gemm;
   if (std::strcmp(fn, "qr_linear_fused") == 0) {
     if (M == 0 || N == 0) return 0;
-    return qr::kCounterBytes + p.part_bytes + align256((size_t)M * (size_t)K) +
-           align256((size_t)M * 4);
+    return p.part_bytes + align256((size_t)M * (size_t)K) + align256((size_t)M * 4);
   }
   return (size_t)-1;
 }
@@ -219,10 +230,8 @@ int check_gemm_io(const char* fn, int64_t M, int64_t N, int64_t K, int out, bool
     if (out == QR_OUT_BF16 && ((need_sx && !sx) || !sw))
       return fail(QR_ERR_INVALID_ARG, "%s: null scales", fn);
   }
-  if (ldy % (out == QR_OUT_BF16 ? 8 : 4) != 0)
-    return fail(QR_ERR_UNSUPPORTED, "%s: ldy must be a multiple of %d", fn, out == QR_OUT_BF16 ? 8 : 4);
-  if (!aligned(Wq, 16) || !aligned(Y, 16) || !aligned(sx, 4) || !aligned(sw, 16))
-    return fail(QR_ERR_UNSUPPORTED, "%s: misaligned pointer (16 bytes for Wq, Y, scale_w)", fn);
+  if (!aligned(Wq, 16) || !aligned(Y, 16) || !aligned(sx, 4) || !aligned(sw, 4))
+    return fail(QR_ERR_UNSUPPORTED, "%s: misaligned pointer (16 bytes for Wq, Y)", fn);
   return QR_OK;
 }
 
@@ -246,9 +255,7 @@ int run_gemm(const char* fn, const qr::GemmPlan& plan, const void* Xq, const flo
   a.M = M; a.N = N; a.K = K;
   a.Y = Y; a.ldy = ldy;
   a.out_raw = out == QR_OUT_RAW;
-  // gemm_ws is the start of the workspace: counters first, then partials.
-  a.counters = plan.splitk > 1 ? static_cast<int*>(gemm_ws) : nullptr;
-  a.part = plan.splitk > 1 ? static_cast<char*>(gemm_ws) + qr::kCounterBytes : nullptr;
+  a.part = plan.splitk > 1 ? gemm_ws : nullptr;
   return hip_status(qr::launch_gemm(plan, qt, a, hs), fn);
 }
 
@@ -264,6 +271,8 @@ int qr_w8a8_gemm(const void* Xq, const float* scale_x, const void* Wq, const flo
   if (st != QR_OK) return st;
   if (M > 0 && N > 0 && K > 0 && !Xq) return fail(QR_ERR_INVALID_ARG, "%s: null Xq", fn);
   if (!aligned(Xq, 16)) return fail(QR_ERR_UNSUPPORTED, "%s: misaligned Xq", fn);
+  if (N * K >= kMaxCodeBytes || M * K >= kMaxCodeBytes)
+    return fail(QR_ERR_UNSUPPORTED, "%s: a code matrix of 2 GiB or more", fn);
   if (M == 0 || N == 0) return ok();
   const qr::GemmPlan plan = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk);
   st = check_ws(fn, workspace, workspace_bytes, plan.ws_bytes());
@@ -287,11 +296,13 @@ int qr_linear_fused(const void* X, int64_t ldx, float act_mult, const void* Wq, 
   if (M > 0 && N > 0 && K > 0 && !X) return fail(QR_ERR_INVALID_ARG, "%s: null X", fn);
   if (ldx % 8 != 0) return fail(QR_ERR_UNSUPPORTED, "%s: ldx must be a multiple of 8", fn);
   if (!aligned(X, 16)) return fail(QR_ERR_UNSUPPORTED, "%s: misaligned X", fn);
+  if (N * K >= kMaxCodeBytes || M * K >= kMaxCodeBytes)
+    return fail(QR_ERR_UNSUPPORTED, "%s: a code matrix of 2 GiB or more", fn);
   if (M == 0 || N == 0) return ok();
   const qr::GemmPlan plan = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk);
   const size_t xq_bytes = align256((size_t)M * (size_t)K);
   const size_t sx_bytes = align256((size_t)M * 4);
-  const size_t head = qr::kCounterBytes + plan.part_bytes;
+  const size_t head = plan.part_bytes;
   st = check_ws(fn, workspace, workspace_bytes, head + xq_bytes + sx_bytes);
   if (st != QR_OK) return st;
   char* ws = static_cast<char*>(workspace);

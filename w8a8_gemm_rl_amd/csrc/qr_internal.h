@@ -26,25 +26,14 @@ struct TileDesc {
 int num_tiles();
 const TileDesc& tile_desc(int tile);
 
-// Workspace layout shared by every call that takes one:
-//   [0, kCounterBytes)   split-K arrival counters, one int per macro tile.
-//                        Zero between calls: the caller zeroes the workspace
-//                        once, and the block that consumes a counter resets
-//                        it. Nothing else is ever stored here, so any
-//                        sequence of calls may share one workspace.
-//   [kCounterBytes, ...) split-K partial sums, then (qr_linear_fused) the
-//                        activation codes and scales.
-constexpr size_t kCounterBytes = 16384;
-constexpr int64_t kMaxSplitTiles = (int64_t)(kCounterBytes / 4);
-
 // A launch plan for one product shape.
 struct GemmPlan {
   int tile;
   int splitk;
   int64_t tiles_n, tiles_m, nks;
-  size_t part_bytes;  // split-K partial sums (0 without split)
-  // Workspace qr_w8a8_gemm needs: none without split-K.
-  size_t ws_bytes() const { return splitk > 1 ? kCounterBytes + part_bytes : 0; }
+  size_t part_bytes;  // split-K partial sums [splitk][M][N] (0 without split)
+  // Workspace qr_w8a8_gemm needs: the partial sums, none without split-K.
+  size_t ws_bytes() const { return part_bytes; }
 };
 
 GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int force_splitk);
@@ -58,8 +47,7 @@ struct GemmArgs {
   void* Y;
   int64_t ldy;
   int out_raw;
-  void* part;
-  int* counters;
+  void* part;  // split-K partial sums (workspace)
 };
 
 hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStream_t st);
