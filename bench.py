@@ -182,6 +182,13 @@ def committed_traffic(key):
     return None
 
 
+def is_gemm_kernel(name):
+    """True for the main GEMM kernels (any tile family), not the split-K reduction."""
+    import re
+
+    return re.search(r"gemm_\w*kernel", name) is not None
+
+
 def summarize_rocprof(paths, grid):
     """Print the figures used from rocprofv3 CSV outputs (kernel trace, or a
     --pmc counter collection) for dispatches of the given grid size."""
@@ -193,7 +200,7 @@ def summarize_rocprof(paths, grid):
         if rows and "Counter_Name" in rows[0]:
             by = {}
             for r in rows:
-                if int(r["Grid_Size"]) == grid and "gemm_kernel" in r["Kernel_Name"]:
+                if int(r["Grid_Size"]) == grid and is_gemm_kernel(r["Kernel_Name"]):
                     by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
             for c, v in by.items():
                 print(f"{path}: {c} per dispatch (grid {grid}): mean {statistics.mean(v):.1f} KiB, "
@@ -204,7 +211,7 @@ def summarize_rocprof(paths, grid):
                           f"{r['Counter_Name']} {float(r['Counter_Value']):.1f}")
         else:
             ds = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in rows
-                  if int(r["Grid_Size_X"]) == grid and "gemm_kernel" in r["Kernel_Name"]]
+                  if int(r["Grid_Size_X"]) == grid and is_gemm_kernel(r["Kernel_Name"])]
             if ds:
                 print(f"{path}: gemm dispatches of grid {grid}: n={len(ds)} mean {statistics.mean(ds):.2f} us "
                       f"median {statistics.median(ds):.2f} us min {min(ds):.2f} us")
@@ -402,7 +409,8 @@ def main():
                           plan=list(B.gemm_plan(M, N_, K_, qt)))
 
     dom_plan = B.gemm_plan(M, Nd, Kd, qt)
-    traffic_key = f"{args.workload}:{dom}:M{M}:N{Nd}:K{Kd}:tile{dom_plan[0]}:split{dom_plan[1]}"
+    traffic_key = (f"{args.workload}:{dom}:M{M}:N{Nd}:K{Kd}:tile{dom_plan[0]}:split{dom_plan[1]}"
+                   f":rows{dom_plan[2]}")
     traffic = committed_traffic(traffic_key)
     achieved = gemm_bytes[dom] / (dom_us * 1e-6) / 1e9 if dom_bound == "hbm" else dom_ops / (dom_us * 1e-6) / 1e12
     peak = HBM_PEAK_GBS if dom_bound == "hbm" else MFMA8_PEAK_TOPS

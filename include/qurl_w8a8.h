@@ -30,7 +30,8 @@
  *            scales and master weights are IEEE fp32.
  * Shapes     M, N >= 0 (0 makes the call a successful no-op); K >= 0 with
  *            K % 16 == 0; INT8 needs K <= 133144 so that K*127^2 < 2^31;
- *            the GEMM needs N*K and M*K below 2^31 (code matrices < 2 GiB).
+ *            the GEMM needs N*K and M*K below 2^31 - 2^16 (code matrices
+ *            just under 2 GiB).
  *            ldx % 8 == 0, ldw % 4 == 0, any ldy >= N (ldy % 4 == 0 lets the
  *            epilogue store four outputs at a time).
  * Ownership  The caller allocates and owns every buffer, including the
@@ -176,10 +177,12 @@ size_t qr_workspace_size(const char* fn, int64_t M, int64_t N, int64_t K, int qt
 /*
  * qr_gemm_plan -- report the kernel plan qr_w8a8_gemm uses for a shape:
  *   *tile    index of the tile configuration (see qr_tile_name),
- *   *splitk  number of K splits (1 = none).
+ *   *splitk  number of K splits (1 = none),
+ *   *rows    output channels (weight rows) per tile, a multiple of 8 no
+ *            larger than the configuration's tile height.
  * Pure host function; returns QR_OK or QR_ERR_INVALID_ARG.
  */
-int qr_gemm_plan(int64_t M, int64_t N, int64_t K, int qt, int* tile, int* splitk);
+int qr_gemm_plan(int64_t M, int64_t N, int64_t K, int qt, int* tile, int* splitk, int* rows);
 
 /* Name of tile configuration `tile` (static string) or NULL if out of range. */
 const char* qr_tile_name(int tile);
@@ -188,13 +191,14 @@ const char* qr_tile_name(int tile);
 int qr_num_tiles(void);
 
 /*
- * qr_set_plan_override -- tuning hook: force tile configuration `tile` and
- * `splitk` splits for every later qr_w8a8_gemm / qr_linear_fused /
- * qr_workspace_size call in the process (tile < 0 restores automatic
- * planning). Not thread-safe; meant for benchmarks and tests.
- * Returns QR_OK or QR_ERR_INVALID_ARG.
+ * qr_set_plan_override -- tuning hook: force tile configuration `tile`,
+ * `splitk` splits (0 = automatic) and `rows` weight rows per tile (0 = the
+ * tile height; else a multiple of 8 no larger than it) for every later
+ * qr_w8a8_gemm / qr_linear_fused / qr_workspace_size / qr_gemm_plan call in
+ * the process (tile < 0 restores automatic planning). Not thread-safe;
+ * meant for benchmarks and tests. Returns QR_OK or QR_ERR_INVALID_ARG.
  */
-int qr_set_plan_override(int tile, int splitk);
+int qr_set_plan_override(int tile, int splitk, int rows);
 
 /* Thread-local message describing the last non-QR_OK status ("" if none). */
 const char* qr_last_error(void);

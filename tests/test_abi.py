@@ -141,14 +141,18 @@ def test_workspace_size_and_plan_are_pure(B):
     a = L.qr_workspace_size(b"qr_linear_fused", 256, 3584, 3584, I8)
     b = L.qr_workspace_size(b"qr_w8a8_gemm", 256, 3584, 3584, I8)
     assert a >= b + 256 * 3584 + 256 * 4 and a % 256 == 0
-    t, s = B.gemm_plan(256, 3584, 3584, "int8")
-    assert 0 <= t < B.num_tiles() and s >= 1
+    t, s, r = B.gemm_plan(256, 3584, 3584, "int8")
+    assert 0 <= t < B.num_tiles() and s >= 1 and r >= 8 and r % 8 == 0
     # big grids need no split
     assert B.gemm_plan(4096, 27648, 5120, "int8")[1] == 1
-    # override hook round-trips
+    # override hook round-trips; rows 0 means the full tile height
     B.set_plan_override(0, 3)
-    assert B.gemm_plan(256, 3584, 3584, "fp8") == (0, 3)
+    assert B.gemm_plan(256, 3584, 3584, "fp8") == (0, 3, 64)
+    B.set_plan_override(0, 2, 40)
+    assert B.gemm_plan(256, 3584, 3584, "fp8") == (0, 2, 40)
     B.set_plan_override(-1)
-    assert B.gemm_plan(256, 3584, 3584, "int8") == (t, s)
-    with pytest.raises(B.QRError):
-        B.set_plan_override(999, 1)
+    assert B.gemm_plan(256, 3584, 3584, "int8") == (t, s, r)
+    for bad in [(999, 1, 0), (0, 1, 12), (0, 1, 72), (0, 1, -8), (0, -1, 0)]:
+        with pytest.raises(B.QRError):
+            B.set_plan_override(*bad)
+    B.set_plan_override(-1)

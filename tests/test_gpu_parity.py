@@ -8,6 +8,8 @@ the relative tolerance 1e-2 (tests/gpu_helpers.assert_bf16_close).
 Inputs come from the seeded generators in w8a8_gemm_rl_amd.inputs.
 """
 
+import re
+
 import numpy as np
 import pytest
 import torch
@@ -164,22 +166,48 @@ def test_gemm_auto_plan(qt, M, N, K):
     _check_gemm(xq, sx, wq, sw, qt, f"{qt} M={M} N={N} K={K} plan={B.gemm_plan(M, N, K, qt)}")
 
 
+NUM_TILES = 51  # entries of the library's tile table
+
+
 @pytest.mark.parametrize("qt", QTS)
-@pytest.mark.parametrize("tile", range(11))
-@pytest.mark.parametrize("splitk", [1, 3])
-def test_gemm_every_tile_and_split(qt, tile, splitk):
-    assert B.num_tiles() == 11
-    M, N, K = 70, 300, 1152  # ragged in M and N for every tile, 9 K steps of 128
-    xq, sx, wq, sw = _codes_pair(M, N, K, qt, seed=tile * 10 + splitk)
+@pytest.mark.parametrize("tile", range(NUM_TILES))
+@pytest.mark.parametrize("splitk", [1, 3, 9])
+@pytest.mark.parametrize("M,N,K", [(70, 300, 1152), (45, 136, 1040), (40, 72, 96)])
+def test_gemm_every_tile_and_split(qt, tile, splitk, M, N, K):
+    # Ragged in M and N for every tile; 9 K steps of 128, the second shape
+    # with a 16-byte last step, the third a single step shorter than 128
+    # bytes. Split 9 leaves one or two K steps per block, fewer than the LDS
+    # ring holds.
+    assert B.num_tiles() == NUM_TILES
+    xq, sx, wq, sw = _codes_pair(M, N, K, qt, seed=tile * 10 + splitk + M)
     B.set_plan_override(tile, splitk)
-    _check_gemm(xq, sx, wq, sw, qt, f"{qt} tile={tile} splitk={splitk}")
+    _check_gemm(xq, sx, wq, sw, qt, f"{qt} tile={tile} splitk={splitk} M={M} N={N} K={K}")
+
+
+def _tile_height(tile):
+    return int(re.search(r"_n(\d+)_", B.tile_name(tile)).group(1))
+
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("tile", range(NUM_TILES))
+@pytest.mark.parametrize("splitk", [1, 3])
+def test_gemm_partial_tile_rows(qt, tile, splitk):
+    # Tiles that own fewer weight rows than their height: 8 rows, and the
+    # largest multiple of 8 below 5/8 of the height.
+    M, N, K = 45, 136, 1040
+    bn = _tile_height(tile)
+    for rows in sorted({8, max(8, (5 * bn // 8) // 8 * 8)}):
+        xq, sx, wq, sw = _codes_pair(M, N, K, qt, seed=tile * 7 + splitk + rows)
+        B.set_plan_override(tile, splitk, rows)
+        assert B.gemm_plan(M, N, K, qt) == (tile, splitk, rows)
+        _check_gemm(xq, sx, wq, sw, qt, f"{qt} tile={tile} splitk={splitk} rows={rows}")
 
 
 @pytest.mark.parametrize("qt", QTS)
 def test_gemm_split_deterministic_and_reusable(qt):
     M, N, K = 32, 1024, 4096
     xq, sx, wq, sw = _codes_pair(M, N, K, qt, seed=77)
-    t, s = B.gemm_plan(M, N, K, qt)
+    t, s, _ = B.gemm_plan(M, N, K, qt)
     assert s > 1
     a = [_run_gemm(xq, sx, wq, sw, qt, "raw") for _ in range(3)]
     torch.cuda.synchronize()

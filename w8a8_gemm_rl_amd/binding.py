@@ -46,10 +46,11 @@ _SIGS = {
     "qr_w8a8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _sz, _vp]),
     "qr_linear_fused": (_int, [_vp, _i64, _f32, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _sz, _vp]),
     "qr_workspace_size": (_sz, [ctypes.c_char_p, _i64, _i64, _i64, _int]),
-    "qr_gemm_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_int), ctypes.POINTER(_int)]),
+    "qr_gemm_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_int), ctypes.POINTER(_int),
+                            ctypes.POINTER(_int)]),
     "qr_tile_name": (ctypes.c_char_p, [_int]),
     "qr_num_tiles": (_int, []),
-    "qr_set_plan_override": (_int, [_int, _int]),
+    "qr_set_plan_override": (_int, [_int, _int, _int]),
     "qr_last_error": (ctypes.c_char_p, []),
     "qr_version": (ctypes.c_char_p, []),
 }
@@ -148,14 +149,16 @@ def tile_name(i):
     return None if r is None else r.decode()
 
 
-def set_plan_override(tile=-1, splitk=0):
-    _check("qr_set_plan_override", lib().qr_set_plan_override(tile, splitk))
+def set_plan_override(tile=-1, splitk=0, rows=0):
+    _check("qr_set_plan_override", lib().qr_set_plan_override(tile, splitk, rows))
 
 
 def gemm_plan(M, N, K, qt):
-    t, s = ctypes.c_int(), ctypes.c_int()
-    _check("qr_gemm_plan", lib().qr_gemm_plan(M, N, K, _qt(qt), ctypes.byref(t), ctypes.byref(s)))
-    return t.value, s.value
+    """(tile, splitk, rows) of the plan qr_w8a8_gemm uses for this shape."""
+    t, s, r = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check("qr_gemm_plan", lib().qr_gemm_plan(M, N, K, _qt(qt), ctypes.byref(t), ctypes.byref(s),
+                                              ctypes.byref(r)))
+    return t.value, s.value, r.value
 
 
 def workspace_size(fn, M, N, K, qt):

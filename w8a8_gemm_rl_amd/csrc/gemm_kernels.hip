@@ -12,12 +12,13 @@
 //    tiles), exact int32 accumulation. FP8 E4M3FN uses
 //    v_mfma_scale_f32_{16x16x128,32x32x64}_f8f6f4 with unit block scales
 //    (E8M0 127 = 2^0), accumulating in fp32.
-//  * A block owns a BN x BM macro tile and a contiguous range of K. Both
-//    operand tiles go global -> registers -> LDS. Global loads run two K
-//    steps ahead of the MFMAs (two register stages), LDS is double-buffered,
-//    and one barrier separates K steps. 16-byte LDS chunks are XOR-swizzled
-//    by row so the 16-byte fragment reads of the MFMA operands are free of
-//    bank conflicts.
+//  * A block owns a BN x BM macro tile (of which the first `rn` weight rows
+//    are its own) and a contiguous range of K. Four kernel families move the
+//    operands: register-staged (global -> registers -> LDS), LDS-DMA
+//    (global -> LDS with buffer_load ... lds, an S-slot ring), the same with
+//    dedicated copy waves, and direct (global -> MFMA registers, no LDS) for
+//    small token counts. 16-byte LDS chunks are XOR-swizzled by row so the
+//    16-byte fragment reads of the MFMA operands are free of bank conflicts.
 //  * Each lane feeds the MFMA a contiguous 16- or 32-byte run of K for its row.
 //    The K order inside one instruction is the same for A and B, so any lane
 //    placement of K gives the same dot product.
@@ -102,6 +103,7 @@ struct KParams {
   int vec;       // ldy % 4 == 0: four consecutive outputs may be stored as one vector
   int splitk;
   int tiles_n, tiles_m, nks;
+  int rn;  // weight rows per tile: a multiple of 8, at most the tile's BN
 };
 
 // XOR swizzle of the 16-byte chunk index inside an LDS row. The LDS serves
@@ -122,6 +124,113 @@ __device__ __forceinline__ uint32_t epi_bf16(float a, float sx, float sw) {
   return f32_to_bf16_rne(y);
 }
 
+// Logical tile of this block. Blocks are dealt to the 8 XCDs round-robin,
+// so block b is renumbered to make runs of consecutive logical tiles (the K
+// splits of one output tile, then neighbouring token tiles of one weight
+// tile) land on one XCD and share its L2.
+__device__ __forceinline__ void block_tile(const KParams& p, int& tn, int& tm, int& z, int& ks0,
+                                           int& ks1) {
+  const int G = gridDim.x;
+  int b = blockIdx.x;
+  const int G8 = G & ~7;
+  if (b < G8) b = (b & 7) * (G8 >> 3) + (b >> 3);
+  z = b % p.splitk;
+  const int t2 = b / p.splitk;
+  tm = t2 % p.tiles_m;
+  tn = t2 / p.tiles_m;
+  ks0 = (int)(((int64_t)z * p.nks) / p.splitk);
+  ks1 = (int)(((int64_t)(z + 1) * p.nks) / p.splitk);
+}
+
+// ---- epilogue. Lane layout of an MFMA result: for T = 16 register r of
+// lane l is (i = 4*(l/16) + r, j = l%16); for T = 32 it is
+// (i = 8*(r/4) + 4*(l/32) + r%4, j = l%32). Four consecutive registers are
+// four consecutive output channels n of one token m. All scale loads are
+// issued together (buffer loads, zero outside the vectors), then the
+// outputs are converted and stored.
+template <int QT, int T, int BN, int BM, int WN, int WM, typename acc_t, int FN, int FM>
+__device__ __forceinline__ void store_tile(const KParams& p, const acc_t (&acc)[FN][FM], int tn,
+                                           int tm, int z, int wn, int wm, int lane) {
+  constexpr int WTN = BN / WN, WTM = BM / WM;
+  constexpr int NACC = Mfma<QT, T>::NACC;
+  constexpr uint32_t kOOB = 0x80000000u;
+  const int64_t N = p.N, M = p.M;
+  const bool split = p.splitk > 1;
+  const bool raw = split || p.out_raw;
+  constexpr int NG = NACC / 4;  // groups of four registers per fragment
+  const int jj = lane % T;
+  int64_t mrow[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) mrow[j] = (int64_t)tm * BM + wm * WTM + j * T + jj;
+  // Local output channel of register group g of fragment i. Rows at or past
+  // rn belong to the next tile (rn is a multiple of 8, so a group of four
+  // never straddles it).
+  auto nloc = [&](int i, int g) -> int {
+    const int ii = (T == 16) ? 4 * (lane / 16) : 8 * g + 4 * (lane / 32);
+    return wn * WTN + i * T + ii;
+  };
+  auto ncol = [&](int i, int g) -> int64_t { return (int64_t)tn * p.rn + nloc(i, g); };
+  float sxv[FM];
+  float swv[FN][NG][4];
+  if (!raw) {
+    const __amdgpu_buffer_rsrc_t rsx_ = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.sx, (short)0, (int)(uint32_t)(M * 4), kBufWord3);
+    const __amdgpu_buffer_rsrc_t rsw_ = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.sw, (short)0, (int)(uint32_t)(N * 4), kBufWord3);
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+      sxv[j] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+          rsx_, mrow[j] < M ? (int)(mrow[j] * 4) : (int)kOOB, 0, 0));
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int64_t n0 = ncol(i, g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          swv[i][g][e] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+              rsw_, n0 + e < N ? (int)((n0 + e) * 4) : (int)kOOB, 0, 0));
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int r = 4 * g;
+        const int64_t n0 = ncol(i, g);
+        const int64_t m = mrow[j];
+        if (m >= M || n0 >= N || nloc(i, g) >= p.rn) continue;
+        const bool full4 = p.vec && n0 + 3 < N;
+        if (raw) {
+          // int32 or fp32 words, 16 bytes when four outputs fit
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (QT == kQInt8) w[e] = (uint32_t)acc[i][j][r + e];
+            else w[e] = __float_as_uint(acc[i][j][r + e]);
+          }
+          uint32_t* y = static_cast<uint32_t*>(p.Y) + (split ? (int64_t)z * M * N : 0) + m * p.ldy + n0;
+          if (full4) {
+            *reinterpret_cast<uint4*>(y) = make_uint4(w[0], w[1], w[2], w[3]);
+          } else {
+            for (int e = 0; e < 4 && n0 + e < N; ++e) y[e] = w[e];
+          }
+        } else {
+          uint32_t bb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bb[e] = epi_bf16((float)acc[i][j][r + e], sxv[j], swv[i][g][e]);
+          uint16_t* y = static_cast<uint16_t*>(p.Y) + m * p.ldy + n0;
+          if (full4) {
+            *reinterpret_cast<uint2*>(y) = make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
+          } else {
+            for (int e = 0; e < 4 && n0 + e < N; ++e) y[e] = (uint16_t)bb[e];
+          }
+        }
+      }
+}
+
 template <int QT, int T, int BN, int BM, int BK, int WN, int WM>
 __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_kernel(const KParams p) {
   using MF = Mfma<QT, T>;
@@ -134,7 +243,6 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_kernel(const KParams p) 
   constexpr int RSTEP = NT / CPR;   // rows between one thread's consecutive chunks
   constexpr int CA = BN * CPR, CB = BM * CPR;
   constexpr int LA = (CA + NT - 1) / NT, LBn = (CB + NT - 1) / NT;
-  constexpr int NACC = MF::NACC;
   constexpr int KI = MF::KI, LB = MF::LB;
   constexpr int NKK = BK / KI;
   constexpr int STAGE = (BN + BM) * BK;
@@ -145,17 +253,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_kernel(const KParams p) 
 
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
-  // ---- logical tile of this block (XCD-aware, see the file comment)
-  const int G = gridDim.x;
-  int b = blockIdx.x;
-  const int G8 = G & ~7;
-  if (b < G8) b = (b & 7) * (G8 >> 3) + (b >> 3);
-  const int z = b % p.splitk;
-  const int t2 = b / p.splitk;
-  const int tm = t2 % p.tiles_m;
-  const int tn = t2 / p.tiles_m;
-  const int ks0 = (int)(((int64_t)z * p.nks) / p.splitk);
-  const int ks1 = (int)(((int64_t)(z + 1) * p.nks) / p.splitk);
+  int tn, tm, z, ks0, ks1;
+  block_tile(p, tn, tm, z, ks0, ks1);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -186,8 +285,9 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_kernel(const KParams p) 
   uint32_t oa[LA], ob[LBn];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    const int64_t row = (int64_t)tn * BN + r_ld + i * RSTEP;
-    oa[i] = row < N ? (uint32_t)(row * K + c_ld * 16) : kOOB;
+    const int r = r_ld + i * RSTEP;
+    const int64_t row = (int64_t)tn * p.rn + r;
+    oa[i] = (r < p.rn && row < N) ? (uint32_t)(row * K + c_ld * 16) : kOOB;
   }
 #pragma unroll
   for (int i = 0; i < LBn; ++i) {
@@ -305,82 +405,586 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_kernel(const KParams p) 
     }
   }
 
-  // ---- epilogue. Lane layout of an MFMA result: for T = 16 register r of
-  // lane l is (i = 4*(l/16) + r, j = l%16); for T = 32 it is
-  // (i = 8*(r/4) + 4*(l/32) + r%4, j = l%32). Four consecutive registers are
-  // four consecutive output channels n of one token m. All scale loads are
-  // issued together (buffer loads, zero outside the vectors), then the
-  // outputs are converted and stored.
-  const bool split = p.splitk > 1;
-  const bool raw = split || p.out_raw;
-  constexpr int NG = NACC / 4;  // groups of four registers per fragment
-  const int jj = lane % T;
-  int64_t mrow[FM];
-#pragma unroll
-  for (int j = 0; j < FM; ++j) mrow[j] = (int64_t)tm * BM + wm * WTM + j * T + jj;
-  auto ncol = [&](int i, int g) -> int64_t {
-    const int ii = (T == 16) ? 4 * (lane / 16) : 8 * g + 4 * (lane / 32);
-    return (int64_t)tn * BN + wn * WTN + i * T + ii;
-  };
-  float sxv[FM];
-  float swv[FN][NG][4];
-  if (!raw) {
-    const __amdgpu_buffer_rsrc_t rsx_ = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)p.sx, (short)0, (int)(uint32_t)(M * 4), kBufWord3);
-    const __amdgpu_buffer_rsrc_t rsw_ = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)p.sw, (short)0, (int)(uint32_t)(N * 4), kBufWord3);
-#pragma unroll
-    for (int j = 0; j < FM; ++j)
-      sxv[j] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-          rsx_, mrow[j] < M ? (int)(mrow[j] * 4) : (int)kOOB, 0, 0));
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int64_t n0 = ncol(i, g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          swv[i][g][e] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-              rsw_, n0 + e < N ? (int)((n0 + e) * 4) : (int)kOOB, 0, 0));
-      }
+  store_tile<QT, T, BN, BM, WN, WM>(p, acc, tn, tm, z, wn, wm, lane);
+}
+
+// ---------------------------------------------------------------------------
+// LDS-DMA variant. Operand tiles move from global memory straight into LDS
+// with buffer_load_dwordx4 ... lds: one wave instruction writes 64 x 16
+// bytes to LDS at M0 + offset + 16 * lane, where the 12-bit instruction
+// offset also advances the global address. A wave's copies go to
+// consecutive 1 KB LDS blocks, so up to four share one M0 write (offsets 0,
+// 1 KB, 2 KB, 3 KB; the per-lane global offsets are pre-biased by minus the
+// instruction offset). An S-slot LDS ring keeps S - 1 K steps in flight;
+// each wave waits for its own copies with an explicit vmcnt and one barrier
+// per K step publishes them (and frees the slot the next copies overwrite).
+// The copies of step it + S - 1 are issued in groups between the MFMA
+// sub-steps of step it, so their issue overlaps the matrix work. The
+// swizzle is applied on the global side: the lane that owns physical chunk
+// c of LDS row r fetches logical chunk c ^ swz(r).
+// ---------------------------------------------------------------------------
+template <int CNT>
+__device__ __forceinline__ void dma_group(uint32_t lds_addr, const uint32_t* vo,
+                                          __amdgpu_buffer_rsrc_t r, int soff) {
+  static_assert(CNT >= 1 && CNT <= 4, "one M0 covers at most 4 KB of offsets");
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  if constexpr (CNT == 1)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(lds_addr), "v"(vo[0]), "s"(r), "s"(soff)
+        : "memory", "m0");
+  else if constexpr (CNT == 2)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds"
+        :
+        : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "s"(r), "s"(soff)
+        : "memory", "m0");
+  else if constexpr (CNT == 3)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %4, %5 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %4, %5 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %3, %4, %5 offen offset:2048 lds"
+        :
+        : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "s"(r), "s"(soff)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
+        "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
+        "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
+        :
+        : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(r), "s"(soff)
+        : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// Single-copy form (M0 per copy), used by the warp-specialized kernel.
+__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, __amdgpu_buffer_rsrc_t r,
+                                      int soff) {
+  dma_group<1>(lds_addr, &voff, r, soff);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most min(ahead, A) stages of this wave's copies (NI
+// instructions each) are still in flight; A = S - 2 is the most a ring of S
+// slots ever has outstanding behind the step being consumed.
+template <int NI, int A>
+__device__ __forceinline__ void wait_stages(int ahead) {
+  if constexpr (A > 0) {
+    if (ahead >= A) {
+      wait_vm<A * NI>();
+      return;
+    }
+    wait_stages<NI, A - 1>(ahead);
+  } else {
+    wait_vm<0>();
   }
+}
+
+template <int QT, int T, int BN, int BM, int WN, int WM, int S>
+__global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams p) {
+  using MF = Mfma<QT, T>;
+  using acc_t = typename MF::acc_t;
+  using op_t = typename MF::op_t;
+  constexpr int BK = 128;
+  constexpr int NW = WN * WM;
+  constexpr int WTN = BN / WN, WTM = BM / WM;
+  constexpr int FN = WTN / T, FM = WTM / T;
+  constexpr int KI = MF::KI, LB = MF::LB;
+  constexpr int NKK = BK / KI;
+  // 1 KB row blocks (8 rows of 128 bytes) per stage; the token part is
+  // padded so every wave issues the same number of copies.
+  constexpr int IA = BN / 8;
+  constexpr int IB0 = BM / 8;
+  constexpr int IB = IB0 + (NW - IB0 % NW) % NW;
+  constexpr int NA = IA / NW, NB = IB / NW, NI = NA + NB;
+  constexpr int GA = (NA + 3) / 4, GB = (NB + 3) / 4, NG = GA + GB;  // M0 groups
+  constexpr int STAGE = (IA + IB) * 1024;
+  static_assert(BN % 8 == 0 && BM % 8 == 0 && IA % NW == 0, "row blocks per wave");
+  static_assert(WTN % T == 0 && WTM % T == 0, "wave tile");
+  static_assert(S >= 2 && S <= 8 && (S - 2) * NI <= 63, "ring depth");
+  static_assert(S * STAGE <= 160 * 1024, "LDS");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+
+  int tn, tm, z, ks0, ks1;
+  block_tile(p, tn, tm, z, ks0, ks1);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wid % WN, wm = wid / WN;
+  const int64_t N = p.N, M = p.M, K = p.K;
+
+  acc_t acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
+    for (int j = 0; j < FM; ++j) acc[i][j] = acc_t{};
+
+  // ---- copy addressing. Wave wid moves weight row blocks wid*NA + i and
+  // token row blocks wid*NB + i. Lane l covers row 8*rb + l/8 of the block,
+  // physical chunk l%8. Rows past the tile (rn), past N or M, or in the
+  // padded token rows point at offset 2^31 (beyond any code matrix, which is
+  // kept below 2^31 - 2^16 bytes so the bias below stays out of range) and
+  // read as zero. Offsets are biased by -1 KB * (i % 4), the instruction
+  // offset of copy i within its M0 group.
+  constexpr uint32_t kOOB = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t rsw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.Wq, (short)0, (int)(uint32_t)(N * K), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rsx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.Xq, (short)0, (int)(uint32_t)(M * K), kBufWord3);
+  const int lrow = lane >> 3, pch = lane & 7;
+  uint32_t oa[NA], ob[NB];
+  bool ka[NA], kb[NB];  // copy i holds real K bytes on the ragged last step
+  const bool ktail = (K % BK) != 0;
+  const int krem = (int)(K % BK);
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int r = 4 * g;
-        const int64_t n0 = ncol(i, g);
-        const int64_t m = mrow[j];
-        if (m >= M || n0 >= N) continue;
-        const bool full4 = p.vec && n0 + 3 < N;
-        if (raw) {
-          // int32 or fp32 words, 16 bytes when four outputs fit
-          uint32_t w[4];
+  for (int i = 0; i < NA; ++i) {
+    const int r = (wid * NA + i) * 8 + lrow;
+    const int c = pch ^ swz<BK>(r);
+    const int64_t row = (int64_t)tn * p.rn + r;
+    const uint32_t bias = 1024u * (uint32_t)(i % 4);
+    ka[i] = c * 16 < krem;
+    oa[i] = ((r < p.rn && row < N) ? (uint32_t)(row * K + c * 16) : kOOB) - bias;
+  }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if constexpr (QT == kQInt8) w[e] = (uint32_t)acc[i][j][r + e];
-            else w[e] = __float_as_uint(acc[i][j][r + e]);
-          }
-          uint32_t* y = static_cast<uint32_t*>(p.Y) + (split ? (int64_t)z * M * N : 0) + m * p.ldy + n0;
-          if (full4) {
-            *reinterpret_cast<uint4*>(y) = make_uint4(w[0], w[1], w[2], w[3]);
-          } else {
-            for (int e = 0; e < 4 && n0 + e < N; ++e) y[e] = w[e];
-          }
-        } else {
-          uint32_t bb[4];
+  for (int i = 0; i < NB; ++i) {
+    const int r = (wid * NB + i) * 8 + lrow;
+    const int c = pch ^ swz<BK>(r);
+    const int64_t row = (int64_t)tm * BM + r;
+    const uint32_t bias = 1024u * (uint32_t)(i % 4);
+    kb[i] = c * 16 < krem;
+    ob[i] = ((r < BM && row < M) ? (uint32_t)(row * K + c * 16) : kOOB) - bias;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const uint32_t la0 = lds0 + (uint32_t)(wid * NA) * 1024u;
+  const uint32_t lb0 = lds0 + (uint32_t)(IA + wid * NB) * 1024u;
+  const bool small_k = K < BK;
+
+  // Issue M0 group g (0 <= g < NG) of the copies of K step ks into `slot`.
+  auto issue_group = [&](int g, int slot, int ks) {
+    const int soff = ks * BK;
+    const uint32_t so = (uint32_t)(slot * STAGE);
+    const bool tail = ktail && ks + 1 == p.nks;
+    const bool isA = g < GA;
+    const int i0 = (isA ? g : g - GA) * 4;
+    const uint32_t base = (isA ? la0 : lb0) + so + (uint32_t)i0 * 1024u;
+    uint32_t vo[4];
+    auto run = [&](auto cnt_c) {
+      constexpr int C = decltype(cnt_c)::value;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bb[e] = epi_bf16((float)acc[i][j][r + e], sxv[j], swv[i][g][e]);
-          uint16_t* y = static_cast<uint16_t*>(p.Y) + m * p.ldy + n0;
-          if (full4) {
-            *reinterpret_cast<uint2*>(y) = make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
-          } else {
-            for (int e = 0; e < 4 && n0 + e < N; ++e) y[e] = (uint16_t)bb[e];
-          }
-        }
+      for (int e = 0; e < C; ++e) {
+        const int i = i0 + e;
+        const uint32_t o = isA ? oa[i] : ob[i];
+        const bool k_ok = isA ? ka[i] : kb[i];
+        vo[e] = (!tail || k_ok) ? o : kOOB - 1024u * (uint32_t)e;
       }
+      if (small_k) {
+        // K < 128: the first rows' biased offsets would wrap below zero, so
+        // each copy gets its own M0 and an unbiased offset.
+#pragma unroll
+        for (int e = 0; e < C; ++e) {
+          const uint32_t u = vo[e] + 1024u * (uint32_t)e;
+          dma_group<1>(base + 1024u * (uint32_t)e, &u, isA ? rsw : rsx, soff);
+        }
+      } else {
+        dma_group<C>(base, vo, isA ? rsw : rsx, soff);
+      }
+    };
+    const int cnt = isA ? (NA - i0 < 4 ? NA - i0 : 4) : (NB - i0 < 4 ? NB - i0 : 4);
+    if (cnt == 4) run(std::integral_constant<int, 4>{});
+    else if (cnt == 3) run(std::integral_constant<int, 3>{});
+    else if (cnt == 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 1>{});
+  };
+  auto issue_all = [&](int slot, int ks) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) issue_group(g, slot, ks);
+  };
+
+  // ---- MFMA fragment reads
+  const int lr = lane % T;
+  const int lg = (lane / T) * (LB / 16);
+  const int sl = swz<BK>(lr);
+  const int rbaseA = (wn * WTN + lr) * BK;
+  const int rbaseB = IA * 1024 + (wm * WTM + lr) * BK;
+  int xo0[NKK], xo1[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int c0 = kk * (KI / 16) + lg;
+    xo0[kk] = (c0 ^ sl) << 4;
+    xo1[kk] = ((c0 + 1) ^ sl) << 4;
+  }
+  auto lds_op = [&](const uint8_t* base, int kk) -> op_t {
+    const uint4 u0 = *reinterpret_cast<const uint4*>(base + xo0[kk]);
+    if constexpr (LB == 16) {
+      return op_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w};
+    } else {
+      const uint4 u1 = *reinterpret_cast<const uint4*>(base + xo1[kk]);
+      return op_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                  (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+    }
+  };
+  // MFMAs of one K step; the copy groups of a later step (if any) are
+  // spread over its NKK sub-steps.
+  auto compute = [&](int slot, bool do_issue, int islot, int iks) {
+    const uint8_t* A = smem + slot * STAGE + rbaseA;
+    const uint8_t* B = smem + slot * STAGE + rbaseB;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      op_t a[FN], bb[FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) a[i] = lds_op(A + i * T * BK, kk);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) bb[j] = lds_op(B + j * T * BK, kk);
+      if (do_issue) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          if (g * NKK / NG == kk) issue_group(g, islot, iks);
+      }
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = MF::run(a[i], bb[j], acc[i][j]);
+    }
+  };
+
+  // ---- main loop. K step ks0 + it lives in slot it % S. At the top of step
+  // it the copies of steps up to it + S - 2 have been issued; this wave
+  // waits for its copies of step it, the barrier makes every wave's copies
+  // visible and guarantees slot (it - 1) % S is no longer read, and the
+  // copies of step it + S - 1 go into that slot while the MFMAs of step it
+  // run.
+  const int nk = ks1 - ks0;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue_all(s, ks0 + s);
+  int cs = 0, is = S - 1;
+  for (int it = 0; it < nk; ++it) {
+    const int ahead = nk - 1 - it;
+    wait_stages<NI, S - 2>(ahead);
+    __syncthreads();
+    compute(cs, it + S - 1 < nk, is, ks0 + it + S - 1);
+    cs = cs + 1 == S ? 0 : cs + 1;
+    is = is + 1 == S ? 0 : is + 1;
+  }
+
+  store_tile<QT, T, BN, BM, WN, WM>(p, acc, tn, tm, z, wn, wm, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Warp-specialized LDS-DMA variant. NP producer waves only issue the LDS DMA
+// copies; WN x WM consumer waves only read LDS and run the MFMAs. With one
+// barrier per K step the copy issue of step it + S - 1 (bound by the
+// texture-address unit, 1 KB per instruction) overlaps the MFMAs of step it
+// instead of following them. Producers skip 8-row blocks that hold no valid
+// row (tiles that own fewer than BN weight rows, token tiles past M), so
+// their per-step copy count is a block-uniform runtime value and their
+// vmcnt waits use a runtime-selected immediate.
+// ---------------------------------------------------------------------------
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_rt(int x) {
+  if constexpr (LO == HI) {
+    wait_vm<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (x <= MID) wait_vm_rt<LO, MID>(x);
+    else wait_vm_rt<MID + 1, HI>(x);
+  }
+}
+
+template <int QT, int T, int BN, int BM, int WN, int WM, int NP, int S>
+__global__ __launch_bounds__(64 * (WN * WM + NP), 1) void gemm_ws_kernel(const KParams p) {
+  using MF = Mfma<QT, T>;
+  using acc_t = typename MF::acc_t;
+  using op_t = typename MF::op_t;
+  constexpr int BK = 128;
+  constexpr int NC = WN * WM;
+  constexpr int WTN = BN / WN, WTM = BM / WM;
+  constexpr int FN = WTN / T, FM = WTM / T;
+  constexpr int KI = MF::KI, LB = MF::LB;
+  constexpr int NKK = BK / KI;
+  constexpr int IA = BN / 8, IB = BM / 8;
+  constexpr int MAXJ = (IA + NP - 1) / NP + (IB + NP - 1) / NP;  // copies per producer per stage
+  constexpr int STAGE = (IA + IB) * 1024;
+  static_assert(BN % 8 == 0 && BM % 8 == 0, "8-row copy blocks");
+  static_assert(WTN % T == 0 && WTM % T == 0, "wave tile");
+  static_assert(S >= 2 && S <= 8 && (S - 2) * MAXJ <= 63, "ring depth vs vmcnt");
+  static_assert(S * STAGE <= 160 * 1024, "LDS");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+
+  int tn, tm, z, ks0, ks1;
+  block_tile(p, tn, tm, z, ks0, ks1);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool producer = wid >= NC;
+  const int64_t N = p.N, M = p.M, K = p.K;
+  // Valid rows of this tile: weight rows [tn * rn, tn * rn + limA), token
+  // rows [tm * BM, tm * BM + limB).
+  const int limA = (int)((N - (int64_t)tn * p.rn) < p.rn ? (N - (int64_t)tn * p.rn) : p.rn);
+  const int limB = (int)((M - (int64_t)tm * BM) < BM ? (M - (int64_t)tm * BM) : BM);
+  const int nA = (limA + 7) >> 3, nB = (limB + 7) >> 3;
+  const int nk = ks1 - ks0;
+  const bool ktail = (K % BK) != 0;
+  const int krem = (int)(K % BK);
+  constexpr uint32_t kOOB = 0x80000000u;
+
+  if (producer) {
+    // ---- copy issue. Producer pi moves row blocks j = pi, pi + NP, ... of
+    // each operand. Lane l covers row 8 j + l/8, physical chunk l % 8, and
+    // fetches logical chunk (l % 8) ^ swz(row); swz depends on the row's bits
+    // 1..3, i.e. on j & 1 and l / 16.
+    const int pi = wid - NC;
+    const int cntA = nA > pi ? (nA - pi + NP - 1) / NP : 0;
+    const int cntB = nB > pi ? (nB - pi + NP - 1) / NP : 0;
+    const int cnt = cntA + cntB;
+    const __amdgpu_buffer_rsrc_t rsw =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.Wq, (short)0, (int)(uint32_t)(N * K), kBufWord3);
+    const __amdgpu_buffer_rsrc_t rsx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.Xq, (short)0, (int)(uint32_t)(M * K), kBufWord3);
+    const int lrow = lane >> 3;
+    const int c0 = (lane & 7) ^ (lane >> 4);        // chunk for even j
+    const int c1 = (lane & 7) ^ (4 + (lane >> 4));  // chunk for odd j (swz differs by 4)
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+    const int64_t baseA = (int64_t)tn * p.rn;
+    const int64_t baseB = (int64_t)tm * BM;
+
+    auto issue = [&](int slot, int ks) {
+      const int soff = ks * BK;
+      const bool tail = ktail && ks + 1 == p.nks;
+      const uint32_t so = lds0 + (uint32_t)(slot * STAGE);
+      for (int j = pi; j < nA; j += NP) {
+        const int r = j * 8 + lrow;
+        const int c = (j & 1) ? c1 : c0;
+        const bool ok = r < limA && (!tail || c * 16 < krem);
+        const uint32_t vo = ok ? (uint32_t)((baseA + r) * K + c * 16) : kOOB;
+        dma16(so + j * 1024, vo, rsw, soff);
+      }
+      for (int j = pi; j < nB; j += NP) {
+        const int r = j * 8 + lrow;
+        const int c = (j & 1) ? c1 : c0;
+        const bool ok = r < limB && (!tail || c * 16 < krem);
+        const uint32_t vo = ok ? (uint32_t)((baseB + r) * K + c * 16) : kOOB;
+        dma16(so + IA * 1024 + j * 1024, vo, rsx, soff);
+      }
+    };
+
+    for (int s = 0; s < S - 1; ++s)
+      if (s < nk) issue(s, ks0 + s);
+    int is = S - 1;
+    for (int it = 0; it < nk; ++it) {
+      // stage it must have landed; later issued stages may stay in flight
+      const int behind = (nk - 1 - it) < (S - 2) ? (nk - 1 - it) : (S - 2);
+      const int allow = behind * cnt;
+      wait_vm_rt<0, 63>(allow > 63 ? 63 : allow);
+      __syncthreads();
+      if (it + S - 1 < nk) issue(is, ks0 + it + S - 1);
+      is = is + 1 == S ? 0 : is + 1;
+    }
+    return;
+  }
+
+  // ---- consumers
+  const int wn = wid % WN, wm = wid / WN;
+  const bool active = wn * WTN < limA && wm * WTM < limB;
+  acc_t acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = acc_t{};
+
+  const int lr = lane % T;
+  const int lg = (lane / T) * (LB / 16);
+  const int sl = swz<BK>(lr);
+  const int rbaseA = (wn * WTN + lr) * BK;
+  const int rbaseB = IA * 1024 + (wm * WTM + lr) * BK;
+  int xo0[NKK], xo1[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int cc = kk * (KI / 16) + lg;
+    xo0[kk] = (cc ^ sl) << 4;
+    xo1[kk] = ((cc + 1) ^ sl) << 4;
+  }
+  auto lds_op = [&](const uint8_t* base, int kk) -> op_t {
+    const uint4 u0 = *reinterpret_cast<const uint4*>(base + xo0[kk]);
+    if constexpr (LB == 16) {
+      return op_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w};
+    } else {
+      const uint4 u1 = *reinterpret_cast<const uint4*>(base + xo1[kk]);
+      return op_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
+                  (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+    }
+  };
+  auto compute = [&](int slot) {
+    const uint8_t* A = smem + slot * STAGE + rbaseA;
+    const uint8_t* B = smem + slot * STAGE + rbaseB;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      op_t a[FN], bb[FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) a[i] = lds_op(A + i * T * BK, kk);
+#pragma unroll
+      for (int j = 0; j < FM; ++j) bb[j] = lds_op(B + j * T * BK, kk);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = MF::run(a[i], bb[j], acc[i][j]);
+    }
+  };
+  int cs = 0;
+  for (int it = 0; it < nk; ++it) {
+    __syncthreads();
+    if (active) compute(cs);
+    cs = cs + 1 == S ? 0 : cs + 1;
+  }
+  if (active) store_tile<QT, T, BN, BM, WN, WM>(p, acc, tn, tm, z, wn, wm, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Direct (LDS-free) variant for small token counts, where the product is a
+// weight stream. Every wave owns 16 * FN weight rows and all BM tokens of
+// the tile and loads its MFMA operands straight from global memory into
+// registers, D K steps ahead (a register ring, unrolled so stage indices
+// are compile-time constants). There is no LDS and no barrier, so waves
+// never wait for each other and the hardware interleaves many of them per
+// SIMD. Lane l of a 16x16 fragment holds row l % 16 and the 32 bytes
+// [32 (l / 16), 32 (l / 16) + 32) of each 128-byte K step: the first 16
+// feed the INT8 MFMA of half-step 0 and the next 16 that of half-step 1
+// (the FP8 MFMA takes all 32 at once). A and B use the same K placement.
+// ---------------------------------------------------------------------------
+template <int QT, int BN, int BM, int WPB, int D>
+__global__ __launch_bounds__(64 * WPB, 1) void gemm_direct_kernel(const KParams p) {
+  constexpr int T = 16;
+  using MF = Mfma<QT, T>;
+  using acc_t = typename MF::acc_t;
+  constexpr int FN = BN / (16 * WPB), FM = BM / 16;
+  static_assert(FN * 16 * WPB == BN && FM * 16 == BM && FN >= 1 && FM >= 1, "direct tile");
+  static_assert(D >= 1 && D <= 8, "prefetch depth");
+
+  int tn, tm, z, ks0, ks1;
+  block_tile(p, tn, tm, z, ks0, ks1);
+  const int lane = threadIdx.x & 63;
+  const int wn = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t N = p.N, M = p.M, K = p.K;
+  constexpr uint32_t kOOB = 0x80000000u;
+  const int limA = (int)((N - (int64_t)tn * p.rn) < p.rn ? (N - (int64_t)tn * p.rn) : p.rn);
+  const int r0 = wn * 16 * FN;  // first local row of this wave
+  if (r0 >= limA) return;       // no valid row: nothing to load or store
+
+  const __amdgpu_buffer_rsrc_t rsw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.Wq, (short)0, (int)(uint32_t)(N * K), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rsx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.Xq, (short)0, (int)(uint32_t)(M * K), kBufWord3);
+  const int lrow = lane & 15, g = lane >> 4;
+  uint32_t oa[FN], ob[FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    const int r = r0 + i * 16 + lrow;
+    const int64_t row = (int64_t)tn * p.rn + r;
+    oa[i] = (r < limA) ? (uint32_t)(row * K + g * 32) : kOOB;
+  }
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int64_t row = (int64_t)tm * BM + j * 16 + lrow;
+    ob[j] = row < M ? (uint32_t)(row * K + g * 32) : kOOB;
+  }
+  const bool ktail = (K % 128) != 0;
+  const int krem = (int)(K % 128);
+  // In the ragged last step, 16-byte half h of this lane is valid when
+  // 32 g + 16 h < krem.
+  const bool h0 = g * 32 < krem, h1 = g * 32 + 16 < krem;
+
+  acc_t acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = acc_t{};
+
+  uint4 ra[D][FN][2], rb[D][FM][2];
+  auto ld = [&](__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) -> uint4 {
+    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+  };
+  auto load = [&](uint4 (&a)[FN][2], uint4 (&b)[FM][2], int ks) {
+    const int soff = ks * 128;
+    if (!ktail || ks + 1 < p.nks) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        a[i][0] = ld(rsw, oa[i], soff);
+        a[i][1] = ld(rsw, oa[i] + 16, soff);
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        b[j][0] = ld(rsx, ob[j], soff);
+        b[j][1] = ld(rsx, ob[j] + 16, soff);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        a[i][0] = ld(rsw, h0 ? oa[i] : kOOB, soff);
+        a[i][1] = ld(rsw, h1 ? oa[i] + 16 : kOOB, soff);
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        b[j][0] = ld(rsx, h0 ? ob[j] : kOOB, soff);
+        b[j][1] = ld(rsx, h1 ? ob[j] + 16 : kOOB, soff);
+      }
+    }
+  };
+  auto op16 = [](const uint4& u) -> v4i { return v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w}; };
+  auto compute = [&](const uint4 (&a)[FN][2], const uint4 (&b)[FM][2]) {
+    if constexpr (QT == kQInt8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+          for (int j = 0; j < FM; ++j) acc[i][j] = MF::run(op16(a[i][h]), op16(b[j][h]), acc[i][j]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const v8i av{(int)a[i][0].x, (int)a[i][0].y, (int)a[i][0].z, (int)a[i][0].w,
+                       (int)a[i][1].x, (int)a[i][1].y, (int)a[i][1].z, (int)a[i][1].w};
+          const v8i bv{(int)b[j][0].x, (int)b[j][0].y, (int)b[j][0].z, (int)b[j][0].w,
+                       (int)b[j][1].x, (int)b[j][1].y, (int)b[j][1].z, (int)b[j][1].w};
+          acc[i][j] = MF::run(av, bv, acc[i][j]);
+        }
+    }
+  };
+
+  const int nk = ks1 - ks0;
+#pragma unroll
+  for (int s = 0; s < D; ++s)
+    if (s < nk) load(ra[s], rb[s], ks0 + s);
+  for (int it = 0; it < nk; it += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      if (it + s < nk) {
+        compute(ra[s], rb[s]);
+        if (it + s + D < nk) load(ra[s], rb[s], ks0 + it + s + D);
+      }
+    }
+  }
+  store_tile<QT, T, BN, BM, WPB, 1>(p, acc, tn, tm, z, wn, 0, lane);
 }
 
 // Split-K second pass: Y[m, n] = epilogue(sum_{z = 0..S-1} part[z][m][n]),
@@ -439,32 +1043,91 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
 
 // ---------------------------------------------------------------------------
 // Tile table. Order matters: the planner and the tuning hook refer to tiles
-// by index. (T, BN, BM, BK, WN, WM): MFMA edge, macro tile over N and M,
-// K bytes per stage, waves along N and M.
+// by index. (KIND, S, T, BN, BM, WN, WM, NP): KIND 0 is the register-staged
+// kernel (two register stages, two LDS buffers), 1 the LDS-DMA kernel and 2
+// the warp-specialized LDS-DMA kernel, both with an S-slot ring; T is the
+// MFMA edge, BN x BM the macro tile over N and M, WN x WM the MFMA waves
+// along N and M, NP the copy (producer) waves. Every stage holds 128 bytes
+// of K.
 // ---------------------------------------------------------------------------
-#define QR_TILES(X)                                          \
-  X(16, 64, 16, 128, 4, 1)   /* 0: M <= 16, weight streaming */ \
-  X(16, 32, 16, 128, 2, 1)   /* 1: M <= 16, narrow          */ \
-  X(32, 128, 32, 128, 4, 1)  /* 2: M <= 32                  */ \
-  X(32, 64, 64, 128, 2, 2)   /* 3: M <= 64                  */ \
-  X(32, 128, 64, 128, 2, 2)  /* 4: M <= 64, wide            */ \
-  X(32, 64, 128, 128, 2, 2)  /* 5: M <= 128                 */ \
-  X(32, 128, 128, 128, 2, 2) /* 6: M <= 128, wide           */ \
-  X(32, 64, 256, 128, 1, 4)  /* 7: M = 256 decode           */ \
-  X(32, 128, 256, 128, 2, 2) /* 8: M = 256 decode, wide     */ \
-  X(32, 256, 128, 128, 2, 2) /* 9: large M                  */ \
-  X(32, 256, 256, 128, 2, 4) /* 10: large M, 8 waves        */
+#define QR_TILES(X)                                                     \
+  X(0, 0, 16, 64, 16, 4, 1, 0)   /*  0: M <= 16, weight streaming  */ \
+  X(0, 0, 16, 32, 16, 2, 1, 0)   /*  1: M <= 16, narrow            */ \
+  X(0, 0, 32, 128, 32, 4, 1, 0)  /*  2: M <= 32                    */ \
+  X(0, 0, 32, 64, 64, 2, 2, 0)   /*  3: M <= 64                    */ \
+  X(0, 0, 32, 128, 64, 2, 2, 0)  /*  4: M <= 64, wide              */ \
+  X(0, 0, 32, 64, 128, 2, 2, 0)  /*  5: M <= 128                   */ \
+  X(0, 0, 32, 128, 128, 2, 2, 0) /*  6: M <= 128, wide             */ \
+  X(0, 0, 32, 64, 256, 1, 4, 0)  /*  7: M = 256                    */ \
+  X(0, 0, 32, 128, 256, 2, 2, 0) /*  8: M = 256, wide              */ \
+  X(0, 0, 32, 256, 128, 2, 2, 0) /*  9: large M                    */ \
+  X(0, 0, 32, 256, 256, 2, 4, 0) /* 10: large M, 8 waves           */ \
+  X(1, 4, 16, 64, 16, 4, 1, 0)   /* 11: DMA, M <= 16               */ \
+  X(1, 4, 16, 128, 16, 4, 1, 0)  /* 12: DMA, M <= 16, wide         */ \
+  X(1, 4, 32, 128, 32, 4, 1, 0)  /* 13: DMA, M <= 32               */ \
+  X(1, 4, 32, 256, 32, 4, 1, 0)  /* 14: DMA, M <= 32, wide         */ \
+  X(1, 4, 32, 128, 64, 2, 2, 0)  /* 15: DMA, M <= 64               */ \
+  X(1, 4, 32, 128, 128, 2, 2, 0) /* 16: DMA, M <= 128              */ \
+  X(1, 4, 32, 64, 128, 2, 2, 0)  /* 17: DMA, M <= 128, narrow      */ \
+  X(1, 3, 32, 256, 128, 2, 2, 0) /* 18: DMA, large M               */ \
+  X(1, 2, 32, 256, 256, 2, 4, 0) /* 19: DMA, large M, 8 waves      */ \
+  X(1, 3, 32, 128, 256, 2, 2, 0) /* 20: DMA, M = 256               */ \
+  X(1, 4, 32, 64, 256, 1, 4, 0)  /* 21: DMA, M = 256, narrow       */ \
+  X(1, 8, 32, 128, 32, 4, 1, 0)  /* 22: DMA deep ring, M <= 32     */ \
+  X(1, 8, 16, 128, 16, 4, 1, 0)  /* 23: DMA deep ring, M <= 16     */ \
+  X(1, 6, 32, 128, 64, 2, 2, 0)  /* 24: DMA deep ring, M <= 64     */ \
+  X(1, 5, 32, 128, 128, 2, 2, 0) /* 25: DMA deep ring, M <= 128    */ \
+  X(1, 8, 16, 64, 16, 4, 1, 0)   /* 26: DMA deep ring, narrow      */ \
+  X(1, 8, 32, 64, 32, 2, 1, 0)   /* 27: DMA deep ring, 2 waves     */ \
+  X(2, 6, 16, 128, 16, 4, 1, 2)  /* 28: WS, M <= 16                */ \
+  X(2, 5, 32, 128, 32, 4, 1, 1)  /* 29: WS, M <= 32                */ \
+  X(2, 4, 32, 128, 64, 2, 2, 1)  /* 30: WS, M <= 64                */ \
+  X(2, 4, 32, 128, 128, 2, 2, 2) /* 31: WS, M <= 128               */ \
+  X(2, 3, 32, 96, 256, 1, 4, 2)  /* 32: WS, M = 256, 96-row tiles  */ \
+  X(2, 3, 32, 128, 256, 1, 4, 2) /* 33: WS, M = 256                */ \
+  X(2, 2, 32, 256, 192, 2, 3, 2) /* 34: WS, large M                */ \
+  X(2, 3, 32, 256, 128, 2, 2, 2) /* 35: WS, large M, 128 tokens    */ \
+  X(2, 8, 16, 64, 16, 4, 1, 1)   /* 36: WS, M <= 16, narrow        */ \
+  X(2, 5, 32, 64, 32, 2, 1, 1)   /* 37: WS, M <= 32, narrow        */ \
+  X(2, 2, 32, 192, 256, 3, 2, 2) /* 38: WS, large M, 256 tokens    */ \
+  X(1, 3, 32, 256, 128, 4, 2, 0) /* 39: DMA 8 waves, large M       */ \
+  X(1, 4, 32, 128, 128, 2, 4, 0) /* 40: DMA 8 waves, M <= 128      */ \
+  X(1, 3, 32, 128, 256, 2, 4, 0) /* 41: DMA 8 waves, M = 256       */ \
+  X(1, 4, 32, 64, 256, 1, 8, 0)  /* 42: DMA 8 waves, M = 256, narrow */ \
+  X(1, 4, 32, 128, 64, 4, 2, 0)  /* 43: DMA 8 waves, M <= 64       */ \
+  X(1, 4, 16, 128, 32, 8, 1, 0)  /* 44: DMA 8 waves, M <= 32       */ \
+  X(3, 4, 16, 64, 16, 4, 1, 0)   /* 45: direct, M <= 16            */ \
+  X(3, 4, 16, 128, 16, 4, 1, 0)  /* 46: direct, M <= 16, 2 frags   */ \
+  X(3, 2, 16, 64, 32, 4, 1, 0)   /* 47: direct, M <= 32            */ \
+  X(3, 4, 16, 128, 16, 8, 1, 0)  /* 48: direct, M <= 16, 8 waves   */ \
+  X(3, 8, 16, 64, 16, 4, 1, 0)   /* 49: direct, M <= 16, depth 8   */ \
+  X(3, 2, 16, 128, 32, 4, 1, 0)  /* 50: direct, M <= 32, 2 frags   */
 
-#define QR_DESC(T, BN, BM, BK, WN, WM) \
-  {"t" #T "_n" #BN "_m" #BM "_k" #BK "_w" #WN "x" #WM, T, BN, BM, BK, 64 * WN * WM},
+#define QR_STR(x) #x
+#define QR_DESC(KIND, S, T, BN, BM, WN, WM, NP)                                  \
+  {KIND == 3   ? "dir" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN                \
+   : KIND == 2 ? "ws" QR_STR(S) "p" #NP "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM \
+   : KIND == 1 ? "dma" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM        \
+               : "reg_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM,                    \
+   T, BN, BM, 128, 64 * (WN * WM + NP), S},
 const TileDesc kTiles[] = {QR_TILES(QR_DESC)};
 #undef QR_DESC
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-template <int QT, int T, int BN, int BM, int BK, int WN, int WM>
+template <int QT, int KIND, int S, int T, int BN, int BM, int WN, int WM, int NP>
 hipError_t launch_one(const KParams& kp, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<QT, T, BN, BM, BK, WN, WM>), dim3(grid), dim3(64 * WN * WM), 0,
-                     st, kp);
+  if constexpr (KIND == 0)
+    hipLaunchKernelGGL((gemm_kernel<QT, T, BN, BM, 128, WN, WM>), dim3(grid), dim3(64 * WN * WM),
+                       0, st, kp);
+  else if constexpr (KIND == 1)
+    hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S>), dim3(grid),
+                       dim3(64 * WN * WM), 0, st, kp);
+  else if constexpr (KIND == 2)
+    hipLaunchKernelGGL((gemm_ws_kernel<QT, T, BN, BM, WN, WM, NP, S>), dim3(grid),
+                       dim3(64 * (WN * WM + NP)), 0, st, kp);
+  else
+    hipLaunchKernelGGL((gemm_direct_kernel<QT, BN, BM, WN, S>), dim3(grid), dim3(64 * WN), 0, st,
+                       kp);
   return hipGetLastError();
 }
 
@@ -479,6 +1142,7 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   kp.M = a.M; kp.N = a.N; kp.K = a.K;
   kp.splitk = plan.splitk;
   kp.tiles_n = (int)plan.tiles_n; kp.tiles_m = (int)plan.tiles_m; kp.nks = (int)plan.nks;
+  kp.rn = plan.rows;
   if (plan.splitk > 1) {
     kp.Y = a.part; kp.ldy = a.N; kp.out_raw = 1; kp.vec = (a.N % 4) == 0;
   } else {
@@ -487,11 +1151,11 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   const unsigned grid = (unsigned)(plan.tiles_n * plan.tiles_m * plan.splitk);
   hipError_t e = hipErrorInvalidValue;
   int idx = 0;
-#define QR_CASE(T, BN, BM, BK, WN, WM)                                               \
-  if (plan.tile == idx) {                                                             \
-    e = qt == kQInt8 ? launch_one<kQInt8, T, BN, BM, BK, WN, WM>(kp, grid, st)       \
-                     : launch_one<kQFp8, T, BN, BM, BK, WN, WM>(kp, grid, st);       \
-  }                                                                                   \
+#define QR_CASE(KIND, S, T, BN, BM, WN, WM, NP)                                        \
+  if (plan.tile == idx) {                                                               \
+    e = qt == kQInt8 ? launch_one<kQInt8, KIND, S, T, BN, BM, WN, WM, NP>(kp, grid, st) \
+                     : launch_one<kQFp8, KIND, S, T, BN, BM, WN, WM, NP>(kp, grid, st); \
+  }                                                                                     \
   ++idx;
   QR_TILES(QR_CASE)
 #undef QR_CASE

@@ -17,10 +17,13 @@ namespace {
 thread_local std::string g_err;
 int g_force_tile = -1;
 int g_force_splitk = 0;
+int g_force_rows = 0;
 
 constexpr int64_t kMaxKInt8 = 133144;  // K * 127^2 < 2^31
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
-constexpr int64_t kMaxCodeBytes = (int64_t)1 << 31;  // GEMM: 32-bit buffer offsets, 2^31 = out of range
+// GEMM: 32-bit buffer offsets; 2^31 (minus at most 3 KB of copy bias) marks
+// out-of-range rows, so code matrices stay below 2^31 - 2^16 bytes.
+constexpr int64_t kMaxCodeBytes = ((int64_t)1 << 31) - ((int64_t)1 << 16);
 constexpr int kCUs = 256;  // MI355X compute units: the plan targets this chip
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -70,58 +73,83 @@ int check_shape(const char* fn, int64_t M, int64_t N, int64_t K, int qt) {
 
 namespace qr {
 
-GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int force_splitk) {
+GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int force_splitk,
+                   int force_rows) {
   (void)qt;
   GemmPlan p{};
-  // Tile by token count (indices into the tile table, measured on MI355X):
-  // narrow 16-token tiles stream the weights for single-token decode; 32- to
-  // 128-token tiles for small batches; 64x64 (narrow layers) or 128x64 tiles
-  // for 256-token decode; 256x256 tiles with 8 waves for large token counts
-  // on wide layers.
+  // Tile by token count (indices into the tile table; choices measured on
+  // MI355X with graph-replayed launches). Up to 32 tokens the product is a
+  // weight stream: 8-wave LDS-DMA tiles of 128 weight rows. 256-token decode
+  // uses 32-token tiles on narrow layers (more blocks) and 128 x 256 tiles
+  // on wide ones; large token counts use 256 x 256 tiles.
+  const int64_t nks = (K + 127) / 128;
   int tile;
   if (force_tile >= 0) {
     tile = force_tile;
-  } else if (M <= 16) {
-    tile = 1;
   } else if (M <= 32) {
-    tile = 2;
+    tile = 44;
   } else if (M <= 64) {
-    tile = 3;
+    tile = 43;
   } else if (M <= 128) {
-    tile = 5;
+    tile = 40;
   } else if (M <= 256) {
-    tile = N <= 8192 ? 3 : 4;
+    if (N >= 8192) tile = 41;
+    else tile = nks >= 64 ? 40 : 44;
   } else if (M <= 1024) {
-    tile = N >= 16384 ? 10 : 4;
+    tile = N >= 16384 ? 19 : 41;
   } else {
-    tile = 10;
+    tile = 19;
   }
   const TileDesc& d = tile_desc(tile);
   p.tile = tile;
-  p.tiles_n = (N + d.BN - 1) / d.BN;
   p.tiles_m = (M + d.BM - 1) / d.BM;
   p.nks = (K + d.BK - 1) / d.BK;
-  const int64_t tiles = p.tiles_n * p.tiles_m;
-  const int64_t target = (M <= 16 ? 4 : 2) * kCUs;  // blocks wanted in flight
+  const int64_t full = ((N + d.BN - 1) / d.BN) * p.tiles_m;  // blocks at full tile height
+  // Balance the grid over the CUs: first by shrinking the weight rows per
+  // tile (a multiple of 8, at least half the tile height) so that about one
+  // block per CU remains; where even full-height tiles leave CUs idle, split
+  // K (every split keeps four or more K steps, and the partial sums, 4 M N
+  // bytes per split, stay within a quarter of the weight bytes) and then
+  // rebalance the rows.
+  // Only the weight-streaming tiles (64 tokens or fewer) shrink: tiles of
+  // more tokens are bound by their MFMA work, which does not shrink with the
+  // row count.
+  // With more full-height blocks than CUs the rows shrink to fill whole
+  // rounds of kCUs blocks instead of leaving a short last round.
+  auto balanced_rows = [&](int64_t splits) -> int64_t {
+    if (d.BM > 64) return d.BN;
+    const int64_t base = ((N + d.BN - 1) / d.BN) * p.tiles_m * splits;
+    const int64_t per = kCUs * ((base + kCUs - 1) / kCUs);  // blocks wanted
+    const int64_t want = 8 * ((N * p.tiles_m * splits + 8 * per - 1) / (8 * per));
+    return (want >= d.BN / 2 && want < d.BN) ? want : d.BN;
+  };
   int64_t s = 1;
-  if (force_splitk > 0) {
-    s = force_splitk;
-  } else if (tiles > 0 && tiles < target) {
-    // Split K towards the target block count while the partial sums (4*M*N
-    // bytes per split) stay within a quarter of the weight bytes and every
-    // split keeps at least four K steps.
-    s = (target + tiles - 1) / tiles;
+  int64_t rows = d.BN;
+  if (force_tile >= 0) {
+    s = force_splitk > 0 ? force_splitk : 1;
+    rows = force_rows > 0 ? force_rows : d.BN;
+  } else if (full == 0) {
+    // M = 0 or N = 0: nothing to launch
+  } else if (full >= kCUs) {
+    rows = balanced_rows(1);
+  } else if (8 * ((N * p.tiles_m + 8 * kCUs - 1) / (8 * kCUs)) >= d.BN / 2) {
+    rows = balanced_rows(1);
+  } else {
+    s = (kCUs + full - 1) / full;
     const int64_t by_bytes = K / (16 * (M > 0 ? M : 1));
     const int64_t by_steps = p.nks / 4;
     if (s > by_bytes) s = by_bytes;
     if (s > by_steps) s = by_steps;
-    if (s > 32) s = 32;
+    if (s > 4) s = 4;
     if (s < 1) s = 1;
+    rows = balanced_rows(s);
   }
   if (p.nks > 0 && s > p.nks) s = p.nks;
   if (s < 1) s = 1;
+  p.rows = (int)rows;
+  p.tiles_n = (N + p.rows - 1) / p.rows;
   p.splitk = (int)s;
-  if (p.splitk > 1 && tiles > 0)
+  if (p.splitk > 1 && p.tiles_n * p.tiles_m > 0)
     p.part_bytes = align256((size_t)p.splitk * (size_t)M * (size_t)N * 4);
   return p;
 }
@@ -141,29 +169,36 @@ const char* qr_tile_name(int tile) {
   return qr::tile_desc(tile).name;
 }
 
-int qr_set_plan_override(int tile, int splitk) {
+int qr_set_plan_override(int tile, int splitk, int rows) {
   if (tile >= qr::num_tiles() || splitk < 0 || splitk > 1024)
     return fail(QR_ERR_INVALID_ARG, "qr_set_plan_override: tile %d / splitk %d out of range", tile,
                 splitk);
+  if (tile >= 0 && rows != 0 && (rows < 8 || rows % 8 != 0 || rows > qr::tile_desc(tile).BN))
+    return fail(QR_ERR_INVALID_ARG,
+                "qr_set_plan_override: rows %d must be 0 or a multiple of 8 in [8, %d]", rows,
+                qr::tile_desc(tile).BN);
   g_force_tile = tile < 0 ? -1 : tile;
   g_force_splitk = tile < 0 ? 0 : splitk;
+  g_force_rows = tile < 0 ? 0 : rows;
   return ok();
 }
 
-int qr_gemm_plan(int64_t M, int64_t N, int64_t K, int qt, int* tile, int* splitk) {
+int qr_gemm_plan(int64_t M, int64_t N, int64_t K, int qt, int* tile, int* splitk, int* rows) {
   int st = check_shape("qr_gemm_plan", M, N, K, qt);
   if (st != QR_OK) return st;
-  if (!tile || !splitk) return fail(QR_ERR_INVALID_ARG, "qr_gemm_plan: null output pointer");
-  const qr::GemmPlan p = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk);
+  if (!tile || !splitk || !rows)
+    return fail(QR_ERR_INVALID_ARG, "qr_gemm_plan: null output pointer");
+  const qr::GemmPlan p = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk, g_force_rows);
   *tile = p.tile;
   *splitk = p.splitk;
+  *rows = p.rows;
   return ok();
 }
 
 size_t qr_workspace_size(const char* fn, int64_t M, int64_t N, int64_t K, int qt) {
   if (!fn) return (size_t)-1;
   if (check_shape("qr_workspace_size", M, N, K, qt) != QR_OK) return (size_t)-1;
-  const qr::GemmPlan p = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk);
+  const qr::GemmPlan p = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk, g_force_rows);
   const size_t gemm = (M == 0 || N == 0) ? 0 : p.ws_bytes();
   if (std::strcmp(fn, "qr_w8a8_gemm") == 0) return gemm;
   if (std::strcmp(fn, "qr_linear_fused") == 0) {
@@ -272,9 +307,9 @@ int qr_w8a8_gemm(const void* Xq, const float* scale_x, const void* Wq, const flo
   if (M > 0 && N > 0 && K > 0 && !Xq) return fail(QR_ERR_INVALID_ARG, "%s: null Xq", fn);
   if (!aligned(Xq, 16)) return fail(QR_ERR_UNSUPPORTED, "%s: misaligned Xq", fn);
   if (N * K >= kMaxCodeBytes || M * K >= kMaxCodeBytes)
-    return fail(QR_ERR_UNSUPPORTED, "%s: a code matrix of 2 GiB or more", fn);
+    return fail(QR_ERR_UNSUPPORTED, "%s: a code matrix of 2^31 - 2^16 bytes or more", fn);
   if (M == 0 || N == 0) return ok();
-  const qr::GemmPlan plan = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk);
+  const qr::GemmPlan plan = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk, g_force_rows);
   st = check_ws(fn, workspace, workspace_bytes, plan.ws_bytes());
   if (st != QR_OK) return st;
   (void)hipGetLastError();
@@ -297,9 +332,9 @@ int qr_linear_fused(const void* X, int64_t ldx, float act_mult, const void* Wq, 
   if (ldx % 8 != 0) return fail(QR_ERR_UNSUPPORTED, "%s: ldx must be a multiple of 8", fn);
   if (!aligned(X, 16)) return fail(QR_ERR_UNSUPPORTED, "%s: misaligned X", fn);
   if (N * K >= kMaxCodeBytes || M * K >= kMaxCodeBytes)
-    return fail(QR_ERR_UNSUPPORTED, "%s: a code matrix of 2 GiB or more", fn);
+    return fail(QR_ERR_UNSUPPORTED, "%s: a code matrix of 2^31 - 2^16 bytes or more", fn);
   if (M == 0 || N == 0) return ok();
-  const qr::GemmPlan plan = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk);
+  const qr::GemmPlan plan = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk, g_force_rows);
   const size_t xq_bytes = align256((size_t)M * (size_t)K);
   const size_t sx_bytes = align256((size_t)M * 4);
   const size_t head = plan.part_bytes;

@@ -21,6 +21,7 @@ struct TileDesc {
   int BM;  // macro-tile extent along M (tokens)
   int BK;  // bytes of K per pipeline stage
   int NT;  // threads per block
+  int S;   // LDS-DMA ring slots; 0 for the register-staged kernel
 };
 
 int num_tiles();
@@ -30,13 +31,15 @@ const TileDesc& tile_desc(int tile);
 struct GemmPlan {
   int tile;
   int splitk;
+  int rows;  // weight rows per tile (multiple of 8, <= the tile's BN)
   int64_t tiles_n, tiles_m, nks;
   size_t part_bytes;  // split-K partial sums [splitk][M][N] (0 without split)
   // Workspace qr_w8a8_gemm needs: the partial sums, none without split-K.
   size_t ws_bytes() const { return part_bytes; }
 };
 
-GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int force_splitk);
+GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int force_splitk,
+                   int force_rows);
 
 struct GemmArgs {
   const uint8_t* Xq;
