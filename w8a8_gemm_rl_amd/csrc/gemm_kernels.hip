@@ -494,7 +494,7 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   }
 }
 
-template <int QT, int T, int BN, int BM, int WN, int WM, int S>
+template <int QT, int T, int BN, int BM, int WN, int WM, int S, int PF>
 __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams p) {
   using MF = Mfma<QT, T>;
   using acc_t = typename MF::acc_t;
@@ -516,6 +516,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
   static_assert(BN % 8 == 0 && BM % 8 == 0 && IA % NW == 0, "row blocks per wave");
   static_assert(WTN % T == 0 && WTM % T == 0, "wave tile");
   static_assert(S >= 2 && S <= 8 && (S - 2) * NI <= 63, "ring depth");
+  static_assert(PF != 2 || S >= 3, "prefetch across the barrier needs a third slot");
   static_assert(S * STAGE <= 160 * 1024, "LDS");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
@@ -663,22 +664,104 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
     }
   };
 
+  // With PF the operands of the next MFMA sub-step are read from LDS one
+  // sub-step ahead, across the end of a K step too: the last sub-step of
+  // step it prefetches sub-step 0 of step it + 1, so the MFMAs resume
+  // right after the barrier. That needs step it + 1 visible at the barrier
+  // of step it, one stage earlier than without PF.
+  op_t na[FN], nb[FM];
+  auto load_ops = [&](int slot, int kk) {
+    const uint8_t* A = smem + slot * STAGE + rbaseA;
+    const uint8_t* B = smem + slot * STAGE + rbaseB;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) na[i] = lds_op(A + i * T * BK, kk);
+#pragma unroll
+    for (int j = 0; j < FM; ++j) nb[j] = lds_op(B + j * T * BK, kk);
+  };
+  auto compute_pf = [&](int slot, int nslot, bool has_next, bool do_issue, int islot, int iks) {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      op_t a[FN], bb[FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) a[i] = na[i];
+#pragma unroll
+      for (int j = 0; j < FM; ++j) bb[j] = nb[j];
+      if (kk + 1 < NKK) load_ops(slot, kk + 1);
+      else if (has_next) load_ops(nslot, 0);
+      if (do_issue) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          if (g * NKK / NG == kk) issue_group(g, islot, iks);
+      }
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = MF::run(a[i], bb[j], acc[i][j]);
+    }
+  };
+
+  // PF == 1: operands double-buffered in registers within a K step, and the
+  // LDS reads of sub-step kk + 1 interleaved one by one with the MFMAs of
+  // sub-step kk (scheduling groups), so the reads' latency hides behind the
+  // matrix work.
+  auto compute_ip = [&](int slot, bool do_issue, int islot, int iks) {
+    constexpr int NM = FN * FM, NR = (FN + FM) * (LB / 16);
+    load_ops(slot, 0);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      op_t a[FN], bb[FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) a[i] = na[i];
+#pragma unroll
+      for (int j = 0; j < FM; ++j) bb[j] = nb[j];
+      if (do_issue) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          if (g * NKK / NG == kk) issue_group(g, islot, iks);
+      }
+      if (kk + 1 < NKK) load_ops(slot, kk + 1);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = MF::run(a[i], bb[j], acc[i][j]);
+      if (kk + 1 < NKK) {
+#pragma unroll
+        for (int q = 0; q < NM; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        if (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR > NM ? NR - NM : 0, 0);
+      }
+    }
+  };
+
   // ---- main loop. K step ks0 + it lives in slot it % S. At the top of step
   // it the copies of steps up to it + S - 2 have been issued; this wave
-  // waits for its copies of step it, the barrier makes every wave's copies
-  // visible and guarantees slot (it - 1) % S is no longer read, and the
-  // copies of step it + S - 1 go into that slot while the MFMAs of step it
-  // run.
+  // waits for its copies of step it (with PF 2: of step it + 1), the barrier
+  // makes every wave's copies visible and guarantees slot (it - 1) % S is no
+  // longer read, and the copies of step it + S - 1 go into that slot while
+  // the MFMAs of step it run.
   const int nk = ks1 - ks0;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < nk) issue_all(s, ks0 + s);
   int cs = 0, is = S - 1;
   for (int it = 0; it < nk; ++it) {
-    const int ahead = nk - 1 - it;
-    wait_stages<NI, S - 2>(ahead);
-    __syncthreads();
-    compute(cs, it + S - 1 < nk, is, ks0 + it + S - 1);
+    if constexpr (PF == 1) {
+      wait_stages<NI, S - 2>(nk - 1 - it);
+      __syncthreads();
+      compute_ip(cs, it + S - 1 < nk, is, ks0 + it + S - 1);
+    } else if constexpr (PF == 2) {
+      wait_stages<NI, S - 3>(nk - 2 - it);
+      __syncthreads();
+      if (it == 0) load_ops(cs, 0);
+      compute_pf(cs, cs + 1 == S ? 0 : cs + 1, it + 1 < nk, it + S - 1 < nk, is,
+                 ks0 + it + S - 1);
+    } else {
+      wait_stages<NI, S - 2>(nk - 1 - it);
+      __syncthreads();
+      compute(cs, it + S - 1 < nk, is, ks0 + it + S - 1);
+    }
     cs = cs + 1 == S ? 0 : cs + 1;
     is = is + 1 == S ? 0 : is + 1;
   }
@@ -1044,8 +1127,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
 // ---------------------------------------------------------------------------
 // Tile table. Order matters: the planner and the tuning hook refer to tiles
 // by index. (KIND, S, T, BN, BM, WN, WM, NP): KIND 0 is the register-staged
-// kernel (two register stages, two LDS buffers), 1 the LDS-DMA kernel and 2
-// the warp-specialized LDS-DMA kernel, both with an S-slot ring; T is the
+// kernel (two register stages, two LDS buffers), 1 the LDS-DMA kernel, 4 the
+// same with MFMA operands read one sub-step ahead across K steps, 2 the
+// warp-specialized LDS-DMA kernel (all with an S-slot ring) and 3 the direct
+// register-path kernel (S = its prefetch depth); T is the
 // MFMA edge, BN x BM the macro tile over N and M, WN x WM the MFMA waves
 // along N and M, NP the copy (producer) waves. Every stage holds 128 bytes
 // of K.
@@ -1101,12 +1186,38 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
   X(3, 2, 16, 64, 32, 4, 1, 0)   /* 47: direct, M <= 32            */ \
   X(3, 4, 16, 128, 16, 8, 1, 0)  /* 48: direct, M <= 16, 8 waves   */ \
   X(3, 8, 16, 64, 16, 4, 1, 0)   /* 49: direct, M <= 16, depth 8   */ \
-  X(3, 2, 16, 128, 32, 4, 1, 0)  /* 50: direct, M <= 32, 2 frags   */
+  X(3, 2, 16, 128, 32, 4, 1, 0)  /* 50: direct, M <= 32, 2 frags   */ \
+  X(1, 3, 32, 128, 256, 1, 4, 0) /* 51: DMA, M = 256, 128x64 waves */ \
+  X(1, 2, 32, 128, 256, 2, 4, 0) /* 52: DMA, M = 256, 2-slot ring  */ \
+  X(4, 3, 32, 128, 256, 2, 4, 0) /* 53: DMA+PF, M = 256            */ \
+  X(4, 4, 32, 128, 128, 2, 4, 0) /* 54: DMA+PF, M <= 128           */ \
+  X(4, 5, 32, 128, 128, 2, 4, 0) /* 55: DMA+PF, M <= 128, 5 slots  */ \
+  X(4, 3, 32, 256, 128, 4, 2, 0) /* 56: DMA+PF, large M            */ \
+  X(4, 3, 32, 128, 256, 1, 4, 0) /* 57: DMA+PF, M = 256, 4 waves   */ \
+  X(4, 4, 16, 128, 32, 8, 1, 0)  /* 58: DMA+PF, M <= 32            */ \
+  X(4, 6, 32, 128, 64, 4, 2, 0)  /* 59: DMA+PF, M <= 64            */ \
+  X(1, 3, 32, 96, 256, 1, 4, 0)  /* 60: DMA, M = 256, 96-row tiles */ \
+  X(1, 3, 32, 96, 256, 3, 2, 0)  /* 61: DMA, M = 256, 96 rows, 6 waves */ \
+  X(5, 3, 32, 128, 256, 2, 4, 0) /* 62: DMA+IP, M = 256, 8 waves    */ \
+  X(5, 3, 32, 128, 256, 1, 4, 0) /* 63: DMA+IP, M = 256, 128x64 waves */ \
+  X(5, 3, 32, 128, 256, 2, 2, 0) /* 64: DMA+IP, M = 256, 64x128 waves */ \
+  X(5, 3, 32, 96, 256, 1, 4, 0)  /* 65: DMA+IP, M = 256, 96-row tiles */ \
+  X(5, 2, 32, 256, 256, 2, 4, 0) /* 66: DMA+IP, large M             */ \
+  X(5, 4, 32, 128, 128, 2, 4, 0) /* 67: DMA+IP, M <= 128            */ \
+  X(5, 4, 16, 128, 32, 8, 1, 0)  /* 68: DMA+IP, M <= 32             */ \
+  X(5, 4, 32, 128, 64, 4, 2, 0)  /* 69: DMA+IP, M <= 64             */ \
+  X(1, 4, 32, 192, 128, 2, 2, 0) /* 70: DMA, 192x128, 4 waves       */ \
+  X(1, 3, 32, 192, 128, 2, 2, 0) /* 71: DMA, 192x128, 3 slots       */ \
+  X(5, 4, 32, 192, 128, 2, 2, 0) /* 72: DMA+IP, 192x128             */ \
+  X(1, 4, 32, 160, 128, 5, 1, 0) /* 73: DMA, 160x128, 5 waves       */ \
+  X(1, 4, 32, 192, 64, 2, 2, 0)  /* 74: DMA, 192x64                 */
 
 #define QR_STR(x) #x
 #define QR_DESC(KIND, S, T, BN, BM, WN, WM, NP)                                  \
   {KIND == 3   ? "dir" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN                \
    : KIND == 2 ? "ws" QR_STR(S) "p" #NP "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM \
+   : KIND == 5 ? "dmaip" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM      \
+   : KIND == 4 ? "dmapf" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM      \
    : KIND == 1 ? "dma" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM        \
                : "reg_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM,                    \
    T, BN, BM, 128, 64 * (WN * WM + NP), S},
@@ -1119,9 +1230,10 @@ hipError_t launch_one(const KParams& kp, unsigned grid, hipStream_t st) {
   if constexpr (KIND == 0)
     hipLaunchKernelGGL((gemm_kernel<QT, T, BN, BM, 128, WN, WM>), dim3(grid), dim3(64 * WN * WM),
                        0, st, kp);
-  else if constexpr (KIND == 1)
-    hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S>), dim3(grid),
-                       dim3(64 * WN * WM), 0, st, kp);
+  else if constexpr (KIND == 1 || KIND == 4 || KIND == 5)
+    hipLaunchKernelGGL(
+        (gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, KIND == 4 ? 2 : KIND == 5 ? 1 : 0>),
+        dim3(grid), dim3(64 * WN * WM), 0, st, kp);
   else if constexpr (KIND == 2)
     hipLaunchKernelGGL((gemm_ws_kernel<QT, T, BN, BM, WN, WM, NP, S>), dim3(grid),
                        dim3(64 * (WN * WM + NP)), 0, st, kp);

@@ -80,8 +80,10 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
   // Tile by token count (indices into the tile table; choices measured on
   // MI355X with graph-replayed launches). Up to 32 tokens the product is a
   // weight stream: 8-wave LDS-DMA tiles of 128 weight rows. 256-token decode
-  // uses 32-token tiles on narrow layers (more blocks) and 128 x 256 tiles
-  // on wide ones; large token counts use 256 x 256 tiles.
+  // uses 192 x 128 tiles on wide layers, 128 x 128 with split K on long-K
+  // ones and 128 x 64 / 128 x 32 tiles on narrow ones (more blocks); up to
+  // 1024 tokens 256 x 256 tiles on wide layers and 128 x 128 below; large
+  // token counts use 256 x 256 tiles.
   const int64_t nks = (K + 127) / 128;
   int tile;
   if (force_tile >= 0) {
@@ -93,10 +95,12 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
   } else if (M <= 128) {
     tile = 40;
   } else if (M <= 256) {
-    if (N >= 8192) tile = 41;
-    else tile = nks >= 64 ? 40 : 44;
+    if (N >= 8192) tile = 71;
+    else if (nks >= 64) tile = 40;
+    else tile = N >= 4096 ? 43 : 44;
   } else if (M <= 1024) {
-    tile = N >= 16384 ? 19 : 41;
+    if (N >= 16384) tile = 19;
+    else tile = N > 2048 ? 40 : 44;
   } else {
     tile = 19;
   }
