@@ -33,6 +33,8 @@ METRIC = "W8A8 linear TOPS & HBM GB/s vs roofline; decode-layer µs at 7B/32B sh
 HBM_PEAK_GBS = 8000.0
 MFMA8_PEAK_TOPS = 5000.0  # dense INT8 / FP8 MFMA
 
+DOM_BATCH = 20  # dominant-GEMM launches per timing graph
+
 WORKLOADS = {
     "7b_decode_int8": dict(M=256, qt="int8", chain="7b", sets=4, kind="outliers"),
     "7b_decode_fp8": dict(M=256, qt="fp8", chain="7b", sets=4, kind="outliers"),
@@ -124,30 +126,6 @@ class Layer:
             f()
             if e:
                 e[1].record()
-
-    def capture_split(self, dom):
-        """Graphs of the ops before and after GEMM `dom`, and `dom` itself as an
-        eager callable (so stream events can bracket exactly that kernel)."""
-        import torch
-
-        ops = self.ops()
-        k = next(i for i, (kind, n, _) in enumerate(ops) if kind == "gemm" and n == dom)
-        parts = [ops[:k], ops[k + 1:]]
-        graphs = []
-        st = torch.cuda.Stream()
-        st.wait_stream(torch.cuda.current_stream())
-        for part in parts:
-            if not part:
-                graphs.append(None)
-                continue
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(st):
-                with torch.cuda.graph(g, stream=st):
-                    for _, _, f in part:
-                        f()
-            graphs.append(g)
-        torch.cuda.synchronize()
-        return graphs[0], ops[k][2], graphs[1]
 
 
 def gemm_source_sha256():
@@ -359,34 +337,66 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(K)]
-    mode = "eager" if args.eager else "hip_graph_split"
-    if not args.eager:
-        log("bench: capturing per-layer graphs (ops before / after the dominant GEMM)")
-        split = [L.capture_split(dom) for L in layers]
-
-    log(f"bench: timing {K} steps ({mode})")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    mode = "eager" if args.eager else "hip_graph"
     if args.eager:
+        # Every op launched from the host; events around the dominant GEMM.
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(K)]
+        log(f"bench: timing {K} steps ({mode})")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         for i in range(K):
             layers[i % len(layers)].run(per_linear={dom: evs[i]})
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        dom_us = 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / K
     else:
+        # One HIP graph per weight set holds the whole step (what a rollout
+        # engine that captures its decode step replays); K replays, walking
+        # the weight sets, between two synchronizations.
+        log("bench: capturing one graph per weight set")
+        whole = []
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        for L in layers:
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(st):
+                with torch.cuda.graph(gph, stream=st):
+                    L.run()
+            whole.append(gph)
+        # The dominant GEMM alone: a graph of DOM_BATCH back-to-back launches
+        # over the weight sets, so events around its replays measure the
+        # kernels with no host launch gap in between.
+        dom_graph = torch.cuda.CUDAGraph()
+        dom_fns = [next(f for kind, n, f in L.ops() if kind == "gemm" and n == dom) for L in layers]
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(dom_graph, stream=st):
+                for j in range(DOM_BATCH):
+                    dom_fns[j % len(dom_fns)]()
+        torch.cuda.synchronize()
+        for gph in whole:  # one untimed replay each
+            gph.replay()
+        dom_graph.replay()
+        torch.cuda.synchronize()
+
+        log(f"bench: timing {K} steps ({mode})")
+        t0 = time.perf_counter()
         for i in range(K):
-            pre, mid, post = split[i % len(split)]
-            if pre is not None:
-                pre.replay()
-            evs[i][0].record()
-            mid()
-            evs[i][1].record()
-            if post is not None:
-                post.replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+            whole[i % len(whole)].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+
+        reps = max(3, min(20, K // DOM_BATCH))
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            dom_graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        dom_us = 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / (reps * DOM_BATCH)
+        del whole, dom_graph
     sec_step = (t1 - t0) / K
-    dom_ms = [a.elapsed_time(b) for a, b in evs]
-    dom_us = 1000.0 * sum(dom_ms) / len(dom_ms)
 
     # ---- per-linear breakdown (eager, events around every GEMM; not timed)
     per = {L["name"]: [] for L in chain}

@@ -82,8 +82,10 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
   // weight stream: 8-wave LDS-DMA tiles of 128 weight rows. 256-token decode
   // uses 192 x 128 tiles on wide layers, 128 x 128 with split K on long-K
   // ones and 128 x 64 / 128 x 32 tiles on narrow ones (more blocks); up to
-  // 1024 tokens 256 x 256 tiles on wide layers and 128 x 128 below; large
-  // token counts use 256 x 256 tiles.
+  // 1024 tokens 256 x 256 tiles on wide layers, 256 x 128 with split K on
+  // long-K ones, 128 x 128 on the others and split 128 x 32 tiles on very
+  // narrow ones; large token counts use 256 x 256 tiles, 256 x 128 below
+  // N = 7168.
   const int64_t nks = (K + 127) / 128;
   int tile;
   if (force_tile >= 0) {
@@ -100,9 +102,10 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
     else tile = N >= 4096 ? 43 : 44;
   } else if (M <= 1024) {
     if (N >= 16384) tile = 19;
-    else tile = N > 2048 ? 40 : 44;
+    else if (N <= 2048) tile = 44;
+    else tile = nks >= 64 ? 39 : 40;
   } else {
-    tile = 19;
+    tile = N >= 7168 ? 19 : 39;
   }
   const TileDesc& d = tile_desc(tile);
   p.tile = tile;
@@ -113,8 +116,8 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
   // tile (a multiple of 8, at least half the tile height) so that about one
   // block per CU remains; where even full-height tiles leave CUs idle, split
   // K (every split keeps four or more K steps, and the partial sums, 4 M N
-  // bytes per split, stay within a quarter of the weight bytes) and then
-  // rebalance the rows.
+  // bytes per split, stay within the weight bytes) and then rebalance the
+  // rows.
   // Only the weight-streaming tiles (64 tokens or fewer) shrink: tiles of
   // more tokens are bound by their MFMA work, which does not shrink with the
   // row count.
@@ -139,8 +142,10 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
   } else if (8 * ((N * p.tiles_m + 8 * kCUs - 1) / (8 * kCUs)) >= d.BN / 2) {
     rows = balanced_rows(1);
   } else {
-    s = (kCUs + full - 1) / full;
-    const int64_t by_bytes = K / (16 * (M > 0 ? M : 1));
+    // As many splits as keep the grid within one round of kCUs blocks (a
+    // second, partial round costs more than the split saves).
+    s = kCUs / full;
+    const int64_t by_bytes = K / (4 * (M > 0 ? M : 1));
     const int64_t by_steps = p.nks / 4;
     if (s > by_bytes) s = by_bytes;
     if (s > by_steps) s = by_steps;

@@ -67,15 +67,23 @@ __global__ __launch_bounds__(NT) void act_quant_kernel(const uint16_t* __restric
 
   uint4 r[MAXC];
   float amax = 0.0f;
-  if (valid) {
+  if (valid && nch > 0) {
     if (fits) {
+      // The loads of one row are guarded by a block-uniform trip count
+      // only: lanes past the row end re-read its last chunk and drop it,
+      // so no load sits behind a divergent branch and all are in flight
+      // at once.
+      const int64_t last = nch - 1;
+      const int niter = (int)((nch + TPR - 1) / TPR);
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
         const int64_t c = lt + (int64_t)i * TPR;
-        if (c < nch) {
-          r[i] = xr[c];
-          amax = fmaxf(amax, absmax8_bf16(r[i]));
-        }
+        if (i < niter) r[i] = xr[c < nch ? c : last];
+      }
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int64_t c = lt + (int64_t)i * TPR;
+        if (i < niter && c < nch) amax = fmaxf(amax, absmax8_bf16(r[i]));
       }
     } else {
       for (int64_t c = lt; c < nch; c += TPR) amax = fmaxf(amax, absmax8_bf16(xr[c]));
@@ -122,16 +130,27 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(const float* W, int64
 
   float4 r[MAXC];
   float amax = 0.0f;
-  if (valid) {
+  if (valid && nch > 0) {
     if (fits) {
+      // Loads guarded only by a block-uniform trip count (lanes past the
+      // row end re-read its last chunk and drop it), so they are in flight
+      // together.
+      const int64_t last = nch - 1;
+      const int niter = (int)((nch + TPR - 1) / TPR);
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
         const int64_t c = lt + (int64_t)i * TPR;
-        if (c < nch) {
-          float4 v = wr[c];
+        if (i < niter) r[i] = wr[c < nch ? c : last];
+      }
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int64_t c = lt + (int64_t)i * TPR;
+        if (i < niter) {
+          float4 v = r[i];
           v.x = v.x / s; v.y = v.y / s; v.z = v.z / s; v.w = v.w / s;
           r[i] = v;
-          amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+          if (c < nch)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
         }
       }
     } else {
