@@ -147,12 +147,12 @@ def test_workspace_size_and_plan_are_pure(B):
     assert B.gemm_plan(4096, 27648, 5120, "int8")[1] == 1
     # override hook round-trips; rows 0 means the full tile height
     B.set_plan_override(0, 3)
-    assert B.gemm_plan(256, 3584, 3584, "fp8") == (0, 3, 64)
+    assert B.gemm_plan(256, 3584, 3584, "fp8") == (0, 3, 128)  # tile 0 is 128 rows high
     B.set_plan_override(0, 2, 40)
     assert B.gemm_plan(256, 3584, 3584, "fp8") == (0, 2, 40)
     B.set_plan_override(-1)
     assert B.gemm_plan(256, 3584, 3584, "int8") == (t, s, r)
-    for bad in [(999, 1, 0), (0, 1, 12), (0, 1, 72), (0, 1, -8), (0, -1, 0)]:
+    for bad in [(999, 1, 0), (0, 1, 12), (0, 1, 136), (0, 1, -8), (0, -1, 0)]:
         with pytest.raises(B.QRError):
             B.set_plan_override(*bad)
     B.set_plan_override(-1)

@@ -13,12 +13,12 @@
 //    v_mfma_scale_f32_{16x16x128,32x32x64}_f8f6f4 with unit block scales
 //    (E8M0 127 = 2^0), accumulating in fp32.
 //  * A block owns a BN x BM macro tile (of which the first `rn` weight rows
-//    are its own) and a contiguous range of K. Four kernel families move the
-//    operands: register-staged (global -> registers -> LDS), LDS-DMA
-//    (global -> LDS with buffer_load ... lds, an S-slot ring), the same with
-//    dedicated copy waves, and direct (global -> MFMA registers, no LDS) for
-//    small token counts. 16-byte LDS chunks are XOR-swizzled by row so the
-//    16-byte fragment reads of the MFMA operands are free of bank conflicts.
+//    are its own) and a contiguous range of K. Two kernel families move the
+//    operands: LDS-DMA (global -> LDS with buffer_load ... lds into an S-slot
+//    ring, optionally with the MFMA operands double-buffered in registers)
+//    and direct (global -> MFMA registers, no LDS) for small token counts.
+//    16-byte LDS chunks are XOR-swizzled by row so the 16-byte fragment
+//    reads of the MFMA operands are free of bank conflicts.
 //  * Each lane feeds the MFMA a contiguous 16- or 32-byte run of K for its row.
 //    The K order inside one instruction is the same for A and B, so any lane
 //    placement of K gives the same dot product.
@@ -231,183 +231,6 @@ __device__ __forceinline__ void store_tile(const KParams& p, const acc_t (&acc)[
       }
 }
 
-template <int QT, int T, int BN, int BM, int BK, int WN, int WM>
-__global__ __launch_bounds__(64 * WN * WM, 1) void gemm_kernel(const KParams p) {
-  using MF = Mfma<QT, T>;
-  using acc_t = typename MF::acc_t;
-  using op_t = typename MF::op_t;
-  constexpr int NT = 64 * WN * WM;
-  constexpr int WTN = BN / WN, WTM = BM / WM;
-  constexpr int FN = WTN / T, FM = WTM / T;
-  constexpr int CPR = BK / 16;      // 16-byte chunks per LDS row
-  constexpr int RSTEP = NT / CPR;   // rows between one thread's consecutive chunks
-  constexpr int CA = BN * CPR, CB = BM * CPR;
-  constexpr int LA = (CA + NT - 1) / NT, LBn = (CB + NT - 1) / NT;
-  constexpr int KI = MF::KI, LB = MF::LB;
-  constexpr int NKK = BK / KI;
-  constexpr int STAGE = (BN + BM) * BK;
-  static_assert(BK == 64 || BK == 128, "BK");
-  static_assert(NT % CPR == 0 && RSTEP % 16 == 0, "load rows keep one swizzle");
-  static_assert(WTN % T == 0 && WTM % T == 0, "wave tile");
-  static_assert(BK % KI == 0, "BK vs MFMA depth");
-
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
-
-  int tn, tm, z, ks0, ks1;
-  block_tile(p, tn, tm, z, ks0, ks1);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = tid >> 6;
-  const int wn = wid % WN, wm = wid / WN;
-
-  const int64_t N = p.N, M = p.M, K = p.K;
-
-  acc_t acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = acc_t{};
-
-  // ---- per-thread load addressing, computed once. Thread tid moves chunk
-  // c_ld of rows r_ld + i * RSTEP with buffer loads: a 32-bit per-thread
-  // offset plus the K advance as a scalar offset. Reads outside the buffer
-  // return zero: rows past N (or M) and chunks past K on a ragged last step
-  // point at offset 2^31, beyond any code matrix (each is under 2 GiB).
-  const int c_ld = tid % CPR;
-  const int r_ld = tid / CPR;
-  const bool ktail = (K % BK) != 0;
-  constexpr uint32_t kOOB = 0x80000000u;
-  const __amdgpu_buffer_rsrc_t rsw =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.Wq, (short)0, (int)(uint32_t)(N * K), kBufWord3);
-  const __amdgpu_buffer_rsrc_t rsx =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.Xq, (short)0, (int)(uint32_t)(M * K), kBufWord3);
-  uint32_t oa[LA], ob[LBn];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) {
-    const int r = r_ld + i * RSTEP;
-    const int64_t row = (int64_t)tn * p.rn + r;
-    oa[i] = (r < p.rn && row < N) ? (uint32_t)(row * K + c_ld * 16) : kOOB;
-  }
-#pragma unroll
-  for (int i = 0; i < LBn; ++i) {
-    const int64_t row = (int64_t)tm * BM + r_ld + i * RSTEP;
-    ob[i] = row < M ? (uint32_t)(row * K + c_ld * 16) : kOOB;
-  }
-  // LDS write offset of chunk 0 (chunk i adds i * RSTEP rows, same swizzle)
-  const int wofs = r_ld * BK + ((c_ld ^ swz<BK>(r_ld)) << 4);
-
-  // LDS read offsets of the MFMA fragments: lane row lr of a fragment, whose
-  // base row is a multiple of 16, so the swizzle depends on lr only.
-  const int lr = lane % T;
-  const int lg = (lane / T) * (LB / 16);
-  const int sl = swz<BK>(lr);
-  const int rbaseA = (wn * WTN + lr) * BK;
-  const int rbaseB = BN * BK + (wm * WTM + lr) * BK;
-  int xo0[NKK], xo1[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const int c0 = kk * (KI / 16) + lg;
-    xo0[kk] = (c0 ^ sl) << 4;
-    xo1[kk] = ((c0 + 1) ^ sl) << 4;
-  }
-
-  uint4 ra[2][LA], rb[2][LBn];
-
-  auto ld16 = [&](__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) -> uint4 {
-    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
-    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
-  };
-  auto gload = [&](int ks, uint4* da, uint4* db) {
-    const int kb = ks * BK;  // scalar offset
-    if (!ktail || ks + 1 < p.nks) {
-#pragma unroll
-      for (int i = 0; i < LA; ++i)
-        if (CA % NT == 0 || tid + i * NT < CA) da[i] = ld16(rsw, oa[i], kb);
-#pragma unroll
-      for (int i = 0; i < LBn; ++i)
-        if (CB % NT == 0 || tid + i * NT < CB) db[i] = ld16(rsx, ob[i], kb);
-    } else {
-      const bool kin = kb + c_ld * 16 < K;  // ragged last step
-#pragma unroll
-      for (int i = 0; i < LA; ++i)
-        if (CA % NT == 0 || tid + i * NT < CA) da[i] = ld16(rsw, kin ? oa[i] : kOOB, kb);
-#pragma unroll
-      for (int i = 0; i < LBn; ++i)
-        if (CB % NT == 0 || tid + i * NT < CB) db[i] = ld16(rsx, kin ? ob[i] : kOOB, kb);
-    }
-  };
-
-  auto sstore = [&](int buf, const uint4* da, const uint4* db) {
-    uint8_t* A = smem + buf * STAGE + wofs;
-    uint8_t* B = smem + buf * STAGE + BN * BK + wofs;
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      if (CA % NT == 0 || tid + i * NT < CA)
-        *reinterpret_cast<uint4*>(A + i * RSTEP * BK) = da[i];
-#pragma unroll
-    for (int i = 0; i < LBn; ++i)
-      if (CB % NT == 0 || tid + i * NT < CB)
-        *reinterpret_cast<uint4*>(B + i * RSTEP * BK) = db[i];
-  };
-
-  auto lds_op = [&](const uint8_t* base, int kk) -> op_t {
-    const uint4 u0 = *reinterpret_cast<const uint4*>(base + xo0[kk]);
-    if constexpr (LB == 16) {
-      return op_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w};
-    } else {
-      const uint4 u1 = *reinterpret_cast<const uint4*>(base + xo1[kk]);
-      return op_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
-                  (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-    }
-  };
-
-  auto compute = [&](int buf) {
-    const uint8_t* A = smem + buf * STAGE + rbaseA;
-    const uint8_t* B = smem + buf * STAGE + rbaseB;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      op_t a[FN], bb[FM];
-#pragma unroll
-      for (int i = 0; i < FN; ++i) a[i] = lds_op(A + i * T * BK, kk);
-#pragma unroll
-      for (int j = 0; j < FM; ++j) bb[j] = lds_op(B + j * T * BK, kk);
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = MF::run(a[i], bb[j], acc[i][j]);
-    }
-  };
-
-  // ---- main loop: data of K step j lives in register stage j & 1. Step it
-  // first writes step it+1 (loaded two steps earlier) to the other LDS
-  // buffer, refills those registers with the loads of step it+3, and then
-  // runs the MFMAs of step it, so the loads are in flight while the matrix
-  // cores work. The loop is unrolled by two so every register stage index is
-  // a compile-time constant (a runtime index moves the stages to scratch).
-  const int nk = ks1 - ks0;
-  auto step = [&](int it, auto stage_c) {
-    constexpr int s1 = decltype(stage_c)::value;  // == (it + 1) & 1
-    if (it + 1 < nk) sstore(s1, ra[s1], rb[s1]);
-    if (it + 3 < nk) gload(ks0 + it + 3, ra[s1], rb[s1]);
-    compute(s1 ^ 1);
-    __syncthreads();
-  };
-  if (nk > 0) {
-    gload(ks0, ra[0], rb[0]);
-    if (nk > 1) gload(ks0 + 1, ra[1], rb[1]);
-    sstore(0, ra[0], rb[0]);
-    if (nk > 2) gload(ks0 + 2, ra[0], rb[0]);
-    __syncthreads();
-    for (int it = 0; it < nk; it += 2) {
-      step(it, std::integral_constant<int, 1>{});
-      if (it + 1 < nk) step(it + 1, std::integral_constant<int, 0>{});
-    }
-  }
-
-  store_tile<QT, T, BN, BM, WN, WM>(p, acc, tn, tm, z, wn, wm, lane);
-}
-
 // ---------------------------------------------------------------------------
 // LDS-DMA variant. Operand tiles move from global memory straight into LDS
 // with buffer_load_dwordx4 ... lds: one wave instruction writes 64 x 16
@@ -466,12 +289,6 @@ __device__ __forceinline__ void dma_group(uint32_t lds_addr, const uint32_t* vo,
 #pragma clang diagnostic pop
 }
 
-// Single-copy form (M0 per copy), used by the warp-specialized kernel.
-__device__ __forceinline__ void dma16(uint32_t lds_addr, uint32_t voff, __amdgpu_buffer_rsrc_t r,
-                                      int soff) {
-  dma_group<1>(lds_addr, &voff, r, soff);
-}
-
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
@@ -494,7 +311,7 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   }
 }
 
-template <int QT, int T, int BN, int BM, int WN, int WM, int S, int PF>
+template <int QT, int T, int BN, int BM, int WN, int WM, int S, bool IP>
 __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams p) {
   using MF = Mfma<QT, T>;
   using acc_t = typename MF::acc_t;
@@ -516,7 +333,6 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
   static_assert(BN % 8 == 0 && BM % 8 == 0 && IA % NW == 0, "row blocks per wave");
   static_assert(WTN % T == 0 && WTM % T == 0, "wave tile");
   static_assert(S >= 2 && S <= 8 && (S - 2) * NI <= 63, "ring depth");
-  static_assert(PF != 2 || S >= 3, "prefetch across the barrier needs a third slot");
   static_assert(S * STAGE <= 160 * 1024, "LDS");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
@@ -664,12 +480,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
     }
   };
 
-  // With PF the operands of the next MFMA sub-step are read from LDS one
-  // sub-step ahead, across the end of a K step too: the last sub-step of
-  // step it prefetches sub-step 0 of step it + 1, so the MFMAs resume
-  // right after the barrier. That needs step it + 1 visible at the barrier
-  // of step it, one stage earlier than without PF.
-  op_t na[FN], nb[FM];
+  op_t na[FN], nb[FM];  // operands of the next sub-step (IP)
   auto load_ops = [&](int slot, int kk) {
     const uint8_t* A = smem + slot * STAGE + rbaseA;
     const uint8_t* B = smem + slot * STAGE + rbaseB;
@@ -678,29 +489,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
 #pragma unroll
     for (int j = 0; j < FM; ++j) nb[j] = lds_op(B + j * T * BK, kk);
   };
-  auto compute_pf = [&](int slot, int nslot, bool has_next, bool do_issue, int islot, int iks) {
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      op_t a[FN], bb[FM];
-#pragma unroll
-      for (int i = 0; i < FN; ++i) a[i] = na[i];
-#pragma unroll
-      for (int j = 0; j < FM; ++j) bb[j] = nb[j];
-      if (kk + 1 < NKK) load_ops(slot, kk + 1);
-      else if (has_next) load_ops(nslot, 0);
-      if (do_issue) {
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-          if (g * NKK / NG == kk) issue_group(g, islot, iks);
-      }
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = MF::run(a[i], bb[j], acc[i][j]);
-    }
-  };
 
-  // PF == 1: operands double-buffered in registers within a K step, and the
+  // IP: operands double-buffered in registers within a K step, and the
   // LDS reads of sub-step kk + 1 interleaved one by one with the MFMAs of
   // sub-step kk (scheduling groups), so the reads' latency hides behind the
   // matrix work.
@@ -737,207 +527,25 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
 
   // ---- main loop. K step ks0 + it lives in slot it % S. At the top of step
   // it the copies of steps up to it + S - 2 have been issued; this wave
-  // waits for its copies of step it (with PF 2: of step it + 1), the barrier
-  // makes every wave's copies visible and guarantees slot (it - 1) % S is no
-  // longer read, and the copies of step it + S - 1 go into that slot while
-  // the MFMAs of step it run.
+  // waits for its copies of step it, the barrier makes every wave's copies
+  // visible and guarantees slot (it - 1) % S is no longer read, and the
+  // copies of step it + S - 1 go into that slot while the MFMAs of step it
+  // run.
   const int nk = ks1 - ks0;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < nk) issue_all(s, ks0 + s);
   int cs = 0, is = S - 1;
   for (int it = 0; it < nk; ++it) {
-    if constexpr (PF == 1) {
-      wait_stages<NI, S - 2>(nk - 1 - it);
-      __syncthreads();
-      compute_ip(cs, it + S - 1 < nk, is, ks0 + it + S - 1);
-    } else if constexpr (PF == 2) {
-      wait_stages<NI, S - 3>(nk - 2 - it);
-      __syncthreads();
-      if (it == 0) load_ops(cs, 0);
-      compute_pf(cs, cs + 1 == S ? 0 : cs + 1, it + 1 < nk, it + S - 1 < nk, is,
-                 ks0 + it + S - 1);
-    } else {
-      wait_stages<NI, S - 2>(nk - 1 - it);
-      __syncthreads();
-      compute(cs, it + S - 1 < nk, is, ks0 + it + S - 1);
-    }
+    wait_stages<NI, S - 2>(nk - 1 - it);
+    __syncthreads();
+    if constexpr (IP) compute_ip(cs, it + S - 1 < nk, is, ks0 + it + S - 1);
+    else compute(cs, it + S - 1 < nk, is, ks0 + it + S - 1);
     cs = cs + 1 == S ? 0 : cs + 1;
     is = is + 1 == S ? 0 : is + 1;
   }
 
   store_tile<QT, T, BN, BM, WN, WM>(p, acc, tn, tm, z, wn, wm, lane);
-}
-
-// ---------------------------------------------------------------------------
-// Warp-specialized LDS-DMA variant. NP producer waves only issue the LDS DMA
-// copies; WN x WM consumer waves only read LDS and run the MFMAs. With one
-// barrier per K step the copy issue of step it + S - 1 (bound by the
-// texture-address unit, 1 KB per instruction) overlaps the MFMAs of step it
-// instead of following them. Producers skip 8-row blocks that hold no valid
-// row (tiles that own fewer than BN weight rows, token tiles past M), so
-// their per-step copy count is a block-uniform runtime value and their
-// vmcnt waits use a runtime-selected immediate.
-// ---------------------------------------------------------------------------
-template <int LO, int HI>
-__device__ __forceinline__ void wait_vm_rt(int x) {
-  if constexpr (LO == HI) {
-    wait_vm<LO>();
-  } else {
-    constexpr int MID = (LO + HI) / 2;
-    if (x <= MID) wait_vm_rt<LO, MID>(x);
-    else wait_vm_rt<MID + 1, HI>(x);
-  }
-}
-
-template <int QT, int T, int BN, int BM, int WN, int WM, int NP, int S>
-__global__ __launch_bounds__(64 * (WN * WM + NP), 1) void gemm_ws_kernel(const KParams p) {
-  using MF = Mfma<QT, T>;
-  using acc_t = typename MF::acc_t;
-  using op_t = typename MF::op_t;
-  constexpr int BK = 128;
-  constexpr int NC = WN * WM;
-  constexpr int WTN = BN / WN, WTM = BM / WM;
-  constexpr int FN = WTN / T, FM = WTM / T;
-  constexpr int KI = MF::KI, LB = MF::LB;
-  constexpr int NKK = BK / KI;
-  constexpr int IA = BN / 8, IB = BM / 8;
-  constexpr int MAXJ = (IA + NP - 1) / NP + (IB + NP - 1) / NP;  // copies per producer per stage
-  constexpr int STAGE = (IA + IB) * 1024;
-  static_assert(BN % 8 == 0 && BM % 8 == 0, "8-row copy blocks");
-  static_assert(WTN % T == 0 && WTM % T == 0, "wave tile");
-  static_assert(S >= 2 && S <= 8 && (S - 2) * MAXJ <= 63, "ring depth vs vmcnt");
-  static_assert(S * STAGE <= 160 * 1024, "LDS");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
-
-  int tn, tm, z, ks0, ks1;
-  block_tile(p, tn, tm, z, ks0, ks1);
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool producer = wid >= NC;
-  const int64_t N = p.N, M = p.M, K = p.K;
-  // Valid rows of this tile: weight rows [tn * rn, tn * rn + limA), token
-  // rows [tm * BM, tm * BM + limB).
-  const int limA = (int)((N - (int64_t)tn * p.rn) < p.rn ? (N - (int64_t)tn * p.rn) : p.rn);
-  const int limB = (int)((M - (int64_t)tm * BM) < BM ? (M - (int64_t)tm * BM) : BM);
-  const int nA = (limA + 7) >> 3, nB = (limB + 7) >> 3;
-  const int nk = ks1 - ks0;
-  const bool ktail = (K % BK) != 0;
-  const int krem = (int)(K % BK);
-  constexpr uint32_t kOOB = 0x80000000u;
-
-  if (producer) {
-    // ---- copy issue. Producer pi moves row blocks j = pi, pi + NP, ... of
-    // each operand. Lane l covers row 8 j + l/8, physical chunk l % 8, and
-    // fetches logical chunk (l % 8) ^ swz(row); swz depends on the row's bits
-    // 1..3, i.e. on j & 1 and l / 16.
-    const int pi = wid - NC;
-    const int cntA = nA > pi ? (nA - pi + NP - 1) / NP : 0;
-    const int cntB = nB > pi ? (nB - pi + NP - 1) / NP : 0;
-    const int cnt = cntA + cntB;
-    const __amdgpu_buffer_rsrc_t rsw =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.Wq, (short)0, (int)(uint32_t)(N * K), kBufWord3);
-    const __amdgpu_buffer_rsrc_t rsx =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.Xq, (short)0, (int)(uint32_t)(M * K), kBufWord3);
-    const int lrow = lane >> 3;
-    const int c0 = (lane & 7) ^ (lane >> 4);        // chunk for even j
-    const int c1 = (lane & 7) ^ (4 + (lane >> 4));  // chunk for odd j (swz differs by 4)
-    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
-    const int64_t baseA = (int64_t)tn * p.rn;
-    const int64_t baseB = (int64_t)tm * BM;
-
-    auto issue = [&](int slot, int ks) {
-      const int soff = ks * BK;
-      const bool tail = ktail && ks + 1 == p.nks;
-      const uint32_t so = lds0 + (uint32_t)(slot * STAGE);
-      for (int j = pi; j < nA; j += NP) {
-        const int r = j * 8 + lrow;
-        const int c = (j & 1) ? c1 : c0;
-        const bool ok = r < limA && (!tail || c * 16 < krem);
-        const uint32_t vo = ok ? (uint32_t)((baseA + r) * K + c * 16) : kOOB;
-        dma16(so + j * 1024, vo, rsw, soff);
-      }
-      for (int j = pi; j < nB; j += NP) {
-        const int r = j * 8 + lrow;
-        const int c = (j & 1) ? c1 : c0;
-        const bool ok = r < limB && (!tail || c * 16 < krem);
-        const uint32_t vo = ok ? (uint32_t)((baseB + r) * K + c * 16) : kOOB;
-        dma16(so + IA * 1024 + j * 1024, vo, rsx, soff);
-      }
-    };
-
-    for (int s = 0; s < S - 1; ++s)
-      if (s < nk) issue(s, ks0 + s);
-    int is = S - 1;
-    for (int it = 0; it < nk; ++it) {
-      // stage it must have landed; later issued stages may stay in flight
-      const int behind = (nk - 1 - it) < (S - 2) ? (nk - 1 - it) : (S - 2);
-      const int allow = behind * cnt;
-      wait_vm_rt<0, 63>(allow > 63 ? 63 : allow);
-      __syncthreads();
-      if (it + S - 1 < nk) issue(is, ks0 + it + S - 1);
-      is = is + 1 == S ? 0 : is + 1;
-    }
-    return;
-  }
-
-  // ---- consumers
-  const int wn = wid % WN, wm = wid / WN;
-  const bool active = wn * WTN < limA && wm * WTM < limB;
-  acc_t acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = acc_t{};
-
-  const int lr = lane % T;
-  const int lg = (lane / T) * (LB / 16);
-  const int sl = swz<BK>(lr);
-  const int rbaseA = (wn * WTN + lr) * BK;
-  const int rbaseB = IA * 1024 + (wm * WTM + lr) * BK;
-  int xo0[NKK], xo1[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const int cc = kk * (KI / 16) + lg;
-    xo0[kk] = (cc ^ sl) << 4;
-    xo1[kk] = ((cc + 1) ^ sl) << 4;
-  }
-  auto lds_op = [&](const uint8_t* base, int kk) -> op_t {
-    const uint4 u0 = *reinterpret_cast<const uint4*>(base + xo0[kk]);
-    if constexpr (LB == 16) {
-      return op_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w};
-    } else {
-      const uint4 u1 = *reinterpret_cast<const uint4*>(base + xo1[kk]);
-      return op_t{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w,
-                  (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-    }
-  };
-  auto compute = [&](int slot) {
-    const uint8_t* A = smem + slot * STAGE + rbaseA;
-    const uint8_t* B = smem + slot * STAGE + rbaseB;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      op_t a[FN], bb[FM];
-#pragma unroll
-      for (int i = 0; i < FN; ++i) a[i] = lds_op(A + i * T * BK, kk);
-#pragma unroll
-      for (int j = 0; j < FM; ++j) bb[j] = lds_op(B + j * T * BK, kk);
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = MF::run(a[i], bb[j], acc[i][j]);
-    }
-  };
-  int cs = 0;
-  for (int it = 0; it < nk; ++it) {
-    __syncthreads();
-    if (active) compute(cs);
-    cs = cs + 1 == S ? 0 : cs + 1;
-  }
-  if (active) store_tile<QT, T, BN, BM, WN, WM>(p, acc, tn, tm, z, wn, wm, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1126,120 +734,47 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
 
 // ---------------------------------------------------------------------------
 // Tile table. Order matters: the planner and the tuning hook refer to tiles
-// by index. (KIND, S, T, BN, BM, WN, WM, NP): KIND 0 is the register-staged
-// kernel (two register stages, two LDS buffers), 1 the LDS-DMA kernel, 4 the
-// same with MFMA operands read one sub-step ahead across K steps, 2 the
-// warp-specialized LDS-DMA kernel (all with an S-slot ring) and 3 the direct
-// register-path kernel (S = its prefetch depth); T is the
-// MFMA edge, BN x BM the macro tile over N and M, WN x WM the MFMA waves
-// along N and M, NP the copy (producer) waves. Every stage holds 128 bytes
-// of K.
+// by index. (KIND, S, T, BN, BM, WN, WM): KIND 0 is the LDS-DMA kernel, 1 the
+// same with MFMA operands double-buffered and interleaved with the MFMAs
+// (scheduling groups), 2 the direct register-path kernel; S is the LDS ring
+// depth (the prefetch depth in K steps for KIND 2), T the MFMA edge, BN x BM
+// the macro tile over N and M, WN x WM the waves along N and M. Every K step
+// covers 128 bytes of K.
 // ---------------------------------------------------------------------------
-#define QR_TILES(X)                                                     \
-  X(0, 0, 16, 64, 16, 4, 1, 0)   /*  0: M <= 16, weight streaming  */ \
-  X(0, 0, 16, 32, 16, 2, 1, 0)   /*  1: M <= 16, narrow            */ \
-  X(0, 0, 32, 128, 32, 4, 1, 0)  /*  2: M <= 32                    */ \
-  X(0, 0, 32, 64, 64, 2, 2, 0)   /*  3: M <= 64                    */ \
-  X(0, 0, 32, 128, 64, 2, 2, 0)  /*  4: M <= 64, wide              */ \
-  X(0, 0, 32, 64, 128, 2, 2, 0)  /*  5: M <= 128                   */ \
-  X(0, 0, 32, 128, 128, 2, 2, 0) /*  6: M <= 128, wide             */ \
-  X(0, 0, 32, 64, 256, 1, 4, 0)  /*  7: M = 256                    */ \
-  X(0, 0, 32, 128, 256, 2, 2, 0) /*  8: M = 256, wide              */ \
-  X(0, 0, 32, 256, 128, 2, 2, 0) /*  9: large M                    */ \
-  X(0, 0, 32, 256, 256, 2, 4, 0) /* 10: large M, 8 waves           */ \
-  X(1, 4, 16, 64, 16, 4, 1, 0)   /* 11: DMA, M <= 16               */ \
-  X(1, 4, 16, 128, 16, 4, 1, 0)  /* 12: DMA, M <= 16, wide         */ \
-  X(1, 4, 32, 128, 32, 4, 1, 0)  /* 13: DMA, M <= 32               */ \
-  X(1, 4, 32, 256, 32, 4, 1, 0)  /* 14: DMA, M <= 32, wide         */ \
-  X(1, 4, 32, 128, 64, 2, 2, 0)  /* 15: DMA, M <= 64               */ \
-  X(1, 4, 32, 128, 128, 2, 2, 0) /* 16: DMA, M <= 128              */ \
-  X(1, 4, 32, 64, 128, 2, 2, 0)  /* 17: DMA, M <= 128, narrow      */ \
-  X(1, 3, 32, 256, 128, 2, 2, 0) /* 18: DMA, large M               */ \
-  X(1, 2, 32, 256, 256, 2, 4, 0) /* 19: DMA, large M, 8 waves      */ \
-  X(1, 3, 32, 128, 256, 2, 2, 0) /* 20: DMA, M = 256               */ \
-  X(1, 4, 32, 64, 256, 1, 4, 0)  /* 21: DMA, M = 256, narrow       */ \
-  X(1, 8, 32, 128, 32, 4, 1, 0)  /* 22: DMA deep ring, M <= 32     */ \
-  X(1, 8, 16, 128, 16, 4, 1, 0)  /* 23: DMA deep ring, M <= 16     */ \
-  X(1, 6, 32, 128, 64, 2, 2, 0)  /* 24: DMA deep ring, M <= 64     */ \
-  X(1, 5, 32, 128, 128, 2, 2, 0) /* 25: DMA deep ring, M <= 128    */ \
-  X(1, 8, 16, 64, 16, 4, 1, 0)   /* 26: DMA deep ring, narrow      */ \
-  X(1, 8, 32, 64, 32, 2, 1, 0)   /* 27: DMA deep ring, 2 waves     */ \
-  X(2, 6, 16, 128, 16, 4, 1, 2)  /* 28: WS, M <= 16                */ \
-  X(2, 5, 32, 128, 32, 4, 1, 1)  /* 29: WS, M <= 32                */ \
-  X(2, 4, 32, 128, 64, 2, 2, 1)  /* 30: WS, M <= 64                */ \
-  X(2, 4, 32, 128, 128, 2, 2, 2) /* 31: WS, M <= 128               */ \
-  X(2, 3, 32, 96, 256, 1, 4, 2)  /* 32: WS, M = 256, 96-row tiles  */ \
-  X(2, 3, 32, 128, 256, 1, 4, 2) /* 33: WS, M = 256                */ \
-  X(2, 2, 32, 256, 192, 2, 3, 2) /* 34: WS, large M                */ \
-  X(2, 3, 32, 256, 128, 2, 2, 2) /* 35: WS, large M, 128 tokens    */ \
-  X(2, 8, 16, 64, 16, 4, 1, 1)   /* 36: WS, M <= 16, narrow        */ \
-  X(2, 5, 32, 64, 32, 2, 1, 1)   /* 37: WS, M <= 32, narrow        */ \
-  X(2, 2, 32, 192, 256, 3, 2, 2) /* 38: WS, large M, 256 tokens    */ \
-  X(1, 3, 32, 256, 128, 4, 2, 0) /* 39: DMA 8 waves, large M       */ \
-  X(1, 4, 32, 128, 128, 2, 4, 0) /* 40: DMA 8 waves, M <= 128      */ \
-  X(1, 3, 32, 128, 256, 2, 4, 0) /* 41: DMA 8 waves, M = 256       */ \
-  X(1, 4, 32, 64, 256, 1, 8, 0)  /* 42: DMA 8 waves, M = 256, narrow */ \
-  X(1, 4, 32, 128, 64, 4, 2, 0)  /* 43: DMA 8 waves, M <= 64       */ \
-  X(1, 4, 16, 128, 32, 8, 1, 0)  /* 44: DMA 8 waves, M <= 32       */ \
-  X(3, 4, 16, 64, 16, 4, 1, 0)   /* 45: direct, M <= 16            */ \
-  X(3, 4, 16, 128, 16, 4, 1, 0)  /* 46: direct, M <= 16, 2 frags   */ \
-  X(3, 2, 16, 64, 32, 4, 1, 0)   /* 47: direct, M <= 32            */ \
-  X(3, 4, 16, 128, 16, 8, 1, 0)  /* 48: direct, M <= 16, 8 waves   */ \
-  X(3, 8, 16, 64, 16, 4, 1, 0)   /* 49: direct, M <= 16, depth 8   */ \
-  X(3, 2, 16, 128, 32, 4, 1, 0)  /* 50: direct, M <= 32, 2 frags   */ \
-  X(1, 3, 32, 128, 256, 1, 4, 0) /* 51: DMA, M = 256, 128x64 waves */ \
-  X(1, 2, 32, 128, 256, 2, 4, 0) /* 52: DMA, M = 256, 2-slot ring  */ \
-  X(4, 3, 32, 128, 256, 2, 4, 0) /* 53: DMA+PF, M = 256            */ \
-  X(4, 4, 32, 128, 128, 2, 4, 0) /* 54: DMA+PF, M <= 128           */ \
-  X(4, 5, 32, 128, 128, 2, 4, 0) /* 55: DMA+PF, M <= 128, 5 slots  */ \
-  X(4, 3, 32, 256, 128, 4, 2, 0) /* 56: DMA+PF, large M            */ \
-  X(4, 3, 32, 128, 256, 1, 4, 0) /* 57: DMA+PF, M = 256, 4 waves   */ \
-  X(4, 4, 16, 128, 32, 8, 1, 0)  /* 58: DMA+PF, M <= 32            */ \
-  X(4, 6, 32, 128, 64, 4, 2, 0)  /* 59: DMA+PF, M <= 64            */ \
-  X(1, 3, 32, 96, 256, 1, 4, 0)  /* 60: DMA, M = 256, 96-row tiles */ \
-  X(1, 3, 32, 96, 256, 3, 2, 0)  /* 61: DMA, M = 256, 96 rows, 6 waves */ \
-  X(5, 3, 32, 128, 256, 2, 4, 0) /* 62: DMA+IP, M = 256, 8 waves    */ \
-  X(5, 3, 32, 128, 256, 1, 4, 0) /* 63: DMA+IP, M = 256, 128x64 waves */ \
-  X(5, 3, 32, 128, 256, 2, 2, 0) /* 64: DMA+IP, M = 256, 64x128 waves */ \
-  X(5, 3, 32, 96, 256, 1, 4, 0)  /* 65: DMA+IP, M = 256, 96-row tiles */ \
-  X(5, 2, 32, 256, 256, 2, 4, 0) /* 66: DMA+IP, large M             */ \
-  X(5, 4, 32, 128, 128, 2, 4, 0) /* 67: DMA+IP, M <= 128            */ \
-  X(5, 4, 16, 128, 32, 8, 1, 0)  /* 68: DMA+IP, M <= 32             */ \
-  X(5, 4, 32, 128, 64, 4, 2, 0)  /* 69: DMA+IP, M <= 64             */ \
-  X(1, 4, 32, 192, 128, 2, 2, 0) /* 70: DMA, 192x128, 4 waves       */ \
-  X(1, 3, 32, 192, 128, 2, 2, 0) /* 71: DMA, 192x128, 3 slots       */ \
-  X(5, 4, 32, 192, 128, 2, 2, 0) /* 72: DMA+IP, 192x128             */ \
-  X(1, 4, 32, 160, 128, 5, 1, 0) /* 73: DMA, 160x128, 5 waves       */ \
-  X(1, 4, 32, 192, 64, 2, 2, 0)  /* 74: DMA, 192x64                 */
+#define QR_TILES(X)                                                       \
+  X(0, 4, 16, 128, 32, 8, 1)  /*  0: M <= 32, weight streaming        */ \
+  X(0, 4, 32, 128, 64, 4, 2)  /*  1: M <= 64; narrow 256-token layers */ \
+  X(0, 4, 32, 128, 128, 2, 4) /*  2: M <= 128; long-K 256-token ones  */ \
+  X(0, 3, 32, 192, 128, 2, 2) /*  3: wide 256-token layers            */ \
+  X(0, 3, 32, 256, 128, 4, 2) /*  4: long-K / narrow large-M layers   */ \
+  X(0, 2, 32, 256, 256, 2, 4) /*  5: wide large-M layers              */ \
+  X(0, 3, 32, 128, 256, 2, 4) /*  6: 256-token alternative            */ \
+  X(0, 3, 32, 96, 256, 1, 4)  /*  7: 256-token alternative, 96 rows   */ \
+  X(0, 4, 32, 128, 32, 4, 1)  /*  8: M <= 32 alternative, 4 waves     */ \
+  X(0, 4, 16, 64, 16, 4, 1)   /*  9: M <= 16 alternative, narrow      */ \
+  X(1, 3, 32, 192, 128, 2, 2) /* 10: interleaved variant of tile 3    */ \
+  X(1, 4, 16, 128, 32, 8, 1)  /* 11: interleaved variant of tile 0    */ \
+  X(2, 4, 16, 128, 16, 8, 1)  /* 12: direct, M <= 16                  */ \
+  X(2, 2, 16, 128, 32, 4, 1)  /* 13: direct, M <= 32                  */
 
 #define QR_STR(x) #x
-#define QR_DESC(KIND, S, T, BN, BM, WN, WM, NP)                                  \
-  {KIND == 3   ? "dir" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN                \
-   : KIND == 2 ? "ws" QR_STR(S) "p" #NP "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM \
-   : KIND == 5 ? "dmaip" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM      \
-   : KIND == 4 ? "dmapf" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM      \
-   : KIND == 1 ? "dma" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM        \
-               : "reg_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM,                    \
-   T, BN, BM, 128, 64 * (WN * WM + NP), S},
+#define QR_DESC(KIND, S, T, BN, BM, WN, WM)                                        \
+  {KIND == 2   ? "dir" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN                \
+   : KIND == 1 ? "dmaip" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM      \
+               : "dma" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM,       \
+   T, BN, BM, 128, 64 * WN * WM, S},
 const TileDesc kTiles[] = {QR_TILES(QR_DESC)};
 #undef QR_DESC
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-template <int QT, int KIND, int S, int T, int BN, int BM, int WN, int WM, int NP>
+template <int QT, int KIND, int S, int T, int BN, int BM, int WN, int WM>
 hipError_t launch_one(const KParams& kp, unsigned grid, hipStream_t st) {
-  if constexpr (KIND == 0)
-    hipLaunchKernelGGL((gemm_kernel<QT, T, BN, BM, 128, WN, WM>), dim3(grid), dim3(64 * WN * WM),
-                       0, st, kp);
-  else if constexpr (KIND == 1 || KIND == 4 || KIND == 5)
-    hipLaunchKernelGGL(
-        (gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, KIND == 4 ? 2 : KIND == 5 ? 1 : 0>),
-        dim3(grid), dim3(64 * WN * WM), 0, st, kp);
-  else if constexpr (KIND == 2)
-    hipLaunchKernelGGL((gemm_ws_kernel<QT, T, BN, BM, WN, WM, NP, S>), dim3(grid),
-                       dim3(64 * (WN * WM + NP)), 0, st, kp);
-  else
+  if constexpr (KIND == 2)
     hipLaunchKernelGGL((gemm_direct_kernel<QT, BN, BM, WN, S>), dim3(grid), dim3(64 * WN), 0, st,
                        kp);
+  else
+    hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, KIND == 1>), dim3(grid),
+                       dim3(64 * WN * WM), 0, st, kp);
   return hipGetLastError();
 }
 
@@ -1263,11 +798,11 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   const unsigned grid = (unsigned)(plan.tiles_n * plan.tiles_m * plan.splitk);
   hipError_t e = hipErrorInvalidValue;
   int idx = 0;
-#define QR_CASE(KIND, S, T, BN, BM, WN, WM, NP)                                        \
-  if (plan.tile == idx) {                                                               \
-    e = qt == kQInt8 ? launch_one<kQInt8, KIND, S, T, BN, BM, WN, WM, NP>(kp, grid, st) \
-                     : launch_one<kQFp8, KIND, S, T, BN, BM, WN, WM, NP>(kp, grid, st); \
-  }                                                                                     \
+#define QR_CASE(KIND, S, T, BN, BM, WN, WM)                                        \
+  if (plan.tile == idx) {                                                           \
+    e = qt == kQInt8 ? launch_one<kQInt8, KIND, S, T, BN, BM, WN, WM>(kp, grid, st) \
+                     : launch_one<kQFp8, KIND, S, T, BN, BM, WN, WM>(kp, grid, st); \
+  }                                                                                 \
   ++idx;
   QR_TILES(QR_CASE)
 #undef QR_CASE

@@ -91,21 +91,21 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
   if (force_tile >= 0) {
     tile = force_tile;
   } else if (M <= 32) {
-    tile = 44;
+    tile = 0;
   } else if (M <= 64) {
-    tile = 43;
+    tile = 1;
   } else if (M <= 128) {
-    tile = 40;
+    tile = 2;
   } else if (M <= 256) {
-    if (N >= 8192) tile = 71;
-    else if (nks >= 64) tile = 40;
-    else tile = N >= 4096 ? 43 : 44;
+    if (N >= 8192) tile = 3;
+    else if (nks >= 64) tile = 2;
+    else tile = N >= 4096 ? 1 : 0;
   } else if (M <= 1024) {
-    if (N >= 16384) tile = 19;
-    else if (N <= 2048) tile = 44;
-    else tile = nks >= 64 ? 39 : 40;
+    if (N >= 16384) tile = 5;
+    else if (N <= 2048) tile = 0;
+    else tile = nks >= 64 ? 4 : 2;
   } else {
-    tile = N >= 7168 ? 19 : 39;
+    tile = N >= 7168 ? 5 : 4;
   }
   const TileDesc& d = tile_desc(tile);
   p.tile = tile;

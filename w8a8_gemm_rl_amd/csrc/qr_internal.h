@@ -21,7 +21,7 @@ struct TileDesc {
   int BM;  // macro-tile extent along M (tokens)
   int BK;  // bytes of K per pipeline stage
   int NT;  // threads per block
-  int S;   // LDS-DMA ring slots; 0 for the register-staged kernel
+  int S;   // LDS-DMA ring slots (prefetch depth in K steps for the direct kernel)
 };
 
 int num_tiles();
