@@ -38,6 +38,7 @@ DOM_BATCH = 20  # dominant-GEMM launches per timing graph
 WORKLOADS = {
     "7b_decode_int8": dict(M=256, qt="int8", chain="7b", sets=4, kind="outliers"),
     "7b_decode_fp8": dict(M=256, qt="fp8", chain="7b", sets=4, kind="outliers"),
+    "7b_decode_int8_gateup": dict(M=256, qt="int8", chain="7b_gateup", sets=4, kind="outliers"),
     "32b_decode_int8": dict(M=512, qt="int8", chain="32b", sets=2, kind="normal"),
     "32b_decode_fp8": dict(M=512, qt="fp8", chain="32b", sets=2, kind="normal"),
     "32b_prefill_int8": dict(M=4096, qt="int8", chain="32b_prefill", sets=2, kind="heavy"),
@@ -53,6 +54,8 @@ def chain_spec(name):
 
     if name == "7b":
         return I.CHAIN_7B, I.LINEARS_7B, I.W_SIGMA_7B
+    if name == "7b_gateup":
+        return I.CHAIN_7B_GATEUP, I.LINEARS_7B, I.W_SIGMA_7B
     if name == "32b":
         return I.CHAIN_32B, I.LINEARS_32B, I.W_SIGMA_32B
     if name == "32b_prefill":

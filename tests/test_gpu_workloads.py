@@ -88,6 +88,30 @@ def test_7b_decode_chain_int8_full():
     _int8_chain("7b", 2, I.CHAIN_7B, I.LINEARS_7B, I.W_SIGMA_7B, 256, "outliers", 256)
 
 
+def test_7b_decode_chain_int8_gate_up_stacked():
+    # gate and up as one GEMM over [W_gate; W_up] (N = 37888): the device
+    # chain with the stacked linear equals the oracle chain with separate
+    # gate and up, bit for bit, on sampled tokens.
+    idx, M = 2, 256
+    x0 = I.activations(M, 3584, seed=I.matrix_seed(idx, 0), kind="outliers")
+    Wdev, layers = {}, []
+    for L in I.CHAIN_7B:
+        N, K = I.LINEARS_7B[L["name"]]
+        ref, dev = _quant_full_int8(_weights("7b", L["name"], N, K, I.W_SIGMA_7B, idx))
+        Wdev[L["name"]] = dev
+        layers.append(dict(L, Wq=ref["Wq"], scale_w=ref["scale_w"], act_mult=I.UAQ_S))
+    Wdev["gateup"] = (torch.cat([Wdev["gate"][0], Wdev["up"][0]]),
+                      torch.cat([Wdev["gate"][1], Wdev["up"][1]]))
+    got = _device_chain(I.CHAIN_7B_GATEUP, x0, Wdev, "int8")
+    rows = _sample(M, 48, seed=7)
+    oref = O.decode_chain(x0[rows], layers, "int8")
+    n = I.LINEARS_7B["gate"][0]
+    assert np.array_equal(got["gateup"][rows, :n], oref["gate"]["y"])
+    assert np.array_equal(got["gateup"][rows, n:], oref["up"]["y"])
+    for name in ("qkv", "o", "down"):
+        assert np.array_equal(got[name][rows], oref[name]["y"]), name
+
+
 def test_32b_decode_chain_int8_m512_sampled_tokens():
     _int8_chain("32b", 5, I.CHAIN_32B, I.LINEARS_32B, I.W_SIGMA_32B, 512, "normal", 128)
 

@@ -27,6 +27,7 @@ LINEARS_7B = {
     "gate": (18944, 3584),
     "up": (18944, 3584),
     "down": (3584, 18944),
+    "gateup": (37888, 3584),  # gate and up stacked along N (one GEMM, shared input)
 }
 W_SIGMA_7B = 0.02
 
@@ -53,6 +54,15 @@ CHAIN_7B = [
     dict(name="gate", src="o", cols=None),
     dict(name="up", src="o", cols=None),
     dict(name="down", src="up", cols=None),
+]
+# The same layer with gate and up as one GEMM over the stacked weights
+# [W_gate; W_up]: per-channel codes and scales are per row, so its outputs are
+# the gate outputs followed by the up outputs, bit for bit.
+CHAIN_7B_GATEUP = [
+    dict(name="qkv", src="x0", cols=None),
+    dict(name="o", src="qkv", cols=(0, 3584)),
+    dict(name="gateup", src="o", cols=None),
+    dict(name="down", src="gateup", cols=(18944, 37888)),
 ]
 CHAIN_32B = [
     dict(name="q", src="x0", cols=None),
