@@ -219,6 +219,35 @@ def decode_chain(x0_bits, layers, qt):
 # The update-masking experiment (paper notes, "Key designs > UAQ", motivation)
 # ----------------------------------------------------------------------------
 
+def count_flips(codes_old, codes_new, qt):
+    """Number of positions whose code now stands for a different value.
+
+    INT8: codes differ. FP8 (E4M3FN bytes): codes differ, except that +0
+    (0x00) and -0 (0x80) are the same value (reading: a sign change below
+    the smallest step is no change of the quantized weight).
+    """
+    _check_qt(qt)
+    a = np.asarray(codes_old).view(np.uint8).reshape(-1)
+    b = np.asarray(codes_new).view(np.uint8).reshape(-1)
+    if a.shape != b.shape:
+        raise ValueError("count_flips: shapes differ")
+    diff = a != b
+    if qt == "fp8":
+        diff &= ~(((a | b) == 0x80) & ((a & b) == 0))
+    return int(np.count_nonzero(diff))
+
+
+def requantize_weights(Wp, qt, codes_old=None):
+    """Per-RL-step refresh theta_old -> theta_hat_old (paper notes, "Overall
+    framework"; the stored parameter is already W' = W / s under UAQ, so s = 1
+    here): per-output-channel quantization of W', and the number of codes that
+    changed since the previous refresh (codes_old), if given.
+    Returns (codes, scale, flips or None)."""
+    codes, scale = quantize_rows(Wp, qt)
+    flips = None if codes_old is None else count_flips(codes_old, codes, qt)
+    return codes, scale, flips
+
+
 def flip_counts(W, dW, s, qt):
     """Count weight codes changed by a small update, with and without UAQ.
 
@@ -243,12 +272,12 @@ def flip_counts(W, dW, s, qt):
     Ws = (W / s32).astype(np.float32)
     cs = codes(Ws)
     out = {
-        "base": int(np.count_nonzero(codes((W + dW).astype(np.float32)) != c0)),
-        "uaq_same": int(np.count_nonzero(codes((Ws + dW).astype(np.float32)) != cs)),
-        "uaq_pages": int(np.count_nonzero(
-            codes((Ws + (dW * s32).astype(np.float32)).astype(np.float32)) != cs)),
-        "control": int(np.count_nonzero(
-            codes((Ws + (dW / s32).astype(np.float32)).astype(np.float32)) != cs)),
+        "base": count_flips(c0, codes((W + dW).astype(np.float32)), qt),
+        "uaq_same": count_flips(cs, codes((Ws + dW).astype(np.float32)), qt),
+        "uaq_pages": count_flips(cs, codes((Ws + (dW * s32).astype(np.float32)).astype(np.float32)),
+                                 qt),
+        "control": count_flips(cs, codes((Ws + (dW / s32).astype(np.float32)).astype(np.float32)),
+                               qt),
         "n": int(W.size),
     }
     return out

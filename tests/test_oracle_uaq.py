@@ -165,3 +165,56 @@ def test_flip_expectation_closed_form_special_case():
     v = 0.01 / (a / 127)
     p = np.sqrt(2 / np.pi) * sigma * np.sqrt((127 / a) ** 2 + (v / a) ** 2)
     assert O.flip_expectation(W, sigma, "int8") == pytest.approx(3 * p, rel=1e-12)
+
+
+# ------------------------------------------------- per-step refresh and flip counting
+
+def test_count_flips_special_cases():
+    rng = np.random.default_rng(3)
+    a = rng.integers(-127, 128, size=1000, dtype=np.int64).astype(np.int8)
+    assert O.count_flips(a, a, "int8") == 0
+    b = a.copy()
+    b[[5, 17, 999]] += 1
+    b[[5, 17, 999]] = np.where(b[[5, 17, 999]] == a[[5, 17, 999]], b[[5, 17, 999]] - 2, b[[5, 17, 999]])
+    assert O.count_flips(a, b, "int8") == 3
+    # INT8: byte 0x80 (-128) is a different value from 0 (it is never produced, but if present it counts)
+    assert O.count_flips(np.array([0], np.int8), np.array([-128], np.int8), "int8") == 1
+    # FP8: +0 and -0 are one value; every other byte change is a change of value
+    assert O.count_flips(np.array([0x00, 0x80, 0x01], np.uint8),
+                         np.array([0x80, 0x00, 0x81], np.uint8), "fp8") == 1
+
+
+def test_count_flips_fp8_matches_decoded_values_for_every_pair():
+    """Exhaustive over all pairs of finite E4M3FN bytes: a flip is a change of decoded value."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)  # drop the NaNs
+    a = np.repeat(codes, codes.size)
+    b = np.tile(codes, codes.size)
+    expect = int(np.count_nonzero(F.e4m3fn_decode(a) != F.e4m3fn_decode(b)))
+    assert O.count_flips(a, b, "fp8") == expect
+    # brute force on a random sample against a plain Python loop over values
+    rng = np.random.default_rng(4)
+    x = rng.choice(codes, 4000)
+    y = rng.choice(codes, 4000)
+    loop = sum(1 for u, v in zip(x.tolist(), y.tolist())
+               if float(F.e4m3fn_decode(np.array([u], np.uint8))[0])
+               != float(F.e4m3fn_decode(np.array([v], np.uint8))[0]))
+    assert O.count_flips(x, y, "fp8") == loop
+
+
+@pytest.mark.parametrize("qt", ["int8", "fp8"])
+def test_requantize_weights_is_quantize_rows_plus_count(qt):
+    Wp = I.weights(48, 256, 0.02, seed=7)
+    c0, s0, f0 = O.requantize_weights(Wp, qt)
+    assert f0 is None
+    rc, rs = O.quantize_rows(Wp, qt)
+    assert np.array_equal(c0.view(np.uint8), rc.view(np.uint8)) and np.array_equal(s0, rs)
+    # an update far below one step changes few codes; the refresh counts exactly those
+    Wn = (Wp + I.normal_f32(Wp.shape, 1e-4, seed=8)).astype(np.float32)
+    c1, s1, f1 = O.requantize_weights(Wn, qt, c0)
+    assert f1 == O.count_flips(c0, c1, qt) and 0 < f1 < c0.size // 4
+    # s = 1 requantization of W' equals the UAQ quantizer's codes of W with W' = fl32(W / s)
+    W = I.weights(16, 128, 0.02, seed=9)
+    ref = O.quantize_weights_uaq(W, 1.5, qt)
+    c2, s2, _ = O.requantize_weights(ref["W_scaled"], qt)
+    assert np.array_equal(c2.view(np.uint8), ref["Wq"].view(np.uint8))
+    assert np.array_equal(s2, ref["scale_w"])
