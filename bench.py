@@ -45,6 +45,17 @@ WORKLOADS = {
 }
 
 
+# Per-RL-step weight refresh of a whole model's layer stack: every stored
+# parameter matrix W' (fp32) is requantized into its codes, counting the codes
+# the last update changed. One step = one refresh of the whole stack.
+REFRESH = {
+    "refresh_7b_int8": dict(stack="7b", qt="int8"),
+    "refresh_7b_fp8": dict(stack="7b", qt="fp8"),
+    "refresh_32b_int8": dict(stack="32b", qt="int8"),
+}
+REFRESH_METRIC = "per-RL-step weight refresh (requantize + flip count) GB/s vs HBM roofline"
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -131,13 +142,19 @@ class Layer:
                 e[1].record()
 
 
-def gemm_source_sha256():
-    """Hash of the sources that define the GEMM kernels and their plans."""
+KERNEL_SOURCES = {
+    "gemm": ("gemm_kernels.hip", "qr_api.hip", "qr_internal.h", "qr_device.h"),
+    "refresh": ("quant_kernels.hip", "qr_api.hip", "qr_internal.h", "qr_device.h"),
+}
+
+
+def kernel_source_sha256(kind="gemm"):
+    """Hash of the sources that define a kernel family (GEMM or refresh) and its launch."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w8a8_gemm_rl_amd", "csrc")
-    for f in ("gemm_kernels.hip", "qr_api.hip", "qr_internal.h", "qr_device.h"):
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -146,13 +163,13 @@ def gemm_source_sha256():
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
-def committed_traffic(key):
+def committed_traffic(key, kind="gemm"):
     """HBM bytes per launch of a kernel from the committed rocprofv3 counter
-    summary, or None if there is none for `key` or the GEMM sources changed
-    since the counters were taken."""
+    summary, or None if there is none for `key` or the kernel's sources
+    changed since the counters were taken."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    sha = gemm_source_sha256()
+    sha = kernel_source_sha256(kind)
     with open(TRAFFIC_FILE) as f:
         for line in f:
             cells = [c.strip() for c in line.strip().strip("|").split("|")]
@@ -163,14 +180,19 @@ def committed_traffic(key):
     return None
 
 
-def is_gemm_kernel(name):
-    """True for the main GEMM kernels (any tile family), not the split-K reduction."""
+KERNEL_PATTERNS = {
+    "gemm": r"gemm_\w*kernel",  # the main GEMM kernels (any tile family), not the split-K reduction
+    "refresh": r"weight_quant_kernel<[^>]*true>",  # the weight quantizer with flip counting
+}
+
+
+def is_kernel(name, kind="gemm"):
     import re
 
-    return re.search(r"gemm_\w*kernel", name) is not None
+    return re.search(KERNEL_PATTERNS[kind], name) is not None
 
 
-def summarize_rocprof(paths, grid):
+def summarize_rocprof(paths, grid, kind="gemm"):
     """Print the figures used from rocprofv3 CSV outputs (kernel trace, or a
     --pmc counter collection) for dispatches of the given grid size."""
     import csv
@@ -181,7 +203,7 @@ def summarize_rocprof(paths, grid):
         if rows and "Counter_Name" in rows[0]:
             by = {}
             for r in rows:
-                if int(r["Grid_Size"]) == grid and is_gemm_kernel(r["Kernel_Name"]):
+                if int(r["Grid_Size"]) == grid and is_kernel(r["Kernel_Name"], kind):
                     by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
             for c, v in by.items():
                 print(f"{path}: {c} per dispatch (grid {grid}): mean {statistics.mean(v):.1f} KiB, "
@@ -192,9 +214,9 @@ def summarize_rocprof(paths, grid):
                           f"{r['Counter_Name']} {float(r['Counter_Value']):.1f}")
         else:
             ds = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0 for r in rows
-                  if int(r["Grid_Size_X"]) == grid and is_gemm_kernel(r["Kernel_Name"])]
+                  if int(r["Grid_Size_X"]) == grid and is_kernel(r["Kernel_Name"], kind)]
             if ds:
-                print(f"{path}: gemm dispatches of grid {grid}: n={len(ds)} mean {statistics.mean(ds):.2f} us "
+                print(f"{path}: {kind} dispatches of grid {grid}: n={len(ds)} mean {statistics.mean(ds):.2f} us "
                       f"median {statistics.median(ds):.2f} us min {min(ds):.2f} us")
 
 
@@ -233,29 +255,223 @@ def cpu_baseline(chain, shapes, M, qt, sigma, kind, s):
     return dt / steps, steps, threads
 
 
+def refresh_bytes(N, K):
+    """Algorithmic bytes of one refresh launch: fp32 parameters read, previous
+    codes read, new codes written, scales and per-row change counts written."""
+    return 6 * N * K + 8 * N
+
+
+def refresh_cpu_baseline(qt, N, K, sigma, s):
+    """Time the CPU oracle's refresh (requantize + flip count) of one matrix."""
+    import numpy as np
+
+    import oracle as O
+    from w8a8_gemm_rl_amd import inputs as I
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    s32 = np.float32(s)
+    Wp = (I.weights(N, K, sigma, seed=I.matrix_seed(9, 0)) / s32).astype(np.float32)
+    c0, _, _ = O.requantize_weights(Wp, qt)
+    Wp += (I.normal_f32((N, K), I.DW_SIGMA, seed=I.matrix_seed(9, 1)) * s32).astype(np.float32)
+    log("cpu baseline: timing oracle refreshes (about 10 s) ...")
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        O.requantize_weights(Wp, qt, codes_old=c0)
+        n += 1
+        dt = time.perf_counter() - t0
+        if dt >= 10.0 or n >= 30:
+            break
+    return dt / n, n, threads
+
+
+def run_refresh(args, dev):
+    """Per-RL-step refresh of a whole layer stack (one step = every matrix of
+    every layer requantized, with the codes each update changed counted)."""
+    import numpy as np
+    import torch
+
+    from w8a8_gemm_rl_amd import binding as B
+    from w8a8_gemm_rl_amd import inputs as I
+
+    wl = REFRESH[args.workload]
+    stack = I.STACK_7B if wl["stack"] == "7b" else I.STACK_32B
+    qt, s, nl = wl["qt"], args.uaq_s, stack["layers"]
+    names = stack["names"]
+    shapes = {n: stack["linears"][n] for n in names}
+    sigma_p = stack["sigma"] / s  # stored parameters W' = W / s
+    upd = s * I.DW_SIGMA  # the update on W' (the pages' size, grown by s)
+
+    # Stored parameters and codes of every layer, generated on the device.
+    log(f"bench: {args.workload}: {nl} layers x {', '.join(f'{n} {shapes[n][0]}x{shapes[n][1]}' for n in names)}")
+    g = torch.Generator(device=dev)
+    Wp, Wq, Sw = [], [], []
+    for l in range(nl):
+        Wp.append({}), Wq.append({}), Sw.append({})
+        for j, n in enumerate(names):
+            N, K = shapes[n]
+            g.manual_seed(7000 + 16 * l + j)
+            Wp[l][n] = torch.randn((N, K), generator=g, device=dev).mul_(sigma_p)
+            Wq[l][n] = torch.empty((N, K), dtype=B.code_dtype(qt), device=dev)
+            Sw[l][n] = torch.empty(N, dtype=torch.float32, device=dev)
+            B.requantize_weights(Wp[l][n], qt, Wq[l][n], Sw[l][n])
+    # Per-row change counts of every matrix: slices of one int32 buffer.
+    offs, o = {}, 0
+    for l in range(nl):
+        for n in names:
+            offs[l, n] = (o, o + shapes[n][0])
+            o += shapes[n][0]
+    row_flips = torch.zeros(o, dtype=torch.int32, device=dev)
+    rf = {k: row_flips[a:b] for k, (a, b) in offs.items()}
+    spare = torch.zeros(max(N for N, _ in shapes.values()), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    params = nl * sum(N * K for N, K in shapes.values())
+    bytes_step = nl * sum(refresh_bytes(N, K) for N, K in shapes.values())
+
+    def refresh_all():
+        for l in range(nl):
+            for j, n in enumerate(names):
+                B.requantize_weights(Wp[l][n], qt, Wq[l][n], Sw[l][n], row_flips=rf[l, n])
+
+    def update():
+        for l in range(nl):
+            for n in names:
+                Wp[l][n].add_(torch.randn(Wp[l][n].shape, generator=g, device=dev), alpha=upd)
+
+    # The whole refresh as one HIP graph; the dominant launch (the largest
+    # matrix) alone in a graph of DOM_BATCH launches over the layers.
+    dom = max(names, key=lambda n: shapes[n][0] * shapes[n][1])
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    whole, dom_graph = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        refresh_all()  # untimed: codes now match the parameters
+        with torch.cuda.graph(whole, stream=st):
+            refresh_all()
+        with torch.cuda.graph(dom_graph, stream=st):
+            for i in range(DOM_BATCH):
+                l = i % nl
+                B.requantize_weights(Wp[l][dom], qt, Wq[l][dom], Sw[l][dom],
+                                     row_flips=spare[:shapes[dom][0]])
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        whole.replay()
+    torch.cuda.synchronize()
+
+    # Timed: K refreshes, each after an untimed update of every parameter.
+    g.manual_seed(99)
+    K = args.steps
+    log(f"bench: timing {K} refresh steps (updates between them untimed)")
+    total = 0.0
+    acc = torch.zeros(row_flips.shape, dtype=torch.int64, device=dev)
+    for _ in range(K):
+        update()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        whole.replay()
+        torch.cuda.synchronize()
+        total += time.perf_counter() - t0
+        acc += row_flips
+    sec_step = total / K
+
+    reps = 5
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        dom_graph.replay()
+        b.record()
+    torch.cuda.synchronize()
+    dom_us = 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / (reps * DOM_BATCH)
+
+    acc = acc.cpu().numpy()
+    fl = np.array([[acc[offs[l, n][0]:offs[l, n][1]].sum() for n in names] for l in range(nl)],
+                  dtype=float) / max(K, 1)
+    flip_stats = {
+        n: dict(N=shapes[n][0], K=shapes[n][1], mean_flips=round(float(fl[:, j].mean()), 1),
+                frac=float(f"{fl[:, j].mean() / (shapes[n][0] * shapes[n][1]):.3e}"),
+                min_layer=round(float(fl[:, j].min()), 1), max_layer=round(float(fl[:, j].max()), 1))
+        for j, n in enumerate(names)}
+    per_layer = [round(float(v), 1) for v in fl.sum(axis=1)]
+
+    Nd, Kd = shapes[dom]
+    dbytes = refresh_bytes(Nd, Kd)
+    achieved = dbytes / (dom_us * 1e-6) / 1e9
+    key = f"{args.workload}:{dom}:N{Nd}:K{Kd}"
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(key, "refresh"),
+        "traffic_key": key, "kernel": f"refresh of {dom} {Nd}x{Kd} ({qt}, flip count)",
+        "kernel_us": round(dom_us, 2), "alg_bytes_per_launch": dbytes,
+    }
+    cpu = None
+    if not args.no_cpu_baseline:
+        Nq, Kq = shapes["qkv"]
+        dt, n, threads = refresh_cpu_baseline(qt, Nq, Kq, stack["sigma"], s)
+        cpu = {"value": round(refresh_bytes(Nq, Kq) / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{n} refreshes of one {Nq}x{Kq} QKV matrix (requantize + flip count) by "
+                         f"the numpy oracle, {dt:.3f} s each",
+               "seconds_per_refresh": round(dt, 4), "host_cpus": os.cpu_count()}
+    code_bytes = params + 4 * nl * sum(N for N, _ in shapes.values())
+    out = {
+        "metric": REFRESH_METRIC,
+        "value": round(bytes_step / sec_step / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(sec_step * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: refresh of {nl} layers x ({', '.join(f'{n} {shapes[n][0]}x{shapes[n][1]}' for n in names)}) "
+                        f"= {params / 1e9:.2f} B parameters into {qt} codes, after an update "
+                        f"N(0, ({s} x 1e-7)^2) of every stored W' = W / {s}",
+            "layers": nl, "qtype": qt, "uaq_s": s, "params": params, "timing": "hip_graph",
+            "parallelism": "none (1 GPU)",
+        },
+        "params_per_s": float(f"{params / sec_step:.4e}"),
+        "alg_bytes_per_step": bytes_step,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "flips": flip_stats,
+        "flips_per_layer": per_layer,
+        "broadcast_bytes": {"codes_and_scales": code_bytes, "bf16": 2 * params,
+                            "ratio": round(code_bytes / (2 * params), 4)},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="7b_decode_int8", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="7b_decode_int8", choices=sorted(WORKLOADS) + sorted(REFRESH))
     ap.add_argument("--m", type=int, default=None, help="override the token count M")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--summarize-rocprof", nargs="+", metavar="CSV",
                     help="print the figures used from rocprofv3 CSV files (with --grid) and exit")
     ap.add_argument("--grid", type=int, default=0, help="grid size (threads) of the dispatches to summarize")
-    ap.add_argument("--source-sha", action="store_true", help="print the GEMM source hash and exit")
+    ap.add_argument("--kernel-kind", default="gemm", choices=sorted(KERNEL_PATTERNS),
+                    help="kernel family for --summarize-rocprof and --source-sha")
+    ap.add_argument("--source-sha", action="store_true", help="print the kernel family's source hash and exit")
+    ap.add_argument("--uaq-s", type=float, default=1.5,
+                    help="refresh workloads: UAQ factor s (stored W' = W / s, update s * dW)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
     args = ap.parse_args()
 
     if args.summarize_rocprof:
-        summarize_rocprof(args.summarize_rocprof, args.grid)
+        summarize_rocprof(args.summarize_rocprof, args.grid, args.kernel_kind)
         return
     if args.source_sha:
-        print(gemm_source_sha256()[:16])
+        print(kernel_source_sha256(args.kernel_kind)[:16])
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -283,6 +499,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
         return
     B.lib()
+    if args.workload in REFRESH:
+        run_refresh(args, dev)
+        return
 
     wl = dict(WORKLOADS[args.workload])
     if args.m is not None:

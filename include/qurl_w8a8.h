@@ -109,6 +109,31 @@ int qr_quantize_weights_uaq(const float* W, int64_t N, int64_t K, int64_t ldw, f
                             void* stream);
 
 /*
+ * qr_requantize_weights -- the per-RL-step refresh theta_old -> theta_hat_old
+ * [Notes/Framework] of a stored parameter that is already W' = W / s, with,
+ * per output channel, the number of codes the update changed [Notes/UAQ:
+ * updates far below one step leave almost every code unchanged].
+ *
+ * Per output channel n of Wp (s = 1, so W' itself is quantized):
+ *   scale_w[n] = fl32(max_k |Wp[n,k]| / Q), codes from fl32(Wp[n,k] / scale_w[n])
+ * exactly as qr_quantize_weights_uaq with s = 1. If row_flips is non-NULL,
+ * Wq must hold the previous codes on entry: every code is compared with the
+ * one it overwrites and row_flips[n] receives the number of positions of
+ * row n whose value changed (INT8: any byte change; E4M3FN: any byte change
+ * except +0 <-> -0). Counts are written, not accumulated, with plain stores
+ * (no atomics: many waves adding to one device counter serialize).
+ *
+ *   Wp        [N, ldw] fp32 stored parameters (read).
+ *   qt        QR_INT8 or QR_FP8_E4M3FN.
+ *   Wq        [N, K] codes (previous codes read when counting, new codes written).
+ *   scale_w   [N] fp32 per-channel scales (written).
+ *   row_flips NULL, or [N] uint32 per-channel change counts (written).
+ * Errors as for qr_quantize_weights_uaq; nothing is launched on an error.
+ */
+int qr_requantize_weights(const float* Wp, int64_t N, int64_t K, int64_t ldw, int qt, void* Wq,
+                          float* scale_w, uint32_t* row_flips, void* stream);
+
+/*
  * qr_quantize_act_per_token -- token-wise absmax quantization [Notes/Training].
  *
  * For every token m (row of X), with x = X[m,:] widened exactly to fp32:

@@ -219,32 +219,47 @@ def decode_chain(x0_bits, layers, qt):
 # The update-masking experiment (paper notes, "Key designs > UAQ", motivation)
 # ----------------------------------------------------------------------------
 
-def count_flips(codes_old, codes_new, qt):
-    """Number of positions whose code now stands for a different value.
+def _changed(a, b, qt):
+    """Positions whose code now stands for a different value.
 
     INT8: codes differ. FP8 (E4M3FN bytes): codes differ, except that +0
     (0x00) and -0 (0x80) are the same value (reading: a sign change below
     the smallest step is no change of the quantized weight).
     """
+    diff = a != b
+    if qt == "fp8":
+        diff &= ~(((a | b) == 0x80) & ((a & b) == 0))
+    return diff
+
+
+def count_flips(codes_old, codes_new, qt):
+    """Number of positions whose code now stands for a different value."""
     _check_qt(qt)
     a = np.asarray(codes_old).view(np.uint8).reshape(-1)
     b = np.asarray(codes_new).view(np.uint8).reshape(-1)
     if a.shape != b.shape:
         raise ValueError("count_flips: shapes differ")
-    diff = a != b
-    if qt == "fp8":
-        diff &= ~(((a | b) == 0x80) & ((a & b) == 0))
-    return int(np.count_nonzero(diff))
+    return int(np.count_nonzero(_changed(a, b, qt)))
+
+
+def count_flips_rows(codes_old, codes_new, qt):
+    """count_flips of each row (output channel) of two [N, K] code matrices."""
+    _check_qt(qt)
+    a = np.asarray(codes_old).view(np.uint8)
+    b = np.asarray(codes_new).view(np.uint8)
+    if a.ndim != 2 or a.shape != b.shape:
+        raise ValueError("count_flips_rows: two [N, K] matrices of one shape expected")
+    return _changed(a, b, qt).sum(axis=1, dtype=np.int64)
 
 
 def requantize_weights(Wp, qt, codes_old=None):
     """Per-RL-step refresh theta_old -> theta_hat_old (paper notes, "Overall
     framework"; the stored parameter is already W' = W / s under UAQ, so s = 1
-    here): per-output-channel quantization of W', and the number of codes that
-    changed since the previous refresh (codes_old), if given.
-    Returns (codes, scale, flips or None)."""
+    here): per-output-channel quantization of W', and per channel the number
+    of codes that changed since the previous refresh (codes_old), if given.
+    Returns (codes, scale, row_flips or None)."""
     codes, scale = quantize_rows(Wp, qt)
-    flips = None if codes_old is None else count_flips(codes_old, codes, qt)
+    flips = None if codes_old is None else count_flips_rows(codes_old, codes, qt)
     return codes, scale, flips
 
 

@@ -38,7 +38,8 @@ def _reset_plan():
 
 @pytest.mark.parametrize("qt", QTS)
 @pytest.mark.parametrize("N,K,s", [(512, 512, 1.5), (37, 48, 1.5), (5, 16, 2.0), (64, 3584, 1.5),
-                                   (3, 40960, 1.5), (300, 1024, 1.0)])
+                                   (3, 40960, 1.5), (300, 1024, 1.0), (33, 5120, 1.5),
+                                   (17, 18944, 1.5), (9, 27648, 1.5)])
 def test_weight_quant_bit_exact(qt, N, K, s):
     W = I.weights(N, K, 0.02, seed=N * 7 + K)
     W[min(2, N - 1)] = 0.0  # an all-zero channel
@@ -287,16 +288,121 @@ def test_flip_counts_from_device_codes(qt):
         return codes_np(B.quantize_weights_uaq(to_dev_f32(A), 1.0, qt)[0])
 
     c0, cs = dev_codes(W), dev_codes(Ws)
+    def flips(A, c):
+        return O.count_flips(c, dev_codes(A.astype(np.float32)), qt)
+
     got = {
-        "base": int(np.count_nonzero(dev_codes((W + dW).astype(np.float32)) != c0)),
-        "uaq_same": int(np.count_nonzero(dev_codes((Ws + dW).astype(np.float32)) != cs)),
-        "uaq_pages": int(np.count_nonzero(
-            dev_codes((Ws + (dW * s32).astype(np.float32)).astype(np.float32)) != cs)),
-        "control": int(np.count_nonzero(
-            dev_codes((Ws + (dW / s32).astype(np.float32)).astype(np.float32)) != cs)),
+        "base": flips(W + dW, c0),
+        "uaq_same": flips(Ws + dW, cs),
+        "uaq_pages": flips(Ws + (dW * s32).astype(np.float32), cs),
+        "control": flips(Ws + (dW / s32).astype(np.float32), cs),
     }
     for k in got:
         assert got[k] == ref[k], (k, got[k], ref[k])
     # UAQ's effect as quantized on the device: same-size W/s quantization == the device's s path
     cq = codes_np(B.quantize_weights_uaq(to_dev_f32(W), s, qt)[0])
     assert np.array_equal(cq, cs)
+
+
+# ------------------------------------------------------------ per-step weight refresh
+
+def _refresh_case(N, K, qt, seed, ld=None):
+    """Stored parameters W' = W / s before and after one update s * dW (fp32)."""
+    s32 = np.float32(I.UAQ_S)
+    W = I.weights(N, ld or K, 0.02, seed=seed)
+    W[min(1, N - 1)] = 0.0  # an all-zero channel stays all zero
+    Wp0 = (W / s32).astype(np.float32)
+    dW = I.normal_f32(Wp0.shape, I.DW_SIGMA * 30, seed=seed + 1)
+    Wp1 = (Wp0 + (dW * s32).astype(np.float32)).astype(np.float32)
+    Wp1[min(1, N - 1)] = 0.0
+    return Wp0, Wp1
+
+
+def _row_flips(N):
+    return torch.full((N,), -1, dtype=torch.int32, device=DEV)
+
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("N,K", [(512, 512), (37, 48), (300, 1024), (64, 3584), (3, 40960),
+                                 (129, 1040), (33, 5120), (17, 18944), (9, 27648)])
+def test_requantize_codes_scales_and_flips(qt, N, K):
+    """Refresh after an update: codes, scales and per-row flip counts bit-exact."""
+    Wp0, Wp1 = _refresh_case(N, K, qt, seed=N * 13 + K)
+    c0, _, _ = O.requantize_weights(Wp0, qt)
+    c1, s1, f1 = O.requantize_weights(Wp1, qt, codes_old=c0)
+    assert f1.sum() > 0
+    Wq = to_dev_codes(c0, qt)
+    rf = _row_flips(N)
+    _, sw = B.requantize_weights(to_dev_f32(Wp1), qt, Wq, row_flips=rf)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes_np(Wq), c1.view(np.uint8))
+    assert np.array_equal(sw.cpu().numpy(), s1)
+    assert np.array_equal(rf.cpu().numpy().astype(np.int64), f1)
+    # without counts: the same codes
+    Wq2 = to_dev_codes(c0, qt)
+    _, sw2 = B.requantize_weights(to_dev_f32(Wp1), qt, Wq2)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes_np(Wq2), c1.view(np.uint8))
+    assert np.array_equal(sw2.cpu().numpy(), s1)
+
+
+@pytest.mark.parametrize("qt", QTS)
+def test_requantize_strided_params_and_repeat(qt):
+    """Row stride > K; counts are written, so a second refresh of unchanged
+    parameters reports zero changes per row."""
+    N, K, ld = 96, 512, 640
+    Wp0, Wp1 = _refresh_case(N, K, qt, seed=77, ld=ld)
+    c0, _, _ = O.requantize_weights(Wp0[:, :K], qt)
+    c1, s1, f1 = O.requantize_weights(Wp1[:, :K], qt, codes_old=c0)
+    Wq = to_dev_codes(c0, qt)
+    Wd = to_dev_f32(Wp1)[:, :K]
+    rf = _row_flips(N)
+    B.requantize_weights(Wd, qt, Wq, row_flips=rf)
+    torch.cuda.synchronize()
+    assert np.array_equal(rf.cpu().numpy().astype(np.int64), f1)
+    B.requantize_weights(Wd, qt, Wq, row_flips=rf)
+    torch.cuda.synchronize()
+    assert not rf.cpu().numpy().any()
+    assert np.array_equal(codes_np(Wq), c1.view(np.uint8))
+
+
+def test_requantize_fp8_signed_zero_is_no_flip():
+    """E4M3FN +0 and -0 are one value: previous codes planted with the other
+    zero, or with random other codes, give exactly the oracle's counts."""
+    N, K = 64, 256
+    rng = np.random.default_rng(5)
+    Wp = np.zeros((N, K), np.float32)
+    Wp[:, 0] = 1.0  # absmax 1 per row: v = 448 w
+    tiny = rng.choice(np.array([-1e-9, 1e-9, 0.0, -0.0], np.float32), size=(N, K - 1))
+    Wp[:, 1:] = tiny
+    Wp[::3, 1:] += rng.normal(0, 0.05, size=(len(range(0, N, 3)), K - 1)).astype(np.float32)
+    c1, s1, _ = O.requantize_weights(Wp, "fp8")
+    zeros = (c1 & 0x7F) == 0
+    assert zeros.sum() > 1000 and ((c1 == 0x80).sum() > 100) and ((c1 == 0x00).sum() > 100)
+    prev = c1.copy()
+    prev[zeros] ^= 0x80  # the other zero everywhere: no flips
+    other = rng.random(prev.shape) < 0.02
+    prev[other] = rng.integers(0, 0x7F, size=int(other.sum()), dtype=np.uint8)  # some real changes
+    expect = O.count_flips_rows(prev, c1, "fp8")
+    assert 0 < expect.sum() <= other.sum()
+    Wq = to_dev_codes(prev, "fp8")
+    rf = _row_flips(N)
+    _, sw = B.requantize_weights(to_dev_f32(Wp), "fp8", Wq, row_flips=rf)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes_np(Wq), c1)
+    assert np.array_equal(sw.cpu().numpy(), s1)
+    assert np.array_equal(rf.cpu().numpy().astype(np.int64), expect)
+
+
+def test_requantize_rejects_bad_arguments():
+    Wp = torch.zeros((4, 64), dtype=torch.float32, device=DEV)
+    Wq = torch.zeros((4, 64), dtype=torch.int8, device=DEV)
+    with pytest.raises(ValueError):
+        B.requantize_weights(Wp, "int8", Wq.view(torch.float8_e4m3fn))
+    with pytest.raises(ValueError):
+        B.requantize_weights(Wp, "int8", Wq, row_flips=torch.zeros(4, dtype=torch.int64, device=DEV))
+    with pytest.raises(ValueError):
+        B.requantize_weights(Wp, "int8", Wq, row_flips=torch.zeros(3, dtype=torch.int32, device=DEV))
+    with pytest.raises(B.QRError):
+        B.requantize_weights(torch.zeros((4, 66), dtype=torch.float32, device=DEV)[:, :64], "int8",
+                             Wq)

@@ -14,6 +14,10 @@ in seconds:
   input rows (quantization is per token, so a token's outputs depend only on
   its own row) and compared bit for bit. INT8 weight codes and scales are
   compared in full.
+* Per-RL-step weight refresh of the 7B-shaped stacked gate+up and down
+  matrices after one update of the pages' size: codes, scales and the flip
+  count against the oracle in full, and the count against the closed-form
+  first-order expectation.
 """
 
 import numpy as np
@@ -157,3 +161,36 @@ def test_7b_linears_fp8_sampled_channels(name):
 def test_32b_linears_fp8_m512_sampled_channels(name):
     N, K = I.LINEARS_32B[name]
     _fp8_linear_sampled("32b", 5, name, N, K, I.W_SIGMA_32B, 512, "normal")
+
+
+@pytest.mark.parametrize("qt", ["int8", "fp8"])
+@pytest.mark.parametrize("name", ["o", "gateup", "down"])
+def test_7b_refresh_full_size(qt, name):
+    """Refresh after W' += s * dW, dW ~ N(0, 1e-7^2), at the stack's matrix
+    sizes, in the launch the refresh benchmark uses. The closed-form check is
+    made on O and down (the two row lengths of the stack; skipped on gate+up
+    to keep the test within seconds)."""
+    N, K = I.LINEARS_7B[name]
+    s32 = np.float32(I.UAQ_S)
+    seed = I.matrix_seed(7, _NAMES.index("gate" if name == "gateup" else name))
+    Wp0 = (I.weights(N, K, I.W_SIGMA_7B, seed=seed) / s32).astype(np.float32)
+    Wp1 = I.normal_f32((N, K), I.DW_SIGMA, seed=seed + 1)
+    Wp1 *= s32
+    Wp1 += Wp0
+    Wd = to_dev_f32(Wp0)
+    Wq, _ = B.requantize_weights(Wd, qt, torch.empty((N, K), dtype=B.code_dtype(qt), device=Wd.device))
+    Wd.copy_(torch.from_numpy(Wp1))
+    rf = torch.empty(N, dtype=torch.int32, device=Wd.device)
+    _, sw = B.requantize_weights(Wd, qt, Wq, row_flips=rf)
+    c0, _, _ = O.requantize_weights(Wp0, qt)
+    c1, s1, f1 = O.requantize_weights(Wp1, qt, codes_old=c0)
+    del c0
+    torch.cuda.synchronize()
+    assert np.array_equal(codes_np(Wq), c1.view(np.uint8))
+    assert np.array_equal(sw.cpu().numpy(), s1)
+    assert np.array_equal(rf.cpu().numpy().astype(np.int64), f1)
+    del Wq, Wd, c1, Wp1
+    if name != "gateup":
+        total = int(f1.sum())
+        e = O.flip_expectation(Wp0, I.DW_SIGMA * I.UAQ_S, qt)
+        assert abs(total - e) <= 5 * np.sqrt(e) + 0.02 * e, (total, e)

@@ -211,7 +211,9 @@ def test_requantize_weights_is_quantize_rows_plus_count(qt):
     # an update far below one step changes few codes; the refresh counts exactly those
     Wn = (Wp + I.normal_f32(Wp.shape, 1e-4, seed=8)).astype(np.float32)
     c1, s1, f1 = O.requantize_weights(Wn, qt, c0)
-    assert f1 == O.count_flips(c0, c1, qt) and 0 < f1 < c0.size // 4
+    assert f1.shape == (48,) and f1.sum() == O.count_flips(c0, c1, qt) and 0 < f1.sum() < c0.size // 4
+    assert all(f1[r] == O.count_flips(c0[r], c1[r], qt) for r in range(48))
+    assert all(f1[r] == sum(int(x) != int(y) for x, y in zip(c0[r], c1[r])) for r in range(0, 48, 7))
     # s = 1 requantization of W' equals the UAQ quantizer's codes of W with W' = fl32(W / s)
     W = I.weights(16, 128, 0.02, seed=9)
     ref = O.quantize_weights_uaq(W, 1.5, qt)

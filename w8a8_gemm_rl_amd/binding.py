@@ -24,7 +24,8 @@ STATUS = {
 }
 # Every function include/qurl_w8a8.h declares.
 EXPORTS = [
-    "qr_quantize_weights_uaq", "qr_quantize_act_per_token", "qr_w8a8_gemm", "qr_linear_fused",
+    "qr_quantize_weights_uaq", "qr_requantize_weights", "qr_quantize_act_per_token",
+    "qr_w8a8_gemm", "qr_linear_fused",
     "qr_workspace_size", "qr_gemm_plan", "qr_tile_name", "qr_num_tiles", "qr_set_plan_override",
     "qr_last_error", "qr_version",
 ]
@@ -42,6 +43,7 @@ _lock = threading.Lock()
 _i64, _f32, _vp, _int, _sz = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 _SIGS = {
     "qr_quantize_weights_uaq": (_int, [_vp, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "qr_requantize_weights": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp]),
     "qr_quantize_act_per_token": (_int, [_vp, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp]),
     "qr_w8a8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _sz, _vp]),
     "qr_linear_fused": (_int, [_vp, _i64, _f32, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _sz, _vp]),
@@ -186,6 +188,31 @@ def quantize_weights_uaq(W, s, qt, Wq=None, scale_w=None, W_scaled=None, gamma=N
                                            _ptr(scale_w), _ptr(W_scaled), _ptr(gamma), _ptr(beta),
                                            _stream(W.device))
     _check("qr_quantize_weights_uaq", st)
+    return Wq, scale_w
+
+
+def requantize_weights(Wp, qt, Wq, scale_w=None, row_flips=None):
+    """Refresh the codes of stored parameters Wp = W / s [N, K] fp32 in place in Wq.
+
+    With row_flips (an int32 device tensor of N entries) entry n receives the
+    number of codes of row n whose value changed. Returns (Wq, scale_w).
+    """
+    _need_cuda(Wp, Wq, scale_w, row_flips)
+    if Wp.dtype != torch.float32:
+        raise ValueError("Wp must be float32")
+    N, K = Wp.shape
+    ldw = _rows(Wp, "Wp")
+    if Wq.shape != (N, K) or Wq.dtype != code_dtype(qt) or not Wq.is_contiguous():
+        raise ValueError("Wq must be a contiguous [N, K] code tensor of the quantized type")
+    if scale_w is None:
+        scale_w = torch.empty(N, dtype=torch.float32, device=Wp.device)
+    if row_flips is not None and (row_flips.dtype != torch.int32 or row_flips.numel() != N
+                                  or not row_flips.is_contiguous()):
+        raise ValueError("row_flips must be a contiguous int32 tensor of N entries")
+    with torch.cuda.device(Wp.device):
+        st = lib().qr_requantize_weights(_ptr(Wp), N, K, ldw, _qt(qt), _ptr(Wq), _ptr(scale_w),
+                                         _ptr(row_flips), _stream(Wp.device))
+    _check("qr_requantize_weights", st)
     return Wq, scale_w
 
 

@@ -243,6 +243,25 @@ int qr_quantize_weights_uaq(const float* W, int64_t N, int64_t K, int64_t ldw, f
   return hip_status(qr::launch_weight_quant(W, N, K, ldw, s, qt, Wq, scale_w, W_scaled, hs), fn);
 }
 
+int qr_requantize_weights(const float* Wp, int64_t N, int64_t K, int64_t ldw, int qt, void* Wq,
+                          float* scale_w, uint32_t* row_flips, void* stream) {
+  const char* fn = "qr_requantize_weights";
+  int st = check_shape(fn, 0, N, K, qt);
+  if (st != QR_OK) return st;
+  if (ldw < K) return fail(QR_ERR_INVALID_ARG, "%s: ldw=%lld < K=%lld", fn, (long long)ldw, (long long)K);
+  if (N > 0 && K > 0 && (!Wp || !Wq)) return fail(QR_ERR_INVALID_ARG, "%s: null Wp or Wq", fn);
+  if (N > 0 && !scale_w) return fail(QR_ERR_INVALID_ARG, "%s: null scale_w", fn);
+  if (ldw % 4 != 0) return fail(QR_ERR_UNSUPPORTED, "%s: ldw must be a multiple of 4", fn);
+  if (!aligned(Wp, 16) || !aligned(Wq, 16) || !aligned(scale_w, 4) || !aligned(row_flips, 4))
+    return fail(QR_ERR_UNSUPPORTED, "%s: misaligned pointer (16 bytes for Wp, Wq; 4 for the rest)",
+                fn);
+  if (N == 0) return ok();
+  (void)hipGetLastError();
+  return hip_status(qr::launch_requant(Wp, N, K, ldw, qt, Wq, scale_w, row_flips,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int qr_quantize_act_per_token(const void* X, int64_t M, int64_t K, int64_t ldx, float act_mult,
                               int qt, void* Xq, float* scale_x, void* stream) {
   const char* fn = "qr_quantize_act_per_token";

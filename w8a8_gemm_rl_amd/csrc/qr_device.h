@@ -31,39 +31,31 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
-// fp32 (finite) -> E4M3FN byte, saturating to +-448, round to nearest even.
-// The sign of v is kept, also when the magnitude rounds to zero.
-__device__ __forceinline__ uint32_t f32_to_e4m3fn_sat_rne(float v) {
-  v = fminf(fmaxf(v, -448.0f), 448.0f);
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const float av = fabsf(v);
-  uint32_t mag;
-  if (av < 0.015625f) {
-    // Below the smallest normal 2^-6 the spacing is 2^-9: scale exactly by
-    // 2^9 and round to an integer 0..8 (8 is the code of 2^-6 itself).
-    mag = (uint32_t)rintf(av * 512.0f);
-  } else {
-    const uint32_t a = b & 0x7fffffffu;
-    const uint32_t e = (a >> 23) - 120u;  // biased exponent for bias 7: 1..15
-    const uint32_t m = a & 0x7fffffu;
-    const uint32_t keep = m >> 20;
-    const uint32_t rem = m & 0xfffffu;
-    const uint32_t up = (rem > 0x80000u) | ((rem == 0x80000u) & (keep & 1u));
-    mag = (e << 3) + keep + up;  // a mantissa carry moves into the exponent
-  }
-  return sign | mag;
-}
-
-// One quantized code from fp32 x and the row's step t (t > 0).
+// Four codes from fp32 values and the row's step t (t > 0), packed
+// little-endian (a -> byte 0). Each value is first divided by t with IEEE
+// division (correctly rounded).
+//   INT8:    round half to even, clamp to [-127, 127].
+//   E4M3FN:  clamp to [-448, 448], then the gfx950 conversion
+//            v_cvt_pk_fp8_f32 (OCP E4M3FN, round to nearest even; a negative
+//            value that rounds to zero keeps its sign, 0x80). Checked equal
+//            to a bit-level software encoder for every fp32 value in
+//            [-448, 448], subnormals included.
 template <int QT>
-__device__ __forceinline__ uint32_t quant_code(float x, float t) {
-  const float v = x / t;  // IEEE division, correctly rounded
+__device__ __forceinline__ uint32_t quant_codes4(float a, float b, float c, float d, float t) {
+  a = a / t;
+  b = b / t;
+  c = c / t;
+  d = d / t;
   if constexpr (QT == kQInt8) {
-    const float r = fminf(fmaxf(rintf(v), -127.0f), 127.0f);
-    return (uint32_t)(int32_t)r & 0xffu;
+    auto q = [](float v) {
+      return (uint32_t)(int32_t)fminf(fmaxf(rintf(v), -127.0f), 127.0f) & 0xffu;
+    };
+    return q(a) | (q(b) << 8) | (q(c) << 16) | (q(d) << 24);
   } else {
-    return f32_to_e4m3fn_sat_rne(v);
+    auto cl = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+    return (uint32_t)w;
   }
 }
 

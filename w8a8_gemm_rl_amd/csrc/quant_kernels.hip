@@ -27,12 +27,8 @@ __device__ __forceinline__ float absmax8_bf16(const uint4 v) {
 
 template <int QT>
 __device__ __forceinline__ uint2 codes8_bf16(const uint4 v, float t) {
-  uint2 o;
-  o.x = quant_code<QT>(bf16_lo(v.x), t) | (quant_code<QT>(bf16_hi(v.x), t) << 8) |
-        (quant_code<QT>(bf16_lo(v.y), t) << 16) | (quant_code<QT>(bf16_hi(v.y), t) << 24);
-  o.y = quant_code<QT>(bf16_lo(v.z), t) | (quant_code<QT>(bf16_hi(v.z), t) << 8) |
-        (quant_code<QT>(bf16_lo(v.w), t) << 16) | (quant_code<QT>(bf16_hi(v.w), t) << 24);
-  return o;
+  return make_uint2(quant_codes4<QT>(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y), t),
+                    quant_codes4<QT>(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w), t));
 }
 
 // Block-wide max when one 256-thread block owns a row (TPR == 256), or a
@@ -110,23 +106,48 @@ __global__ __launch_bounds__(NT) void act_quant_kernel(const uint16_t* __restric
   }
 }
 
-// Weights: W' = fl32(W / s) per element, then per-row absmax quantization of
-// W'. Optionally stores W' (may alias W: every element is read by the thread
-// that overwrites it, before it does).
-template <int QT, int TPR, int MAXC>
+// Positions among four code bytes whose value changed: INT8 any byte
+// difference; E4M3FN too, except +0 (0x00) against -0 (0x80).
+template <int QT>
+__device__ __forceinline__ int changed4(uint32_t a, uint32_t b) {
+  int n = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t x = (a >> (8 * e)) & 0xFFu, y = (b >> (8 * e)) & 0xFFu;
+    bool d = x != y;
+    if constexpr (QT == kQFp8) d = d && !(((x | y) == 0x80u) && ((x & y) == 0u));
+    n += d ? 1 : 0;
+  }
+  return n;
+}
+
+// Weights: per-row absmax quantization of W' = fl32(W / s) (DIVS), or of W
+// itself when it already holds W' (the per-step refresh). Optionally stores
+// W' (may alias W: every element is read by the thread that overwrites it,
+// before it does). With CNT, the previous contents of Wq are read just
+// before they are overwritten and the number of codes of the row whose value
+// changed is stored to row_flips[row].
+template <int QT, int TPR, int MAXC, bool DIVS, bool CNT>
 __global__ __launch_bounds__(256) void weight_quant_kernel(const float* W, int64_t N, int64_t K,
                                                            int64_t ldw, float s,
                                                            uint8_t* __restrict__ Wq,
                                                            float* __restrict__ scale_w,
-                                                           float* Wsc) {
+                                                           float* Wsc, uint32_t* row_flips) {
   constexpr int RPB = 256 / TPR;
   __shared__ float red[4];
+  __shared__ int cnt[4];
   const int lt = threadIdx.x % TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   const bool valid = row < N;
   const int64_t nch = K >> 2;
   const float4* wr = reinterpret_cast<const float4*>(W + (valid ? row : 0) * ldw);
   const bool fits = nch <= (int64_t)MAXC * TPR;
+  auto div4 = [&](float4 v) {
+    if constexpr (DIVS) {
+      v.x = v.x / s; v.y = v.y / s; v.z = v.z / s; v.w = v.w / s;
+    }
+    return v;
+  };
 
   float4 r[MAXC];
   float amax = 0.0f;
@@ -146,8 +167,7 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(const float* W, int64
       for (int i = 0; i < MAXC; ++i) {
         const int64_t c = lt + (int64_t)i * TPR;
         if (i < niter) {
-          float4 v = r[i];
-          v.x = v.x / s; v.y = v.y / s; v.z = v.z / s; v.w = v.w / s;
+          const float4 v = div4(r[i]);
           r[i] = v;
           if (c < nch)
             amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
@@ -155,39 +175,45 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(const float* W, int64
       }
     } else {
       for (int64_t c = lt; c < nch; c += TPR) {
-        const float4 v = wr[c];
-        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x / s), fabsf(v.y / s)),
-                                 fmaxf(fabsf(v.z / s), fabsf(v.w / s))));
+        const float4 v = div4(wr[c]);
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
       }
     }
   }
   amax = row_max<TPR>(amax, red);
-  if (!valid) return;
-
-  const float t = amax / qmax<QT>();
-  if (lt == 0) scale_w[row] = t;
-  uint32_t* qr_ = reinterpret_cast<uint32_t*>(Wq + row * K);
-  float4* sr = Wsc ? reinterpret_cast<float4*>(Wsc + row * ldw) : nullptr;
-  auto emit = [&](int64_t c, float4 v) {
-    if (sr) sr[c] = v;
-    uint32_t q = 0u;
-    if (t != 0.0f)
-      q = quant_code<QT>(v.x, t) | (quant_code<QT>(v.y, t) << 8) |
-          (quant_code<QT>(v.z, t) << 16) | (quant_code<QT>(v.w, t) << 24);
-    qr_[c] = q;
-  };
-  if (fits) {
+  int nflip = 0;
+  if (valid) {
+    const float t = amax / qmax<QT>();
+    if (lt == 0) scale_w[row] = t;
+    uint32_t* qr_ = reinterpret_cast<uint32_t*>(Wq + row * K);
+    float4* sr = Wsc ? reinterpret_cast<float4*>(Wsc + row * ldw) : nullptr;
+    auto emit = [&](int64_t c, float4 v) {
+      if (sr) sr[c] = v;
+      const uint32_t q = t != 0.0f ? quant_codes4<QT>(v.x, v.y, v.z, v.w, t) : 0u;
+      if constexpr (CNT) nflip += changed4<QT>(qr_[c], q);
+      qr_[c] = q;
+    };
+    if (fits) {
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-      const int64_t c = lt + (int64_t)i * TPR;
-      if (c < nch) emit(c, r[i]);
+      for (int i = 0; i < MAXC; ++i) {
+        const int64_t c = lt + (int64_t)i * TPR;
+        if (c < nch) emit(c, r[i]);
+      }
+    } else {
+      for (int64_t c = lt; c < nch; c += TPR) emit(c, div4(wr[c]));
     }
-  } else {
-    for (int64_t c = lt; c < nch; c += TPR) {
-      float4 v = wr[c];
-      v.x = v.x / s; v.y = v.y / s; v.z = v.z / s; v.w = v.w / s;
-      emit(c, v);
+  }
+  if constexpr (CNT) {
+    // Row sum of the per-lane counts: across the wave with lane shuffles,
+    // then (one row per block) across the four waves through LDS.
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) nflip += __shfl_xor(nflip, o, 64);
+    if constexpr (TPR == 256) {
+      if ((threadIdx.x & 63) == 0) cnt[threadIdx.x >> 6] = nflip;
+      __syncthreads();
+      nflip = cnt[0] + cnt[1] + cnt[2] + cnt[3];
     }
+    if (valid && lt == 0) row_flips[row] = (uint32_t)nflip;
   }
 }
 
@@ -205,31 +231,63 @@ inline unsigned grid_for(int64_t rows, int rpb) { return (unsigned)((rows + rpb 
 
 }  // namespace
 
+template <int QT>
+hipError_t launch_act_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float act_mult,
+                           uint8_t* q, float* scale_x, hipStream_t st) {
+  // Short rows: one wave per row, four rows per block. Longer rows take the
+  // four waves of a block (more loads in flight per row; measured faster on
+  // MI355X than one wave per row for 3584-element rows), with the fewest
+  // 16-byte chunks per thread that hold the row.
+  const dim3 b(256);
+  if (K <= 2048)
+    hipLaunchKernelGGL((act_quant_kernel<QT, 64, 4>), dim3(grid_for(M, 4)), b, 0, st, x, M, K, ldx,
+                       act_mult, q, scale_x);
+  else if (K <= 4096)
+    hipLaunchKernelGGL((act_quant_kernel<QT, 256, 2>), dim3(grid_for(M, 1)), b, 0, st, x, M, K,
+                       ldx, act_mult, q, scale_x);
+  else if (K <= 8192)
+    hipLaunchKernelGGL((act_quant_kernel<QT, 256, 4>), dim3(grid_for(M, 1)), b, 0, st, x, M, K,
+                       ldx, act_mult, q, scale_x);
+  else
+    hipLaunchKernelGGL((act_quant_kernel<QT, 256, 16>), dim3(grid_for(M, 1)), b, 0, st, x, M, K,
+                       ldx, act_mult, q, scale_x);
+  return hipGetLastError();
+}
+
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int64_t ldx, float act_mult,
                             int qt, void* Xq, float* scale_x, hipStream_t st) {
   if (M == 0) return hipSuccess;
   const uint16_t* x = static_cast<const uint16_t*>(X);
   uint8_t* q = static_cast<uint8_t*>(Xq);
-  // Short rows: one wave per row, four rows per block. Longer rows take the
-  // four waves of a block (more loads in flight per row; measured faster on
-  // MI355X than one wave per row for 3584-element rows).
-  if (K <= 2048) {
-    const unsigned g = grid_for(M, 4);
-    if (qt == kQInt8)
-      hipLaunchKernelGGL((act_quant_kernel<kQInt8, 64, 4>), dim3(g), dim3(256), 0, st, x, M, K,
-                         ldx, act_mult, q, scale_x);
-    else
-      hipLaunchKernelGGL((act_quant_kernel<kQFp8, 64, 4>), dim3(g), dim3(256), 0, st, x, M, K,
-                         ldx, act_mult, q, scale_x);
-  } else {
-    const unsigned g = grid_for(M, 1);
-    if (qt == kQInt8)
-      hipLaunchKernelGGL((act_quant_kernel<kQInt8, 256, 16>), dim3(g), dim3(256), 0, st, x, M, K,
-                         ldx, act_mult, q, scale_x);
-    else
-      hipLaunchKernelGGL((act_quant_kernel<kQFp8, 256, 16>), dim3(g), dim3(256), 0, st, x, M, K,
-                         ldx, act_mult, q, scale_x);
-  }
+  if (qt == kQInt8) return launch_act_rows<kQInt8>(x, M, K, ldx, act_mult, q, scale_x, st);
+  return launch_act_rows<kQFp8>(x, M, K, ldx, act_mult, q, scale_x, st);
+}
+
+// Register budget per thread sized to the row (occupancy falls with the
+// registers a kernel reserves, and a streaming kernel needs every wave it can
+// get): short rows one wave each, four rows per block; longer rows one block
+// each, with the fewest 16-byte chunks per thread that hold the row. Rows
+// longer than 32768 elements are read twice.
+template <int QT, bool DIVS, bool CNT>
+hipError_t launch_weight_rows(const float* W, int64_t N, int64_t K, int64_t ldw, float s,
+                              uint8_t* q, float* scale_w, float* Wsc, uint32_t* flips,
+                              hipStream_t st) {
+  const dim3 b(256);
+  if (K <= 1024)
+    hipLaunchKernelGGL((weight_quant_kernel<QT, 64, 4, DIVS, CNT>), dim3(grid_for(N, 4)), b, 0, st,
+                       W, N, K, ldw, s, q, scale_w, Wsc, flips);
+  else if (K <= 4096)
+    hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 4, DIVS, CNT>), dim3(grid_for(N, 1)), b, 0,
+                       st, W, N, K, ldw, s, q, scale_w, Wsc, flips);
+  else if (K <= 8192)
+    hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 8, DIVS, CNT>), dim3(grid_for(N, 1)), b, 0,
+                       st, W, N, K, ldw, s, q, scale_w, Wsc, flips);
+  else if (K <= 20480)
+    hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 20, DIVS, CNT>), dim3(grid_for(N, 1)), b, 0,
+                       st, W, N, K, ldw, s, q, scale_w, Wsc, flips);
+  else
+    hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 32, DIVS, CNT>), dim3(grid_for(N, 1)), b, 0,
+                       st, W, N, K, ldw, s, q, scale_w, Wsc, flips);
   return hipGetLastError();
 }
 
@@ -237,24 +295,24 @@ hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, int64_t ldw
                                void* Wq, float* scale_w, float* Wsc, hipStream_t st) {
   if (N == 0) return hipSuccess;
   uint8_t* q = static_cast<uint8_t*>(Wq);
-  if (K <= 1024) {
-    const unsigned g = grid_for(N, 4);
-    if (qt == kQInt8)
-      hipLaunchKernelGGL((weight_quant_kernel<kQInt8, 64, 4>), dim3(g), dim3(256), 0, st, W, N,
-                         K, ldw, s, q, scale_w, Wsc);
-    else
-      hipLaunchKernelGGL((weight_quant_kernel<kQFp8, 64, 4>), dim3(g), dim3(256), 0, st, W, N, K,
-                         ldw, s, q, scale_w, Wsc);
-  } else {
-    const unsigned g = grid_for(N, 1);
-    if (qt == kQInt8)
-      hipLaunchKernelGGL((weight_quant_kernel<kQInt8, 256, 32>), dim3(g), dim3(256), 0, st, W, N,
-                         K, ldw, s, q, scale_w, Wsc);
-    else
-      hipLaunchKernelGGL((weight_quant_kernel<kQFp8, 256, 32>), dim3(g), dim3(256), 0, st, W, N,
-                         K, ldw, s, q, scale_w, Wsc);
-  }
-  return hipGetLastError();
+  if (qt == kQInt8)
+    return launch_weight_rows<kQInt8, true, false>(W, N, K, ldw, s, q, scale_w, Wsc, nullptr, st);
+  return launch_weight_rows<kQFp8, true, false>(W, N, K, ldw, s, q, scale_w, Wsc, nullptr, st);
+}
+
+hipError_t launch_requant(const float* Wp, int64_t N, int64_t K, int64_t ldw, int qt, void* Wq,
+                          float* scale_w, uint32_t* row_flips, hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  uint8_t* q = static_cast<uint8_t*>(Wq);
+  if (qt == kQInt8)
+    return row_flips ? launch_weight_rows<kQInt8, false, true>(Wp, N, K, ldw, 1.0f, q, scale_w,
+                                                               nullptr, row_flips, st)
+                     : launch_weight_rows<kQInt8, false, false>(Wp, N, K, ldw, 1.0f, q, scale_w,
+                                                                nullptr, nullptr, st);
+  return row_flips ? launch_weight_rows<kQFp8, false, true>(Wp, N, K, ldw, 1.0f, q, scale_w,
+                                                            nullptr, row_flips, st)
+                   : launch_weight_rows<kQFp8, false, false>(Wp, N, K, ldw, 1.0f, q, scale_w,
+                                                             nullptr, nullptr, st);
 }
 
 hipError_t launch_fold_norm(float* gamma, float* beta, int64_t K, float s, hipStream_t st) {

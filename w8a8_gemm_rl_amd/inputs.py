@@ -41,8 +41,16 @@ LINEARS_32B = {
     "gate": (27648, 5120),
     "up": (27648, 5120),
     "down": (5120, 27648),
+    "gateup": (55296, 5120),  # gate and up stacked along N
 }
 W_SIGMA_32B = 0.015
+
+# Layer stacks of the whole models (per layer: fused QKV, O, stacked gate+up,
+# down), as the per-RL-step weight refresh walks them.
+STACK_7B = dict(layers=28, linears=LINEARS_7B, names=("qkv", "o", "gateup", "down"),
+                sigma=W_SIGMA_7B)
+STACK_32B = dict(layers=64, linears=LINEARS_32B, names=("qkv", "o", "gateup", "down"),
+                 sigma=W_SIGMA_32B)
 
 # Decode-layer chains. Each linear names its input: "x0" (the layer input) or
 # an earlier linear's bf16 output, optionally a column slice of it. Attention,
