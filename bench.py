@@ -292,7 +292,16 @@ def refresh_cpu_baseline(qt, N, K, sigma, s):
 
 def run_refresh(args, dev):
     """Per-RL-step refresh of a whole layer stack (one step = every matrix of
-    every layer requantized, with the codes each update changed counted)."""
+    every layer requantized, with the codes each update changed counted).
+
+    Layout: the stored parameters of all matrices with the same row length K
+    live in one [rows, K] fp32 slab (every layer's matrices are row ranges of
+    it, as a flat parameter buffer holds them), with codes, scales and change
+    counts in matching slabs. A refresh is one launch per slab: 2 for the
+    7B/32B stacks (K = hidden: QKV, O, gate+up of every layer; K =
+    intermediate: down), instead of one per matrix with a kernel drain and
+    fill between each.
+    """
     import numpy as np
     import torch
 
@@ -306,58 +315,58 @@ def run_refresh(args, dev):
     shapes = {n: stack["linears"][n] for n in names}
     sigma_p = stack["sigma"] / s  # stored parameters W' = W / s
     upd = s * I.DW_SIGMA  # the update on W' (the pages' size, grown by s)
-
-    # Stored parameters and codes of every layer, generated on the device.
     log(f"bench: {args.workload}: {nl} layers x {', '.join(f'{n} {shapes[n][0]}x{shapes[n][1]}' for n in names)}")
-    g = torch.Generator(device=dev)
-    Wp, Wq, Sw = [], [], []
-    for l in range(nl):
-        Wp.append({}), Wq.append({}), Sw.append({})
-        for j, n in enumerate(names):
-            N, K = shapes[n]
-            g.manual_seed(7000 + 16 * l + j)
-            Wp[l][n] = torch.randn((N, K), generator=g, device=dev).mul_(sigma_p)
-            Wq[l][n] = torch.empty((N, K), dtype=B.code_dtype(qt), device=dev)
-            Sw[l][n] = torch.empty(N, dtype=torch.float32, device=dev)
-            B.requantize_weights(Wp[l][n], qt, Wq[l][n], Sw[l][n])
-    # Per-row change counts of every matrix: slices of one int32 buffer.
-    offs, o = {}, 0
+
+    # Slabs by row length; (layer, matrix) -> (K, first row, end row).
+    where, rows = {}, {}
     for l in range(nl):
         for n in names:
-            offs[l, n] = (o, o + shapes[n][0])
-            o += shapes[n][0]
-    row_flips = torch.zeros(o, dtype=torch.int32, device=dev)
-    rf = {k: row_flips[a:b] for k, (a, b) in offs.items()}
-    spare = torch.zeros(max(N for N, _ in shapes.values()), dtype=torch.int32, device=dev)
-    torch.cuda.synchronize()
-    params = nl * sum(N * K for N, K in shapes.values())
-    bytes_step = nl * sum(refresh_bytes(N, K) for N, K in shapes.values())
+            N, K = shapes[n]
+            r0 = rows.get(K, 0)
+            where[l, n] = (K, r0, r0 + N)
+            rows[K] = r0 + N
+    CH = 1 << 28  # elements per generation / update chunk
+    g = torch.Generator(device=dev)
+    slab = {}
+    for gi, K in enumerate(sorted(rows)):
+        R = rows[K]
+        Wp = torch.empty((R, K), dtype=torch.float32, device=dev)
+        g.manual_seed(7000 + gi)
+        step = max(1, CH // K)
+        for a in range(0, R, step):
+            Wp[a:a + step].normal_(0.0, sigma_p, generator=g)
+        slab[K] = dict(Wp=Wp, Wq=torch.empty((R, K), dtype=B.code_dtype(qt), device=dev),
+                       Sw=torch.empty(R, dtype=torch.float32, device=dev),
+                       rf=torch.zeros(R, dtype=torch.int32, device=dev), step=step)
+    params = sum(R * K for K, R in rows.items())
+    bytes_step = sum(refresh_bytes(R, K) for K, R in rows.items())
 
     def refresh_all():
-        for l in range(nl):
-            for j, n in enumerate(names):
-                B.requantize_weights(Wp[l][n], qt, Wq[l][n], Sw[l][n], row_flips=rf[l, n])
+        for K, d in slab.items():
+            B.requantize_weights(d["Wp"], qt, d["Wq"], d["Sw"], row_flips=d["rf"])
 
     def update():
-        for l in range(nl):
-            for n in names:
-                Wp[l][n].add_(torch.randn(Wp[l][n].shape, generator=g, device=dev), alpha=upd)
+        for K, d in slab.items():
+            W, step = d["Wp"], d["step"]
+            for a in range(0, W.shape[0], step):
+                c = W[a:a + step]
+                c.add_(torch.randn(c.shape, generator=g, device=dev), alpha=upd)
 
     # The whole refresh as one HIP graph; the dominant launch (the largest
-    # matrix) alone in a graph of DOM_BATCH launches over the layers.
-    dom = max(names, key=lambda n: shapes[n][0] * shapes[n][1])
+    # slab) alone in a graph of a few launches.
+    domK = max(rows, key=lambda K: refresh_bytes(rows[K], K))
+    dom_batch = 3
     st = torch.cuda.Stream()
     st.wait_stream(torch.cuda.current_stream())
     whole, dom_graph = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    d = slab[domK]
     with torch.cuda.stream(st):
         refresh_all()  # untimed: codes now match the parameters
         with torch.cuda.graph(whole, stream=st):
             refresh_all()
         with torch.cuda.graph(dom_graph, stream=st):
-            for i in range(DOM_BATCH):
-                l = i % nl
-                B.requantize_weights(Wp[l][dom], qt, Wq[l][dom], Sw[l][dom],
-                                     row_flips=spare[:shapes[dom][0]])
+            for _ in range(dom_batch):
+                B.requantize_weights(d["Wp"], qt, d["Wq"], d["Sw"], row_flips=d["rf"])
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         whole.replay()
@@ -365,19 +374,20 @@ def run_refresh(args, dev):
 
     # Timed: K refreshes, each after an untimed update of every parameter.
     g.manual_seed(99)
-    K = args.steps
-    log(f"bench: timing {K} refresh steps (updates between them untimed)")
+    steps = args.steps
+    log(f"bench: timing {steps} refresh steps (updates between them untimed)")
     total = 0.0
-    acc = torch.zeros(row_flips.shape, dtype=torch.int64, device=dev)
-    for _ in range(K):
+    acc = {K: torch.zeros(rows[K], dtype=torch.int64, device=dev) for K in rows}
+    for _ in range(steps):
         update()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         whole.replay()
         torch.cuda.synchronize()
         total += time.perf_counter() - t0
-        acc += row_flips
-    sec_step = total / K
+        for K in rows:
+            acc[K] += slab[K]["rf"]
+    sec_step = total / steps
 
     reps = 5
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
@@ -386,11 +396,11 @@ def run_refresh(args, dev):
         dom_graph.replay()
         b.record()
     torch.cuda.synchronize()
-    dom_us = 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / (reps * DOM_BATCH)
+    dom_us = 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / (reps * dom_batch)
 
-    acc = acc.cpu().numpy()
-    fl = np.array([[acc[offs[l, n][0]:offs[l, n][1]].sum() for n in names] for l in range(nl)],
-                  dtype=float) / max(K, 1)
+    acc = {K: v.cpu().numpy() for K, v in acc.items()}
+    fl = np.array([[acc[where[l, n][0]][where[l, n][1]:where[l, n][2]].sum() for n in names]
+                   for l in range(nl)], dtype=float) / max(steps, 1)
     flip_stats = {
         n: dict(N=shapes[n][0], K=shapes[n][1], mean_flips=round(float(fl[:, j].mean()), 1),
                 frac=float(f"{fl[:, j].mean() / (shapes[n][0] * shapes[n][1]):.3e}"),
@@ -398,14 +408,16 @@ def run_refresh(args, dev):
         for j, n in enumerate(names)}
     per_layer = [round(float(v), 1) for v in fl.sum(axis=1)]
 
-    Nd, Kd = shapes[dom]
-    dbytes = refresh_bytes(Nd, Kd)
+    Nd = rows[domK]
+    dbytes = refresh_bytes(Nd, domK)
     achieved = dbytes / (dom_us * 1e-6) / 1e9
-    key = f"{args.workload}:{dom}:N{Nd}:K{Kd}"
+    key = f"{args.workload}:slab:N{Nd}:K{domK}"
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(key, "refresh"),
-        "traffic_key": key, "kernel": f"refresh of {dom} {Nd}x{Kd} ({qt}, flip count)",
+        "traffic_key": key,
+        "kernel": f"refresh of the K={domK} slab ({Nd} rows: every layer's "
+                  f"{', '.join(n for n in names if shapes[n][1] == domK)}; {qt}, per-row change counts)",
         "kernel_us": round(dom_us, 2), "alg_bytes_per_launch": dbytes,
     }
     cpu = None
@@ -414,23 +426,25 @@ def run_refresh(args, dev):
         dt, n, threads = refresh_cpu_baseline(qt, Nq, Kq, stack["sigma"], s)
         cpu = {"value": round(refresh_bytes(Nq, Kq) / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"{n} refreshes of one {Nq}x{Kq} QKV matrix (requantize + flip count) by "
-                         f"the numpy oracle, {dt:.3f} s each",
+               "sample": f"{n} refreshes of one {Nq}x{Kq} QKV matrix (requantize + per-row change "
+                         f"counts) by the numpy oracle, {dt:.3f} s each",
                "seconds_per_refresh": round(dt, 4), "host_cpus": os.cpu_count()}
-    code_bytes = params + 4 * nl * sum(N for N, _ in shapes.values())
+    code_bytes = params + 4 * sum(rows.values())
     out = {
         "metric": REFRESH_METRIC,
         "value": round(bytes_step / sec_step / 1e9, 1),
         "unit": "GB/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "n_gpus": 1, "steps": steps, "warmup": args.warmup,
         "ms_per_step": round(sec_step * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {
             "workload": f"{args.workload}: refresh of {nl} layers x ({', '.join(f'{n} {shapes[n][0]}x{shapes[n][1]}' for n in names)}) "
                         f"= {params / 1e9:.2f} B parameters into {qt} codes, after an update "
-                        f"N(0, ({s} x 1e-7)^2) of every stored W' = W / {s}",
+                        f"N(0, ({s} x 1e-7)^2) of every stored W' = W / {s}; one launch per "
+                        f"row-length slab ({len(rows)})",
             "layers": nl, "qtype": qt, "uaq_s": s, "params": params, "timing": "hip_graph",
+            "slabs": {str(K): [R, K] for K, R in sorted(rows.items())},
             "parallelism": "none (1 GPU)",
         },
         "params_per_s": float(f"{params / sec_step:.4e}"),

@@ -74,6 +74,80 @@ def test_weight_quant_in_place_strided_and_norm_fold(qt):
     assert np.array_equal(bd.cpu().numpy(), ref["beta"])
 
 
+_CAP = 1 << 20  # blocks per quantizer launch; more rows loop inside the grid
+
+
+def _loop_rows(N, rpb):
+    """Rows at the start, around each multiple of the grid's row span, and at the end."""
+    span = _CAP * rpb
+    r = [0, 1, 2, N - 3, N - 2, N - 1]
+    for m in range(span, N, span):
+        r += [m - 2, m - 1, m, m + 1]
+    return np.unique(np.array(r, np.int64))
+
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("N,K,rpb", [(4 * _CAP + 37, 16, 4), (_CAP + 5, 1040, 1)])
+def test_weight_quantizers_loop_past_the_grid_cap(qt, N, K, rpb):
+    """More rows than the launch's blocks cover: every row is still quantized,
+    by the UAQ quantizer and by the refresh (with per-row change counts)."""
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(N + K)
+    W = torch.randn((N, K), generator=gen, device=DEV).mul_(0.02)
+    rows = _loop_rows(N, rpb)
+    Wh = W[torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    ref = O.quantize_weights_uaq(Wh, 1.5, qt)
+    Wq, sw = B.quantize_weights_uaq(W, 1.5, qt)
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(rows).to(DEV)
+    assert np.array_equal(codes_np(Wq[idx]), ref["Wq"].view(np.uint8))
+    assert np.array_equal(sw[idx].cpu().numpy(), ref["scale_w"])
+    # refresh of W itself over zeroed codes: counts = nonzero-valued codes per row
+    Wq.zero_()
+    rf = torch.full((N,), -1, dtype=torch.int32, device=DEV)
+    B.requantize_weights(W, qt, Wq, sw, row_flips=rf)
+    c1, s1, f1 = O.requantize_weights(Wh, qt, codes_old=np.zeros((len(rows), K), np.uint8))
+    torch.cuda.synchronize()
+    assert np.array_equal(codes_np(Wq[idx]), c1.view(np.uint8))
+    assert np.array_equal(sw[idx].cpu().numpy(), s1)
+    assert np.array_equal(rf[idx].cpu().numpy().astype(np.int64), f1)
+    assert int((rf < 0).sum().item()) == 0  # every row written
+
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("M,K,rpb", [(4 * _CAP + 37, 16, 4), (_CAP + 5, 2064, 1)])
+def test_act_quantizer_loops_past_the_grid_cap(qt, M, K, rpb):
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(M + K)
+    X = torch.randn((M, K), generator=gen, device=DEV).to(torch.bfloat16)
+    rows = _loop_rows(M, rpb)
+    idx = torch.from_numpy(rows).to(DEV)
+    Xh = bf16_np(X[idx])
+    codes, sx = O.quantize_act_per_token(Xh, 1.5, qt)
+    Xq, sxd = B.quantize_act_per_token(X, 1.5, qt)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes_np(Xq[idx]), codes.view(np.uint8))
+    assert np.array_equal(sxd[idx].cpu().numpy(), sx)
+
+
+def test_norm_fold_longer_than_the_grid():
+    """gamma/beta of more elements than one pass of the fold's grid covers
+    (FP8: INT8 rows are limited far below this by the int32 accumulator)."""
+    K = (1 << 28) + 16
+    W = torch.zeros((1, K), dtype=torch.float32, device=DEV)
+    W[0, 0] = 1.0
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(3)
+    gd = torch.randn(K, generator=gen, device=DEV)
+    g0 = gd.clone()
+    B.quantize_weights_uaq(W, 1.5, "fp8", gamma=gd)
+    torch.cuda.synchronize()
+    pos = torch.tensor([0, 1, (1 << 28) - 1, 1 << 28, K - 1], device=DEV)
+    ref = (g0[pos].cpu().numpy() * np.float32(1.5)).astype(np.float32)
+    assert np.array_equal(gd[pos].cpu().numpy(), ref)
+    assert torch.equal(gd, g0 * 1.5)
+
+
 # ------------------------------------------------------------ activation quantizer
 
 @pytest.mark.parametrize("qt", QTS)

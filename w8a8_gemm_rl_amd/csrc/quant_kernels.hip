@@ -45,17 +45,16 @@ __device__ __forceinline__ float row_max(float v, float* red) {
   return v;
 }
 
-// One row per TPR threads; NT threads per block. MAXC 16-byte chunks per
-// thread are kept in registers (row length <= MAXC * TPR * 8 elements).
-template <int QT, int TPR, int MAXC, int NT = 256>
-__global__ __launch_bounds__(NT) void act_quant_kernel(const uint16_t* __restrict__ X, int64_t M,
-                                                       int64_t K, int64_t ldx, float act_mult,
-                                                       uint8_t* __restrict__ Xq,
-                                                       float* __restrict__ scale_x) {
-  constexpr int RPB = NT / TPR;
-  __shared__ float red[4];
+// The rows base .. base + 256/TPR - 1, one per TPR threads. MAXC 16-byte
+// chunks per thread are kept in registers (row length <= MAXC * TPR * 8).
+template <int QT, int TPR, int MAXC>
+__device__ __forceinline__ void act_quant_rows(const uint16_t* __restrict__ X, int64_t M,
+                                               int64_t K, int64_t ldx, float act_mult,
+                                               uint8_t* __restrict__ Xq,
+                                               float* __restrict__ scale_x, int64_t base,
+                                               float* red) {
   const int lt = threadIdx.x % TPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int64_t row = base + threadIdx.x / TPR;
   const bool valid = row < M;
   const int64_t nch = K >> 3;
   const uint4* xr = reinterpret_cast<const uint4*>(X + (valid ? row : 0) * ldx);
@@ -106,6 +105,16 @@ __global__ __launch_bounds__(NT) void act_quant_kernel(const uint16_t* __restric
   }
 }
 
+template <int QT, int TPR, int MAXC>
+__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ X, int64_t M,
+                                                        int64_t K, int64_t ldx, float act_mult,
+                                                        uint8_t* __restrict__ Xq,
+                                                        float* __restrict__ scale_x) {
+  __shared__ float red[4];
+  act_quant_rows<QT, TPR, MAXC>(X, M, K, ldx, act_mult, Xq, scale_x,
+                                (int64_t)blockIdx.x * (256 / TPR), red);
+}
+
 // Positions among four code bytes whose value changed: INT8 any byte
 // difference; E4M3FN too, except +0 (0x00) against -0 (0x80).
 template <int QT>
@@ -128,16 +137,13 @@ __device__ __forceinline__ int changed4(uint32_t a, uint32_t b) {
 // before they are overwritten and the number of codes of the row whose value
 // changed is stored to row_flips[row].
 template <int QT, int TPR, int MAXC, bool DIVS, bool CNT>
-__global__ __launch_bounds__(256) void weight_quant_kernel(const float* W, int64_t N, int64_t K,
-                                                           int64_t ldw, float s,
-                                                           uint8_t* __restrict__ Wq,
-                                                           float* __restrict__ scale_w,
-                                                           float* Wsc, uint32_t* row_flips) {
-  constexpr int RPB = 256 / TPR;
-  __shared__ float red[4];
-  __shared__ int cnt[4];
+__device__ __forceinline__ void weight_quant_rows(const float* W, int64_t N, int64_t K,
+                                                  int64_t ldw, float s, uint8_t* __restrict__ Wq,
+                                                  float* __restrict__ scale_w, float* Wsc,
+                                                  uint32_t* row_flips, int64_t base, float* red,
+                                                  int* cnt) {
   const int lt = threadIdx.x % TPR;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int64_t row = base + threadIdx.x / TPR;
   const bool valid = row < N;
   const int64_t nch = K >> 2;
   const float4* wr = reinterpret_cast<const float4*>(W + (valid ? row : 0) * ldw);
@@ -217,17 +223,33 @@ __global__ __launch_bounds__(256) void weight_quant_kernel(const float* W, int64
   }
 }
 
+template <int QT, int TPR, int MAXC, bool DIVS, bool CNT>
+__global__ __launch_bounds__(256) void weight_quant_kernel(const float* W, int64_t N, int64_t K,
+                                                           int64_t ldw, float s,
+                                                           uint8_t* __restrict__ Wq,
+                                                           float* __restrict__ scale_w,
+                                                           float* Wsc, uint32_t* row_flips) {
+  __shared__ float red[4];
+  __shared__ int cnt[4];
+  weight_quant_rows<QT, TPR, MAXC, DIVS, CNT>(W, N, K, ldw, s, Wq, scale_w, Wsc, row_flips,
+                                              (int64_t)blockIdx.x * (256 / TPR), red, cnt);
+}
+
 // gamma' = fl32(gamma * s), beta' = fl32(beta * s): the activation-side s of
 // UAQ folded into the norm that produces the linear's input.
 __global__ __launch_bounds__(256) void fold_norm_kernel(float* gamma, float* beta, int64_t K,
                                                          float s) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= K) return;
-  if (gamma) gamma[i] = gamma[i] * s;
-  if (beta) beta[i] = beta[i] * s;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < K; i += (int64_t)gridDim.x * 256) {
+    if (gamma) gamma[i] = gamma[i] * s;
+    if (beta) beta[i] = beta[i] * s;
+  }
 }
 
 inline unsigned grid_for(int64_t rows, int rpb) { return (unsigned)((rows + rpb - 1) / rpb); }
+
+// Rows per launch: a launch stays far inside the dispatch limits (2^20
+// blocks); longer row ranges are split into several launches on the host.
+constexpr int64_t kRowBlocks = int64_t(1) << 20;
 
 }  // namespace
 
@@ -239,19 +261,26 @@ hipError_t launch_act_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
   // MI355X than one wave per row for 3584-element rows), with the fewest
   // 16-byte chunks per thread that hold the row.
   const dim3 b(256);
-  if (K <= 2048)
-    hipLaunchKernelGGL((act_quant_kernel<QT, 64, 4>), dim3(grid_for(M, 4)), b, 0, st, x, M, K, ldx,
-                       act_mult, q, scale_x);
-  else if (K <= 4096)
-    hipLaunchKernelGGL((act_quant_kernel<QT, 256, 2>), dim3(grid_for(M, 1)), b, 0, st, x, M, K,
-                       ldx, act_mult, q, scale_x);
-  else if (K <= 8192)
-    hipLaunchKernelGGL((act_quant_kernel<QT, 256, 4>), dim3(grid_for(M, 1)), b, 0, st, x, M, K,
-                       ldx, act_mult, q, scale_x);
-  else
-    hipLaunchKernelGGL((act_quant_kernel<QT, 256, 16>), dim3(grid_for(M, 1)), b, 0, st, x, M, K,
-                       ldx, act_mult, q, scale_x);
-  return hipGetLastError();
+  const int rpb = K <= 2048 ? 4 : 1;
+  for (int64_t r0 = 0; r0 < M; r0 += kRowBlocks * rpb) {
+    const int64_t m = M - r0 < kRowBlocks * rpb ? M - r0 : kRowBlocks * rpb;
+    const uint16_t* xs = x + r0 * ldx;
+    uint8_t* qs = q + r0 * K;
+    float* ss = scale_x + r0;
+    const dim3 g(grid_for(m, rpb));
+    if (K <= 2048)
+      hipLaunchKernelGGL((act_quant_kernel<QT, 64, 4>), g, b, 0, st, xs, m, K, ldx, act_mult, qs, ss);
+    else if (K <= 4096)
+      hipLaunchKernelGGL((act_quant_kernel<QT, 256, 2>), g, b, 0, st, xs, m, K, ldx, act_mult, qs, ss);
+    else if (K <= 8192)
+      hipLaunchKernelGGL((act_quant_kernel<QT, 256, 4>), g, b, 0, st, xs, m, K, ldx, act_mult, qs, ss);
+    else
+      hipLaunchKernelGGL((act_quant_kernel<QT, 256, 16>), g, b, 0, st, xs, m, K, ldx, act_mult, qs,
+                         ss);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int64_t ldx, float act_mult,
@@ -273,22 +302,34 @@ hipError_t launch_weight_rows(const float* W, int64_t N, int64_t K, int64_t ldw,
                               uint8_t* q, float* scale_w, float* Wsc, uint32_t* flips,
                               hipStream_t st) {
   const dim3 b(256);
-  if (K <= 1024)
-    hipLaunchKernelGGL((weight_quant_kernel<QT, 64, 4, DIVS, CNT>), dim3(grid_for(N, 4)), b, 0, st,
-                       W, N, K, ldw, s, q, scale_w, Wsc, flips);
-  else if (K <= 4096)
-    hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 4, DIVS, CNT>), dim3(grid_for(N, 1)), b, 0,
-                       st, W, N, K, ldw, s, q, scale_w, Wsc, flips);
-  else if (K <= 8192)
-    hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 8, DIVS, CNT>), dim3(grid_for(N, 1)), b, 0,
-                       st, W, N, K, ldw, s, q, scale_w, Wsc, flips);
-  else if (K <= 20480)
-    hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 20, DIVS, CNT>), dim3(grid_for(N, 1)), b, 0,
-                       st, W, N, K, ldw, s, q, scale_w, Wsc, flips);
-  else
-    hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 32, DIVS, CNT>), dim3(grid_for(N, 1)), b, 0,
-                       st, W, N, K, ldw, s, q, scale_w, Wsc, flips);
-  return hipGetLastError();
+  const int rpb = K <= 1024 ? 4 : 1;
+  for (int64_t r0 = 0; r0 < N; r0 += kRowBlocks * rpb) {
+    const int64_t n = N - r0 < kRowBlocks * rpb ? N - r0 : kRowBlocks * rpb;
+    const float* ws = W + r0 * ldw;
+    uint8_t* qs = q + r0 * K;
+    float* ss = scale_w + r0;
+    float* wsc = Wsc ? Wsc + r0 * ldw : nullptr;
+    uint32_t* fs = flips ? flips + r0 : nullptr;
+    const dim3 g(grid_for(n, rpb));
+    if (K <= 1024)
+      hipLaunchKernelGGL((weight_quant_kernel<QT, 64, 4, DIVS, CNT>), g, b, 0, st, ws, n, K, ldw, s,
+                         qs, ss, wsc, fs);
+    else if (K <= 4096)
+      hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 4, DIVS, CNT>), g, b, 0, st, ws, n, K, ldw,
+                         s, qs, ss, wsc, fs);
+    else if (K <= 8192)
+      hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 8, DIVS, CNT>), g, b, 0, st, ws, n, K, ldw,
+                         s, qs, ss, wsc, fs);
+    else if (K <= 20480)
+      hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 20, DIVS, CNT>), g, b, 0, st, ws, n, K, ldw,
+                         s, qs, ss, wsc, fs);
+    else
+      hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 32, DIVS, CNT>), g, b, 0, st, ws, n, K, ldw,
+                         s, qs, ss, wsc, fs);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, int64_t ldw, float s, int qt,
