@@ -31,22 +31,27 @@ __device__ __forceinline__ uint2 codes8_bf16(const uint4 v, float t) {
                     quant_codes4<QT>(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w), t));
 }
 
-// Block-wide max when one 256-thread block owns a row (TPR == 256), or a
-// wave-wide max when each wave owns a row (TPR == 64).
+// Threads per block: 256 (four rows of one wave each) when TPR == 64, else
+// one row per block of TPR threads (256, 512 or 1024).
+constexpr int block_threads(int tpr) { return tpr < 256 ? 256 : tpr; }
+
+// Row maximum: across the wave when each wave owns a row (TPR == 64), else
+// across the block's TPR / 64 waves through LDS.
 template <int TPR>
 __device__ __forceinline__ float row_max(float v, float* red) {
   v = wave_max(v);
-  if constexpr (TPR == 256) {
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[w] = v;
+  if constexpr (TPR > 64) {
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    v = red[0];
+#pragma unroll
+    for (int w = 1; w < TPR / 64; ++w) v = fmaxf(v, red[w]);
   }
   return v;
 }
 
-// The rows base .. base + 256/TPR - 1, one per TPR threads. MAXC 16-byte
-// chunks per thread are kept in registers (row length <= MAXC * TPR * 8).
+// The rows of one block, one per TPR threads. MAXC 16-byte chunks per
+// thread are kept in registers (row length <= MAXC * TPR * 8).
 template <int QT, int TPR, int MAXC>
 __device__ __forceinline__ void act_quant_rows(const uint16_t* __restrict__ X, int64_t M,
                                                int64_t K, int64_t ldx, float act_mult,
@@ -106,13 +111,12 @@ __device__ __forceinline__ void act_quant_rows(const uint16_t* __restrict__ X, i
 }
 
 template <int QT, int TPR, int MAXC>
-__global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restrict__ X, int64_t M,
-                                                        int64_t K, int64_t ldx, float act_mult,
-                                                        uint8_t* __restrict__ Xq,
-                                                        float* __restrict__ scale_x) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(block_threads(TPR)) void act_quant_kernel(
+    const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t ldx, float act_mult,
+    uint8_t* __restrict__ Xq, float* __restrict__ scale_x) {
+  __shared__ float red[16];
   act_quant_rows<QT, TPR, MAXC>(X, M, K, ldx, act_mult, Xq, scale_x,
-                                (int64_t)blockIdx.x * (256 / TPR), red);
+                                (int64_t)blockIdx.x * (block_threads(TPR) / TPR), red);
 }
 
 // Positions among four code bytes whose value changed: INT8 any byte
@@ -211,28 +215,29 @@ __device__ __forceinline__ void weight_quant_rows(const float* W, int64_t N, int
   }
   if constexpr (CNT) {
     // Row sum of the per-lane counts: across the wave with lane shuffles,
-    // then (one row per block) across the four waves through LDS.
+    // then (one row per block) across the block's waves through LDS.
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) nflip += __shfl_xor(nflip, o, 64);
-    if constexpr (TPR == 256) {
+    if constexpr (TPR > 64) {
       if ((threadIdx.x & 63) == 0) cnt[threadIdx.x >> 6] = nflip;
       __syncthreads();
-      nflip = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+      nflip = cnt[0];
+#pragma unroll
+      for (int w = 1; w < TPR / 64; ++w) nflip += cnt[w];
     }
     if (valid && lt == 0) row_flips[row] = (uint32_t)nflip;
   }
 }
 
 template <int QT, int TPR, int MAXC, bool DIVS, bool CNT>
-__global__ __launch_bounds__(256) void weight_quant_kernel(const float* W, int64_t N, int64_t K,
-                                                           int64_t ldw, float s,
-                                                           uint8_t* __restrict__ Wq,
-                                                           float* __restrict__ scale_w,
-                                                           float* Wsc, uint32_t* row_flips) {
-  __shared__ float red[4];
-  __shared__ int cnt[4];
+__global__ __launch_bounds__(block_threads(TPR)) void weight_quant_kernel(
+    const float* W, int64_t N, int64_t K, int64_t ldw, float s, uint8_t* __restrict__ Wq,
+    float* __restrict__ scale_w, float* Wsc, uint32_t* row_flips) {
+  __shared__ float red[16];
+  __shared__ int cnt[16];
   weight_quant_rows<QT, TPR, MAXC, DIVS, CNT>(W, N, K, ldw, s, Wq, scale_w, Wsc, row_flips,
-                                              (int64_t)blockIdx.x * (256 / TPR), red, cnt);
+                                              (int64_t)blockIdx.x * (block_threads(TPR) / TPR),
+                                              red, cnt);
 }
 
 // gamma' = fl32(gamma * s), beta' = fl32(beta * s): the activation-side s of
@@ -253,30 +258,36 @@ constexpr int64_t kRowBlocks = int64_t(1) << 20;
 
 }  // namespace
 
+template <int QT, int TPR, int MAXC>
+void launch_act_kernel(const uint16_t* x, int64_t m, int64_t K, int64_t ldx, float act_mult,
+                       uint8_t* q, float* scale_x, hipStream_t st) {
+  constexpr int NT = block_threads(TPR);
+  hipLaunchKernelGGL((act_quant_kernel<QT, TPR, MAXC>), dim3(grid_for(m, NT / TPR)), dim3(NT), 0,
+                     st, x, m, K, ldx, act_mult, q, scale_x);
+}
+
 template <int QT>
 hipError_t launch_act_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, float act_mult,
                            uint8_t* q, float* scale_x, hipStream_t st) {
-  // Short rows: one wave per row, four rows per block. Longer rows take the
-  // four waves of a block (more loads in flight per row; measured faster on
-  // MI355X than one wave per row for 3584-element rows), with the fewest
-  // 16-byte chunks per thread that hold the row.
-  const dim3 b(256);
+  // Short rows: one wave per row, four rows per block. Longer rows: one
+  // block per row, sized so that each thread holds at most 2-4 16-byte
+  // chunks (few registers: high occupancy for a streaming kernel).
   const int rpb = K <= 2048 ? 4 : 1;
   for (int64_t r0 = 0; r0 < M; r0 += kRowBlocks * rpb) {
     const int64_t m = M - r0 < kRowBlocks * rpb ? M - r0 : kRowBlocks * rpb;
     const uint16_t* xs = x + r0 * ldx;
     uint8_t* qs = q + r0 * K;
     float* ss = scale_x + r0;
-    const dim3 g(grid_for(m, rpb));
     if (K <= 2048)
-      hipLaunchKernelGGL((act_quant_kernel<QT, 64, 4>), g, b, 0, st, xs, m, K, ldx, act_mult, qs, ss);
+      launch_act_kernel<QT, 64, 4>(xs, m, K, ldx, act_mult, qs, ss, st);
     else if (K <= 4096)
-      hipLaunchKernelGGL((act_quant_kernel<QT, 256, 2>), g, b, 0, st, xs, m, K, ldx, act_mult, qs, ss);
+      launch_act_kernel<QT, 256, 2>(xs, m, K, ldx, act_mult, qs, ss, st);
     else if (K <= 8192)
-      hipLaunchKernelGGL((act_quant_kernel<QT, 256, 4>), g, b, 0, st, xs, m, K, ldx, act_mult, qs, ss);
+      launch_act_kernel<QT, 256, 4>(xs, m, K, ldx, act_mult, qs, ss, st);
+    else if (K <= 16384)
+      launch_act_kernel<QT, 512, 4>(xs, m, K, ldx, act_mult, qs, ss, st);
     else
-      hipLaunchKernelGGL((act_quant_kernel<QT, 256, 16>), g, b, 0, st, xs, m, K, ldx, act_mult, qs,
-                         ss);
+      launch_act_kernel<QT, 1024, 4>(xs, m, K, ldx, act_mult, qs, ss, st);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -297,11 +308,23 @@ hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int64_t ldx, fl
 // get): short rows one wave each, four rows per block; longer rows one block
 // each, with the fewest 16-byte chunks per thread that hold the row. Rows
 // longer than 32768 elements are read twice.
+template <int QT, int TPR, int MAXC, bool DIVS, bool CNT>
+void launch_weight_kernel(const float* W, int64_t n, int64_t K, int64_t ldw, float s, uint8_t* q,
+                          float* scale_w, float* Wsc, uint32_t* flips, hipStream_t st) {
+  constexpr int NT = block_threads(TPR);
+  hipLaunchKernelGGL((weight_quant_kernel<QT, TPR, MAXC, DIVS, CNT>), dim3(grid_for(n, NT / TPR)),
+                     dim3(NT), 0, st, W, n, K, ldw, s, q, scale_w, Wsc, flips);
+}
+
 template <int QT, bool DIVS, bool CNT>
 hipError_t launch_weight_rows(const float* W, int64_t N, int64_t K, int64_t ldw, float s,
                               uint8_t* q, float* scale_w, float* Wsc, uint32_t* flips,
                               hipStream_t st) {
-  const dim3 b(256);
+  // Short rows: one wave per row, four rows per block. Longer rows: one
+  // block per row, sized so that each thread holds 4-8 16-byte chunks
+  // (measured on MI355X: 256 threads x 4 chunks for 3584-element rows and
+  // 1024 x 5 for 18944 beat fewer threads with more chunks each, which cost
+  // registers and so waves in flight).
   const int rpb = K <= 1024 ? 4 : 1;
   for (int64_t r0 = 0; r0 < N; r0 += kRowBlocks * rpb) {
     const int64_t n = N - r0 < kRowBlocks * rpb ? N - r0 : kRowBlocks * rpb;
@@ -310,22 +333,16 @@ hipError_t launch_weight_rows(const float* W, int64_t N, int64_t K, int64_t ldw,
     float* ss = scale_w + r0;
     float* wsc = Wsc ? Wsc + r0 * ldw : nullptr;
     uint32_t* fs = flips ? flips + r0 : nullptr;
-    const dim3 g(grid_for(n, rpb));
     if (K <= 1024)
-      hipLaunchKernelGGL((weight_quant_kernel<QT, 64, 4, DIVS, CNT>), g, b, 0, st, ws, n, K, ldw, s,
-                         qs, ss, wsc, fs);
+      launch_weight_kernel<QT, 64, 4, DIVS, CNT>(ws, n, K, ldw, s, qs, ss, wsc, fs, st);
     else if (K <= 4096)
-      hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 4, DIVS, CNT>), g, b, 0, st, ws, n, K, ldw,
-                         s, qs, ss, wsc, fs);
+      launch_weight_kernel<QT, 256, 4, DIVS, CNT>(ws, n, K, ldw, s, qs, ss, wsc, fs, st);
     else if (K <= 8192)
-      hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 8, DIVS, CNT>), g, b, 0, st, ws, n, K, ldw,
-                         s, qs, ss, wsc, fs);
+      launch_weight_kernel<QT, 512, 4, DIVS, CNT>(ws, n, K, ldw, s, qs, ss, wsc, fs, st);
     else if (K <= 20480)
-      hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 20, DIVS, CNT>), g, b, 0, st, ws, n, K, ldw,
-                         s, qs, ss, wsc, fs);
+      launch_weight_kernel<QT, 1024, 5, DIVS, CNT>(ws, n, K, ldw, s, qs, ss, wsc, fs, st);
     else
-      hipLaunchKernelGGL((weight_quant_kernel<QT, 256, 32, DIVS, CNT>), g, b, 0, st, ws, n, K, ldw,
-                         s, qs, ss, wsc, fs);
+      launch_weight_kernel<QT, 1024, 8, DIVS, CNT>(ws, n, K, ldw, s, qs, ss, wsc, fs, st);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
