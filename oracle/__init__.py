@@ -46,6 +46,10 @@ from .qurl import (
     flip_counts,
     count_flips,
     count_flips_rows,
+    norm_folded,
+    norm_quant,
+    silu_mul,
+    silu_mul_quant,
     requantize_weights,
     flip_expectation,
     decode_chain,
@@ -56,6 +60,7 @@ __all__ = [
     "E4M3FN_MAX", "QMAX", "uaq_reparameterize", "quantize_rows",
     "quantize_weights_uaq", "quantize_act_per_token", "acc_int8", "acc_fp8",
     "dequant_epilogue", "w8a8_linear", "flip_counts", "flip_expectation",
-    "count_flips", "count_flips_rows", "requantize_weights",
+    "count_flips", "count_flips_rows",
+    "norm_folded", "norm_quant", "silu_mul", "silu_mul_quant", "requantize_weights",
     "decode_chain",
 ]

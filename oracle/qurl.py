@@ -137,6 +137,84 @@ def quantize_act_per_token(X_bits, act_mult, qt):
 
 
 # ----------------------------------------------------------------------------
+# Producers fused with the per-token quantization (the step before the linear)
+# ----------------------------------------------------------------------------
+#
+# Paper notes, "Method > Key designs > UAQ": the activation-side factor s is
+# merged into the norm that produces the linear's input (gain gamma' = gamma*s,
+# bias beta' = beta*s). The pages do not fix the norm's own arithmetic; the
+# reading taken: the per-row statistic is computed in float64 and rounded to
+# fp32 once, every later step is fp32 in the order written. The norm output is
+# quantized as fp32 (a fused kernel never stores it as bf16).
+
+def _row_stat_f32(x64):
+    return np.asarray(x64, np.float64).astype(np.float32)
+
+
+def norm_folded(H_bits, gamma_s, beta_s=None, eps=1e-6, kind="rms"):
+    """Norm of bf16 rows with the UAQ-folded gain (and bias), per row h:
+
+    kind "rms":   ms = sum_k h_k^2 / K                        (float64)
+                  r  = fl32(1 / sqrt(ms + eps))               (float64, one rounding)
+                  y_k = fl32(fl32(h_k * r) * gamma'_k) [+ beta'_k, fl32]
+    kind "layer": mu = fl32(sum_k h_k / K)                    (float64, one rounding)
+                  var = sum_k (h_k - mu)^2 / K                (float64, mu as rounded)
+                  r  = fl32(1 / sqrt(var + eps))              (float64, one rounding)
+                  y_k = fl32(fl32(fl32(h_k - mu) * r) * gamma'_k) [+ beta'_k, fl32]
+    Returns (y float32 [M, K], r float32 [M]).
+    """
+    if kind not in ("rms", "layer"):
+        raise ValueError("kind must be 'rms' or 'layer'")
+    H = bf16_bits_to_f32(H_bits).astype(np.float32)
+    M, K = H.shape
+    if K == 0:
+        return np.zeros((M, 0), np.float32), np.zeros(M, np.float32)
+    g = np.asarray(gamma_s, np.float32)
+    H64 = H.astype(np.float64)
+    if kind == "rms":
+        ms = (H64 * H64).sum(axis=1) / K
+        d = H
+    else:
+        mu = _row_stat_f32(H64.sum(axis=1) / K)
+        dev = H64 - mu.astype(np.float64)[:, None]
+        ms = (dev * dev).sum(axis=1) / K
+        d = (H - mu[:, None]).astype(np.float32)
+    r = _row_stat_f32(1.0 / np.sqrt(ms + float(eps)))
+    y = ((d * r[:, None]).astype(np.float32) * g[None, :]).astype(np.float32)
+    if beta_s is not None:
+        y = (y + np.asarray(beta_s, np.float32)[None, :]).astype(np.float32)
+    return y, r
+
+
+def norm_quant(H_bits, gamma_s, beta_s=None, eps=1e-6, kind="rms", qt="int8"):
+    """The folded norm followed by per-token quantization of its fp32 output.
+    s already sits in gamma' (and beta'), so the scale carries no extra factor
+    (reading R9's norm-fed case). Returns (codes, scale_x)."""
+    y, _ = norm_folded(H_bits, gamma_s, beta_s, eps, kind)
+    return quantize_rows(y, qt)
+
+
+def silu_mul(G_bits, U_bits):
+    """SiLU(gate) times up, a = fl32(g * u / (1 + exp(-g))) evaluated in
+    float64 from the bf16 inputs (g * u is exact there; exp overflow gives a
+    signed zero)."""
+    g = bf16_bits_to_f32(G_bits).astype(np.float64)
+    u = bf16_bits_to_f32(U_bits).astype(np.float64)
+    with np.errstate(over="ignore"):
+        a = (g * u) / (1.0 + np.exp(-g))
+    return a.astype(np.float32)
+
+
+def silu_mul_quant(G_bits, U_bits, act_mult, qt):
+    """silu_mul followed by per-token quantization; act_mult carries s for the
+    down projection, whose input no norm produces (reading R9).
+    Returns (codes, scale_x) with scale_x = fl32(fl32(a_m / Q) * act_mult)."""
+    a = silu_mul(G_bits, U_bits)
+    codes, t = quantize_rows(a, qt)
+    return codes, (t * np.float32(act_mult)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
 # Quantized product and dequantization
 # ----------------------------------------------------------------------------
 

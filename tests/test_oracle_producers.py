@@ -1,0 +1,223 @@
+"""Pins of the oracle's fused producers (norm with the UAQ-folded gain, SiLU x up),
+each followed by per-token quantization.
+
+They are checked against what the mathematics fixes: exact rationals and
+50-digit decimals rounded once to fp32 by a rounding written here, closed forms
+(constant rows, +-1 rows, power-of-two scaling, SiLU's special values), torch's
+float64 norm and SiLU routines to within the reading's roundings, and the UAQ
+fold end to end (folded norm + W/s weights against the float product of the
+unfolded layer).
+"""
+
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle import formats as F
+from w8a8_gemm_rl_amd import inputs as I
+
+getcontext().prec = 60
+
+
+def _fp32_rn(v):
+    """Nearest fp32 to an exact rational v (ties to even), by exact comparison."""
+    v = Fraction(v)
+    if v == 0:
+        return np.float32(0.0)
+    c = np.float32(float(v))
+    best = None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        d = abs(Fraction(float(cand)) - v)
+        key = (d, int(np.array(cand, np.float32).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return np.float32(best[1])
+
+
+def _dec_sqrt_inv(x):
+    """1 / sqrt(x) of an exact rational to 60 digits, as a Fraction."""
+    d = Decimal(x.numerator) / Decimal(x.denominator)
+    return Fraction(1 / d.sqrt())
+
+
+def _bf16_rows(M, K, seed, scale=1.0):
+    x = I.normal_f32((M, K), scale, seed=seed)
+    return F.f32_to_bf16_bits(x)
+
+
+def _vals(bits):
+    return F.bf16_bits_to_f32(bits)
+
+
+# ------------------------------------------------------------------ RMSNorm
+
+def test_rms_row_statistic_is_the_exact_value_rounded_once():
+    """r = fl32(1/sqrt(mean(h^2) + eps)) against exact rationals and 60-digit roots."""
+    Hb = _bf16_rows(6, 48, seed=1)
+    H = _vals(Hb)
+    eps = 1e-6
+    _, r = O.norm_folded(Hb, np.ones(48, np.float32), eps=eps, kind="rms")
+    for m in range(6):
+        ms = sum(Fraction(float(h)) ** 2 for h in H[m]) / 48 + Fraction(eps)
+        assert r[m] == _fp32_rn(_dec_sqrt_inv(ms)), m
+
+
+def test_rms_elementwise_steps_round_in_order():
+    """y = fl32(fl32(h * r) * gamma'), each product rounded once (exact rationals)."""
+    Hb = _bf16_rows(3, 32, seed=2)
+    H = _vals(Hb)
+    g = I.normal_f32((32,), 1.0, seed=3)
+    y, r = O.norm_folded(Hb, g, eps=1e-6, kind="rms")
+    for m in range(3):
+        for k in range(32):
+            hr = _fp32_rn(Fraction(float(H[m, k])) * Fraction(float(r[m])))
+            assert y[m, k] == _fp32_rn(Fraction(float(hr)) * Fraction(float(g[k])))
+
+
+def test_rms_constant_row_and_power_of_two_scaling():
+    # h = 2 everywhere, eps = 0: mean square 4, r = 1/2 exactly, y = gamma
+    Hb = F.f32_to_bf16_bits(np.full((1, 64), 2.0, np.float32))
+    g = I.normal_f32((64,), 1.0, seed=4)
+    y, r = O.norm_folded(Hb, g, eps=0.0, kind="rms")
+    assert r[0] == np.float32(0.5) and np.array_equal(y[0], g)
+    codes, sc = O.norm_quant(Hb, np.ones(64, np.float32), eps=0.0, kind="rms", qt="int8")
+    assert np.all(codes == 127) and sc[0] == np.float32(1.0 / 127)
+    # doubling every input (exact in bf16) halves r exactly: the output is unchanged
+    Hb = _bf16_rows(5, 96, seed=5)
+    H2 = F.f32_to_bf16_bits(_vals(Hb) * 2)
+    y1, _ = O.norm_folded(Hb, g[:1].repeat(96), eps=0.0)
+    y2, _ = O.norm_folded(H2, g[:1].repeat(96), eps=0.0)
+    assert np.array_equal(y1, y2)
+
+
+@pytest.mark.parametrize("kind", ["rms", "layer"])
+def test_norm_matches_torch_float64_within_the_readings_roundings(kind):
+    Hb = _bf16_rows(16, 512, seed=6, scale=3.0)
+    H = _vals(Hb).astype(np.float64)
+    g = I.normal_f32((512,), 1.0, seed=7)
+    b = I.normal_f32((512,), 0.1, seed=8)
+    eps = 1e-5
+    y, _ = O.norm_folded(Hb, g, b if kind == "layer" else None, eps=eps, kind=kind)
+    Ht = torch.from_numpy(H)
+    gt = torch.from_numpy(g.astype(np.float64))
+    if kind == "rms":
+        ref = torch.nn.functional.rms_norm(Ht, (512,), gt, eps).numpy()
+    else:
+        ref = torch.nn.functional.layer_norm(Ht, (512,), gt, torch.from_numpy(b.astype(np.float64)),
+                                             eps).numpy()
+    # three or four fp32 roundings of values of size |ref| (plus |beta| for the bias add)
+    tol = 4 * 2.0 ** -24 * (np.abs(ref) + np.abs(b if kind == "layer" else 0) + 1e-30)
+    assert np.all(np.abs(y - ref) <= tol)
+
+
+# ------------------------------------------------------------------ LayerNorm
+
+def test_layer_norm_closed_forms():
+    # constant row: zero variance, output = beta'
+    Hb = F.f32_to_bf16_bits(np.full((1, 32), 0.75, np.float32))
+    g = I.normal_f32((32,), 1.0, seed=9)
+    b = I.normal_f32((32,), 0.1, seed=10)
+    y, _ = O.norm_folded(Hb, g, b, eps=1e-5, kind="layer")
+    assert np.array_equal(y[0], b)
+    # no bias: all-zero output quantizes to scale 0, codes 0
+    codes, sc = O.norm_quant(Hb, g, None, eps=1e-5, kind="layer", qt="fp8")
+    assert sc[0] == 0 and not codes.view(np.uint8).any()
+    # +-1 halves: mu = 0, var = 1, r = fl32(1/sqrt(1 + eps)), y = fl32(+-r * gamma')
+    h = np.where(np.arange(64) % 2 == 0, 1.0, -1.0).astype(np.float32)[None, :]
+    y, r = O.norm_folded(F.f32_to_bf16_bits(h), np.ones(64, np.float32), eps=1e-5, kind="layer")
+    assert r[0] == _fp32_rn(_dec_sqrt_inv(1 + Fraction(1e-5)))
+    assert np.array_equal(y[0], (h[0] * r[0]).astype(np.float32))
+
+
+def test_layer_norm_mean_and_deviation_rounding():
+    """mu = fl32(mean) (exact rational rounded once), d = fl32(h - mu)."""
+    Hb = _bf16_rows(2, 40, seed=11)
+    H = _vals(Hb)
+    y, r = O.norm_folded(Hb, np.ones(40, np.float32), eps=1e-6, kind="layer")
+    for m in range(2):
+        mu = _fp32_rn(sum(Fraction(float(h)) for h in H[m]) / 40)
+        var = sum((Fraction(float(h)) - Fraction(float(mu))) ** 2 for h in H[m]) / 40
+        assert r[m] == _fp32_rn(_dec_sqrt_inv(var + Fraction(1e-6)))
+        d = [_fp32_rn(Fraction(float(h)) - Fraction(float(mu))) for h in H[m]]
+        assert all(y[m, k] == _fp32_rn(Fraction(float(d[k])) * Fraction(float(r[m])))
+                   for k in range(40))
+
+
+# ------------------------------------------------------------------ UAQ fold through the norm
+
+def test_folded_norm_feeds_the_uaq_linear():
+    """Norm with gamma' = fl32(gamma * s), quantized, times the quantized W/s,
+    equals the float product of the unfolded layer W (norm(h) with gamma) within
+    the quantization error; the per-token scale carries s."""
+    M, K, N, s = 8, 256, 64, 1.5
+    Hb = _bf16_rows(M, K, seed=12)
+    g = np.abs(I.normal_f32((K,), 1.0, seed=13)) + 0.5
+    W = I.weights(N, K, 0.02, seed=14)
+    _, g_s, _ = O.uaq_reparameterize(W, s, gamma=g)
+    codes, sx = O.norm_quant(Hb, g_s, eps=1e-6, kind="rms", qt="int8")
+    codes0, sx0 = O.norm_quant(Hb, g, eps=1e-6, kind="rms", qt="int8")
+    # the fold multiplies the activation side by s: scales grow by s (up to fp32 roundings)
+    assert np.allclose(sx, sx0 * s, rtol=4 * 2.0 ** -24, atol=0)
+    wq = O.quantize_weights_uaq(W, s, "int8")
+    acc = O.acc_int8(codes, wq["Wq"])
+    y = acc * sx[:, None].astype(np.float64) * wq["scale_w"][None, :].astype(np.float64)
+    yn, _ = O.norm_folded(Hb, g, eps=1e-6, kind="rms")
+    ref = yn.astype(np.float64) @ W.astype(np.float64).T
+    # error bound of two symmetric absmax quantizations (half a step each, per element)
+    bound = (0.5 * sx[:, None] * np.abs(wq["Wq"].astype(np.float64)).sum(axis=1)[None, :]
+             * wq["scale_w"][None, :]
+             + 0.5 * wq["scale_w"][None, :] * np.abs(codes.astype(np.float64)).sum(axis=1)[:, None]
+             * sx[:, None]) * 1.01 + 1e-6
+    assert np.all(np.abs(y - ref) <= bound)
+    # a fold the wrong way (gamma / s) leaves the scale too small by s^2
+    bad = O.uaq_reparameterize(W, 1 / s, gamma=g)[1]
+    _, sxb = O.norm_quant(Hb, bad, eps=1e-6, kind="rms", qt="int8")
+    assert np.allclose(sxb * s * s, sx, rtol=1e-6)
+
+
+# ------------------------------------------------------------------ SiLU x up
+
+def test_silu_special_values():
+    def run(g, u):
+        a = O.silu_mul(F.f32_to_bf16_bits(np.array([[g]], np.float32)),
+                       F.f32_to_bf16_bits(np.array([[u]], np.float32)))
+        return a[0, 0]
+    assert run(0.0, 3.0) == 0.0
+    # 1 / (1 + e^-1), rounded once to fp32
+    e1 = Fraction(Decimal(1) / (1 + Decimal(-1).exp()))
+    assert run(1.0, 1.0) == _fp32_rn(e1)
+    assert run(100.0, 0.5) == np.float32(50.0)  # 1 + e^-100 rounds to 1 in float64
+    v = run(-1000.0, 2.0)
+    assert v == 0.0 and np.signbit(v)  # exp overflow: -2000 / inf = -0
+    tiny = Fraction(Decimal(-100) * Decimal(0.5) / (1 + Decimal(100).exp()))
+    assert run(-100.0, 0.5) == _fp32_rn(tiny)  # an fp32 subnormal
+
+
+def test_silu_mul_against_decimals_and_torch():
+    Gb = _bf16_rows(4, 64, seed=15, scale=3.0)
+    Ub = _bf16_rows(4, 64, seed=16)
+    a = O.silu_mul(Gb, Ub)
+    G, U = _vals(Gb), _vals(Ub)
+    for m in range(4):
+        for k in range(0, 64, 5):
+            gd, ud = Decimal(float(G[m, k])), Decimal(float(U[m, k]))
+            exact = Fraction(gd * ud / (1 + (-gd).exp()))
+            assert a[m, k] == _fp32_rn(exact), (m, k)
+    ref = (torch.nn.functional.silu(torch.from_numpy(G.astype(np.float64)))
+           * torch.from_numpy(U.astype(np.float64))).numpy()
+    assert np.all(np.abs(a - ref) <= 2.0 ** -24 * np.abs(ref) + 1e-45)
+
+
+def test_silu_mul_quant_scale_carries_act_mult():
+    Gb = _bf16_rows(3, 128, seed=17, scale=2.0)
+    Ub = _bf16_rows(3, 128, seed=18)
+    c1, s1 = O.silu_mul_quant(Gb, Ub, 1.0, "fp8")
+    c2, s2 = O.silu_mul_quant(Gb, Ub, 1.5, "fp8")
+    assert np.array_equal(c1.view(np.uint8), c2.view(np.uint8))
+    assert np.array_equal(s2, (s1 * np.float32(1.5)).astype(np.float32))
+    a = O.silu_mul(Gb, Ub)
+    assert np.allclose(s1, np.abs(a).max(axis=1) / 448, rtol=2.0 ** -23)
