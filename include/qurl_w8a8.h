@@ -152,6 +152,63 @@ int qr_requantize_weights(const float* Wp, int64_t N, int64_t K, int64_t ldw, in
 int qr_quantize_act_per_token(const void* X, int64_t M, int64_t K, int64_t ldx, float act_mult,
                               int qt, void* Xq, float* scale_x, void* stream);
 
+/* Norm kinds of qr_norm_quant. */
+enum { QR_NORM_RMS = 0, QR_NORM_LAYER = 1 };
+
+/*
+ * qr_norm_quant -- the norm that produces a linear's input, with the UAQ
+ * factor s merged into its gain and bias [Notes/UAQ], fused with the
+ * token-wise quantization [Notes/Training] of its output: one pass over H,
+ * the normalized values never reach memory.
+ *
+ * For every token m, with h = H[m,:] widened exactly to fp32 and K = row length:
+ *   QR_NORM_RMS:   ms = sum_k h_k^2 / K                       (float64)
+ *                  r  = fl32(1 / sqrt(ms + eps))              (float64, rounded once)
+ *                  y_k = fl32(fl32(h_k * r) * gamma[k])
+ *   QR_NORM_LAYER: mu = fl32(sum_k h_k / K)                   (float64, rounded once)
+ *                  ms = sum_k (h_k - mu)^2 / K                (float64)
+ *                  r  = fl32(1 / sqrt(ms + eps))
+ *                  y_k = fl32(fl32(fl32(h_k - mu) * r) * gamma[k])
+ *   with beta: y_k = fl32(y_k + beta[k]).
+ *   Codes and scale_x[m] = fl32(max_k |y_k| / Q) as qr_quantize_act_per_token
+ *   with act_mult = 1 (s is already in gamma and beta).
+ * The float64 sums may be taken in any order: r is the same fp32 value unless
+ * the exact value lies within about 2^-45 (relative) of an fp32 rounding
+ * boundary.
+ *
+ *   H        [M, ldh] bf16 bit patterns (read).
+ *   norm     QR_NORM_RMS or QR_NORM_LAYER.
+ *   gamma    [K] fp32 folded gain gamma*s (e.g. from qr_quantize_weights_uaq's
+ *            fold); 16-byte aligned. beta: NULL or [K] fp32 folded bias beta*s.
+ *   eps      finite, >= 0.
+ *   Xq       [M, K] codes (written); scale_x [M] fp32 (written).
+ * K <= 32768 (rows are held in registers). Errors as qr_quantize_act_per_token.
+ */
+int qr_norm_quant(const void* H, int64_t M, int64_t K, int64_t ldh, int norm, const float* gamma,
+                  const float* beta, float eps, int qt, void* Xq, float* scale_x, void* stream);
+
+/*
+ * qr_silu_mul_quant -- the input of the down projection, SiLU(gate) * up,
+ * fused with its token-wise quantization [Notes/Training]; its scale carries
+ * the UAQ factor through act_mult = s ([Notes/UAQ]: no norm produces it).
+ *
+ *   a[m,n] = fl32(g * u / (1 + exp(-g))) evaluated in float64,
+ *            g = G[m,n], u = U[m,n] (bf16, exact in float64)
+ *   codes and scale_x[m] = fl32(fl32(max_n |a[m,n]| / Q) * act_mult) as
+ *   qr_quantize_act_per_token.
+ * The device exp and the host's may differ in the last float64 bit, which
+ * changes a only where the exact value lies within about 2^-50 (relative) of
+ * an fp32 rounding boundary.
+ *
+ *   G, U     [M, ldg] / [M, ldu] bf16 (read): e.g. the two halves of one
+ *            stacked gate+up GEMM output, G = Y, U = Y + N, ldg = ldu = 2N.
+ *   act_mult finite, > 0.
+ *   Xq       [M, N] codes (written); scale_x [M] fp32 (written).
+ * N <= 32768. Errors as qr_quantize_act_per_token.
+ */
+int qr_silu_mul_quant(const void* G, const void* U, int64_t M, int64_t N, int64_t ldg, int64_t ldu,
+                      float act_mult, int qt, void* Xq, float* scale_x, void* stream);
+
 /*
  * qr_w8a8_gemm -- quantized product and dequantization epilogue
  *   [Notes/System] (INT8/FP8 matmul), [Notes/Training].

@@ -155,7 +155,8 @@ def norm_folded(H_bits, gamma_s, beta_s=None, eps=1e-6, kind="rms"):
     """Norm of bf16 rows with the UAQ-folded gain (and bias), per row h:
 
     kind "rms":   ms = sum_k h_k^2 / K                        (float64)
-                  r  = fl32(1 / sqrt(ms + eps))               (float64, one rounding)
+                  r  = fl32(1 / sqrt(ms + eps))               (float64, one rounding;
+                                                               eps is an fp32 value)
                   y_k = fl32(fl32(h_k * r) * gamma'_k) [+ beta'_k, fl32]
     kind "layer": mu = fl32(sum_k h_k / K)                    (float64, one rounding)
                   var = sum_k (h_k - mu)^2 / K                (float64, mu as rounded)
@@ -179,7 +180,7 @@ def norm_folded(H_bits, gamma_s, beta_s=None, eps=1e-6, kind="rms"):
         dev = H64 - mu.astype(np.float64)[:, None]
         ms = (dev * dev).sum(axis=1) / K
         d = (H - mu[:, None]).astype(np.float32)
-    r = _row_stat_f32(1.0 / np.sqrt(ms + float(eps)))
+    r = _row_stat_f32(1.0 / np.sqrt(ms + float(np.float32(eps))))
     y = ((d * r[:, None]).astype(np.float32) * g[None, :]).astype(np.float32)
     if beta_s is not None:
         y = (y + np.asarray(beta_s, np.float32)[None, :]).astype(np.float32)

@@ -74,11 +74,11 @@ def test_weight_quant_in_place_strided_and_norm_fold(qt):
     assert np.array_equal(bd.cpu().numpy(), ref["beta"])
 
 
-_CAP = 1 << 20  # blocks per quantizer launch; more rows loop inside the grid
+_CAP = 1 << 21  # blocks per quantizer launch; more rows take several launches
 
 
 def _loop_rows(N, rpb):
-    """Rows at the start, around each multiple of the grid's row span, and at the end."""
+    """Rows at the start, around each multiple of one launch's row span, and at the end."""
     span = _CAP * rpb
     r = [0, 1, 2, N - 3, N - 2, N - 1]
     for m in range(span, N, span):
@@ -88,8 +88,8 @@ def _loop_rows(N, rpb):
 
 @pytest.mark.parametrize("qt", QTS)
 @pytest.mark.parametrize("N,K,rpb", [(4 * _CAP + 37, 16, 4), (_CAP + 5, 1040, 1)])
-def test_weight_quantizers_loop_past_the_grid_cap(qt, N, K, rpb):
-    """More rows than the launch's blocks cover: every row is still quantized,
+def test_weight_quantizers_past_the_launch_cap(qt, N, K, rpb):
+    """More rows than one launch's blocks cover: every row is still quantized,
     by the UAQ quantizer and by the refresh (with per-row change counts)."""
     gen = torch.Generator(device=DEV)
     gen.manual_seed(N + K)
@@ -116,10 +116,10 @@ def test_weight_quantizers_loop_past_the_grid_cap(qt, N, K, rpb):
 
 @pytest.mark.parametrize("qt", QTS)
 @pytest.mark.parametrize("M,K,rpb", [(4 * _CAP + 37, 16, 4), (_CAP + 5, 2064, 1)])
-def test_act_quantizer_loops_past_the_grid_cap(qt, M, K, rpb):
+def test_act_quantizer_past_the_launch_cap(qt, M, K, rpb):
     gen = torch.Generator(device=DEV)
     gen.manual_seed(M + K)
-    X = torch.randn((M, K), generator=gen, device=DEV).to(torch.bfloat16)
+    X = torch.randn((M, K), generator=gen, device=DEV, dtype=torch.bfloat16)
     rows = _loop_rows(M, rpb)
     idx = torch.from_numpy(rows).to(DEV)
     Xh = bf16_np(X[idx])

@@ -62,7 +62,7 @@ def test_rms_row_statistic_is_the_exact_value_rounded_once():
     eps = 1e-6
     _, r = O.norm_folded(Hb, np.ones(48, np.float32), eps=eps, kind="rms")
     for m in range(6):
-        ms = sum(Fraction(float(h)) ** 2 for h in H[m]) / 48 + Fraction(eps)
+        ms = sum(Fraction(float(h)) ** 2 for h in H[m]) / 48 + Fraction(float(np.float32(eps)))
         assert r[m] == _fp32_rn(_dec_sqrt_inv(ms)), m
 
 
@@ -129,7 +129,7 @@ def test_layer_norm_closed_forms():
     # +-1 halves: mu = 0, var = 1, r = fl32(1/sqrt(1 + eps)), y = fl32(+-r * gamma')
     h = np.where(np.arange(64) % 2 == 0, 1.0, -1.0).astype(np.float32)[None, :]
     y, r = O.norm_folded(F.f32_to_bf16_bits(h), np.ones(64, np.float32), eps=1e-5, kind="layer")
-    assert r[0] == _fp32_rn(_dec_sqrt_inv(1 + Fraction(1e-5)))
+    assert r[0] == _fp32_rn(_dec_sqrt_inv(1 + Fraction(float(np.float32(1e-5)))))
     assert np.array_equal(y[0], (h[0] * r[0]).astype(np.float32))
 
 
@@ -141,7 +141,7 @@ def test_layer_norm_mean_and_deviation_rounding():
     for m in range(2):
         mu = _fp32_rn(sum(Fraction(float(h)) for h in H[m]) / 40)
         var = sum((Fraction(float(h)) - Fraction(float(mu))) ** 2 for h in H[m]) / 40
-        assert r[m] == _fp32_rn(_dec_sqrt_inv(var + Fraction(1e-6)))
+        assert r[m] == _fp32_rn(_dec_sqrt_inv(var + Fraction(float(np.float32(1e-6)))))
         d = [_fp32_rn(Fraction(float(h)) - Fraction(float(mu))) for h in H[m]]
         assert all(y[m, k] == _fp32_rn(Fraction(float(d[k])) * Fraction(float(r[m])))
                    for k in range(40))

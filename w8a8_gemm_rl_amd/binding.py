@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libqurl_w8a8.so")
 
 QT = {"int8": 0, "fp8": 1}
 OUT = {"bf16": 0, "raw": 1}
+NORM = {"rms": 0, "layer": 1}
 STATUS = {
     0: "QR_OK", -1: "QR_ERR_INVALID_ARG", -2: "QR_ERR_UNSUPPORTED", -3: "QR_ERR_WORKSPACE",
     -4: "QR_ERR_HIP", -5: "QR_ERR_NO_DEVICE",
@@ -25,7 +26,7 @@ STATUS = {
 # Every function include/qurl_w8a8.h declares.
 EXPORTS = [
     "qr_quantize_weights_uaq", "qr_requantize_weights", "qr_quantize_act_per_token",
-    "qr_w8a8_gemm", "qr_linear_fused",
+    "qr_norm_quant", "qr_silu_mul_quant", "qr_w8a8_gemm", "qr_linear_fused",
     "qr_workspace_size", "qr_gemm_plan", "qr_tile_name", "qr_num_tiles", "qr_set_plan_override",
     "qr_last_error", "qr_version",
 ]
@@ -45,6 +46,8 @@ _SIGS = {
     "qr_quantize_weights_uaq": (_int, [_vp, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp, _vp, _vp, _vp]),
     "qr_requantize_weights": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp]),
     "qr_quantize_act_per_token": (_int, [_vp, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp]),
+    "qr_norm_quant": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _f32, _int, _vp, _vp, _vp]),
+    "qr_silu_mul_quant": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp]),
     "qr_w8a8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _sz, _vp]),
     "qr_linear_fused": (_int, [_vp, _i64, _f32, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _sz, _vp]),
     "qr_workspace_size": (_sz, [ctypes.c_char_p, _i64, _i64, _i64, _int]),
@@ -214,6 +217,51 @@ def requantize_weights(Wp, qt, Wq, scale_w=None, row_flips=None):
                                          _ptr(row_flips), _stream(Wp.device))
     _check("qr_requantize_weights", st)
     return Wq, scale_w
+
+
+def norm_quant(H, gamma, qt, beta=None, eps=1e-6, kind="rms", Xq=None, scale_x=None):
+    """Norm of bf16 rows H [M, K] with the folded gain gamma (= gamma*s, fp32 [K]) and
+    optional folded bias beta, fused with per-token quantization -> (Xq, scale_x)."""
+    _need_cuda(H, gamma, beta, Xq, scale_x)
+    if H.dtype != torch.bfloat16:
+        raise ValueError("H must be bfloat16")
+    if kind not in NORM:
+        raise ValueError(f"kind must be one of {list(NORM)}")
+    M, K = H.shape
+    ldh = _rows(H, "H")
+    for name, t in (("gamma", gamma), ("beta", beta)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != K or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 tensor of K entries")
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=code_dtype(qt), device=H.device)
+    if scale_x is None:
+        scale_x = torch.empty(M, dtype=torch.float32, device=H.device)
+    with torch.cuda.device(H.device):
+        st = lib().qr_norm_quant(_ptr(H), M, K, ldh, NORM[kind], _ptr(gamma), _ptr(beta),
+                                 float(eps), _qt(qt), _ptr(Xq), _ptr(scale_x), _stream(H.device))
+    _check("qr_norm_quant", st)
+    return Xq, scale_x
+
+
+def silu_mul_quant(G, U, act_mult, qt, Xq=None, scale_x=None):
+    """SiLU(G) * U for bf16 [M, N] views (rows contiguous, any row strides), fused with
+    per-token quantization; scale_x carries act_mult -> (Xq, scale_x)."""
+    _need_cuda(G, U, Xq, scale_x)
+    if G.dtype != torch.bfloat16 or U.dtype != torch.bfloat16:
+        raise ValueError("G and U must be bfloat16")
+    if G.shape != U.shape:
+        raise ValueError("G and U must have one shape")
+    M, N = G.shape
+    ldg, ldu = _rows(G, "G"), _rows(U, "U")
+    if Xq is None:
+        Xq = torch.empty((M, N), dtype=code_dtype(qt), device=G.device)
+    if scale_x is None:
+        scale_x = torch.empty(M, dtype=torch.float32, device=G.device)
+    with torch.cuda.device(G.device):
+        st = lib().qr_silu_mul_quant(_ptr(G), _ptr(U), M, N, ldg, ldu, float(act_mult), _qt(qt),
+                                     _ptr(Xq), _ptr(scale_x), _stream(G.device))
+    _check("qr_silu_mul_quant", st)
+    return Xq, scale_x
 
 
 def quantize_act_per_token(X, act_mult, qt, Xq=None, scale_x=None):

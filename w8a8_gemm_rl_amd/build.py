@@ -19,7 +19,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqurl_w8a8.so")
-SOURCES = ["quant_kernels.hip", "gemm_kernels.hip", "qr_api.hip"]
+SOURCES = ["quant_kernels.hip", "producer_kernels.hip", "gemm_kernels.hip", "qr_api.hip"]
+# Per-source flags: the fused producers fix the order of their fp32 roundings,
+# so no multiply-add may be contracted there.
+EXTRA = {"producer_kernels.hip": ["-ffp-contract=off"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CFLAGS = [
@@ -50,7 +53,7 @@ def build(verbose=True, jobs=None):
 
     def compile_one(i):
         src = os.path.join(CSRC, SOURCES[i])
-        return _run([HIPCC, *CFLAGS, "-c", src, "-o", objs[i]])
+        return _run([HIPCC, *CFLAGS, *EXTRA.get(SOURCES[i], []), "-c", src, "-o", objs[i]])
 
     jobs = jobs or min(len(SOURCES), 8)
     with ThreadPoolExecutor(max_workers=jobs) as ex:

@@ -282,6 +282,54 @@ int qr_quantize_act_per_token(const void* X, int64_t M, int64_t K, int64_t ldx, 
                     fn);
 }
 
+int qr_norm_quant(const void* H, int64_t M, int64_t K, int64_t ldh, int norm, const float* gamma,
+                  const float* beta, float eps, int qt, void* Xq, float* scale_x, void* stream) {
+  const char* fn = "qr_norm_quant";
+  int st = check_shape(fn, M, 0, K, qt);
+  if (st != QR_OK) return st;
+  if (norm != QR_NORM_RMS && norm != QR_NORM_LAYER)
+    return fail(QR_ERR_INVALID_ARG, "%s: unknown norm kind %d", fn, norm);
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(QR_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  if (ldh < K) return fail(QR_ERR_INVALID_ARG, "%s: ldh=%lld < K=%lld", fn, (long long)ldh, (long long)K);
+  if (K > 32768) return fail(QR_ERR_UNSUPPORTED, "%s: K=%lld > 32768", fn, (long long)K);
+  if (M > 0 && K > 0 && (!H || !Xq || !gamma))
+    return fail(QR_ERR_INVALID_ARG, "%s: null H, Xq or gamma", fn);
+  if (M > 0 && !scale_x) return fail(QR_ERR_INVALID_ARG, "%s: null scale_x", fn);
+  if (K > 0 && ldh % 8 != 0) return fail(QR_ERR_UNSUPPORTED, "%s: ldh must be a multiple of 8", fn);
+  if (!aligned(H, 16) || !aligned(Xq, 16) || !aligned(gamma, 16) || !aligned(beta, 16) ||
+      !aligned(scale_x, 4))
+    return fail(QR_ERR_UNSUPPORTED, "%s: misaligned pointer (16 bytes for H, Xq, gamma, beta)", fn);
+  if (M == 0) return ok();
+  (void)hipGetLastError();
+  return hip_status(qr::launch_norm_quant(H, M, K, ldh, norm, gamma, beta, eps, qt, Xq, scale_x,
+                                          static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int qr_silu_mul_quant(const void* G, const void* U, int64_t M, int64_t N, int64_t ldg, int64_t ldu,
+                      float act_mult, int qt, void* Xq, float* scale_x, void* stream) {
+  const char* fn = "qr_silu_mul_quant";
+  int st = check_shape(fn, M, 0, N, qt);
+  if (st != QR_OK) return st;
+  if (!std::isfinite(act_mult) || !(act_mult > 0.0f))
+    return fail(QR_ERR_INVALID_ARG, "%s: act_mult must be finite and > 0", fn);
+  if (ldg < N || ldu < N)
+    return fail(QR_ERR_INVALID_ARG, "%s: ldg=%lld / ldu=%lld < N=%lld", fn, (long long)ldg,
+                (long long)ldu, (long long)N);
+  if (N > 32768) return fail(QR_ERR_UNSUPPORTED, "%s: N=%lld > 32768", fn, (long long)N);
+  if (M > 0 && N > 0 && (!G || !U || !Xq)) return fail(QR_ERR_INVALID_ARG, "%s: null G, U or Xq", fn);
+  if (M > 0 && !scale_x) return fail(QR_ERR_INVALID_ARG, "%s: null scale_x", fn);
+  if (N > 0 && (ldg % 8 != 0 || ldu % 8 != 0))
+    return fail(QR_ERR_UNSUPPORTED, "%s: ldg and ldu must be multiples of 8", fn);
+  if (!aligned(G, 16) || !aligned(U, 16) || !aligned(Xq, 16) || !aligned(scale_x, 4))
+    return fail(QR_ERR_UNSUPPORTED, "%s: misaligned pointer (16 bytes for G, U, Xq)", fn);
+  if (M == 0) return ok();
+  (void)hipGetLastError();
+  return hip_status(qr::launch_silu_mul_quant(G, U, M, N, ldg, ldu, act_mult, qt, Xq, scale_x,
+                                              static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 namespace {
 
 int check_gemm_io(const char* fn, int64_t M, int64_t N, int64_t K, int out, bool need_sx,

@@ -12,6 +12,12 @@ hipError_t launch_act_quant(const void* X, int64_t M, int64_t K, int64_t ldx, fl
 hipError_t launch_weight_quant(const float* W, int64_t N, int64_t K, int64_t ldw, float s, int qt,
                                void* Wq, float* scale_w, float* Wsc, hipStream_t st);
 hipError_t launch_fold_norm(float* gamma, float* beta, int64_t K, float s, hipStream_t st);
+hipError_t launch_norm_quant(const void* H, int64_t M, int64_t K, int64_t ldh, int kind,
+                             const float* gamma, const float* beta, float eps, int qt, void* Xq,
+                             float* scale_x, hipStream_t st);
+hipError_t launch_silu_mul_quant(const void* G, const void* U, int64_t M, int64_t N, int64_t ldg,
+                                 int64_t ldu, float act_mult, int qt, void* Xq, float* scale_x,
+                                 hipStream_t st);
 hipError_t launch_requant(const float* Wp, int64_t N, int64_t K, int64_t ldw, int qt, void* Wq,
                           float* scale_w, uint32_t* row_flips, hipStream_t st);
 

@@ -252,9 +252,10 @@ __global__ __launch_bounds__(256) void fold_norm_kernel(float* gamma, float* bet
 
 inline unsigned grid_for(int64_t rows, int rpb) { return (unsigned)((rows + rpb - 1) / rpb); }
 
-// Rows per launch: a launch stays far inside the dispatch limits (2^20
-// blocks); longer row ranges are split into several launches on the host.
-constexpr int64_t kRowBlocks = int64_t(1) << 20;
+// Blocks per launch: at most 2^21 (2^31 work-items at 1024 threads, inside
+// the 32-bit dispatch grid); longer row ranges are split into several
+// launches on the host.
+constexpr int64_t kRowBlocks = int64_t(1) << 21;
 
 }  // namespace
 
