@@ -34,11 +34,18 @@ HBM_PEAK_GBS = 8000.0
 MFMA8_PEAK_TOPS = 5000.0  # dense INT8 / FP8 MFMA
 
 DOM_BATCH = 20  # dominant-GEMM launches per timing graph
+EPS = 1e-6  # RMSNorm epsilon of the producer workloads
 
 WORKLOADS = {
     "7b_decode_int8": dict(M=256, qt="int8", chain="7b", sets=4, kind="outliers"),
     "7b_decode_fp8": dict(M=256, qt="fp8", chain="7b", sets=4, kind="outliers"),
     "7b_decode_int8_gateup": dict(M=256, qt="int8", chain="7b_gateup", sets=4, kind="outliers"),
+    # with the producers of the linears' inputs (two RMSNorms, SiLU x up), fused
+    # into the quantizers or run as separate torch ops before them
+    "7b_decode_int8_fused": dict(M=256, qt="int8", chain="7b_producers", sets=4, kind="outliers",
+                                 fused=True),
+    "7b_decode_int8_unfused": dict(M=256, qt="int8", chain="7b_producers", sets=4,
+                                   kind="outliers", fused=False),
     "32b_decode_int8": dict(M=512, qt="int8", chain="32b", sets=2, kind="normal"),
     "32b_decode_fp8": dict(M=512, qt="fp8", chain="32b", sets=2, kind="normal"),
     "32b_prefill_int8": dict(M=4096, qt="int8", chain="32b_prefill", sets=2, kind="heavy"),
@@ -67,6 +74,8 @@ def chain_spec(name):
         return I.CHAIN_7B, I.LINEARS_7B, I.W_SIGMA_7B
     if name == "7b_gateup":
         return I.CHAIN_7B_GATEUP, I.LINEARS_7B, I.W_SIGMA_7B
+    if name == "7b_producers":
+        return I.CHAIN_7B_PRODUCERS, I.LINEARS_7B, I.W_SIGMA_7B
     if name == "32b":
         return I.CHAIN_32B, I.LINEARS_32B, I.W_SIGMA_32B
     if name == "32b_prefill":
@@ -79,30 +88,42 @@ def linear_bytes(M, N, K):
     return N * K + M * K + 4 * (M + N) + 2 * M * N
 
 
-def quant_bytes(M, K):
+def quant_bytes(M, K, prod=None):
+    """Algorithmic bytes of one input quantization: bf16 rows in, codes and
+    scales out; a fused norm also reads its gain, SiLU x up two inputs."""
+    if prod == "norm":
+        return 3 * M * K + 4 * M + 4 * K
+    if prod == "silu":
+        return 5 * M * K + 4 * M
     return 3 * M * K + 4 * M
 
 
 class Layer:
     """One set of quantized weights for the chain, plus the ops of one step."""
 
-    def __init__(self, chain, shapes, M, qt, sigma, seed, dev, x0, bufs, ws, s):
+    def __init__(self, chain, shapes, M, qt, sigma, seed, dev, x0, bufs, ws, s, fused=True):
         import torch
 
         from w8a8_gemm_rl_amd import binding as B
 
         self.B = B
         self.qt = qt
-        self.W = {}
+        self.W, self.gamma = {}, {}
         g = torch.Generator(device=dev)
         for i, L in enumerate(chain):
             N, K = shapes[L["name"]]
             g.manual_seed(seed + i)
             Wf = torch.randn((N, K), generator=g, device=dev, dtype=torch.float32) * sigma
-            self.W[L["name"]] = B.quantize_weights_uaq(Wf, s, qt)
+            gam = None
+            if L.get("prod") == "norm":
+                gam = 1.0 + 0.1 * torch.randn(K, generator=g, device=dev, dtype=torch.float32)
+            # UAQ: W' = W / s, and s folded into the producing norm's gain
+            self.W[L["name"]] = B.quantize_weights_uaq(Wf, s, qt, gamma=gam)
+            if gam is not None:
+                self.gamma[L["name"]] = (gam, gam.to(torch.bfloat16))
             del Wf
         self.x0, self.bufs, self.ws, self.s = x0, bufs, ws, s
-        self.chain, self.M = chain, M
+        self.chain, self.M, self.fused = chain, M, fused
 
     def ops(self):
         """The step as a list of (kind, name, thunk): per-token quantizations
@@ -110,16 +131,35 @@ class Layer:
         B, bufs = self.B, self.bufs
         out, done = [], {}
         for L in self.chain:
-            key = (L["src"], L["cols"])
+            key = (L["src"], L["cols"], L.get("prod"))
             if key not in done:
                 xq, sx = bufs["q_" + L["name"]]
                 done[key] = (xq, sx)
 
                 def q(L=L, xq=xq, sx=sx):
+                    import torch.nn.functional as Fn
+
                     src = self.x0 if L["src"] == "x0" else bufs["y_" + L["src"]]
                     if L["cols"] is not None:
                         src = src[:, L["cols"][0]:L["cols"][1]]
-                    B.quantize_act_per_token(src, self.s, self.qt, Xq=xq, scale_x=sx)
+                    prod = L.get("prod")
+                    if prod == "norm":
+                        g32, g16 = self.gamma[L["name"]]
+                        if self.fused:
+                            B.norm_quant(src, g32, self.qt, eps=EPS, Xq=xq, scale_x=sx)
+                        else:
+                            h = Fn.rms_norm(src, (src.shape[1],), g16, EPS)
+                            B.quantize_act_per_token(h, 1.0, self.qt, Xq=xq, scale_x=sx)
+                    elif prod == "silu":
+                        n = src.shape[1] // 2
+                        if self.fused:
+                            B.silu_mul_quant(src[:, :n], src[:, n:], self.s, self.qt, Xq=xq,
+                                             scale_x=sx)
+                        else:
+                            a = Fn.silu(src[:, :n]) * src[:, n:]
+                            B.quantize_act_per_token(a, self.s, self.qt, Xq=xq, scale_x=sx)
+                    else:
+                        B.quantize_act_per_token(src, self.s, self.qt, Xq=xq, scale_x=sx)
 
                 out.append(("quant", L["name"], q))
             xq, sx = done[key]
@@ -546,8 +586,8 @@ def main():
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
 
     log(f"bench: {args.workload} M={M} qt={qt}: building {wl['sets']} weight sets ...")
-    layers = [Layer(chain, shapes, M, qt, sigma, 1000 * (j + 1), dev, x0, bufs, ws, s)
-              for j in range(wl["sets"])]
+    layers = [Layer(chain, shapes, M, qt, sigma, 1000 * (j + 1), dev, x0, bufs, ws, s,
+                    fused=wl.get("fused", True)) for j in range(wl["sets"])]
     torch.cuda.synchronize()
 
     # ---- per-step algorithmic work
@@ -555,10 +595,10 @@ def main():
     ops_step = sum(2 * M * shapes[L["name"]][0] * shapes[L["name"]][1] for L in chain)
     quant_keys, qbytes = set(), 0
     for L in chain:
-        k = (L["src"], L["cols"])
+        k = (L["src"], L["cols"], L.get("prod"))
         if k not in quant_keys:
             quant_keys.add(k)
-            qbytes += quant_bytes(M, shapes[L["name"]][1])
+            qbytes += quant_bytes(M, shapes[L["name"]][1], L.get("prod"))
     bytes_step = sum(gemm_bytes.values()) + qbytes
     dom = max(chain, key=lambda L: (gemm_bytes[L["name"]], -chain.index(L)))["name"]
     Nd, Kd = shapes[dom]
@@ -675,7 +715,9 @@ def main():
     }
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if any(L.get("prod") for L in chain):
+        log("bench: no CPU baseline for chains with producers (the oracle chain has none)")
+    elif not args.no_cpu_baseline:
         dt, nsteps, threads = cpu_baseline(chain, shapes, M, qt, sigma, wl["kind"], s)
         cpu = {"value": round(bytes_step / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
                "kind": "oracle",
@@ -701,7 +743,11 @@ def main():
             "workload": f"{args.workload}: one decoder layer's W8A8 linears, M={M} tokens, "
                         + ", ".join(f"{L['name']} {shapes[L['name']][0]}x{shapes[L['name']][1]}"
                                     for L in chain)
-                        + f"; {len(quant_keys)} per-token quantizations + {len(chain)} GEMMs",
+                        + f"; {len(quant_keys)} per-token quantizations + {len(chain)} GEMMs"
+                        + ("" if not any(L.get("prod") for L in chain) else
+                           (", producers (RMSNorm x2, SiLU x up) "
+                            + ("fused into the quantizers" if wl.get("fused", True)
+                               else "as separate torch ops"))),
             "M": M, "qtype": qt, "uaq_s": s, "weight_sets": len(layers), "timing": mode,
             "parallelism": "none (1 GPU)",
         },

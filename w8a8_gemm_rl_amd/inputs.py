@@ -72,6 +72,16 @@ CHAIN_7B_GATEUP = [
     dict(name="gateup", src="o", cols=None),
     dict(name="down", src="gateup", cols=(18944, 37888)),
 ]
+# The same layer with the producers of the linears' inputs: the input norm
+# before QKV, the post-attention norm before gate+up (residual adds are not
+# modeled: it normalizes the O output), and SiLU(gate) x up before down.
+CHAIN_7B_PRODUCERS = [
+    dict(name="qkv", src="x0", cols=None, prod="norm"),
+    dict(name="o", src="qkv", cols=(0, 3584)),
+    dict(name="gateup", src="o", cols=None, prod="norm"),
+    dict(name="down", src="gateup", cols=None, prod="silu"),
+]
+NORM_EPS = 1e-6  # RMSNorm epsilon of the 7B/32B-shaped models
 CHAIN_32B = [
     dict(name="q", src="x0", cols=None),
     dict(name="k", src="x0", cols=None),
