@@ -183,8 +183,8 @@ class Layer:
 
 
 KERNEL_SOURCES = {
-    "gemm": ("gemm_kernels.hip", "qr_api.hip", "qr_internal.h", "qr_device.h"),
-    "refresh": ("quant_kernels.hip", "qr_api.hip", "qr_internal.h", "qr_device.h"),
+    "gemm": ("gemm_kernels.hip", "gemm_plan.hip", "qr_gemm.h", "qr_device.h"),
+    "refresh": ("quant_kernels.hip", "qr_device.h"),
 }
 
 

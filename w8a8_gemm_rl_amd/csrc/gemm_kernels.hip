@@ -35,7 +35,7 @@
 #include <type_traits>
 
 #include "qr_device.h"
-#include "qr_internal.h"
+#include "qr_gemm.h"
 
 namespace qr {
 namespace {

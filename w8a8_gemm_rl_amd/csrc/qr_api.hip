@@ -24,7 +24,6 @@ constexpr int64_t kMaxDim = (int64_t)1 << 31;
 // GEMM: 32-bit buffer offsets; 2^31 (minus at most 3 KB of copy bias) marks
 // out-of-range rows, so code matrices stay below 2^31 - 2^16 bytes.
 constexpr int64_t kMaxCodeBytes = ((int64_t)1 << 31) - ((int64_t)1 << 16);
-constexpr int kCUs = 256;  // MI355X compute units: the plan targets this chip
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
@@ -71,101 +70,6 @@ int check_shape(const char* fn, int64_t M, int64_t N, int64_t K, int qt) {
 
 }  // namespace
 
-namespace qr {
-
-GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int force_splitk,
-                   int force_rows) {
-  (void)qt;
-  GemmPlan p{};
-  // Tile by token count (indices into the tile table; choices measured on
-  // MI355X with graph-replayed launches). Up to 32 tokens the product is a
-  // weight stream: 8-wave LDS-DMA tiles of 128 weight rows. 256-token decode
-  // uses 192 x 128 tiles on wide layers (256 x 256 on very wide ones, such
-  // as stacked gate and up projections), 128 x 128 with split K on long-K
-  // ones and 128 x 64 / 128 x 32 tiles on narrow ones (more blocks); up to
-  // 1024 tokens 256 x 256 tiles on wide layers, 256 x 128 with split K on
-  // long-K ones, 128 x 128 on the others and split 128 x 32 tiles on very
-  // narrow ones; large token counts use 256 x 256 tiles, 256 x 128 below
-  // N = 7168.
-  const int64_t nks = (K + 127) / 128;
-  int tile;
-  if (force_tile >= 0) {
-    tile = force_tile;
-  } else if (M <= 32) {
-    tile = 0;
-  } else if (M <= 64) {
-    tile = 1;
-  } else if (M <= 128) {
-    tile = 2;
-  } else if (M <= 256) {
-    if (N >= 24576) tile = 5;
-    else if (N >= 8192) tile = 3;
-    else if (nks >= 64) tile = 2;
-    else tile = N >= 4096 ? 1 : 0;
-  } else if (M <= 1024) {
-    if (N >= 16384) tile = 5;
-    else if (N <= 2048) tile = 0;
-    else tile = nks >= 64 ? 4 : 2;
-  } else {
-    tile = N >= 7168 ? 5 : 4;
-  }
-  const TileDesc& d = tile_desc(tile);
-  p.tile = tile;
-  p.tiles_m = (M + d.BM - 1) / d.BM;
-  p.nks = (K + d.BK - 1) / d.BK;
-  const int64_t full = ((N + d.BN - 1) / d.BN) * p.tiles_m;  // blocks at full tile height
-  // Balance the grid over the CUs: first by shrinking the weight rows per
-  // tile (a multiple of 8, at least half the tile height) so that about one
-  // block per CU remains; where even full-height tiles leave CUs idle, split
-  // K (every split keeps four or more K steps, and the partial sums, 4 M N
-  // bytes per split, stay within the weight bytes) and then rebalance the
-  // rows.
-  // Only the weight-streaming tiles (64 tokens or fewer) shrink: tiles of
-  // more tokens are bound by their MFMA work, which does not shrink with the
-  // row count.
-  // With more full-height blocks than CUs the rows shrink to fill whole
-  // rounds of kCUs blocks instead of leaving a short last round.
-  auto balanced_rows = [&](int64_t splits) -> int64_t {
-    if (d.BM > 64) return d.BN;
-    const int64_t base = ((N + d.BN - 1) / d.BN) * p.tiles_m * splits;
-    const int64_t per = kCUs * ((base + kCUs - 1) / kCUs);  // blocks wanted
-    const int64_t want = 8 * ((N * p.tiles_m * splits + 8 * per - 1) / (8 * per));
-    return (want >= d.BN / 2 && want < d.BN) ? want : d.BN;
-  };
-  int64_t s = 1;
-  int64_t rows = d.BN;
-  if (force_tile >= 0) {
-    s = force_splitk > 0 ? force_splitk : 1;
-    rows = force_rows > 0 ? force_rows : d.BN;
-  } else if (full == 0) {
-    // M = 0 or N = 0: nothing to launch
-  } else if (full >= kCUs) {
-    rows = balanced_rows(1);
-  } else if (8 * ((N * p.tiles_m + 8 * kCUs - 1) / (8 * kCUs)) >= d.BN / 2) {
-    rows = balanced_rows(1);
-  } else {
-    // As many splits as keep the grid within one round of kCUs blocks (a
-    // second, partial round costs more than the split saves).
-    s = kCUs / full;
-    const int64_t by_bytes = K / (4 * (M > 0 ? M : 1));
-    const int64_t by_steps = p.nks / 4;
-    if (s > by_bytes) s = by_bytes;
-    if (s > by_steps) s = by_steps;
-    if (s > 4) s = 4;
-    if (s < 1) s = 1;
-    rows = balanced_rows(s);
-  }
-  if (p.nks > 0 && s > p.nks) s = p.nks;
-  if (s < 1) s = 1;
-  p.rows = (int)rows;
-  p.tiles_n = (N + p.rows - 1) / p.rows;
-  p.splitk = (int)s;
-  if (p.splitk > 1 && p.tiles_n * p.tiles_m > 0)
-    p.part_bytes = align256((size_t)p.splitk * (size_t)M * (size_t)N * 4);
-  return p;
-}
-
-}  // namespace qr
 
 extern "C" {
 
