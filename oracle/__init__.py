@@ -50,6 +50,7 @@ from .qurl import (
     norm_quant,
     silu_mul,
     silu_mul_quant,
+    acr_tis_loss,
     requantize_weights,
     flip_expectation,
     decode_chain,
@@ -61,6 +62,6 @@ __all__ = [
     "quantize_weights_uaq", "quantize_act_per_token", "acc_int8", "acc_fp8",
     "dequant_epilogue", "w8a8_linear", "flip_counts", "flip_expectation",
     "count_flips", "count_flips_rows",
-    "norm_folded", "norm_quant", "silu_mul", "silu_mul_quant", "requantize_weights",
+    "norm_folded", "norm_quant", "silu_mul", "silu_mul_quant", "acr_tis_loss", "requantize_weights",
     "decode_chain",
 ]

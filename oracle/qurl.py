@@ -408,3 +408,43 @@ def flip_expectation(W, sigma, qt):
     p = np.sqrt(2.0 / np.pi) * sd / h
     p[np.abs(W) == a] = 0.0
     return float(p.sum())
+
+
+# ----------------------------------------------------------------------------
+# Adaptive clipping range with truncated importance sampling (trainer side)
+# ----------------------------------------------------------------------------
+
+def acr_tis_loss(logp, logp_prox, logp_behav, adv, mask, eps, C):
+    """Per-token ACR objective (paper notes, "Method > Key designs > ACR") as a
+    loss, in float64.
+
+    Per token: R = pi / pi_prox = exp(logp - logp_prox) (the clipping ratio,
+    against the full-precision old actor), r = pi_prox / pi_behav =
+    exp(logp_prox - logp_behav) (full-precision against the quantized actor
+    that sampled the token; reading of the pages' r_{i,t}), w = min(r, C)
+    (the truncated importance weight), and
+        term = min(R A, clip(R, 1 - eps, (1 + eps) / r) A),
+        clip(x, lo, hi) = min(max(x, lo), hi)   (hi wins if hi < lo),
+        loss = -w term,  dloss/dlogp = -w A R where the first branch is the
+        minimum (R inside the clip range, or clipping would raise the term),
+        0 where the clipped branch is strictly smaller.
+    Masked tokens (mask == 0) give 0 and are not counted.
+    Returns (loss [n], grad [n], loss_sum, n_valid, n_clipped) where n_clipped
+    counts valid tokens whose gradient the clip removes.
+    """
+    lp = np.asarray(logp, np.float64)
+    lx = np.asarray(logp_prox, np.float64)
+    lb = np.asarray(logp_behav, np.float64)
+    A = np.asarray(adv, np.float64)
+    m = np.asarray(mask).astype(bool)
+    R = np.exp(lp - lx)
+    r = np.exp(lx - lb)
+    w = np.minimum(r, float(C))
+    lo, hi = 1.0 - float(eps), (1.0 + float(eps)) / r
+    Rc = np.minimum(np.maximum(R, lo), hi)
+    u, c = R * A, Rc * A
+    unclipped = u <= c
+    loss = np.where(m, -w * np.minimum(u, c), 0.0)
+    grad = np.where(m & unclipped, -w * u, 0.0)
+    return loss, grad, float(loss[m].sum()), int(m.sum()), int((m & ~unclipped).sum())
+

@@ -161,3 +161,28 @@ def matrix_seed(cfg_index, idx):
 
 def sha256(a):
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+# Trainer-side token batch for the ACR / TIS loss: n_seq responses of ragged
+# length (uniform in [1, max_len]) padded to max_len. Log-probabilities of the
+# sampled tokens under the full-precision old actor: -|N(0, 1.5^2)|; the
+# quantized actor that sampled them differs by N(0, 0.1^2) (KL between the two
+# grows from 0.002 to 0.025 over training on the paper-notes page, "Key designs
+# > ACR"); the current policy by N(0, 0.05^2). Advantages: one N(0, 1) value
+# per response (group-normalized, as GRPO/DAPO give them), repeated over its
+# tokens. Returns float32 arrays [n_seq * max_len] and a uint8 mask.
+ACR_EPS = 0.2  # clip epsilon (not on the pages: the common PPO value)
+ACR_C = 2.0  # truncation threshold C (the pages defer to FlashRL; not given)
+
+
+def acr_batch(n_seq, max_len, seed):
+    g = rng(seed)
+    n = n_seq * max_len
+    lens = g.integers(1, max_len + 1, size=n_seq)
+    mask = (np.arange(max_len)[None, :] < lens[:, None]).astype(np.uint8).reshape(n)
+    prox = (-np.abs(g.standard_normal(n)) * 1.5).astype(np.float32)
+    behav = (prox + g.standard_normal(n) * 0.1).astype(np.float32)
+    cur = (prox + g.standard_normal(n) * 0.05).astype(np.float32)
+    adv = np.repeat(g.standard_normal(n_seq), max_len).astype(np.float32)
+    return dict(logp=cur, logp_prox=prox, logp_behav=behav, adv=adv, mask=mask)
+
