@@ -62,6 +62,10 @@ REFRESH = {
 }
 REFRESH_METRIC = "per-RL-step weight refresh (requantize + flip count) GB/s vs HBM roofline"
 
+# Trainer-side ACR / TIS loss over one batch of response tokens.
+ACR = {"acr_tis_512x8192": dict(n_seq=512, max_len=8192)}
+ACR_METRIC = "ACR/TIS per-token loss + gradient GB/s vs HBM roofline"
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -183,6 +187,7 @@ class Layer:
 
 
 KERNEL_SOURCES = {
+    "acr": ("acr_kernels.hip",),
     "gemm": ("gemm_kernels.hip", "gemm_plan.hip", "qr_gemm.h", "qr_device.h"),
     "refresh": ("quant_kernels.hip", "qr_device.h"),
 }
@@ -221,6 +226,7 @@ def committed_traffic(key, kind="gemm"):
 
 
 KERNEL_PATTERNS = {
+    "acr": r"acr_tis_kernel",
     "gemm": r"gemm_\w*kernel",  # the main GEMM kernels (any tile family), not the split-K reduction
     "refresh": r"weight_quant_kernel<[^>]*true>",  # the weight quantizer with flip counting
 }
@@ -499,12 +505,102 @@ def run_refresh(args, dev):
     print(json.dumps(out), flush=True)
 
 
+def run_acr(args, dev):
+    """The ACR / TIS loss and gradient over one batch of response tokens
+    (one step = one pass over the batch), timed as a graph of launches."""
+    import numpy as np
+    import torch
+
+    from w8a8_gemm_rl_amd import binding as B
+    from w8a8_gemm_rl_amd import inputs as I
+
+    wl = ACR[args.workload]
+    b = I.acr_batch(wl["n_seq"], wl["max_len"], seed=11)
+    d = {k: torch.from_numpy(v).to(dev) for k, v in b.items()}
+    n = d["logp"].numel()
+    loss = torch.empty(n, dtype=torch.float32, device=dev)
+    grad = torch.empty(n, dtype=torch.float32, device=dev)
+    args_ = (d["logp"], d["logp_prox"], d["logp_behav"], d["adv"], d["mask"], I.ACR_EPS, I.ACR_C)
+
+    def step():
+        return B.acr_tis_loss(*args_, loss=loss, grad=grad)
+
+    step()
+    torch.cuda.synchronize()
+    batch = 20
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    gph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        step()
+        with torch.cuda.graph(gph, stream=st):
+            for _ in range(batch):
+                step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        gph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // batch)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        gph.replay()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / (reps * batch)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+    for a, e in evs:
+        a.record()
+        gph.replay()
+        e.record()
+    torch.cuda.synchronize()
+    k_us = 1000.0 * sum(a.elapsed_time(e) for a, e in evs) / (3 * batch)
+    per_tok = 4 * 4 + 1 + 2 * 4  # four fp32 inputs, the mask, loss and gradient out
+    alg = per_tok * n
+    _, _, sums = step()
+    sums = sums.cpu().numpy()
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+
+        m = 64 * wl["max_len"]
+        sl = {k: v[:m] for k, v in b.items()}
+        t1 = time.perf_counter()
+        k = 0
+        while time.perf_counter() - t1 < 10.0 and k < 30:
+            O.acr_tis_loss(sl["logp"], sl["logp_prox"], sl["logp_behav"], sl["adv"], sl["mask"],
+                           I.ACR_EPS, I.ACR_C)
+            k += 1
+        dt = (time.perf_counter() - t1) / k
+        cpu = {"value": round(per_tok * m / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"{k} passes of the numpy oracle over 64 of the 512 responses "
+                         f"({m} tokens), {dt:.3f} s each"}
+    out = {
+        "metric": ACR_METRIC, "value": round(alg / sec / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": reps * batch, "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {wl['n_seq']} responses x {wl['max_len']} "
+                               f"tokens (ragged lengths, {int(sums[1])} valid), eps {I.ACR_EPS}, "
+                               f"C {I.ACR_C}; loss, gradient and float64 sums",
+                   "timing": "hip_graph", "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(alg / (k_us * 1e-6) / 1e9, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(alg / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "acr_tis_kernel + acr_sum_kernel",
+                     "kernel_us": round(k_us, 2), "alg_bytes_per_launch": alg},
+        "cpu_baseline": cpu,
+        "mean_loss": float(sums[0] / max(sums[1], 1)), "clipped_frac": float(sums[2] / max(sums[1], 1)),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="7b_decode_int8", choices=sorted(WORKLOADS) + sorted(REFRESH))
+    ap.add_argument("--workload", default="7b_decode_int8",
+                    choices=sorted(WORKLOADS) + sorted(REFRESH) + sorted(ACR))
     ap.add_argument("--m", type=int, default=None, help="override the token count M")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
@@ -555,6 +651,9 @@ def main():
     B.lib()
     if args.workload in REFRESH:
         run_refresh(args, dev)
+        return
+    if args.workload in ACR:
+        run_acr(args, dev)
         return
 
     wl = dict(WORKLOADS[args.workload])

@@ -210,6 +210,37 @@ int qr_silu_mul_quant(const void* G, const void* U, int64_t M, int64_t N, int64_
                       float act_mult, int qt, void* Xq, float* scale_x, void* stream);
 
 /*
+ * qr_acr_tis_loss -- the trainer-side objective that goes with the quantized
+ * rollout: ACR's adaptive clipping range with truncated importance sampling
+ * [Notes/ACR], per token, as a loss, with its gradient and deterministic sums.
+ *
+ * For every token t (fp32 arithmetic):
+ *   R = exp(logp - logp_prox)         ratio to the full-precision old actor
+ *   r = exp(logp_prox - logp_behav)   full-precision over the quantized actor
+ *                                     that sampled the token
+ *   w = min(r, C);  lo = 1 - eps;  hi = (1 + eps) / r
+ *   term = min(R A, min(max(R, lo), hi) A)
+ *   loss[t] = -w term;  grad[t] = d loss[t] / d logp[t] = -w R A where the
+ *   unclipped branch is the minimum, else 0. Masked tokens: 0, not counted.
+ *   sums = {sum of loss over valid tokens, valid tokens, clipped valid tokens}
+ *   (float64, from per-block partials added in index order: the same bits on
+ *   every run). The mean loss is sums[0] / sums[1].
+ *
+ *   logp, logp_prox, logp_behav, adv  [n] fp32, 16-byte aligned (read).
+ *   mask     [n] uint8, nonzero = response token; 4-byte aligned (read).
+ *   eps      in [0, 1);  C  > 0 (may be +inf: no truncation).
+ *   loss     [n] fp32 (written);  grad  NULL or [n] fp32 (written).
+ *   sums     [3] float64 (written).
+ *   workspace  at least qr_workspace_size("qr_acr_tis_loss", n, 0, 0, 0)
+ *            bytes, 8-byte aligned; contents on entry irrelevant.
+ * n < 2^31. Errors as for the other entry points.
+ */
+int qr_acr_tis_loss(const float* logp, const float* logp_prox, const float* logp_behav,
+                    const float* adv, const uint8_t* mask, int64_t n, float eps, float C,
+                    float* loss, float* grad, double* sums, void* workspace, size_t ws_bytes,
+                    void* stream);
+
+/*
  * qr_w8a8_gemm -- quantized product and dequantization epilogue
  *   [Notes/System] (INT8/FP8 matmul), [Notes/Training].
  *
@@ -250,7 +281,8 @@ int qr_linear_fused(const void* X, int64_t ldx, float act_mult, const void* Wq, 
 
 /*
  * qr_workspace_size -- bytes of workspace needed by `fn` ("qr_w8a8_gemm" or
- * "qr_linear_fused") for this shape; 0 if none. Pure host function: it
+ * "qr_linear_fused") for this shape; 0 if none. For "qr_acr_tis_loss" M is
+ * the token count n (N, K and qt are ignored). Pure host function: it
  * depends only on its arguments (and on qr_set_plan_override). Returns
  * (size_t)-1 for an unknown fn or invalid sizes.
  */

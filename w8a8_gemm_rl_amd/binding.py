@@ -26,7 +26,7 @@ STATUS = {
 # Every function include/qurl_w8a8.h declares.
 EXPORTS = [
     "qr_quantize_weights_uaq", "qr_requantize_weights", "qr_quantize_act_per_token",
-    "qr_norm_quant", "qr_silu_mul_quant", "qr_w8a8_gemm", "qr_linear_fused",
+    "qr_norm_quant", "qr_silu_mul_quant", "qr_acr_tis_loss", "qr_w8a8_gemm", "qr_linear_fused",
     "qr_workspace_size", "qr_gemm_plan", "qr_tile_name", "qr_num_tiles", "qr_set_plan_override",
     "qr_last_error", "qr_version",
 ]
@@ -48,6 +48,8 @@ _SIGS = {
     "qr_quantize_act_per_token": (_int, [_vp, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp]),
     "qr_norm_quant": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _f32, _int, _vp, _vp, _vp]),
     "qr_silu_mul_quant": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp]),
+    "qr_acr_tis_loss": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _f32, _f32, _vp, _vp, _vp, _vp, _sz,
+                               _vp]),
     "qr_w8a8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _sz, _vp]),
     "qr_linear_fused": (_int, [_vp, _i64, _f32, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _sz, _vp]),
     "qr_workspace_size": (_sz, [ctypes.c_char_p, _i64, _i64, _i64, _int]),
@@ -262,6 +264,33 @@ def silu_mul_quant(G, U, act_mult, qt, Xq=None, scale_x=None):
                                      _ptr(Xq), _ptr(scale_x), _stream(G.device))
     _check("qr_silu_mul_quant", st)
     return Xq, scale_x
+
+
+def acr_tis_loss(logp, logp_prox, logp_behav, adv, mask, eps, C, loss=None, grad=None,
+                 with_grad=True):
+    """Per-token ACR / TIS loss on fp32 [n] tensors and a uint8 mask ->
+    (loss [n], grad [n] or None, sums float64 [3] = loss sum, valid, clipped)."""
+    ts = (logp, logp_prox, logp_behav, adv)
+    _need_cuda(*ts, mask, loss, grad)
+    n = logp.numel()
+    for t in ts:
+        if t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
+            raise ValueError("log-probabilities and advantages must be contiguous float32 of one size")
+    if mask.dtype != torch.uint8 or mask.numel() != n or not mask.is_contiguous():
+        raise ValueError("mask must be a contiguous uint8 tensor of the same size")
+    dev = logp.device
+    if loss is None:
+        loss = torch.empty(n, dtype=torch.float32, device=dev)
+    if grad is None and with_grad:
+        grad = torch.empty(n, dtype=torch.float32, device=dev)
+    sums = torch.empty(3, dtype=torch.float64, device=dev)
+    ws, ws_bytes = workspace(workspace_size("qr_acr_tis_loss", n, 0, 0, "int8"), dev)
+    with torch.cuda.device(dev):
+        st = lib().qr_acr_tis_loss(*(_ptr(t) for t in ts), _ptr(mask), n, float(eps), float(C),
+                                   _ptr(loss), _ptr(grad), _ptr(sums), _ptr(ws), ws_bytes,
+                                   _stream(dev))
+    _check("qr_acr_tis_loss", st)
+    return loss, grad, sums
 
 
 def quantize_act_per_token(X, act_mult, qt, Xq=None, scale_x=None):

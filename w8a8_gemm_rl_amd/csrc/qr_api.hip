@@ -112,6 +112,10 @@ int qr_gemm_plan(int64_t M, int64_t N, int64_t K, int qt, int* tile, int* splitk
 
 size_t qr_workspace_size(const char* fn, int64_t M, int64_t N, int64_t K, int qt) {
   if (!fn) return (size_t)-1;
+  if (std::strcmp(fn, "qr_acr_tis_loss") == 0) {
+    if (M < 0 || M >= kMaxDim) return (size_t)-1;
+    return align256((size_t)qr::acr_blocks(M) * 3 * sizeof(double));
+  }
   if (check_shape("qr_workspace_size", M, N, K, qt) != QR_OK) return (size_t)-1;
   const qr::GemmPlan p = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk, g_force_rows);
   const size_t gemm = (M == 0 || N == 0) ? 0 : p.ws_bytes();
@@ -231,6 +235,32 @@ int qr_silu_mul_quant(const void* G, const void* U, int64_t M, int64_t N, int64_
   (void)hipGetLastError();
   return hip_status(qr::launch_silu_mul_quant(G, U, M, N, ldg, ldu, act_mult, qt, Xq, scale_x,
                                               static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int qr_acr_tis_loss(const float* logp, const float* logp_prox, const float* logp_behav,
+                    const float* adv, const uint8_t* mask, int64_t n, float eps, float C,
+                    float* loss, float* grad, double* sums, void* workspace, size_t ws_bytes,
+                    void* stream) {
+  const char* fn = "qr_acr_tis_loss";
+  if (n < 0 || n >= kMaxDim) return fail(QR_ERR_INVALID_ARG, "%s: n=%lld out of range", fn, (long long)n);
+  if (!std::isfinite(eps) || eps < 0.0f || eps >= 1.0f)
+    return fail(QR_ERR_INVALID_ARG, "%s: eps must be in [0, 1)", fn);
+  if (std::isnan(C) || !(C > 0.0f)) return fail(QR_ERR_INVALID_ARG, "%s: C must be > 0", fn);
+  if (!sums) return fail(QR_ERR_INVALID_ARG, "%s: null sums", fn);
+  if (n > 0 && (!logp || !logp_prox || !logp_behav || !adv || !mask || !loss))
+    return fail(QR_ERR_INVALID_ARG, "%s: null input or loss", fn);
+  if (!aligned(logp, 16) || !aligned(logp_prox, 16) || !aligned(logp_behav, 16) ||
+      !aligned(adv, 16) || !aligned(loss, 16) || !aligned(grad, 16) || !aligned(mask, 4) ||
+      !aligned(sums, 8))
+    return fail(QR_ERR_UNSUPPORTED, "%s: misaligned pointer (16 bytes for the fp32 arrays, 4 for mask)", fn);
+  const size_t need = align256((size_t)qr::acr_blocks(n) * 3 * sizeof(double));
+  if (need > 0 && (!workspace || ws_bytes < need || !aligned(workspace, 8)))
+    return fail(QR_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, ws_bytes);
+  (void)hipGetLastError();
+  return hip_status(qr::launch_acr_tis(logp, logp_prox, logp_behav, adv, mask, n, eps, C, loss,
+                                       grad, sums, static_cast<double*>(workspace),
+                                       static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -20,6 +20,10 @@ hipError_t launch_norm_quant(const void* H, int64_t M, int64_t K, int64_t ldh, i
 hipError_t launch_silu_mul_quant(const void* G, const void* U, int64_t M, int64_t N, int64_t ldg,
                                  int64_t ldu, float act_mult, int qt, void* Xq, float* scale_x,
                                  hipStream_t st);
+int64_t acr_blocks(int64_t n);
+hipError_t launch_acr_tis(const float* logp, const float* lprox, const float* lbeh,
+                          const float* adv, const uint8_t* mask, int64_t n, float eps, float C,
+                          float* loss, float* grad, double* sums, double* part, hipStream_t st);
 hipError_t launch_requant(const float* Wp, int64_t N, int64_t K, int64_t ldw, int qt, void* Wq,
                           float* scale_w, uint32_t* row_flips, hipStream_t st);
 
