@@ -51,6 +51,10 @@ from .qurl import (
     silu_mul,
     silu_mul_quant,
     acr_tis_loss,
+    MX_BLOCK,
+    mx_exponent,
+    mx_quantize_rows,
+    mx_linear,
     requantize_weights,
     flip_expectation,
     decode_chain,
@@ -62,6 +66,7 @@ __all__ = [
     "quantize_weights_uaq", "quantize_act_per_token", "acc_int8", "acc_fp8",
     "dequant_epilogue", "w8a8_linear", "flip_counts", "flip_expectation",
     "count_flips", "count_flips_rows",
-    "norm_folded", "norm_quant", "silu_mul", "silu_mul_quant", "acr_tis_loss", "requantize_weights",
+    "norm_folded", "norm_quant", "silu_mul", "silu_mul_quant", "acr_tis_loss",
+    "MX_BLOCK", "mx_exponent", "mx_quantize_rows", "mx_linear", "requantize_weights",
     "decode_chain",
 ]

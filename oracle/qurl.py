@@ -448,3 +448,61 @@ def acr_tis_loss(logp, logp_prox, logp_behav, adv, mask, eps, C):
     grad = np.where(m & unclipped, -w * u, 0.0)
     return loss, grad, float(loss[m].sum()), int(m.sum()), int((m & ~unclipped).sum())
 
+
+# ----------------------------------------------------------------------------
+# Block-wise FP8 with power-of-two block scales (the block-wise variant the
+# pages cite, in the form CDNA4's matrix cores scale natively)
+# ----------------------------------------------------------------------------
+
+MX_BLOCK = 32
+
+
+def mx_exponent(amax):
+    """Smallest integer X with amax <= 448 * 2^X (so no element of the block
+    saturates), clamped to [-127, 127]; amax = 0 gives -127. Exact: with
+    amax = f 2^e, f in [0.5, 1) and 448 = 0.875 2^9, X = e - 9 if f <= 0.875
+    else e - 8."""
+    a = np.asarray(amax, np.float64)
+    f, e = np.frexp(a)
+    X = np.where(f <= 0.875, e - 9, e - 8)
+    X = np.where(a == 0, -127, X)
+    return np.clip(X, -127, 127).astype(np.int16)
+
+
+def mx_quantize_rows(A, block=MX_BLOCK):
+    """Block-wise FP8: every `block` consecutive elements of a row share one
+    power-of-two scale 2^X (X = mx_exponent of the block's absmax; E8M0 byte
+    X + 127), and each element is the E4M3FN code of fl32(v * 2^-X) (the
+    scaling is exact for normal results), nearest with ties to even. Reading:
+    the pages cite block-wise FP8 without a block size or scale format; the
+    block of 32 and the power-of-two scale are those of the gfx950 scaled MFMA.
+    Returns (codes uint8 [R, K], X int16 [R, K / block])."""
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    R, K = A.shape
+    if K % block:
+        raise ValueError("K must be a multiple of the block")
+    Ab = A.reshape(R, K // block, block).astype(np.float64)
+    X = mx_exponent(np.abs(Ab).max(axis=2) if K else np.zeros((R, 0)))
+    v = np.ldexp(Ab, -X[:, :, None].astype(np.int64)).astype(np.float32)
+    v = np.clip(v, -E4M3FN_MAX, E4M3FN_MAX)
+    codes = e4m3fn_encode(v.reshape(R, K))
+    return codes, X
+
+
+def mx_linear(Xc, Xe, Wc, We, block=MX_BLOCK):
+    """acc[m, n] = sum_b 2^(Xe[m, b] + We[n, b]) sum_{k in b} x_k w_k with the
+    decoded E4M3FN values; every block partial is exact in float64 (products
+    are multiples of 2^-18 below 2^17.61, 32 of them), scaled exactly, and the
+    blocks are added in float64. Y = bf16_rne(fl32(acc)).
+    Returns (acc float64 [M, N], Y bf16 bits)."""
+    x = e4m3fn_decode(Xc)
+    w = e4m3fn_decode(Wc)
+    M, K = x.shape
+    N = w.shape[0]
+    nb = K // block
+    acc = np.zeros((M, N), np.float64)
+    for b in range(nb):
+        part = x[:, b * block:(b + 1) * block] @ w[:, b * block:(b + 1) * block].T
+        acc += np.ldexp(part, (Xe[:, b:b + 1].astype(np.int64) + We[None, :, b].astype(np.int64)))
+    return acc, f32_to_bf16_bits(acc.astype(np.float32))
+
