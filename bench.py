@@ -62,6 +62,10 @@ REFRESH = {
 }
 REFRESH_METRIC = "per-RL-step weight refresh (requantize + flip count) GB/s vs HBM roofline"
 
+# Block-wise FP8 (power-of-two scales per 32 elements): the 7B gate projection.
+MX = {"mx_7b_gate_m256": dict(M=256, N=18944, K=3584), "mx_7b_gate_m32": dict(M=32, N=18944, K=3584)}
+MX_METRIC = "block-wise FP8 GEMM (E8M0 per-32 scales) GB/s / TOPS vs roofline"
+
 # Trainer-side ACR / TIS loss over one batch of response tokens.
 ACR = {"acr_tis_512x8192": dict(n_seq=512, max_len=8192)}
 ACR_METRIC = "ACR/TIS per-token loss + gradient GB/s vs HBM roofline"
@@ -187,6 +191,7 @@ class Layer:
 
 
 KERNEL_SOURCES = {
+    "mx": ("mx_kernels.hip", "qr_device.h"),
     "acr": ("acr_kernels.hip",),
     "gemm": ("gemm_kernels.hip", "gemm_plan.hip", "qr_gemm.h", "qr_device.h"),
     "refresh": ("quant_kernels.hip", "qr_device.h"),
@@ -226,6 +231,7 @@ def committed_traffic(key, kind="gemm"):
 
 
 KERNEL_PATTERNS = {
+    "mx": r"mx_gemm_kernel",
     "acr": r"acr_tis_kernel",
     "gemm": r"gemm_\w*kernel",  # the main GEMM kernels (any tile family), not the split-K reduction
     "refresh": r"weight_quant_kernel<[^>]*true>",  # the weight quantizer with flip counting
@@ -505,6 +511,75 @@ def run_refresh(args, dev):
     print(json.dumps(out), flush=True)
 
 
+def run_mx(args, dev):
+    """One block-wise FP8 GEMM (activation quantization excluded), timed as a
+    graph of launches walking four weight copies, beside the per-channel FP8
+    GEMM of the same shape."""
+    import torch
+
+    from w8a8_gemm_rl_amd import binding as B
+
+    wl = MX[args.workload]
+    M, N, K = wl["M"], wl["N"], wl["K"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    X = (torch.randn((M, K), generator=g, device=dev)).to(torch.bfloat16)
+    xq, xs = B.mx_quantize(X)
+    sets = []
+    for j in range(4):
+        W = torch.randn((N, K), generator=g, device=dev) * 0.02
+        sets.append(B.mx_quantize(W) + B.quantize_weights_uaq(W, 1.5, "fp8"))
+        del W
+    pxq, psx = B.quantize_act_per_token(X, 1.5, "fp8")
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws, _ = B.workspace(B.workspace_size("qr_w8a8_gemm", M, N, K, "fp8"), dev)
+
+    def timed(fn, batch=20):
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(st):
+            fn(0)
+            with torch.cuda.graph(gph, stream=st):
+                for i in range(batch):
+                    fn(i)
+        torch.cuda.synchronize()
+        gph.replay()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, e in evs:
+            a.record()
+            gph.replay()
+            e.record()
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(e) * 1000.0 / batch for a, e in evs)[2]
+
+    mx_us = timed(lambda i: B.mx_gemm(xq, xs, sets[i % 4][0], sets[i % 4][1], Y=Y))
+    pc_us = timed(lambda i: B.w8a8_gemm(pxq, psx, sets[i % 4][2], sets[i % 4][3], "fp8", Y=Y, ws=ws))
+    alg = N * K + M * K + (N + M) * (K // 32) + 2 * M * N
+    ops = 2 * M * N * K
+    bound = "hbm" if ops / alg < MFMA8_PEAK_TOPS / HBM_PEAK_GBS * 1000 else "mfma"
+    achieved = alg / (mx_us * 1e-6) / 1e9 if bound == "hbm" else ops / (mx_us * 1e-6) / 1e12
+    peak = HBM_PEAK_GBS if bound == "hbm" else MFMA8_PEAK_TOPS
+    out = {
+        "metric": MX_METRIC, "value": round(alg / (mx_us * 1e-6) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": 100, "warmup": 1, "ms_per_step": round(mx_us / 1000, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3/e8m0",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: Y[{M}, {N}] = X[{M}, {K}] W^T, E4M3FN with one "
+                               f"E8M0 scale per 32 elements on both operands",
+                   "timing": "hip_graph", "parallelism": "none (1 GPU)"},
+        "tops": round(ops / (mx_us * 1e-6) / 1e12, 1),
+        "per_channel_fp8_us": round(pc_us, 2),
+        "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
+                     "unit": "GB/s" if bound == "hbm" else "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": None, "kernel": "mx_gemm_kernel", "kernel_us": round(mx_us, 2),
+                     "alg_bytes_per_launch": alg, "alg_ops_per_launch": ops},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def run_acr(args, dev):
     """The ACR / TIS loss and gradient over one batch of response tokens
     (one step = one pass over the batch), timed as a graph of launches."""
@@ -600,7 +675,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="7b_decode_int8",
-                    choices=sorted(WORKLOADS) + sorted(REFRESH) + sorted(ACR))
+                    choices=sorted(WORKLOADS) + sorted(REFRESH) + sorted(ACR) + sorted(MX))
     ap.add_argument("--m", type=int, default=None, help="override the token count M")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
@@ -654,6 +729,9 @@ def main():
         return
     if args.workload in ACR:
         run_acr(args, dev)
+        return
+    if args.workload in MX:
+        run_mx(args, dev)
         return
 
     wl = dict(WORKLOADS[args.workload])

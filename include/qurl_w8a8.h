@@ -241,6 +241,42 @@ int qr_acr_tis_loss(const float* logp, const float* logp_prox, const float* logp
                     void* stream);
 
 /*
+ * qr_mx_quantize -- block-wise FP8: every 32 consecutive elements of a row
+ * share one power-of-two scale (the block-wise FP8 variant the pages cite,
+ * [fugumt] "Related papers"; block of 32 with E8M0 scales as the gfx950
+ * scaled MFMA applies them).
+ *
+ * For every row r and block b of A (values v widened exactly to fp32):
+ *   X = the smallest integer with max |v| <= 448 * 2^X (clamped to
+ *       [-127, 127]; an all-zero block gives -127);  scales[r, b] = X + 127;
+ *   codes[r, 32 b + i] = E4M3FN(min(max(fl32(v_i * 2^-X), -448), 448)),
+ *       nearest, ties to even, sign kept on zero.
+ *
+ *   A        [R, lda] fp32 (src_bf16 = 0) or bf16 bit patterns (src_bf16 = 1).
+ *   K        multiple of 32.
+ *   codes    [R, K] E4M3FN bytes (written); scales [R, K/32] E8M0 bytes (written).
+ * Errors as for qr_quantize_act_per_token.
+ */
+int qr_mx_quantize(const void* A, int64_t R, int64_t K, int64_t lda, int src_bf16, void* codes,
+                   uint8_t* scales, void* stream);
+
+/*
+ * qr_mx_gemm -- product of block-wise FP8 operands:
+ *   acc[m,n] = sum_b 2^(Xx[m,b] + Xw[n,b]) sum_{k in block b} x[m,k] w[n,k]
+ *   (the gfx950 scaled MFMA applies the block scales; products within a
+ *   group of k are added at the FP8 MFMA's reduced precision, groups in
+ *   fp32, as for qr_w8a8_gemm's FP8 path).
+ *   out = QR_OUT_BF16: Y[m,n] = bf16_rne(acc);  QR_OUT_RAW: Y = acc (fp32).
+ *
+ *   Xq, sx   [M, K] codes and [M, K/32] E8M0 scales of the tokens.
+ *   Wq, sw   [N, K] codes and [N, K/32] E8M0 scales of the weights.
+ *   K        multiple of 128; code matrices below 2^31 - 2^16 bytes.
+ *   Y        [M, ldy] bf16 or fp32 (written).
+ */
+int qr_mx_gemm(const void* Xq, const uint8_t* sx, const void* Wq, const uint8_t* sw, int64_t M,
+               int64_t N, int64_t K, int out, void* Y, int64_t ldy, void* stream);
+
+/*
  * qr_w8a8_gemm -- quantized product and dequantization epilogue
  *   [Notes/System] (INT8/FP8 matmul), [Notes/Training].
  *

@@ -26,7 +26,8 @@ STATUS = {
 # Every function include/qurl_w8a8.h declares.
 EXPORTS = [
     "qr_quantize_weights_uaq", "qr_requantize_weights", "qr_quantize_act_per_token",
-    "qr_norm_quant", "qr_silu_mul_quant", "qr_acr_tis_loss", "qr_w8a8_gemm", "qr_linear_fused",
+    "qr_norm_quant", "qr_silu_mul_quant", "qr_acr_tis_loss", "qr_mx_quantize", "qr_mx_gemm",
+    "qr_w8a8_gemm", "qr_linear_fused",
     "qr_workspace_size", "qr_gemm_plan", "qr_tile_name", "qr_num_tiles", "qr_set_plan_override",
     "qr_last_error", "qr_version",
 ]
@@ -50,6 +51,8 @@ _SIGS = {
     "qr_silu_mul_quant": (_int, [_vp, _vp, _i64, _i64, _i64, _i64, _f32, _int, _vp, _vp, _vp]),
     "qr_acr_tis_loss": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _f32, _f32, _vp, _vp, _vp, _vp, _sz,
                                _vp]),
+    "qr_mx_quantize": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp]),
+    "qr_mx_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _vp]),
     "qr_w8a8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _sz, _vp]),
     "qr_linear_fused": (_int, [_vp, _i64, _f32, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _sz, _vp]),
     "qr_workspace_size": (_sz, [ctypes.c_char_p, _i64, _i64, _i64, _int]),
@@ -291,6 +294,45 @@ def acr_tis_loss(logp, logp_prox, logp_behav, adv, mask, eps, C, loss=None, grad
                                    _stream(dev))
     _check("qr_acr_tis_loss", st)
     return loss, grad, sums
+
+
+def mx_quantize(A, codes=None, scales=None):
+    """Block-wise FP8 of fp32 or bf16 rows A [R, K] -> (codes [R, K] fp8, E8M0 scales uint8 [R, K/32])."""
+    _need_cuda(A, codes, scales)
+    if A.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("A must be float32 or bfloat16")
+    R, K = A.shape
+    lda = _rows(A, "A")
+    if codes is None:
+        codes = torch.empty((R, K), dtype=torch.float8_e4m3fn, device=A.device)
+    if scales is None:
+        scales = torch.empty((R, K // 32), dtype=torch.uint8, device=A.device)
+    with torch.cuda.device(A.device):
+        st = lib().qr_mx_quantize(_ptr(A), R, K, lda, int(A.dtype == torch.bfloat16), _ptr(codes),
+                                  _ptr(scales), _stream(A.device))
+    _check("qr_mx_quantize", st)
+    return codes, scales
+
+
+def mx_gemm(Xq, sx, Wq, sw, out="bf16", Y=None):
+    """Block-wise FP8 product: Y [M, N] = bf16(acc) or the fp32 accumulators."""
+    _need_cuda(Xq, sx, Wq, sw, Y)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K or sx.shape != (M, K // 32) or sw.shape != (N, K // 32):
+        raise ValueError("operand shapes do not match")
+    for t in (Xq, sx, Wq, sw):
+        if not t.is_contiguous():
+            raise ValueError("operands must be contiguous")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16 if out == "bf16" else torch.float32,
+                        device=Xq.device)
+    ldy = _rows(Y, "Y")
+    with torch.cuda.device(Xq.device):
+        st = lib().qr_mx_gemm(_ptr(Xq), _ptr(sx), _ptr(Wq), _ptr(sw), M, N, K, OUT[out], _ptr(Y),
+                              ldy, _stream(Xq.device))
+    _check("qr_mx_gemm", st)
+    return Y
 
 
 def quantize_act_per_token(X, act_mult, qt, Xq=None, scale_x=None):

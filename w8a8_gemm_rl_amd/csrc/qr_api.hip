@@ -264,6 +264,43 @@ int qr_acr_tis_loss(const float* logp, const float* logp_prox, const float* logp
                     fn);
 }
 
+int qr_mx_quantize(const void* A, int64_t R, int64_t K, int64_t lda, int src_bf16, void* codes,
+                   uint8_t* scales, void* stream) {
+  const char* fn = "qr_mx_quantize";
+  if (R < 0 || K < 0 || R >= kMaxDim || K >= kMaxDim)
+    return fail(QR_ERR_INVALID_ARG, "%s: bad size (R=%lld K=%lld)", fn, (long long)R, (long long)K);
+  if (K % 32 != 0) return fail(QR_ERR_UNSUPPORTED, "%s: K=%lld is not a multiple of 32", fn, (long long)K);
+  if (src_bf16 != 0 && src_bf16 != 1) return fail(QR_ERR_INVALID_ARG, "%s: src_bf16 must be 0 or 1", fn);
+  if (lda < K) return fail(QR_ERR_INVALID_ARG, "%s: lda=%lld < K=%lld", fn, (long long)lda, (long long)K);
+  if (R > 0 && K > 0 && (!A || !codes || !scales)) return fail(QR_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (K > 0 && lda % (src_bf16 ? 8 : 4) != 0)
+    return fail(QR_ERR_UNSUPPORTED, "%s: rows must start on 16-byte boundaries", fn);
+  if (!aligned(A, 16) || !aligned(codes, 16))
+    return fail(QR_ERR_UNSUPPORTED, "%s: misaligned pointer (16 bytes for A, codes)", fn);
+  (void)hipGetLastError();
+  return hip_status(qr::launch_mx_quant(A, R, K, lda, src_bf16, codes, scales,
+                                        static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int qr_mx_gemm(const void* Xq, const uint8_t* sx, const void* Wq, const uint8_t* sw, int64_t M,
+               int64_t N, int64_t K, int out, void* Y, int64_t ldy, void* stream) {
+  const char* fn = "qr_mx_gemm";
+  if (M < 0 || N < 0 || K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return fail(QR_ERR_INVALID_ARG, "%s: bad size", fn);
+  if (K % 128 != 0) return fail(QR_ERR_UNSUPPORTED, "%s: K=%lld is not a multiple of 128", fn, (long long)K);
+  if (out != QR_OUT_BF16 && out != QR_OUT_RAW) return fail(QR_ERR_INVALID_ARG, "%s: bad out", fn);
+  if (N * K >= kMaxCodeBytes || M * K >= kMaxCodeBytes)
+    return fail(QR_ERR_UNSUPPORTED, "%s: code matrices must stay below 2^31 - 2^16 bytes", fn);
+  if (ldy < N) return fail(QR_ERR_INVALID_ARG, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
+  if (M > 0 && N > 0 && (!Y || (K > 0 && (!Xq || !sx || !Wq || !sw))))
+    return fail(QR_ERR_INVALID_ARG, "%s: null pointer", fn);
+  (void)hipGetLastError();
+  return hip_status(qr::launch_mx_gemm(Xq, sx, Wq, sw, M, N, K, out == QR_OUT_RAW, Y, ldy,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 namespace {
 
 int check_gemm_io(const char* fn, int64_t M, int64_t N, int64_t K, int out, bool need_sx,

@@ -20,6 +20,11 @@ hipError_t launch_norm_quant(const void* H, int64_t M, int64_t K, int64_t ldh, i
 hipError_t launch_silu_mul_quant(const void* G, const void* U, int64_t M, int64_t N, int64_t ldg,
                                  int64_t ldu, float act_mult, int qt, void* Xq, float* scale_x,
                                  hipStream_t st);
+hipError_t launch_mx_quant(const void* A, int64_t R, int64_t K, int64_t lda, int bf16,
+                           void* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_mx_gemm(const void* Xq, const uint8_t* sx, const void* Wq, const uint8_t* sw,
+                          int64_t M, int64_t N, int64_t K, int out_raw, void* Y, int64_t ldy,
+                          hipStream_t st);
 int64_t acr_blocks(int64_t n);
 hipError_t launch_acr_tis(const float* logp, const float* lprox, const float* lbeh,
                           const float* adv, const uint8_t* mask, int64_t n, float eps, float C,
