@@ -242,7 +242,7 @@ def test_gemm_auto_plan(qt, M, N, K):
     _check_gemm(xq, sx, wq, sw, qt, f"{qt} M={M} N={N} K={K} plan={B.gemm_plan(M, N, K, qt)}")
 
 
-NUM_TILES = 14  # entries of the library's tile table
+NUM_TILES = 16  # entries of the library's tile table
 
 
 @pytest.mark.parametrize("qt", QTS)
@@ -258,6 +258,31 @@ def test_gemm_every_tile_and_split(qt, tile, splitk, M, N, K):
     xq, sx, wq, sw = _codes_pair(M, N, K, qt, seed=tile * 10 + splitk + M)
     B.set_plan_override(tile, splitk)
     _check_gemm(xq, sx, wq, sw, qt, f"{qt} tile={tile} splitk={splitk} M={M} N={N} K={K}")
+
+
+def _tile_height(tile):
+    # tile names carry the macro tile as "_n<BN>_m<BM>"
+    name = B.tile_name(tile)
+    return int(name.split("_n")[1].split("_")[0])
+
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("tile", range(NUM_TILES))
+@pytest.mark.parametrize("splitk", [1, 3])
+@pytest.mark.parametrize("shrink", ["min", "one_block_less", "half"])
+def test_gemm_partial_row_tiles(qt, tile, splitk, shrink):
+    # Tiles that own fewer weight rows than their height: the copies of row
+    # blocks past the owned rows are not issued (their LDS rows hold stale
+    # bytes), so every stored output must still come from owned rows only.
+    # 8 rows per tile; one 8-row block less than the height; about half the
+    # height. N = 300 ends the last tile inside a row block; M and K are
+    # ragged too (a 16-byte last K step).
+    M, N, K = 70, 300, 1040
+    bn = _tile_height(tile)
+    rows = {"min": 8, "one_block_less": max(8, bn - 8), "half": max(8, (bn // 2 + 4) // 8 * 8)}[shrink]
+    xq, sx, wq, sw = _codes_pair(M, N, K, qt, seed=tile * 7 + splitk + rows)
+    B.set_plan_override(tile, splitk, rows)
+    _check_gemm(xq, sx, wq, sw, qt, f"{qt} tile={tile} splitk={splitk} rows={rows} M={M} N={N} K={K}")
 
 
 def _tile_height(tile):

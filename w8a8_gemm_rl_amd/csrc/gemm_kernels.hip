@@ -745,7 +745,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
   X(0, 4, 16, 128, 32, 8, 1)  /*  0: M <= 32, weight streaming        */ \
   X(0, 4, 32, 128, 64, 4, 2)  /*  1: M <= 64; narrow 256-token layers */ \
   X(0, 4, 32, 128, 128, 2, 4) /*  2: M <= 128; long-K 256-token ones  */ \
-  X(0, 3, 32, 192, 128, 2, 2) /*  3: wide 256-token layers            */ \
+  X(0, 3, 32, 192, 128, 2, 2) /*  3: 4-wave version of tile 14        */ \
   X(0, 3, 32, 256, 128, 4, 2) /*  4: long-K / narrow large-M layers   */ \
   X(0, 2, 32, 256, 256, 2, 4) /*  5: wide large-M layers              */ \
   X(0, 3, 32, 128, 256, 2, 4) /*  6: 256-token alternative            */ \
@@ -755,7 +755,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
   X(1, 3, 32, 192, 128, 2, 2) /* 10: interleaved variant of tile 3    */ \
   X(1, 4, 16, 128, 32, 8, 1)  /* 11: interleaved variant of tile 0    */ \
   X(2, 4, 16, 128, 16, 8, 1)  /* 12: direct, M <= 16                  */ \
-  X(2, 2, 16, 128, 32, 4, 1)  /* 13: direct, M <= 32                  */
+  X(2, 2, 16, 128, 32, 4, 1)  /* 13: direct, M <= 32                  */ \
+  X(0, 4, 32, 192, 128, 2, 4) /* 14: wide 256-token layers, 8 waves   */ \
+  X(1, 4, 32, 192, 128, 2, 4) /* 15: interleaved variant of tile 14   */
 
 #define QR_STR(x) #x
 #define QR_DESC(KIND, S, T, BN, BM, WN, WM)                                        \
