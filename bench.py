@@ -231,7 +231,7 @@ def committed_traffic(key, kind="gemm"):
 
 
 KERNEL_PATTERNS = {
-    "mx": r"mx_gemm_kernel",
+    "mx": r"mx_dma_kernel",
     "acr": r"acr_tis_kernel",
     "gemm": r"gemm_\w*kernel",  # the main GEMM kernels (any tile family), not the split-K reduction
     "refresh": r"weight_quant_kernel<[^>]*true>",  # the weight quantizer with flip counting
@@ -573,7 +573,7 @@ def run_mx(args, dev):
         "per_channel_fp8_us": round(pc_us, 2),
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": "GB/s" if bound == "hbm" else "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None, "kernel": "mx_gemm_kernel", "kernel_us": round(mx_us, 2),
+                     "traffic": None, "kernel": "mx_dma_kernel", "kernel_us": round(mx_us, 2),
                      "alg_bytes_per_launch": alg, "alg_ops_per_launch": ops},
         "cpu_baseline": None,
     }

@@ -254,7 +254,13 @@ int qr_acr_tis_loss(const float* logp, const float* logp_prox, const float* logp
  *
  *   A        [R, lda] fp32 (src_bf16 = 0) or bf16 bit patterns (src_bf16 = 1).
  *   K        multiple of 32.
- *   codes    [R, K] E4M3FN bytes (written); scales [R, K/32] E8M0 bytes (written).
+ *   codes    [R, K] E4M3FN bytes (written).
+ *   scales   E8M0 bytes in panels of 128 elements of K, [ceil(K/128)][R][4]:
+ *            the byte of block b of row r is at ((b / 4) R + r) 4 + b % 4
+ *            (written; the unused bytes of a partial last panel are left as
+ *            they are). A row's four bytes for one 128-element K step are
+ *            adjacent and a run of rows' bytes for that step is contiguous,
+ *            which is what the GEMM copies per step.
  * Errors as for qr_quantize_act_per_token.
  */
 int qr_mx_quantize(const void* A, int64_t R, int64_t K, int64_t lda, int src_bf16, void* codes,
@@ -268,8 +274,9 @@ int qr_mx_quantize(const void* A, int64_t R, int64_t K, int64_t lda, int src_bf1
  *   fp32, as for qr_w8a8_gemm's FP8 path).
  *   out = QR_OUT_BF16: Y[m,n] = bf16_rne(acc);  QR_OUT_RAW: Y = acc (fp32).
  *
- *   Xq, sx   [M, K] codes and [M, K/32] E8M0 scales of the tokens.
- *   Wq, sw   [N, K] codes and [N, K/32] E8M0 scales of the weights.
+ *   Xq, sx   [M, K] codes and the tokens' E8M0 scales ([K/128][M][4] panels,
+ *            as qr_mx_quantize writes them).
+ *   Wq, sw   [N, K] codes and the weights' E8M0 scales ([K/128][N][4]).
  *   K        multiple of 128; code matrices below 2^31 - 2^16 bytes.
  *   Y        [M, ldy] bf16 or fp32 (written).
  */

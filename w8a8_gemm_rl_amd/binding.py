@@ -297,7 +297,8 @@ def acr_tis_loss(logp, logp_prox, logp_behav, adv, mask, eps, C, loss=None, grad
 
 
 def mx_quantize(A, codes=None, scales=None):
-    """Block-wise FP8 of fp32 or bf16 rows A [R, K] -> (codes [R, K] fp8, E8M0 scales uint8 [R, K/32])."""
+    """Block-wise FP8 of fp32 or bf16 rows A [R, K] -> (codes [R, K] fp8, E8M0 scales uint8
+    [ceil(K/128), R, 4]: scales[p, r, j] belongs to 32-element block 4 p + j of row r)."""
     _need_cuda(A, codes, scales)
     if A.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("A must be float32 or bfloat16")
@@ -306,7 +307,7 @@ def mx_quantize(A, codes=None, scales=None):
     if codes is None:
         codes = torch.empty((R, K), dtype=torch.float8_e4m3fn, device=A.device)
     if scales is None:
-        scales = torch.empty((R, K // 32), dtype=torch.uint8, device=A.device)
+        scales = torch.empty(((K + 127) // 128, R, 4), dtype=torch.uint8, device=A.device)
     with torch.cuda.device(A.device):
         st = lib().qr_mx_quantize(_ptr(A), R, K, lda, int(A.dtype == torch.bfloat16), _ptr(codes),
                                   _ptr(scales), _stream(A.device))
@@ -319,7 +320,8 @@ def mx_gemm(Xq, sx, Wq, sw, out="bf16", Y=None):
     _need_cuda(Xq, sx, Wq, sw, Y)
     M, K = Xq.shape
     N = Wq.shape[0]
-    if Wq.shape[1] != K or sx.shape != (M, K // 32) or sw.shape != (N, K // 32):
+    P = (K + 127) // 128
+    if Wq.shape[1] != K or sx.shape != (P, M, 4) or sw.shape != (P, N, 4):
         raise ValueError("operand shapes do not match")
     for t in (Xq, sx, Wq, sw):
         if not t.is_contiguous():

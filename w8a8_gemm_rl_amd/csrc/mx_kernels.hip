@@ -7,11 +7,16 @@
 //
 //   mx_quant_kernel  one thread per 32-element block: absmax, exponent X (the
 //                    smallest with absmax <= 448 * 2^X), the E8M0 byte X + 127,
-//                    and the codes of fl32(v * 2^-X).
-//   mx_gemm_kernel   weights on the MFMA A operand, tokens on B; operands go
-//                    from global memory straight into registers, D K steps
-//                    ahead (no LDS), with the lane's scale byte per operand;
-//                    output bf16(acc) or the fp32 accumulators.
+//                    and the codes of fl32(v * 2^-X). Scale bytes are stored in
+//                    panels of 128 elements of K: [ceil(K / 128)][R][4], so the
+//                    four bytes a row needs for one 128-byte K step sit together
+//                    and a tile's bytes for that step are one contiguous run.
+//   mx_dma_kernel    weights on the MFMA A operand, tokens on B; code tiles
+//                    and their scale bytes move global -> LDS with LDS-DMA
+//                    copies into an S-slot ring (one barrier per 128-byte K
+//                    step), so the tokens are fetched once per block and
+//                    shared by its 8 waves; output bf16(acc) or the fp32
+//                    accumulators.
 #include "qr_device.h"
 #include "qr_internal.h"
 
@@ -23,7 +28,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kWordBuf = 0x00020000;  // raw buffer resource word 3 (gfx9)
-constexpr uint32_t kOOB = 0x80000000u;
 
 // Exponent of a block: smallest X with amax <= 448 * 2^X; amax = f 2^e with
 // f in [0.5, 1) and 448 = 0.875 2^9. Clamped to the E8M0 range.
@@ -76,7 +80,7 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const void* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
   const int X = mx_exp(amax);
-  scales[row * nb + b] = (uint8_t)(X + 127);
+  scales[((b >> 2) * R + row) * 4 + (b & 3)] = (uint8_t)(X + 127);
   uint32_t q[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) q[i] = mx_codes4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], -X);
@@ -85,36 +89,126 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const void* __restrict__ 
   out[1] = make_uint4(q[4], q[5], q[6], q[7]);
 }
 
-struct MxParams {
+// ---------------------------------------------------------------------------
+// LDS-DMA block-scaled GEMM. A stage holds, for one 128-byte K step, the
+// weight rows of the tile (BN x 128 bytes), the token rows (BM x 128 bytes,
+// padded to whole 1 KB blocks per wave) and the four E8M0 bytes of every
+// row's 32-element blocks in that step (4 bytes per row; 1 KB for up to 256
+// weight rows, then 1 KB for up to 256 token rows). Code rows are copied 8
+// rows (1 KB) per wave instruction with buffer_load_dwordx4 ... lds (64 lanes
+// x 16 bytes at M0 + offset + 16 lane; up to four copies share one M0 write
+// through the instruction offset). The scale bytes of a step are stored
+// contiguously per operand (panels [K / 128][rows][4]), so wave 0 copies the
+// weight tile's and wave 1 the token tile's with one such instruction each;
+// a wave waits for its own copies with a fixed vmcnt (one more for waves 0
+// and 1), and one barrier per K step publishes them. 16-byte LDS chunks are XOR-swizzled by row (chunk c of row r sits at
+// c ^ ((r >> 1) & 7)), applied on the global side of the copy.
+//
+// In the 16x16x128 scaled MFMA, lane l (row l % 16, group g = l / 16) holds
+// K bytes [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16) of the step and
+// the scale byte of 32-element block g of its row (the hardware's layout,
+// measured), so a lane reads LDS chunks g and g + 4 of its row and scale byte
+// g. A tile may own fewer weight rows than its height (rn, a multiple of 8)
+// so the grid can be balanced over the CUs; rows past rn or N read as zero
+// and are not stored.
+// ---------------------------------------------------------------------------
+struct MxDmaParams {
   const uint8_t* Xq;
-  const uint8_t* sx;  // [M, K/32] E8M0
+  const uint8_t* sx;
   const uint8_t* Wq;
-  const uint8_t* sw;  // [N, K/32] E8M0
+  const uint8_t* sw;
   int64_t M, N, K;
   void* Y;
   int64_t ldy;
   int out_raw;
-  int tiles_m;
+  int tiles_m, nks, rn;
 };
 
-// Four waves; wave w owns weight rows [64 FN tn + 16 FN w, + 16 FN) and all
-// 16 FM tokens of the tile. In the 16x16x128 scaled MFMA, lane l (row l % 16,
-// group g = l / 16) supplies the K positions [16 g, 16 g + 16) in its first
-// 16 bytes and [64 + 16 g, + 16) in its last 16, and the scale of the
-// 32-element block g (measured: a block's scale follows the lane group, not
-// the lane's data). So each lane loads those two 16-byte pieces of the
-// 128-byte K step and passes the scale byte of block g.
-template <int FN, int FM, int D>
-__global__ __launch_bounds__(256, 1) void mx_gemm_kernel(const MxParams p) {
-  constexpr int BN = 64 * FN, BM = 16 * FM;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tn = blockIdx.x / p.tiles_m, tm = blockIdx.x % p.tiles_m;
+template <int CNT>
+__device__ __forceinline__ void mx_dma16(uint32_t lds, const uint32_t* vo,
+                                         __amdgpu_buffer_rsrc_t r, int soff) {
+  static_assert(CNT >= 1 && CNT <= 4, "one M0 covers at most 4 KB of offsets");
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+  if constexpr (CNT == 1)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(lds), "v"(vo[0]), "s"(r), "s"(soff) : "memory", "m0");
+  else if constexpr (CNT == 2)
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "buffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds"
+                 :: "s"(lds), "v"(vo[0]), "v"(vo[1]), "s"(r), "s"(soff) : "memory", "m0");
+  else if constexpr (CNT == 3)
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "buffer_load_dwordx4 %1, %4, %5 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %4, %5 offen offset:1024 lds\n\t"
+                 "buffer_load_dwordx4 %3, %4, %5 offen offset:2048 lds"
+                 :: "s"(lds), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "s"(r), "s"(soff)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\t"
+                 "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
+                 "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
+                 "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
+                 "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
+                 :: "s"(lds), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(r), "s"(soff)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+template <int N>
+__device__ __forceinline__ void mx_wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until at most min(ahead, A) stages of NI copies are in flight.
+template <int NI, int A>
+__device__ __forceinline__ void mx_wait_stages(int ahead) {
+  if constexpr (A > 0) {
+    if (ahead >= A) {
+      mx_wait_vm<A * NI>();
+      return;
+    }
+    mx_wait_stages<NI, A - 1>(ahead);
+  } else {
+    mx_wait_vm<0>();
+  }
+}
+
+template <int BN, int BM, int WN, int WM, int S>
+__global__ __launch_bounds__(64 * WN * WM, 1) void mx_dma_kernel(const MxDmaParams p) {
+  constexpr int NW = WN * WM;
+  constexpr int WTN = BN / WN, WTM = BM / WM;
+  constexpr int FN = WTN / 16, FM = WTM / 16;
+  constexpr int IA = BN / 8;
+  constexpr int IB0 = BM / 8;
+  constexpr int IB = IB0 + (NW - IB0 % NW) % NW;
+  constexpr int NA = IA / NW, NB = IB / NW;
+  constexpr int NI = NA + NB;  // code copies per wave per K step
+  constexpr int GA = (NA + 3) / 4, GB = (NB + 3) / 4;
+  constexpr int CODES = (IA + IB) * 1024;
+  constexpr int STAGE = CODES + 2048;  // + weight and token scale bytes
+  static_assert(BN % 16 == 0 && BM % 16 == 0 && IA % NW == 0, "row blocks per wave");
+  static_assert(WTN % 16 == 0 && WTM % 16 == 0, "wave tile");
+  static_assert(BN <= 256 && BM <= 256 && NW >= 2, "one scale copy per operand");
+  static_assert(S >= 2 && (S - 2) * (NI + 1) <= 63, "ring depth");
+  static_assert(S * STAGE <= 160 * 1024, "LDS");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+
+  const int G = gridDim.x;
+  int b = blockIdx.x;
+  const int G8 = G & ~7;
+  if (b < G8) b = (b & 7) * (G8 >> 3) + (b >> 3);  // neighbouring tiles on one XCD
+  const int tm = b % p.tiles_m, tn = b / p.tiles_m;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wid % WN, wm = wid / WN;
   const int64_t N = p.N, M = p.M, K = p.K, nb = K >> 5;
-  const int nks = (int)(K >> 7);
-  const int64_t n0 = (int64_t)tn * BN + 16 * FN * w;
-  if (n0 >= N) return;
-  const int lrow = lane & 15, g = lane >> 4;
+  constexpr uint32_t kBig = 0x80000000u;
 
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.Wq, (short)0, (int)(uint32_t)(N * K), kWordBuf);
@@ -124,19 +218,69 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(const MxParams p) {
       __builtin_amdgcn_make_buffer_rsrc((void*)p.sw, (short)0, (int)(uint32_t)(N * nb), kWordBuf);
   const __amdgpu_buffer_rsrc_t rsx =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.sx, (short)0, (int)(uint32_t)(M * nb), kWordBuf);
-  uint32_t oa[FN], ob[FM], sa[FN], sb[FM];
+
+  // Code copies: wave wid moves weight row blocks wid*NA + i and token row
+  // blocks wid*NB + i; lane l covers row 8 rb + l / 8, physical chunk l % 8.
+  // Offsets are biased by -1 KB * (i % 4), the copy's instruction offset.
+  const int lrow = lane >> 3, pch = lane & 7;
+  uint32_t oa[NA], ob[NB];
 #pragma unroll
-  for (int i = 0; i < FN; ++i) {
-    const int64_t row = n0 + 16 * i + lrow;
-    oa[i] = row < N ? (uint32_t)(row * K + 16 * g) : kOOB;
-    sa[i] = row < N ? (uint32_t)(row * nb + g) : kOOB;
+  for (int i = 0; i < NA; ++i) {
+    const int r = (wid * NA + i) * 8 + lrow;
+    const int c = pch ^ ((r >> 1) & 7);
+    const int64_t row = (int64_t)tn * p.rn + r;
+    oa[i] = ((r < p.rn && row < N) ? (uint32_t)(row * K + c * 16) : kBig) - 1024u * (uint32_t)(i % 4);
   }
 #pragma unroll
-  for (int j = 0; j < FM; ++j) {
-    const int64_t row = (int64_t)tm * BM + 16 * j + lrow;
-    ob[j] = row < M ? (uint32_t)(row * K + 16 * g) : kOOB;
-    sb[j] = row < M ? (uint32_t)(row * nb + g) : kOOB;
+  for (int i = 0; i < NB; ++i) {
+    const int r = (wid * NB + i) * 8 + lrow;
+    const int c = pch ^ ((r >> 1) & 7);
+    const int64_t row = (int64_t)tm * BM + r;
+    ob[i] = ((r < BM && row < M) ? (uint32_t)(row * K + c * 16) : kBig) - 1024u * (uint32_t)(i % 4);
   }
+  // Scale copy (waves 0 and 1): lane l brings the 16 bytes of rows 4 l ..
+  // 4 l + 3 of the tile from panel ks (offset ks * rows * 4 bytes, added per
+  // step). Bytes of rows past the tile's owned rows or past N / M belong to
+  // rows whose outputs are not stored (or read as zero past the array).
+  const bool has_s = wid < 2;
+  const uint32_t os = wid == 0 ? (uint32_t)(((int64_t)tn * p.rn + 4 * lane) * 4)
+                               : (uint32_t)(((int64_t)tm * BM + 4 * lane) * 4);
+  const int64_t spanel = wid == 0 ? N * 4 : M * 4;  // bytes per scale panel
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const uint32_t la0 = lds0 + (uint32_t)(wid * NA) * 1024u;
+  const uint32_t lb0 = lds0 + (uint32_t)(IA + wid * NB) * 1024u;
+  const uint32_t ls0 = lds0 + (uint32_t)CODES + (uint32_t)(wid == 0 ? 0 : 1024);
+
+  auto issue_group = [&](int g, int slot, int ks) {
+    const int soff = ks * 128;
+    const uint32_t so = (uint32_t)(slot * STAGE);
+    const bool isA = g < GA;
+    const int i0 = (isA ? g : g - GA) * 4;
+    const uint32_t base = (isA ? la0 : lb0) + so + (uint32_t)i0 * 1024u;
+    uint32_t vo[4];
+    const int cnt = isA ? (NA - i0 < 4 ? NA - i0 : 4) : (NB - i0 < 4 ? NB - i0 : 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vo[e] = isA ? oa[(i0 + e) < NA ? i0 + e : 0] : ob[(i0 + e) < NB ? i0 + e : 0];
+    if (cnt == 4) mx_dma16<4>(base, vo, isA ? rw : rx, soff);
+    else if (cnt == 3) mx_dma16<3>(base, vo, isA ? rw : rx, soff);
+    else if (cnt == 2) mx_dma16<2>(base, vo, isA ? rw : rx, soff);
+    else mx_dma16<1>(base, vo, isA ? rw : rx, soff);
+  };
+  auto issue_all = [&](int slot, int ks) {
+#pragma unroll
+    for (int g = 0; g < GA + GB; ++g) issue_group(g, slot, ks);
+    if (has_s) {
+      const uint32_t v[1] = {os};
+      mx_dma16<1>(ls0 + (uint32_t)(slot * STAGE), v, wid == 0 ? rsw : rsx, (int)(ks * spanel));
+    }
+  };
+
+  // MFMA operand reads: lane (row lr = l % 16, group g = l / 16) reads
+  // chunks g and g + 4 of its row and scale byte g.
+  const int lr = lane & 15, lg = lane >> 4;
+  const int sl = (lr >> 1) & 7;  // swizzle of rows lr (+ multiples of 16)
+  const int x0 = (lg ^ sl) << 4, x1 = ((lg + 4) ^ sl) << 4;
+  const int rA = wn * WTN + lr, rB = wm * WTM + lr;
 
   v4f acc[FN][FM];
 #pragma unroll
@@ -144,47 +288,43 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(const MxParams p) {
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  v4i ra[D][FN][2], rb[D][FM][2];
-  int ea[D][FN], eb[D][FM];
-  auto load = [&](int s, int ks) {
-    const int so = ks * 128, ss = ks * 4;
+  const int nk = p.nks;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue_all(s, s);
+  int cs = 0, is = S - 1;
+  for (int it = 0; it < nk; ++it) {
+    if (has_s) mx_wait_stages<NI + 1, S - 2>(nk - 1 - it);
+    else mx_wait_stages<NI, S - 2>(nk - 1 - it);
+    __syncthreads();
+    const uint8_t* st = smem + cs * STAGE;
+    v8i a[FN], bb[FM];
+    int ea[FN], eb[FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      ra[s][i][0] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)oa[i], so, 0);
-      ra[s][i][1] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(oa[i] + 64), so, 0);
-      ea[s][i] = __builtin_amdgcn_raw_buffer_load_b8(rsw, (int)sa[i], ss, 0);
+      const uint8_t* row = st + (rA + 16 * i) * 128;
+      const uint4 u0 = *reinterpret_cast<const uint4*>(row + x0);
+      const uint4 u1 = *reinterpret_cast<const uint4*>(row + x1);
+      a[i] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+      ea[i] = st[CODES + (rA + 16 * i) * 4 + lg];
     }
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      rb[s][j][0] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)ob[j], so, 0);
-      rb[s][j][1] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(ob[j] + 64), so, 0);
-      eb[s][j] = __builtin_amdgcn_raw_buffer_load_b8(rsx, (int)sb[j], ss, 0);
+      const uint8_t* row = st + IA * 1024 + (rB + 16 * j) * 128;
+      const uint4 u0 = *reinterpret_cast<const uint4*>(row + x0);
+      const uint4 u1 = *reinterpret_cast<const uint4*>(row + x1);
+      bb[j] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+      eb[j] = st[CODES + 1024 + (rB + 16 * j) * 4 + lg];
     }
-  };
-  auto compute = [&](int s) {
+    if (it + S - 1 < nk) issue_all(is, it + S - 1);
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const v8i av{ra[s][i][0][0], ra[s][i][0][1], ra[s][i][0][2], ra[s][i][0][3],
-                     ra[s][i][1][0], ra[s][i][1][1], ra[s][i][1][2], ra[s][i][1][3]};
-        const v8i bv{rb[s][j][0][0], rb[s][j][0][1], rb[s][j][0][2], rb[s][j][0][3],
-                     rb[s][j][1][0], rb[s][j][1][1], rb[s][j][1][2], rb[s][j][1][3]};
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[i][j], 0, 0, 0,
-                                                                     ea[s][i], 0, eb[s][j]);
-      }
-  };
-#pragma unroll
-  for (int s = 0; s < D; ++s)
-    if (s < nks) load(s, s);
-  for (int it = 0; it < nks; it += D) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      if (it + s < nks) {
-        compute(s);
-        if (it + s + D < nks) load(s, it + s + D);
-      }
-    }
+      for (int j = 0; j < FM; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bb[j], acc[i][j], 0, 0, 0,
+                                                                     ea[i], 0, eb[j]);
+    cs = cs + 1 == S ? 0 : cs + 1;
+    is = is + 1 == S ? 0 : is + 1;
   }
 
   // Register r of lane l: weight row 4 (l / 16) + r, token l % 16.
@@ -192,9 +332,10 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(const MxParams p) {
   for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int64_t m = (int64_t)tm * BM + 16 * j + lrow;
-      const int64_t n = n0 + 16 * i + 4 * g;
-      if (m >= M) continue;
+      const int64_t m = (int64_t)tm * BM + wm * WTM + 16 * j + lr;
+      const int nl = wn * WTN + 16 * i + 4 * lg;  // local weight row of register 0
+      const int64_t n = (int64_t)tn * p.rn + nl;
+      if (m >= M || nl >= p.rn) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (n + r >= N) break;
@@ -206,13 +347,25 @@ __global__ __launch_bounds__(256, 1) void mx_gemm_kernel(const MxParams p) {
     }
 }
 
-template <int FN, int FM, int D>
-hipError_t launch_mx(const MxParams& p, hipStream_t st) {
-  const int64_t tiles_n = (p.N + 64 * FN - 1) / (64 * FN);
-  MxParams q = p;
-  q.tiles_m = (int)((p.M + 16 * FM - 1) / (16 * FM));
-  hipLaunchKernelGGL((mx_gemm_kernel<FN, FM, D>), dim3((unsigned)(tiles_n * q.tiles_m)), dim3(256),
-                     0, st, q);
+constexpr int kCUs = 256;  // MI355X compute units
+
+template <int BN, int BM, int WN, int WM, int S>
+hipError_t launch_mx_dma(const MxDmaParams& p0, int rows, hipStream_t st) {
+  MxDmaParams p = p0;
+  p.tiles_m = (int)((p.M + BM - 1) / BM);
+  p.nks = (int)(p.K >> 7);
+  // Rows per tile: shrink (to a multiple of 8, at least half the height)
+  // so the blocks fill whole rounds of the CUs, unless a row count is given.
+  if (rows <= 0) {
+    const int64_t full = ((p.N + BN - 1) / BN) * p.tiles_m;
+    const int64_t per = kCUs * ((full + kCUs - 1) / kCUs);
+    const int64_t want = 8 * ((p.N * p.tiles_m + 8 * per - 1) / (8 * per));
+    rows = (want >= BN / 2 && want < BN) ? (int)want : BN;
+  }
+  p.rn = rows;
+  const int64_t tiles_n = (p.N + rows - 1) / rows;
+  hipLaunchKernelGGL((mx_dma_kernel<BN, BM, WN, WM, S>), dim3((unsigned)(tiles_n * p.tiles_m)),
+                     dim3(64 * WN * WM), 0, st, p);
   return hipGetLastError();
 }
 
@@ -235,15 +388,14 @@ hipError_t launch_mx_gemm(const void* Xq, const uint8_t* sx, const void* Wq, con
                           int64_t M, int64_t N, int64_t K, int out_raw, void* Y, int64_t ldy,
                           hipStream_t st) {
   if (M == 0 || N == 0) return hipSuccess;
-  MxParams p{static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
-             M, N, K, Y, ldy, out_raw, 0};
-  // Up to 32 tokens: 64 weight rows per block (one 16-row fragment per
-  // wave) for a few hundred blocks; above, 128 rows x 64 tokens (measured
-  // faster at M = 256 than 64 rows x 128 tokens, whose operands need more
-  // registers than leave room for prefetch).
-  if (M <= 16) return launch_mx<1, 1, 4>(p, st);
-  if (M <= 32) return launch_mx<1, 2, 4>(p, st);
-  return launch_mx<2, 4, 2>(p, st);
+  MxDmaParams p{static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
+                M, N, K, Y, ldy, out_raw, 0, 0, 0};
+  // Up to 32 tokens the product is a weight stream: 128-row tiles of 32
+  // tokens, rows balanced over the CUs; above, 8-wave 192 x 128 tiles (two
+  // waves per SIMD, each a 96 x 32 wave tile of six by two 16 x 16 MFMA
+  // fragments), as for the per-channel 256-token GEMM.
+  if (M <= 32) return launch_mx_dma<128, 32, 8, 1, 4>(p, 0, st);
+  return launch_mx_dma<192, 128, 2, 4, 3>(p, 192, st);
 }
 
 }  // namespace qr
