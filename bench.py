@@ -48,6 +48,10 @@ WORKLOADS = {
                                    kind="outliers", fused=False),
     "32b_decode_int8": dict(M=512, qt="int8", chain="32b", sets=2, kind="normal"),
     "32b_decode_fp8": dict(M=512, qt="fp8", chain="32b", sets=2, kind="normal"),
+    # q, k and v stacked into one 7168-row projection (the merged QKV rollout
+    # engines run; the 7B layer's QKV is merged the same way)
+    "32b_decode_int8_qkv": dict(M=512, qt="int8", chain="32b_qkv", sets=2, kind="normal"),
+    "32b_decode_fp8_qkv": dict(M=512, qt="fp8", chain="32b_qkv", sets=2, kind="normal"),
     "32b_prefill_int8": dict(M=4096, qt="int8", chain="32b_prefill", sets=2, kind="heavy"),
 }
 
@@ -86,7 +90,7 @@ def chain_spec(name):
         return I.CHAIN_7B_PRODUCERS, I.LINEARS_7B, I.W_SIGMA_7B
     if name == "32b":
         return I.CHAIN_32B, I.LINEARS_32B, I.W_SIGMA_32B
-    if name == "32b_prefill":
+    if name in ("32b_prefill", "32b_qkv"):
         return I.CHAIN_32B_PREFILL, I.LINEARS_32B, I.W_SIGMA_32B
     raise ValueError(name)
 

@@ -93,6 +93,9 @@ CHAIN_32B = [
 ]
 
 # 32B prefill: the same chain shape as the 7B layer with 32B linears (QKV fused).
+# The decode layer's variant with q, k and v stacked into one projection over
+# [W_q; W_k; W_v] (their shared quantized input, one GEMM; each output column
+# still depends only on its own weight row) uses it too.
 CHAIN_32B_PREFILL = [
     dict(name="qkv", src="x0", cols=None),
     dict(name="o", src="qkv", cols=(0, 5120)),
