@@ -76,10 +76,13 @@ def test_mx_gemm_against_exact_block_sums(M, N, K):
     assert_bf16_close(bf16_np(yd), y, what=f"mx {M}x{N}x{K}")
 
 
-def test_mx_gemm_7b_gate_m256_sampled_channels():
-    """The 7B gate at M = 256, full size on the device; 512 sampled output channels
-    (a channel's codes, scales and outputs depend only on its own weight row)."""
-    M, N, K = 256, 18944, 3584
+@pytest.mark.parametrize("M", [256, 32, 7])
+def test_mx_gemm_7b_gate_sampled_channels(M):
+    """The 7B gate at M = 256 (8-wave 192 x 128 tiles), 32 and 7 (128 x 32 tiles owning
+    80 of their 128 rows, so the grid fills the CUs), full size on the device; 512 sampled
+    output channels (a channel's codes, scales and outputs depend only on its own weight
+    row)."""
+    N, K = 18944, 3584
     rows = np.unique(np.r_[0, np.random.default_rng(4).choice(N, 510, replace=False), N - 1])
     (xc, xe, wc, we), (dxc, dxs, dwc, dws) = _mx_operands(M, N, K, seed=99, rows=rows)
     assert np.array_equal(codes_np(dwc)[rows], wc)
