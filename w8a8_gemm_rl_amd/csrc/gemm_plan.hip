@@ -1,5 +1,6 @@
 // Launch planner of the GEMM family: tile, split-K and rows per tile for one
 // product shape (pure host code; choices measured on MI355X).
+#include "qr_device.h"
 #include "qr_gemm.h"
 
 namespace {
@@ -14,7 +15,6 @@ namespace qr {
 
 GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int force_splitk,
                    int force_rows) {
-  (void)qt;
   GemmPlan p{};
   // Tile by token count (indices into the tile table; choices measured on
   // MI355X with graph-replayed launches). Up to 32 tokens the product is a
@@ -25,9 +25,10 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
   // with split K on long-K
   // ones and 128 x 64 / 128 x 32 tiles on narrow ones (more blocks); up to
   // 1024 tokens 256 x 256 tiles on wide layers, 256 x 128 with split K on
-  // long-K ones, 128 x 128 on the others and split 128 x 32 tiles on very
-  // narrow ones; large token counts use 256 x 256 tiles, 256 x 128 below
-  // N = 7168.
+  // long-K ones, 128 x 128 on the others and 64 x 16 tiles on very narrow
+  // ones (1024-row k / v projections: two rounds of small blocks beat one of
+  // 128 x 32 tiles that own half their rows); large token counts use
+  // 256 x 256 tiles, 256 x 128 below N = 7168.
   const int64_t nks = (K + 127) / 128;
   int tile;
   if (force_tile >= 0) {
@@ -42,10 +43,11 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
     if (N >= 24576) tile = 5;
     else if (N >= 8192) tile = 14;
     else if (nks >= 64) tile = 2;
-    else tile = N >= 4096 ? 1 : 0;
+    else if (N >= 4096) tile = 1;
+    else tile = qt == kQFp8 ? 8 : 0;  // FP8: 32x32 fragments 8% faster here
   } else if (M <= 1024) {
     if (N >= 16384) tile = 5;
-    else if (N <= 2048) tile = 0;
+    else if (N <= 2048) tile = 9;
     else tile = nks >= 64 ? 4 : 2;
   } else {
     tile = N >= 7168 ? 5 : 4;
