@@ -248,7 +248,8 @@ int qr_acr_tis_loss(const float* logp, const float* logp_prox, const float* logp
  *
  * For every row r and block b of A (values v widened exactly to fp32):
  *   X = the smallest integer with max |v| <= 448 * 2^X (clamped to
- *       [-127, 127]; an all-zero block gives -127);  scales[r, b] = X + 127;
+ *       [-127, 127]; an all-zero block gives -127); the scale byte of block b
+ *       of row r is X + 127 (stored as below);
  *   codes[r, 32 b + i] = E4M3FN(min(max(fl32(v_i * 2^-X), -448), 448)),
  *       nearest, ties to even, sign kept on zero.
  *
