@@ -66,13 +66,15 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
   // K (every split keeps four or more K steps, and the partial sums, 4 M N
   // bytes per split, stay within the weight bytes) and then rebalance the
   // rows.
-  // Only the weight-streaming tiles (64 tokens or fewer) shrink: tiles of
-  // more tokens are bound by their MFMA work, which does not shrink with the
-  // row count.
+  // The weight-streaming tiles (64 tokens or fewer) shrink, and so do tiles
+  // of at most 128 rows up to 1024 tokens (a 512-token 5120-row projection
+  // on 80-row tiles is 6% faster); the 256-row tiles of wider layers and
+  // larger token counts are bound by the MFMA work of the full tile, which
+  // does not shrink with the row count, and keep their height.
   // With more full-height blocks than CUs the rows shrink to fill whole
   // rounds of kCUs blocks instead of leaving a short last round.
   auto balanced_rows = [&](int64_t splits) -> int64_t {
-    if (d.BM > 64) return d.BN;
+    if (d.BM > 64 && (M > 1024 || d.BN > 128)) return d.BN;
     const int64_t base = ((N + d.BN - 1) / d.BN) * p.tiles_m * splits;
     const int64_t per = kCUs * ((base + kCUs - 1) / kCUs);  // blocks wanted
     const int64_t want = 8 * ((N * p.tiles_m * splits + 8 * per - 1) / (8 * per));
