@@ -278,6 +278,8 @@ int qr_mx_quantize(const void* A, int64_t R, int64_t K, int64_t lda, int src_bf1
  *   Xq, sx   [M, K] codes and the tokens' E8M0 scales ([K/128][M][4] panels,
  *            as qr_mx_quantize writes them).
  *   Wq, sw   [N, K] codes and the weights' E8M0 scales ([K/128][N][4]).
+ *            Xq, Wq, sx, sw and Y start on 16-byte boundaries (else
+ *            QR_ERR_UNSUPPORTED).
  *   K        multiple of 128; code matrices below 2^31 - 2^16 bytes.
  *   Y        [M, ldy] bf16 or fp32 (written).
  */

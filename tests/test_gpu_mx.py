@@ -101,5 +101,9 @@ def test_mx_rejects_bad_shapes():
     c, s = B.mx_quantize(torch.zeros((4, 96), dtype=torch.float32, device=DEV))
     with pytest.raises(B.QRError):
         B.mx_gemm(c, s, c, s)  # K not a multiple of 128
+    c, s = B.mx_quantize(torch.zeros((4, 128), dtype=torch.float32, device=DEV))
+    Y = torch.empty(4 * 4 + 1, dtype=torch.bfloat16, device=DEV)[1:].view(4, 4)
+    with pytest.raises(B.QRError):
+        B.mx_gemm(c, s, c, s, Y=Y)  # output not on a 16-byte boundary
     z, zs = B.mx_quantize(torch.zeros((0, 128), dtype=torch.float32, device=DEV))
     assert z.shape == (0, 128)

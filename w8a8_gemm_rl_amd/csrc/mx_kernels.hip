@@ -26,6 +26,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kWordBuf = 0x00020000;  // raw buffer resource word 3 (gfx9)
 
@@ -108,7 +109,10 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const void* __restrict__ 
 // K bytes [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16) of the step and
 // the scale byte of 32-element block g of its row (the hardware's layout,
 // measured), so a lane reads LDS chunks g and g + 4 of its row and scale byte
-// g. A tile may own fewer weight rows than its height (rn, a multiple of 8)
+// g. The 32x32x64 form (two per 128-byte step, sub-step h) follows the same
+// pattern with two lane groups: lane l (row l % 32, g = l / 32) holds K bytes
+// [64 h + 16 g, + 16) and [64 h + 32 + 16 g, + 16) and the scale of block
+// 2 h + g (checked by the parity tests against exact block sums). A tile may own fewer weight rows than its height (rn, a multiple of 8)
 // so the grid can be balanced over the CUs; rows past rn or N read as zero
 // and are not stored.
 // ---------------------------------------------------------------------------
@@ -176,11 +180,33 @@ __device__ __forceinline__ void mx_wait_stages(int ahead) {
   }
 }
 
-template <int BN, int BM, int WN, int WM, int S>
+template <int T>
+struct MxMfma;
+template <>
+struct MxMfma<16> {
+  using acc_t = v4f;
+  static constexpr int KI = 128;
+  static __device__ __forceinline__ acc_t run(v8i a, v8i b, acc_t c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  }
+};
+template <>
+struct MxMfma<32> {
+  using acc_t = v16f;
+  static constexpr int KI = 64;
+  static __device__ __forceinline__ acc_t run(v8i a, v8i b, acc_t c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  }
+};
+
+template <int T, int BN, int BM, int WN, int WM, int S>
 __global__ __launch_bounds__(64 * WN * WM, 1) void mx_dma_kernel(const MxDmaParams p) {
+  using MF = MxMfma<T>;
+  using acc_t = typename MF::acc_t;
+  constexpr int KI = MF::KI, NKK = 128 / KI;
   constexpr int NW = WN * WM;
   constexpr int WTN = BN / WN, WTM = BM / WM;
-  constexpr int FN = WTN / 16, FM = WTM / 16;
+  constexpr int FN = WTN / T, FM = WTM / T;
   constexpr int IA = BN / 8;
   constexpr int IB0 = BM / 8;
   constexpr int IB = IB0 + (NW - IB0 % NW) % NW;
@@ -190,7 +216,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void mx_dma_kernel(const MxDmaPara
   constexpr int CODES = (IA + IB) * 1024;
   constexpr int STAGE = CODES + 2048;  // + weight and token scale bytes
   static_assert(BN % 16 == 0 && BM % 16 == 0 && IA % NW == 0, "row blocks per wave");
-  static_assert(WTN % 16 == 0 && WTM % 16 == 0, "wave tile");
+  static_assert(WTN % T == 0 && WTM % T == 0, "wave tile");
   static_assert(BN <= 256 && BM <= 256 && NW >= 2, "one scale copy per operand");
   static_assert(S >= 2 && (S - 2) * (NI + 1) <= 63, "ring depth");
   static_assert(S * STAGE <= 160 * 1024, "LDS");
@@ -275,18 +301,31 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void mx_dma_kernel(const MxDmaPara
     }
   };
 
-  // MFMA operand reads: lane (row lr = l % 16, group g = l / 16) reads
-  // chunks g and g + 4 of its row and scale byte g.
-  const int lr = lane & 15, lg = lane >> 4;
-  const int sl = (lr >> 1) & 7;  // swizzle of rows lr (+ multiples of 16)
-  const int x0 = (lg ^ sl) << 4, x1 = ((lg + 4) ^ sl) << 4;
+  // MFMA operand reads: lane (row lr = l % T, group g = l / T) reads, for
+  // sub-step h, chunks KI h / 16 + g and that + KI / 32 of its row and
+  // scale byte KI h / 32 + g.
+  const int lr = lane % T, lg = lane / T;
+  const int sl = (lr >> 1) & 7;  // swizzle of rows lr (+ multiples of T)
+  int x0[NKK], x1[NKK];
+#pragma unroll
+  for (int h = 0; h < NKK; ++h) {
+    const int c0 = KI * h / 16 + lg;
+    x0[h] = (c0 ^ sl) << 4;
+    x1[h] = ((c0 + KI / 32) ^ sl) << 4;
+  }
   const int rA = wn * WTN + lr, rB = wm * WTM + lr;
 
-  v4f acc[FN][FM];
+  acc_t acc[FN][FM];
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FM; ++j) acc[i][j] = acc_t{};
+
+  auto operand = [](const uint8_t* row, int o0, int o1) -> v8i {
+    const uint4 u0 = *reinterpret_cast<const uint4*>(row + o0);
+    const uint4 u1 = *reinterpret_cast<const uint4*>(row + o1);
+    return v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
+  };
 
   const int nk = p.nks;
 #pragma unroll
@@ -298,58 +337,73 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void mx_dma_kernel(const MxDmaPara
     else mx_wait_stages<NI, S - 2>(nk - 1 - it);
     __syncthreads();
     const uint8_t* st = smem + cs * STAGE;
-    v8i a[FN], bb[FM];
-    int ea[FN], eb[FM];
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const uint8_t* row = st + (rA + 16 * i) * 128;
-      const uint4 u0 = *reinterpret_cast<const uint4*>(row + x0);
-      const uint4 u1 = *reinterpret_cast<const uint4*>(row + x1);
-      a[i] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-      ea[i] = st[CODES + (rA + 16 * i) * 4 + lg];
+    for (int h = 0; h < NKK; ++h) {
+      v8i a[FN], bb[FM];
+      int ea[FN], eb[FM];
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        a[i] = operand(st + (rA + T * i) * 128, x0[h], x1[h]);
+        ea[i] = st[CODES + (rA + T * i) * 4 + KI * h / 32 + lg];
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        bb[j] = operand(st + IA * 1024 + (rB + T * j) * 128, x0[h], x1[h]);
+        eb[j] = st[CODES + 1024 + (rB + T * j) * 4 + KI * h / 32 + lg];
+      }
+      if (h == 0 && it + S - 1 < nk) issue_all(is, it + S - 1);
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) acc[i][j] = MF::run(a[i], bb[j], acc[i][j], ea[i], eb[j]);
     }
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const uint8_t* row = st + IA * 1024 + (rB + 16 * j) * 128;
-      const uint4 u0 = *reinterpret_cast<const uint4*>(row + x0);
-      const uint4 u1 = *reinterpret_cast<const uint4*>(row + x1);
-      bb[j] = v8i{(int)u0.x, (int)u0.y, (int)u0.z, (int)u0.w, (int)u1.x, (int)u1.y, (int)u1.z, (int)u1.w};
-      eb[j] = st[CODES + 1024 + (rB + 16 * j) * 4 + lg];
-    }
-    if (it + S - 1 < nk) issue_all(is, it + S - 1);
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int j = 0; j < FM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], bb[j], acc[i][j], 0, 0, 0,
-                                                                     ea[i], 0, eb[j]);
     cs = cs + 1 == S ? 0 : cs + 1;
     is = is + 1 == S ? 0 : is + 1;
   }
 
-  // Register r of lane l: weight row 4 (l / 16) + r, token l % 16.
+  // Register r of lane l: weight row 8 (r / 4) + 4 (l / T) + r % 4 of the
+  // fragment, token l % T (for T = 16 only r < 4 exist).
+  constexpr int NR = T == 16 ? 4 : 16;
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int64_t m = (int64_t)tm * BM + wm * WTM + 16 * j + lr;
-      const int nl = wn * WTN + 16 * i + 4 * lg;  // local weight row of register 0
-      const int64_t n = (int64_t)tn * p.rn + nl;
-      if (m >= M || nl >= p.rn) continue;
+      const int64_t m = (int64_t)tm * BM + wm * WTM + T * j + lr;
+      if (m >= M) continue;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (n + r >= N) break;
-        if (p.out_raw)
-          static_cast<float*>(p.Y)[m * p.ldy + n + r] = acc[i][j][r];
-        else
-          static_cast<uint16_t*>(p.Y)[m * p.ldy + n + r] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+      for (int q = 0; q < NR / 4; ++q) {
+        const int nl = wn * WTN + T * i + 8 * q + 4 * lg;  // local weight row of register 4 q
+        const int64_t n = (int64_t)tn * p.rn + nl;
+        if (nl >= p.rn || n >= N) continue;
+        // four consecutive outputs of one token: one 8- or 16-byte store
+        // when they are all inside N and the row stride keeps it aligned
+        const bool full4 = n + 3 < N && (p.ldy & 3) == 0;
+        if (p.out_raw) {
+          float* y = static_cast<float*>(p.Y) + m * p.ldy + n;
+          if (full4) {
+            *reinterpret_cast<float4*>(y) = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                        acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+          } else {
+            for (int r = 0; r < 4 && n + r < N; ++r) y[r] = acc[i][j][4 * q + r];
+          }
+        } else {
+          uint32_t bb[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bb[r] = f32_to_bf16_rne(acc[i][j][4 * q + r]);
+          uint16_t* y = static_cast<uint16_t*>(p.Y) + m * p.ldy + n;
+          if (full4) {
+            *reinterpret_cast<uint2*>(y) = make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
+          } else {
+            for (int r = 0; r < 4 && n + r < N; ++r) y[r] = (uint16_t)bb[r];
+          }
+        }
       }
     }
 }
 
 constexpr int kCUs = 256;  // MI355X compute units
 
-template <int BN, int BM, int WN, int WM, int S>
+template <int T, int BN, int BM, int WN, int WM, int S>
 hipError_t launch_mx_dma(const MxDmaParams& p0, int rows, hipStream_t st) {
   MxDmaParams p = p0;
   p.tiles_m = (int)((p.M + BM - 1) / BM);
@@ -364,7 +418,7 @@ hipError_t launch_mx_dma(const MxDmaParams& p0, int rows, hipStream_t st) {
   }
   p.rn = rows;
   const int64_t tiles_n = (p.N + rows - 1) / rows;
-  hipLaunchKernelGGL((mx_dma_kernel<BN, BM, WN, WM, S>), dim3((unsigned)(tiles_n * p.tiles_m)),
+  hipLaunchKernelGGL((mx_dma_kernel<T, BN, BM, WN, WM, S>), dim3((unsigned)(tiles_n * p.tiles_m)),
                      dim3(64 * WN * WM), 0, st, p);
   return hipGetLastError();
 }
@@ -391,11 +445,12 @@ hipError_t launch_mx_gemm(const void* Xq, const uint8_t* sx, const void* Wq, con
   MxDmaParams p{static_cast<const uint8_t*>(Xq), sx, static_cast<const uint8_t*>(Wq), sw,
                 M, N, K, Y, ldy, out_raw, 0, 0, 0};
   // Up to 32 tokens the product is a weight stream: 128-row tiles of 32
-  // tokens, rows balanced over the CUs; above, 8-wave 192 x 128 tiles (two
-  // waves per SIMD, each a 96 x 32 wave tile of six by two 16 x 16 MFMA
-  // fragments), as for the per-channel 256-token GEMM.
-  if (M <= 32) return launch_mx_dma<128, 32, 8, 1, 4>(p, 0, st);
-  return launch_mx_dma<192, 128, 2, 4, 3>(p, 192, st);
+  // tokens (16 x 16 fragments), rows balanced over the CUs; above, 8-wave
+  // 192 x 128 tiles (two waves per SIMD, each a 96 x 32 wave tile of three
+  // 32 x 32 fragments, two MFMA sub-steps per K step), as for the
+  // per-channel 256-token GEMM.
+  if (M <= 32) return launch_mx_dma<16, 128, 32, 8, 1, 4>(p, 0, st);
+  return launch_mx_dma<32, 192, 128, 2, 4, 3>(p, 192, st);
 }
 
 }  // namespace qr

@@ -295,6 +295,8 @@ int qr_mx_gemm(const void* Xq, const uint8_t* sx, const void* Wq, const uint8_t*
   if (ldy < N) return fail(QR_ERR_INVALID_ARG, "%s: ldy=%lld < N=%lld", fn, (long long)ldy, (long long)N);
   if (M > 0 && N > 0 && (!Y || (K > 0 && (!Xq || !sx || !Wq || !sw))))
     return fail(QR_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (!aligned(Xq, 16) || !aligned(Wq, 16) || !aligned(sx, 16) || !aligned(sw, 16) || !aligned(Y, 16))
+    return fail(QR_ERR_UNSUPPORTED, "%s: misaligned pointer (16 bytes for Xq, Wq, sx, sw, Y)", fn);
   (void)hipGetLastError();
   return hip_status(qr::launch_mx_gemm(Xq, sx, Wq, sw, M, N, K, out == QR_OUT_RAW, Y, ldy,
                                        static_cast<hipStream_t>(stream)),
