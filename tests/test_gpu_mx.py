@@ -62,7 +62,7 @@ def _mx_operands(M, N, K, seed, rows=None):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 512, 512), (32, 200, 384), (45, 136, 1024), (1, 64, 128),
-                                   (256, 384, 3584), (100, 4608, 3584)])
+                                   (256, 384, 3584), (100, 4608, 3584), (33, 130, 256), (7, 203, 128)])
 def test_mx_gemm_against_exact_block_sums(M, N, K):
     (xc, xe, wc, we), (dxc, dxs, dwc, dws) = _mx_operands(M, N, K, seed=M * 7 + N + K)
     acc, y = O.mx_linear(xc, xe, wc, we)
@@ -92,6 +92,20 @@ def test_mx_gemm_7b_gate_sampled_channels(M):
     a = raw.cpu().numpy()[:, rows].astype(np.float64)
     bound = (2.0 ** -12 + (K - 1) * 2.0 ** -24) * (np.abs(_scaled(xc, xe)) @ np.abs(_scaled(wc, we)).T)
     assert np.all(np.abs(a - acc) <= bound + 1e-30)
+
+
+@pytest.mark.parametrize("M,N,K,pad", [(40, 130, 256, 6), (9, 64, 384, 1)])
+def test_mx_gemm_strided_output(M, N, K, pad):
+    """Y with a row stride that is not a multiple of 4 elements (outputs stored one by one)
+    and ragged N: the same values as into a packed Y, and the padding left untouched."""
+    (xc, xe, wc, we), (dxc, dxs, dwc, dws) = _mx_operands(M, N, K, seed=M + N + pad)
+    for out, dt in (("bf16", torch.bfloat16), ("raw", torch.float32)):
+        big = torch.full((M, N + pad), -7.0, dtype=dt, device=DEV)
+        B.mx_gemm(dxc, dxs, dwc, dws, out=out, Y=big[:, :N])
+        packed = B.mx_gemm(dxc, dxs, dwc, dws, out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(big[:, :N], packed), out
+        assert bool((big[:, N:] == -7.0).all()), out
 
 
 def test_mx_rejects_bad_shapes():
