@@ -145,53 +145,74 @@ __device__ __forceinline__ void block_tile(const KParams& p, int& tn, int& tm, i
 // ---- epilogue. Lane layout of an MFMA result: for T = 16 register r of
 // lane l is (i = 4*(l/16) + r, j = l%16); for T = 32 it is
 // (i = 8*(r/4) + 4*(l/32) + r%4, j = l%32). Four consecutive registers are
-// four consecutive output channels n of one token m. All scale loads are
-// issued together (buffer loads, zero outside the vectors), then the
-// outputs are converted and stored.
-template <int QT, int T, int BN, int BM, int WN, int WM, typename acc_t, int FN, int FM>
-__device__ __forceinline__ void store_tile(const KParams& p, const acc_t (&acc)[FN][FM], int tn,
-                                           int tm, int z, int wn, int wm, int lane) {
-  constexpr int WTN = BN / WN, WTM = BM / WM;
-  constexpr int NACC = Mfma<QT, T>::NACC;
+// four consecutive output channels n of one token m. The scales a lane
+// needs are loaded before the K loop (buffer loads, zero outside the
+// vectors; they complete before any later copy, so the copy waits stay
+// correct), so the epilogue does not wait for memory; then the outputs are
+// converted and stored.
+template <int FN, int FM, int NG>
+struct EpiScales {
+  float sx[FM];
+  float sw[FN][NG][4];
+};
+
+template <int T, int BN, int BM, int WN, int WM>
+__device__ __forceinline__ int64_t epi_row(const KParams& p, int tm, int wm, int j, int lane) {
+  return (int64_t)tm * BM + wm * (BM / WM) + j * T + lane % T;
+}
+// Local output channel of register group g of fragment i. Rows at or past
+// rn belong to the next tile (rn is a multiple of 8, so a group of four
+// never straddles it).
+template <int T, int BN, int WN>
+__device__ __forceinline__ int epi_nloc(int wn, int i, int g, int lane) {
+  const int ii = (T == 16) ? 4 * (lane / 16) : 8 * g + 4 * (lane / 32);
+  return wn * (BN / WN) + i * T + ii;
+}
+
+template <int QT, int T, int BN, int BM, int WN, int WM, int FN, int FM>
+__device__ __forceinline__ void load_scales(const KParams& p, int tn, int tm, int wn, int wm,
+                                            int lane,
+                                            EpiScales<FN, FM, Mfma<QT, T>::NACC / 4>& sc) {
+  constexpr int NG = Mfma<QT, T>::NACC / 4;
   constexpr uint32_t kOOB = 0x80000000u;
+  if (p.splitk > 1 || p.out_raw) return;
+  const int64_t N = p.N, M = p.M;
+  const __amdgpu_buffer_rsrc_t rsx_ = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.sx, (short)0, (int)(uint32_t)(M * 4), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rsw_ = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.sw, (short)0, (int)(uint32_t)(N * 4), kBufWord3);
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int64_t m = epi_row<T, BN, BM, WN, WM>(p, tm, wm, j, lane);
+    sc.sx[j] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+        rsx_, m < M ? (int)(m * 4) : (int)kOOB, 0, 0));
+  }
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int64_t n0 = (int64_t)tn * p.rn + epi_nloc<T, BN, WN>(wn, i, g, lane);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sc.sw[i][g][e] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            rsw_, n0 + e < N ? (int)((n0 + e) * 4) : (int)kOOB, 0, 0));
+    }
+}
+
+template <int QT, int T, int BN, int BM, int WN, int WM, typename acc_t, int FN, int FM>
+__device__ __forceinline__ void store_tile(const KParams& p, const acc_t (&acc)[FN][FM],
+                                           const EpiScales<FN, FM, Mfma<QT, T>::NACC / 4>& sc,
+                                           int tn, int tm, int z, int wn, int wm, int lane) {
+  constexpr int NACC = Mfma<QT, T>::NACC;
   const int64_t N = p.N, M = p.M;
   const bool split = p.splitk > 1;
   const bool raw = split || p.out_raw;
   constexpr int NG = NACC / 4;  // groups of four registers per fragment
-  const int jj = lane % T;
   int64_t mrow[FM];
 #pragma unroll
-  for (int j = 0; j < FM; ++j) mrow[j] = (int64_t)tm * BM + wm * WTM + j * T + jj;
-  // Local output channel of register group g of fragment i. Rows at or past
-  // rn belong to the next tile (rn is a multiple of 8, so a group of four
-  // never straddles it).
-  auto nloc = [&](int i, int g) -> int {
-    const int ii = (T == 16) ? 4 * (lane / 16) : 8 * g + 4 * (lane / 32);
-    return wn * WTN + i * T + ii;
-  };
+  for (int j = 0; j < FM; ++j) mrow[j] = epi_row<T, BN, BM, WN, WM>(p, tm, wm, j, lane);
+  auto nloc = [&](int i, int g) -> int { return epi_nloc<T, BN, WN>(wn, i, g, lane); };
   auto ncol = [&](int i, int g) -> int64_t { return (int64_t)tn * p.rn + nloc(i, g); };
-  float sxv[FM];
-  float swv[FN][NG][4];
-  if (!raw) {
-    const __amdgpu_buffer_rsrc_t rsx_ = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)p.sx, (short)0, (int)(uint32_t)(M * 4), kBufWord3);
-    const __amdgpu_buffer_rsrc_t rsw_ = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)p.sw, (short)0, (int)(uint32_t)(N * 4), kBufWord3);
-#pragma unroll
-    for (int j = 0; j < FM; ++j)
-      sxv[j] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-          rsx_, mrow[j] < M ? (int)(mrow[j] * 4) : (int)kOOB, 0, 0));
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int64_t n0 = ncol(i, g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          swv[i][g][e] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
-              rsw_, n0 + e < N ? (int)((n0 + e) * 4) : (int)kOOB, 0, 0));
-      }
-  }
 #pragma unroll
   for (int i = 0; i < FN; ++i)
 #pragma unroll
@@ -220,7 +241,7 @@ __device__ __forceinline__ void store_tile(const KParams& p, const acc_t (&acc)[
         } else {
           uint32_t bb[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) bb[e] = epi_bf16((float)acc[i][j][r + e], sxv[j], swv[i][g][e]);
+          for (int e = 0; e < 4; ++e) bb[e] = epi_bf16((float)acc[i][j][r + e], sc.sx[j], sc.sw[i][g][e]);
           uint16_t* y = static_cast<uint16_t*>(p.Y) + m * p.ldy + n0;
           if (full4) {
             *reinterpret_cast<uint2*>(y) = make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
@@ -531,6 +552,9 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
   // visible and guarantees slot (it - 1) % S is no longer read, and the
   // copies of step it + S - 1 go into that slot while the MFMAs of step it
   // run.
+  EpiScales<FN, FM, MF::NACC / 4> sc;
+  load_scales<QT, T, BN, BM, WN, WM>(p, tn, tm, wn, wm, lane, sc);
+
   const int nk = ks1 - ks0;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
@@ -545,7 +569,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
     is = is + 1 == S ? 0 : is + 1;
   }
 
-  store_tile<QT, T, BN, BM, WN, WM>(p, acc, tn, tm, z, wn, wm, lane);
+  store_tile<QT, T, BN, BM, WN, WM>(p, acc, sc, tn, tm, z, wn, wm, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -662,6 +686,9 @@ __global__ __launch_bounds__(64 * WPB, 1) void gemm_direct_kernel(const KParams 
     }
   };
 
+  EpiScales<FN, FM, MF::NACC / 4> sc;
+  load_scales<QT, T, BN, BM, WPB, 1>(p, tn, tm, wn, 0, lane, sc);
+
   const int nk = ks1 - ks0;
 #pragma unroll
   for (int s = 0; s < D; ++s)
@@ -675,7 +702,7 @@ __global__ __launch_bounds__(64 * WPB, 1) void gemm_direct_kernel(const KParams 
       }
     }
   }
-  store_tile<QT, T, BN, BM, WPB, 1>(p, acc, tn, tm, z, wn, 0, lane);
+  store_tile<QT, T, BN, BM, WPB, 1>(p, acc, sc, tn, tm, z, wn, 0, lane);
 }
 
 // Split-K second pass: Y[m, n] = epilogue(sum_{z = 0..S-1} part[z][m][n]),
