@@ -245,6 +245,10 @@ def test_gemm_auto_plan(qt, M, N, K):
 NUM_TILES = 16  # entries of the library's tile table
 
 
+def _tile_height(tile):
+    return int(re.search(r"_n(\d+)_", B.tile_name(tile)).group(1))
+
+
 @pytest.mark.parametrize("qt", QTS)
 @pytest.mark.parametrize("tile", range(NUM_TILES))
 @pytest.mark.parametrize("splitk", [1, 3, 9])
@@ -260,23 +264,16 @@ def test_gemm_every_tile_and_split(qt, tile, splitk, M, N, K):
     _check_gemm(xq, sx, wq, sw, qt, f"{qt} tile={tile} splitk={splitk} M={M} N={N} K={K}")
 
 
-def _tile_height(tile):
-    # tile names carry the macro tile as "_n<BN>_m<BM>"
-    name = B.tile_name(tile)
-    return int(name.split("_n")[1].split("_")[0])
-
-
 @pytest.mark.parametrize("qt", QTS)
 @pytest.mark.parametrize("tile", range(NUM_TILES))
 @pytest.mark.parametrize("splitk", [1, 3])
 @pytest.mark.parametrize("shrink", ["min", "one_block_less", "half"])
 def test_gemm_partial_row_tiles(qt, tile, splitk, shrink):
-    # Tiles that own fewer weight rows than their height: the copies of row
-    # blocks past the owned rows are not issued (their LDS rows hold stale
-    # bytes), so every stored output must still come from owned rows only.
-    # 8 rows per tile; one 8-row block less than the height; about half the
-    # height. N = 300 ends the last tile inside a row block; M and K are
-    # ragged too (a 16-byte last K step).
+    # Tiles that own fewer weight rows than their height (rows past the owned
+    # ones read as zero and are not stored), with split K: 8 rows per tile;
+    # one 8-row block less than the height; about half the height. N = 300
+    # ends the last tile inside a row block; M and K are ragged too (a
+    # 16-byte last K step).
     M, N, K = 70, 300, 1040
     bn = _tile_height(tile)
     rows = {"min": 8, "one_block_less": max(8, bn - 8), "half": max(8, (bn // 2 + 4) // 8 * 8)}[shrink]
@@ -285,8 +282,31 @@ def test_gemm_partial_row_tiles(qt, tile, splitk, shrink):
     _check_gemm(xq, sx, wq, sw, qt, f"{qt} tile={tile} splitk={splitk} rows={rows} M={M} N={N} K={K}")
 
 
-def _tile_height(tile):
-    return int(re.search(r"_n(\d+)_", B.tile_name(tile)).group(1))
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("tile", range(NUM_TILES))
+@pytest.mark.parametrize("pad", [4, 3])
+def test_gemm_strided_output(qt, tile, pad):
+    # Y with a row stride of N + pad elements (N + 4 = 304: bf16 rows staged
+    # through LDS and stored 16 bytes at a time; N + 3: stored from the MFMA
+    # layout), ragged M and N, tiles owning fewer rows than their height:
+    # the same bytes as a packed Y, and the padding columns untouched.
+    M, N, K = 70, 300, 1040
+    rows = max(8, (_tile_height(tile) // 2 + 4) // 8 * 8)
+    xq, sx, wq, sw = _codes_pair(M, N, K, qt, seed=tile * 5 + pad)
+    B.set_plan_override(tile, 1, rows)
+    args = (to_dev_codes(xq, qt), to_dev_f32(sx), to_dev_codes(wq, qt), to_dev_f32(sw), qt)
+    big = torch.full((M, N + pad), -3.0, dtype=torch.bfloat16, device=DEV)
+    B.w8a8_gemm(*args, Y=big[:, :N])
+    packed = B.w8a8_gemm(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(big[:, :N].view(torch.int16), packed.view(torch.int16)), (qt, tile, pad)
+    assert bool((big[:, N:] == -3.0).all()), (qt, tile, pad)
+    acc = O.acc_int8(xq, wq) if qt == "int8" else O.acc_fp8(xq, wq)
+    _, yref = O.dequant_epilogue(acc, sx, sw)
+    if qt == "int8":
+        assert np.array_equal(bf16_np(packed), yref)
+    else:
+        assert_bf16_close(bf16_np(packed), yref, what=f"fp8 tile={tile}")
 
 
 @pytest.mark.parametrize("qt", QTS)
