@@ -605,8 +605,11 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
   // visible and guarantees slot (it - 1) % S is no longer read, and the
   // copies of step it + S - 1 go into that slot while the MFMAs of step it
   // run.
+  // Scales are loaded before the K loop unless the accumulators already
+  // take 128 or more registers per lane (the 256 x 256 tile would spill).
+  constexpr bool kEarlyScales = FN * FM * MF::NACC < 128;
   EpiScales<FN, FM, MF::NACC / 4> sc;
-  load_scales<QT, T, BN, BM, WN, WM>(p, tn, tm, wn, wm, lane, sc);
+  if constexpr (kEarlyScales) load_scales<QT, T, BN, BM, WN, WM>(p, tn, tm, wn, wm, lane, sc);
 
   const int nk = ks1 - ks0;
 #pragma unroll
@@ -621,6 +624,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
     cs = cs + 1 == S ? 0 : cs + 1;
     is = is + 1 == S ? 0 : is + 1;
   }
+
+  if constexpr (!kEarlyScales) load_scales<QT, T, BN, BM, WN, WM>(p, tn, tm, wn, wm, lane, sc);
 
   // bf16 outputs go through LDS (the ring is free once every wave is past
   // its last K step), so each lane stores 16 contiguous bytes of a token's
