@@ -156,3 +156,20 @@ def test_workspace_size_and_plan_are_pure(B):
         with pytest.raises(B.QRError):
             B.set_plan_override(*bad)
     B.set_plan_override(-1)
+
+
+def test_build_rejects_register_spills():
+    # The build reads the compiler's per-kernel resource report and fails on
+    # any kernel that keeps registers in scratch memory.
+    from w8a8_gemm_rl_amd import build as Bu
+
+    report = "\n".join([
+        "k.hip:1:1: remark: Function Name: _Z4fastv [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark: Function Name: _Z5spillv [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark:     VGPRs: 256 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark:     ScratchSize [bytes/lane]: 236 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert Bu._spills(report) == [("_Z5spillv", 236)]
+    assert Bu._spills(report.replace("236", "0")) == []
+    assert "remark" not in Bu._strip_remarks(report + "\nother line")

@@ -7,9 +7,16 @@ objects are linked into ``w8a8_gemm_rl_amd/libqurl_w8a8.so``. The library is
 rebuilt from scratch on every call. Flags: correctly rounded fp32 division and
 IEEE denormals are hipcc's defaults and must stay so (the quantized codes
 depend on them); packed-fp32 instruction selection is switched off.
+
+The compiler's per-kernel resource report is read back, and the build fails
+if any kernel keeps registers in scratch memory: every kernel here is sized
+to fit its register budget, and a spill (for instance from a change that
+keeps more values live across a GEMM's K loop) silently costs a large part
+of its speed.
 """
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -48,13 +55,47 @@ def _run(cmd):
     return out
 
 
+def _spills(report):
+    """(kernel, scratch bytes per lane) for every kernel of a resource report
+    that uses scratch; the report's other remarks are dropped."""
+    bad, name = [], None
+    for line in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            bad.append((name, int(m.group(1))))
+    return bad
+
+
+def _strip_remarks(out):
+    keep, skip = [], False
+    for line in out.splitlines():
+        if "-Rpass-analysis=kernel-resource-usage" in line:
+            skip = True  # the remark's source excerpt follows
+            continue
+        if skip and (line.startswith(" ") or not line.strip()):
+            continue
+        skip = False
+        keep.append(line)
+    return "\n".join(keep)
+
+
 def build(verbose=True, jobs=None):
     os.makedirs(BUILD, exist_ok=True)
     objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
 
     def compile_one(i):
         src = os.path.join(CSRC, SOURCES[i])
-        return _run([HIPCC, *CFLAGS, *EXTRA.get(SOURCES[i], []), "-c", src, "-o", objs[i]])
+        out = _run([HIPCC, *CFLAGS, *EXTRA.get(SOURCES[i], []), "-Rpass-analysis=kernel-resource-usage",
+                    "-c", src, "-o", objs[i]])
+        bad = _spills(out)
+        if bad:
+            raise RuntimeError(f"{SOURCES[i]}: kernels spill registers to scratch memory: "
+                               + ", ".join(f"{n} ({b} bytes per lane)" for n, b in bad))
+        return _strip_remarks(out)
 
     jobs = jobs or min(len(SOURCES), 8)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
