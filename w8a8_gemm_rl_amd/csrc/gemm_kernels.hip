@@ -253,54 +253,65 @@ __device__ __forceinline__ void store_tile(const KParams& p, const acc_t (&acc)[
 }
 
 // bf16 epilogue staged through LDS: every lane converts its groups of four
-// outputs and writes them (8 bytes) to a [BM][LDT] bf16 tile, then the block
+// outputs and writes them (8 bytes) to a [CH][LDT] bf16 tile, then the block
 // stores the owned rows of each token as 16-byte pieces (the N tail one by
-// one). Requires ldy % 8 == 0 and no split (checked by the caller); the
-// tile's first output column tn * rn is a multiple of 8 and Y is 16-byte
-// aligned, so every full piece is an aligned 16-byte store.
-template <int QT, int T, int BN, int BM, int WN, int WM, int LDT, typename acc_t, int FN, int FM>
+// one); tiles whose tokens do not all fit the LDS go in chunks of CH tokens
+// (a multiple of the wave tile's tokens, so each wave writes in one chunk).
+// Requires ldy % 8 == 0 and no split (checked by the caller); the tile's
+// first output column tn * rn is a multiple of 8 and Y is 16-byte aligned,
+// so every full piece is an aligned 16-byte store.
+template <int QT, int T, int BN, int BM, int WN, int WM, int LDT, int CH, typename acc_t, int FN,
+          int FM>
 __device__ __forceinline__ void store_tile_staged(
     const KParams& p, const acc_t (&acc)[FN][FM],
     const EpiScales<FN, FM, Mfma<QT, T>::NACC / 4>& sc, uint8_t* smem, int tn, int tm, int wn,
     int wm, int lane, int tid) {
   constexpr int NG = Mfma<QT, T>::NACC / 4;
   constexpr int NT = 64 * WN * WM;
+  constexpr int WTM = BM / WM;
   static_assert((LDT * 2) % 8 == 0, "8-byte aligned staged rows");
+  static_assert(CH % WTM == 0 && CH >= WTM && CH <= BM, "chunks of whole wave tiles");
   uint16_t* so = reinterpret_cast<uint16_t*>(smem);
-  __syncthreads();  // every wave is done reading the operand ring
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int ml = wm * (BM / WM) + j * T + lane % T;  // token within the tile
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const int nl = epi_nloc<T, BN, WN>(wn, i, g, lane);
-        uint32_t bb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          bb[e] = epi_bf16((float)acc[i][j][4 * g + e], sc.sx[j], sc.sw[i][g][e]);
-        *reinterpret_cast<uint2*>(so + ml * LDT + nl) =
-            make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
-      }
-    }
-  __syncthreads();
   const int64_t N = p.N, M = p.M;
   const int64_t n0 = (int64_t)tn * p.rn;
   const int own = (int)((N - n0) < p.rn ? (N - n0) : p.rn);  // owned output columns
   const int mv = (int)((M - (int64_t)tm * BM) < BM ? (M - (int64_t)tm * BM) : BM);
   const int cpt = (own + 7) / 8;  // 16-byte pieces per token row
   uint16_t* Y = static_cast<uint16_t*>(p.Y) + ((int64_t)tm * BM) * p.ldy + n0;
-  for (int c = tid; c < mv * cpt; c += NT) {
-    const int ml = c / cpt, nl = 8 * (c - (c / cpt) * cpt);
-    const uint16_t* src = so + ml * LDT + nl;
-    uint16_t* dst = Y + (int64_t)ml * p.ldy + nl;
-    if (nl + 8 <= own) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(src);
-      const uint2 hi = *reinterpret_cast<const uint2*>(src + 4);
-      *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    } else {
-      for (int e = 0; nl + e < own; ++e) dst[e] = src[e];
+#pragma unroll
+  for (int c0 = 0; c0 < BM; c0 += CH) {
+    __syncthreads();  // the operand ring (first chunk) or the last chunk is no longer read
+    if (wm * WTM >= c0 && wm * WTM < c0 + CH) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const int ml = wm * WTM + j * T + lane % T - c0;  // token within the chunk
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const int nl = epi_nloc<T, BN, WN>(wn, i, g, lane);
+            uint32_t bb[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              bb[e] = epi_bf16((float)acc[i][j][4 * g + e], sc.sx[j], sc.sw[i][g][e]);
+            *reinterpret_cast<uint2*>(so + ml * LDT + nl) =
+                make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
+          }
+        }
+    }
+    __syncthreads();
+    const int cm = (mv - c0) < CH ? (mv - c0) : CH;  // valid tokens of the chunk
+    for (int c = tid; c < cm * cpt; c += NT) {
+      const int ml = c / cpt, nl = 8 * (c - (c / cpt) * cpt);
+      const uint16_t* src = so + ml * LDT + nl;
+      uint16_t* dst = Y + (int64_t)(c0 + ml) * p.ldy + nl;
+      if (nl + 8 <= own) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(src);
+        const uint2 hi = *reinterpret_cast<const uint2*>(src + 4);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      } else {
+        for (int e = 0; nl + e < own; ++e) dst[e] = src[e];
+      }
     }
   }
 }
@@ -633,9 +644,12 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
   // into each of 32 rows. Split partial sums, raw accumulators and row
   // strides that are not a multiple of 8 take the direct path.
   constexpr int LDT = BN + 4;  // staged row stride in bf16 (8 bytes of padding)
-  if constexpr (BM * LDT * 2 <= S * STAGE) {
+  constexpr int CHF = (S * STAGE) / (LDT * 2);      // tokens that fit the ring
+  constexpr int CH0 = CHF >= BM ? BM : CHF / WTM * WTM;  // chunk: whole wave tiles
+  if constexpr (CH0 >= WTM) {
     if (p.splitk == 1 && !p.out_raw && (p.ldy & 7) == 0) {
-      store_tile_staged<QT, T, BN, BM, WN, WM, LDT>(p, acc, sc, smem, tn, tm, wn, wm, lane, tid);
+      store_tile_staged<QT, T, BN, BM, WN, WM, LDT, CH0>(p, acc, sc, smem, tn, tm, wn, wm, lane,
+                                                          tid);
       return;
     }
   }
