@@ -705,7 +705,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        log(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}, "
+        log(f"bench.py: this library runs on one GPU only (got --gpus {args.gpus}, "
             f"WORLD_SIZE {world}); the path has no multi-GPU mode")
         sys.exit(2)
 
