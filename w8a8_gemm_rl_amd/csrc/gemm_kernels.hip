@@ -790,8 +790,11 @@ __global__ __launch_bounds__(64 * WPB, 1) void gemm_direct_kernel(const KParams 
 }
 
 // Split-K second pass: Y[m, n] = epilogue(sum_{z = 0..S-1} part[z][m][n]),
-// summed in split order. One thread per four consecutive n of one m.
-template <int QT>
+// summed in split order. One thread per four consecutive n of one m. With the
+// split count SC known at compile time (2..8, every count the planner makes)
+// the partials are loaded together before they are added; SC = 0 takes S at
+// run time and loads one split after another.
+template <int QT, int SC>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __restrict__ part, int S,
                                                             int64_t M, int64_t N,
                                                             const float* __restrict__ sx,
@@ -806,19 +809,42 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
   const bool v4 = (N % 4 == 0);
   int32_t si[4] = {0, 0, 0, 0};
   float sf[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int zz = 0; zz < S; ++zz) {
-    const uint32_t* src = part + (int64_t)zz * M * N + m * N + n0;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (v4) {
-      const uint4 u = *reinterpret_cast<const uint4*>(src);
-      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
-    } else {
-      for (int e = 0; e < cnt; ++e) w[e] = src[e];
-    }
+  auto add = [&](const uint32_t (&w)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if constexpr (QT == kQInt8) si[e] += (int32_t)w[e];
       else sf[e] += __uint_as_float(w[e]);
+    }
+  };
+  auto load = [&](int zz, uint32_t (&w)[4]) {
+    const uint32_t* src = part + (int64_t)zz * M * N + m * N + n0;
+    if (v4) {
+      const uint4 u = *reinterpret_cast<const uint4*>(src);
+      w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    } else {
+      w[0] = w[1] = w[2] = w[3] = 0u;
+      for (int e = 0; e < cnt; ++e) w[e] = src[e];
+    }
+  };
+  if constexpr (SC > 0) {
+    uint32_t w[SC][4];
+    if (v4) {
+#pragma unroll
+      for (int q = 0; q < SC; ++q) {
+        const uint4 u = *reinterpret_cast<const uint4*>(part + (int64_t)q * M * N + m * N + n0);
+        w[q][0] = u.x; w[q][1] = u.y; w[q][2] = u.z; w[q][3] = u.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < SC; ++q) load(q, w[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < SC; ++q) add(w[q]);
+  } else {
+    for (int zz = 0; zz < S; ++zz) {
+      uint32_t w[4];
+      load(zz, w);
+      add(w);
     }
   }
   const bool full4 = vec && cnt == 4;
@@ -923,14 +949,26 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   const int64_t work = a.M * ((a.N + 3) / 4);
   const unsigned rgrid = (unsigned)((work + 255) / 256);
   const int vec = (a.ldy % 4) == 0;
-  if (qt == kQInt8)
-    hipLaunchKernelGGL(splitk_reduce_kernel<kQInt8>, dim3(rgrid), dim3(256), 0, st,
+  auto reduce = [&](auto qt_c, auto sc_c) {
+    constexpr int Q = decltype(qt_c)::value, SC = decltype(sc_c)::value;
+    hipLaunchKernelGGL((splitk_reduce_kernel<Q, SC>), dim3(rgrid), dim3(256), 0, st,
                        static_cast<const uint32_t*>(a.part), plan.splitk, a.M, a.N, a.sx, a.sw,
                        a.Y, a.ldy, a.out_raw, vec);
-  else
-    hipLaunchKernelGGL(splitk_reduce_kernel<kQFp8>, dim3(rgrid), dim3(256), 0, st,
-                       static_cast<const uint32_t*>(a.part), plan.splitk, a.M, a.N, a.sx, a.sw,
-                       a.Y, a.ldy, a.out_raw, vec);
+  };
+  auto by_splits = [&](auto qt_c) {
+    switch (plan.splitk) {
+      case 2: reduce(qt_c, std::integral_constant<int, 2>{}); break;
+      case 3: reduce(qt_c, std::integral_constant<int, 3>{}); break;
+      case 4: reduce(qt_c, std::integral_constant<int, 4>{}); break;
+      case 5: reduce(qt_c, std::integral_constant<int, 5>{}); break;
+      case 6: reduce(qt_c, std::integral_constant<int, 6>{}); break;
+      case 7: reduce(qt_c, std::integral_constant<int, 7>{}); break;
+      case 8: reduce(qt_c, std::integral_constant<int, 8>{}); break;
+      default: reduce(qt_c, std::integral_constant<int, 0>{}); break;
+    }
+  };
+  if (qt == kQInt8) by_splits(std::integral_constant<int, kQInt8>{});
+  else by_splits(std::integral_constant<int, kQFp8>{});
   return hipGetLastError();
 }
 
