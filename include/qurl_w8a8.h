@@ -223,8 +223,9 @@ int qr_silu_mul_quant(const void* G, const void* U, int64_t M, int64_t N, int64_
  *   loss[t] = -w term;  grad[t] = d loss[t] / d logp[t] = -w R A where the
  *   unclipped branch is the minimum, else 0. Masked tokens: 0, not counted.
  *   sums = {sum of loss over valid tokens, valid tokens, clipped valid tokens}
- *   (float64, from per-block partials added in index order: the same bits on
- *   every run). The mean loss is sums[0] / sums[1].
+ *   (float64, from per-block partials added in a fixed order, strided runs
+ *   then a pairwise tree: the same bits on every run). The mean loss is
+ *   sums[0] / sums[1].
  *
  *   logp, logp_prox, logp_behav, adv  [n] fp32, 16-byte aligned (read).
  *   mask     [n] uint8, nonzero = response token; 4-byte aligned (read).

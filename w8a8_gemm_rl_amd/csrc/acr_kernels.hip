@@ -97,27 +97,49 @@ __global__ __launch_bounds__(kNT) void acr_tis_kernel(
   }
 }
 
-// Adds the per-block slots in index order: out = {loss sum, valid, clipped}.
+// Adds the per-block slots: out = {loss sum, valid, clipped}. Thread i adds
+// slots i, i + kNT, ... in order (eight slots' loads issued together before
+// they are added), then the kNT partial sums are combined by a fixed
+// pairwise tree (strides kNT/2, ..., 1), so the result is the same bits on
+// every run.
 __global__ __launch_bounds__(kNT) void acr_sum_kernel(const double* __restrict__ part,
                                                       int64_t blocks, double* __restrict__ out) {
   __shared__ double red[3][kNT];
+  constexpr int U = 8;
   double v[3] = {0.0, 0.0, 0.0};
-  // Thread i adds slots i, i + kNT, ... in order; then the threads' sums are
-  // added in thread order by thread 0..2.
-  for (int64_t b = threadIdx.x; b < blocks; b += kNT) {
-    v[0] += part[3 * b];
-    v[1] += part[3 * b + 1];
-    v[2] += part[3 * b + 2];
+  for (int64_t b0 = threadIdx.x; b0 < blocks; b0 += (int64_t)U * kNT) {
+    double w[U][3];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t b = b0 + (int64_t)u * kNT;
+      const int64_t bb = b < blocks ? b : blocks - 1;  // in range; dropped below
+      w[u][0] = part[3 * bb];
+      w[u][1] = part[3 * bb + 1];
+      w[u][2] = part[3 * bb + 2];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (b0 + (int64_t)u * kNT < blocks) {
+        v[0] += w[u][0];
+        v[1] += w[u][1];
+        v[2] += w[u][2];
+      }
+    }
   }
   red[0][threadIdx.x] = v[0];
   red[1][threadIdx.x] = v[1];
   red[2][threadIdx.x] = v[2];
   __syncthreads();
-  if (threadIdx.x < 3) {
-    double s = 0.0;
-    for (int i = 0; i < kNT; ++i) s += red[threadIdx.x][i];
-    out[threadIdx.x] = s;
+#pragma unroll
+  for (int h = kNT / 2; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + h];
+      red[1][threadIdx.x] += red[1][threadIdx.x + h];
+      red[2][threadIdx.x] += red[2][threadIdx.x + h];
+    }
+    __syncthreads();
   }
+  if (threadIdx.x < 3) out[threadIdx.x] = red[threadIdx.x][0];
 }
 
 }  // namespace
