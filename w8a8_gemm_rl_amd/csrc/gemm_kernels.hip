@@ -894,7 +894,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
   X(2, 4, 16, 128, 16, 8, 1)  /* 12: direct, M <= 16                  */ \
   X(2, 2, 16, 128, 32, 4, 1)  /* 13: direct, M <= 32                  */ \
   X(0, 4, 32, 192, 128, 2, 4) /* 14: wide 256-token layers, 8 waves   */ \
-  X(1, 4, 32, 192, 128, 2, 4) /* 15: interleaved variant of tile 14   */
+  X(1, 4, 32, 192, 128, 2, 4) /* 15: interleaved variant of tile 14   */ \
+  X(0, 4, 16, 80, 64, 5, 1)   /* 16: 256-token INT8 QKV, 5 waves      */
 
 #define QR_STR(x) #x
 #define QR_DESC(KIND, S, T, BN, BM, WN, WM)                                        \
