@@ -8,14 +8,17 @@ in seconds:
   in FP8 at M = 512: 512 sampled output channels per matrix. A channel's codes
   and scale depend only on its own weight row, and its outputs only on those
   and the activations, so the oracle quantizes just the sampled rows.
-* 32B-shaped batched decode layer (seven linears), INT8, M = 512, and 32B
+* 32B-shaped batched decode layer (seven linears, or five with q, k and v
+  stacked into one projection; the stacked one also in FP8 on sampled
+  channels), INT8, M = 512, and 32B
   prefill, INT8, M = 4096 (heavy-tailed channels): the device chain runs at
   full size; sampled tokens are computed by the oracle chain from the same
   input rows (quantization is per token, so a token's outputs depend only on
   its own row) and compared bit for bit. INT8 weight codes and scales are
   compared in full.
-* Per-RL-step weight refresh of the 7B-shaped stacked gate+up and down
-  matrices after one update of the pages' size: codes, scales and the flip
+* Per-RL-step weight refresh of the 7B-shaped O, stacked gate+up and down
+  matrices, and of the 32B-shaped O and down (both row lengths of each
+  stack), after one update of the pages' size: codes, scales and the flip
   count against the oracle in full, and the count against the closed-form
   first-order expectation.
 """
@@ -120,6 +123,12 @@ def test_32b_decode_chain_int8_m512_sampled_tokens():
     _int8_chain("32b", 5, I.CHAIN_32B, I.LINEARS_32B, I.W_SIGMA_32B, 512, "normal", 128)
 
 
+def test_32b_decode_chain_int8_m512_stacked_qkv_sampled_tokens():
+    # q, k and v stacked into one 7168x5120 projection over the shared
+    # quantized input (the stacked-QKV decode workload), 512 tokens.
+    _int8_chain("32b", 5, I.CHAIN_32B_PREFILL, I.LINEARS_32B, I.W_SIGMA_32B, 512, "normal", 64)
+
+
 def test_32b_prefill_int8_m4096_sampled_tokens():
     _int8_chain("32b", 5, I.CHAIN_32B_PREFILL, I.LINEARS_32B, I.W_SIGMA_32B, 4096, "heavy", 96)
 
@@ -157,23 +166,22 @@ def test_7b_linears_fp8_sampled_channels(name):
         _fp8_linear_sampled("7b", 3, name, N, K, I.W_SIGMA_7B, M, "outliers")
 
 
-@pytest.mark.parametrize("name", ["q", "k", "v", "o", "gate", "up", "down"])
+@pytest.mark.parametrize("name", ["qkv", "q", "k", "v", "o", "gate", "up", "down"])
 def test_32b_linears_fp8_m512_sampled_channels(name):
     N, K = I.LINEARS_32B[name]
     _fp8_linear_sampled("32b", 5, name, N, K, I.W_SIGMA_32B, 512, "normal")
 
 
-@pytest.mark.parametrize("qt", ["int8", "fp8"])
-@pytest.mark.parametrize("name", ["o", "gateup", "down"])
-def test_7b_refresh_full_size(qt, name):
-    """Refresh after W' += s * dW, dW ~ N(0, 1e-7^2), at the stack's matrix
-    sizes, in the launch the refresh benchmark uses. The closed-form check is
-    made on O and down (the two row lengths of the stack; skipped on gate+up
-    to keep the test within seconds)."""
-    N, K = I.LINEARS_7B[name]
+def _refresh_full_size(qt, name, linears, sigma, idx):
+    """Refresh after W' += s * dW, dW ~ N(0, 1e-7^2), at one of the stack's
+    matrix sizes, in the launch the refresh benchmark uses (the kernel is
+    chosen by row length). The closed-form check is made on O and down (the
+    two row lengths of each stack; skipped on gate+up to keep the test within
+    seconds)."""
+    N, K = linears[name]
     s32 = np.float32(I.UAQ_S)
-    seed = I.matrix_seed(7, _NAMES.index("gate" if name == "gateup" else name))
-    Wp0 = (I.weights(N, K, I.W_SIGMA_7B, seed=seed) / s32).astype(np.float32)
+    seed = I.matrix_seed(idx, _NAMES.index("gate" if name == "gateup" else name))
+    Wp0 = (I.weights(N, K, sigma, seed=seed) / s32).astype(np.float32)
     Wp1 = I.normal_f32((N, K), I.DW_SIGMA, seed=seed + 1)
     Wp1 *= s32
     Wp1 += Wp0
@@ -194,3 +202,16 @@ def test_7b_refresh_full_size(qt, name):
         total = int(f1.sum())
         e = O.flip_expectation(Wp0, I.DW_SIGMA * I.UAQ_S, qt)
         assert abs(total - e) <= 5 * np.sqrt(e) + 0.02 * e, (total, e)
+
+
+@pytest.mark.parametrize("qt", ["int8", "fp8"])
+@pytest.mark.parametrize("name", ["o", "gateup", "down"])
+def test_7b_refresh_full_size(qt, name):
+    _refresh_full_size(qt, name, I.LINEARS_7B, I.W_SIGMA_7B, 7)
+
+
+@pytest.mark.parametrize("qt,name", [("int8", "o"), ("int8", "down"), ("fp8", "o")])
+def test_32b_refresh_full_size(qt, name):
+    # Row lengths 5120 (q/k/v, O, gate, up) and 27648 (down): the two
+    # launches of the 32B-shaped stack's refresh.
+    _refresh_full_size(qt, name, I.LINEARS_32B, I.W_SIGMA_32B, 8)
