@@ -231,3 +231,39 @@ def test_linear_matches_torch_pipeline_int8():
     sx = sc * 1.5
     y = (acc.double().float() * sx[:, None]) * torch.from_numpy(wq["scale_w"])[None, :]
     assert np.array_equal(y.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16), r["y"])
+
+
+def _torch_linear_int8(x_bits, Wq, scale_w, act_mult):
+    """Per-token INT8 linear with torch CPU ops (as above); bf16 bits out."""
+    tx = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).float()
+    sc = tx.abs().amax(dim=1) / 127.0
+    q = torch.round(tx / sc[:, None]).clamp(-127, 127).to(torch.int8)
+    acc = torch._int_mm(q, torch.from_numpy(Wq).t().contiguous())
+    y = (acc.double().float() * (sc * act_mult)[:, None]) * torch.from_numpy(scale_w)[None, :]
+    return y.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_decode_chain_wiring_matches_torch_pipeline():
+    """A chain whose linears read the layer input, an earlier output and a
+    column slice of one: every output equals the torch pipeline fed the same
+    way, so a wrong source or slice fails. Token count and sizes are
+    multiples of 8 (torch's int matmul needs them)."""
+    M = 16
+    x0 = I.activations(M, 32, seed=3, kind="outliers")
+    spec = [("a", "x0", None, 48, 32), ("b", "a", (8, 32), 24, 24), ("c", "a", None, 16, 48),
+            ("d", "b", None, 40, 24)]
+    layers, ref = [], {}
+    for i, (name, src, cols, N, K) in enumerate(spec):
+        wq = O.quantize_weights_uaq(I.weights(N, K, 0.05, seed=10 + i), 1.5, "int8")
+        layers.append(dict(name=name, src=src, cols=cols, Wq=wq["Wq"], scale_w=wq["scale_w"],
+                           act_mult=1.5))
+        inp = x0 if src == "x0" else ref[src]
+        if cols is not None:
+            inp = inp[:, cols[0]:cols[1]]
+        ref[name] = _torch_linear_int8(inp, wq["Wq"], wq["scale_w"], 1.5)
+    got = O.decode_chain(x0, layers, "int8")
+    for name in ref:
+        assert np.array_equal(got[name]["y"], ref[name]), name
+    # the slice matters: feeding b the whole of a's first 24 columns differs
+    alt = _torch_linear_int8(ref["a"][:, :24], layers[1]["Wq"], layers[1]["scale_w"], 1.5)
+    assert not np.array_equal(alt, ref["b"])
