@@ -199,6 +199,68 @@ struct MxMfma<32> {
   }
 };
 
+// bf16 outputs staged through LDS: every lane converts its groups of four
+// outputs (four consecutive channels of one token) and writes them, 8 bytes,
+// to a [CH][LDT] bf16 tile; then the block stores the owned channels of each
+// token as 16-byte pieces (the N tail one by one). Tiles whose tokens do not
+// all fit the LDS go in chunks of CH tokens, a multiple of the wave tile's.
+// Requires ldy % 8 == 0; the tile's first channel tn * rn is a multiple of 8
+// and Y is 16-byte aligned (both checked by the host), so every full piece is
+// an aligned 16-byte store.
+template <int T, int BN, int BM, int WN, int WM, int LDT, int CH, typename acc_t, int FN, int FM>
+__device__ __forceinline__ void mx_store_staged(const MxDmaParams& p, const acc_t (&acc)[FN][FM],
+                                                uint8_t* smem, int tn, int tm, int wn, int wm,
+                                                int lane, int tid) {
+  constexpr int NT = 64 * WN * WM;
+  constexpr int WTN = BN / WN, WTM = BM / WM;
+  constexpr int NR = T == 16 ? 4 : 16;
+  static_assert((LDT * 2) % 8 == 0, "8-byte aligned staged rows");
+  static_assert(CH % WTM == 0 && CH >= WTM && CH <= BM, "chunks of whole wave tiles");
+  uint16_t* so = reinterpret_cast<uint16_t*>(smem);
+  const int64_t N = p.N, M = p.M;
+  const int64_t n0 = (int64_t)tn * p.rn;
+  const int own = (int)((N - n0) < p.rn ? (N - n0) : p.rn);  // owned output channels
+  const int mv = (int)((M - (int64_t)tm * BM) < BM ? (M - (int64_t)tm * BM) : BM);
+  const int cpt = (own + 7) / 8;  // 16-byte pieces per token row
+  const int lr = lane % T, lg = lane / T;
+  uint16_t* Y = static_cast<uint16_t*>(p.Y) + ((int64_t)tm * BM) * p.ldy + n0;
+#pragma unroll
+  for (int c0 = 0; c0 < BM; c0 += CH) {
+    __syncthreads();  // the operand ring (first chunk) or the last chunk is no longer read
+    if (wm * WTM >= c0 && wm * WTM < c0 + CH) {
+#pragma unroll
+      for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          const int ml = wm * WTM + T * j + lr - c0;  // token within the chunk
+#pragma unroll
+          for (int q = 0; q < NR / 4; ++q) {
+            const int nl = wn * WTN + T * i + 8 * q + 4 * lg;  // local channel of register 4 q
+            uint32_t bb[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) bb[r] = f32_to_bf16_rne(acc[i][j][4 * q + r]);
+            *reinterpret_cast<uint2*>(so + ml * LDT + nl) =
+                make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
+          }
+        }
+    }
+    __syncthreads();
+    const int cm = (mv - c0) < CH ? (mv - c0) : CH;  // valid tokens of the chunk
+    for (int c = tid; c < cm * cpt; c += NT) {
+      const int ml = c / cpt, nl = 8 * (c - (c / cpt) * cpt);
+      const uint16_t* src = so + ml * LDT + nl;
+      uint16_t* dst = Y + (int64_t)(c0 + ml) * p.ldy + nl;
+      if (nl + 8 <= own) {
+        const uint2 lo = *reinterpret_cast<const uint2*>(src);
+        const uint2 hi = *reinterpret_cast<const uint2*>(src + 4);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      } else {
+        for (int e = 0; nl + e < own; ++e) dst[e] = src[e];
+      }
+    }
+  }
+}
+
 template <int T, int BN, int BM, int WN, int WM, int S>
 __global__ __launch_bounds__(64 * WN * WM, 1) void mx_dma_kernel(const MxDmaParams p) {
   using MF = MxMfma<T>;
@@ -359,6 +421,20 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void mx_dma_kernel(const MxDmaPara
     }
     cs = cs + 1 == S ? 0 : cs + 1;
     is = is + 1 == S ? 0 : is + 1;
+  }
+
+  // bf16 outputs go through the idle ring (every wave is past its last K
+  // step and every copy has landed) so each lane stores 16 contiguous bytes
+  // of a token's row; raw fp32 outputs and row strides that are not a
+  // multiple of 8 take the direct stores below.
+  constexpr int LDT = BN + 4;  // staged row stride in bf16 (8 bytes of padding)
+  constexpr int CHF = (S * STAGE) / (LDT * 2);           // tokens that fit the ring
+  constexpr int CH0 = CHF >= BM ? BM : CHF / WTM * WTM;  // chunk: whole wave tiles
+  if constexpr (CH0 >= WTM) {
+    if (!p.out_raw && (p.ldy & 7) == 0) {
+      mx_store_staged<T, BN, BM, WN, WM, LDT, CH0>(p, acc, smem, tn, tm, wn, wm, lane, tid);
+      return;
+    }
   }
 
   // Register r of lane l: weight row 8 (r / 4) + 4 (l / T) + r % 4 of the
