@@ -577,7 +577,8 @@ def run_mx(args, dev):
         "per_channel_fp8_us": round(pc_us, 2),
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": "GB/s" if bound == "hbm" else "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": None, "kernel": "mx_dma_kernel", "kernel_us": round(mx_us, 2),
+                     "traffic": committed_traffic(f"{args.workload}:mx:M{M}:N{N}:K{K}", "mx"),
+                     "kernel": "mx_dma_kernel", "kernel_us": round(mx_us, 2),
                      "alg_bytes_per_launch": alg, "alg_ops_per_launch": ops},
         "cpu_baseline": None,
     }
