@@ -21,6 +21,10 @@ in seconds:
   stack), after one update of the pages' size: codes, scales and the flip
   count against the oracle in full, and the count against the closed-form
   first-order expectation.
+* The update-masking experiment on the five 7B matrices, INT8 and FP8:
+  codes changed by one update without UAQ and under the three readings of
+  where it lands with UAQ, counted by the refresh kernel, equal to the
+  oracle's counts and within the closed form's band.
 """
 
 import numpy as np
@@ -215,3 +219,49 @@ def test_32b_refresh_full_size(qt, name):
     # Row lengths 5120 (q/k/v, O, gate, up) and 27648 (down): the two
     # launches of the 32B-shaped stack's refresh.
     _refresh_full_size(qt, name, I.LINEARS_32B, I.W_SIGMA_32B, 8)
+
+
+@pytest.mark.parametrize("qt", ["int8", "fp8"])
+@pytest.mark.parametrize("name", ["qkv", "o", "gate", "up", "down"])
+def test_7b_uaq_flip_readings(qt, name):
+    """The update-masking experiment at the 7B matrix sizes, counted by the
+    library's refresh kernel: codes changed by one update dW ~ N(0, 1e-7^2)
+    without UAQ (base) and with it under the three readings of where the
+    update lands (same size on W/s, the pages' s dW, and the control dW/s).
+    Every count equals the oracle's, and each lies within 5 sqrt(E) + 2% E of
+    the closed-form expectation E (first order in the update)."""
+    N, K = I.LINEARS_7B[name]
+    s32 = np.float32(I.UAQ_S)
+    seed = I.matrix_seed(11, _NAMES.index(name))
+    W = I.weights(N, K, I.W_SIGMA_7B, seed=seed)
+    dW = I.normal_f32((N, K), I.DW_SIGMA, seed=seed + 1)
+    Ws = (W / s32).astype(np.float32)
+    cases = {
+        "base": (W, (W + dW).astype(np.float32), I.DW_SIGMA),
+        "uaq_same": (Ws, (Ws + dW).astype(np.float32), I.DW_SIGMA),
+        "uaq_pages": (Ws, (Ws + (dW * s32).astype(np.float32)).astype(np.float32),
+                      I.DW_SIGMA * I.UAQ_S),
+        "control": (Ws, (Ws + (dW / s32).astype(np.float32)).astype(np.float32),
+                    I.DW_SIGMA / I.UAQ_S),
+    }
+    rf = torch.empty(N, dtype=torch.int32, device="cuda:0")
+    ref_codes = {}
+    got = {}
+    for k, (A0, A1, _) in cases.items():
+        key = "W" if A0 is W else "Ws"
+        if key not in ref_codes:
+            ref_codes[key], _ = B.requantize_weights(
+                to_dev_f32(A0), qt, torch.empty((N, K), dtype=B.code_dtype(qt), device="cuda:0"))
+        Wq = ref_codes[key].clone()
+        B.requantize_weights(to_dev_f32(A1), qt, Wq, row_flips=rf)
+        got[k] = int(rf.sum().item())
+        del Wq
+    del ref_codes
+    torch.cuda.synchronize()
+    ref = O.flip_counts(W, dW, I.UAQ_S, qt)
+    for k, (A0, _, sigma) in cases.items():
+        assert got[k] == ref[k], (k, got[k], ref[k])
+        e = O.flip_expectation(A0, sigma, qt)
+        assert abs(got[k] - e) <= 5 * np.sqrt(e) + 0.02 * e, (k, got[k], e)
+    assert got["base"] < got["uaq_same"] < got["uaq_pages"]
+    print(f"{qt} {name} {N}x{K}: " + ", ".join(f"{k} {v}" for k, v in got.items()))
