@@ -53,6 +53,9 @@ WORKLOADS = {
     "32b_decode_int8_qkv": dict(M=512, qt="int8", chain="32b_qkv", sets=2, kind="normal"),
     "32b_decode_fp8_qkv": dict(M=512, qt="fp8", chain="32b_qkv", sets=2, kind="normal"),
     "32b_prefill_int8": dict(M=4096, qt="int8", chain="32b_prefill", sets=2, kind="heavy"),
+    # one small linear (X[16, 512] x W[512, 512], INT8): launch-bound, timed for
+    # its latency, with no roofline claim behind its fraction
+    "single_int8_16x512x512": dict(M=16, qt="int8", chain="single", sets=4, kind="normal"),
 }
 
 
@@ -92,6 +95,8 @@ def chain_spec(name):
         return I.CHAIN_32B, I.LINEARS_32B, I.W_SIGMA_32B
     if name in ("32b_prefill", "32b_qkv"):
         return I.CHAIN_32B_PREFILL, I.LINEARS_32B, I.W_SIGMA_32B
+    if name == "single":
+        return I.CHAIN_SINGLE, I.LINEARS_SINGLE, I.SINGLE["w_sigma"]
     raise ValueError(name)
 
 

@@ -19,6 +19,8 @@ UAQ_S = 1.5  # paper notes, "Loss / training strategy"
 
 # A single linear: X[16, 512] bf16 ~ N(0, 1), W[512, 512] fp32 ~ N(0, 0.02).
 SINGLE = dict(M=16, N=512, K=512, qt="int8", s=UAQ_S, seed=0, w_sigma=0.02)
+LINEARS_SINGLE = {"linear": (SINGLE["N"], SINGLE["K"])}
+CHAIN_SINGLE = [dict(name="linear", src="x0", cols=None)]
 
 # 7B-shaped decoder linears (hidden 3584, intermediate 18944, QKV 4608).
 LINEARS_7B = {
