@@ -94,10 +94,13 @@ def test_mx_gemm_7b_gate_sampled_channels(M):
     assert np.all(np.abs(a - acc) <= bound + 1e-30)
 
 
-@pytest.mark.parametrize("M,N,K,pad", [(40, 130, 256, 6), (9, 64, 384, 1)])
+@pytest.mark.parametrize("M,N,K,pad", [(40, 130, 256, 6), (9, 130, 384, 6), (9, 64, 384, 1)])
 def test_mx_gemm_strided_output(M, N, K, pad):
-    """Y with a row stride that is not a multiple of 4 elements (outputs stored one by one)
-    and ragged N: the same values as into a packed Y, and the padding left untouched."""
+    """Y with padded rows and ragged N, on both tile shapes (up to 32 tokens and above): a
+    stride that is a multiple of 8 elements (bf16 staged through LDS into 16-byte stores,
+    the last piece of a row partial) or one that is not a multiple of 4 (outputs stored one
+    by one). The same values as into a packed Y of stride N = 130 or 64 (the other store
+    path), and the padding left untouched."""
     (xc, xe, wc, we), (dxc, dxs, dwc, dws) = _mx_operands(M, N, K, seed=M + N + pad)
     for out, dt in (("bf16", torch.bfloat16), ("raw", torch.float32)):
         big = torch.full((M, N + pad), -7.0, dtype=dt, device=DEV)
