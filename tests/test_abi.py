@@ -173,3 +173,36 @@ def test_build_rejects_register_spills():
     assert Bu._spills(report) == [("_Z5spillv", 236)]
     assert Bu._spills(report.replace("236", "0")) == []
     assert "remark" not in Bu._strip_remarks(report + "\nother line")
+
+
+def test_gemm_planner_invariants(B):
+    """The planner (pure host code) over the workloads' shapes and ragged ones, at
+    decode and prefill token counts, INT8 and FP8: a tile of the table, rows a
+    multiple of 8 no higher than the tile, at least one K step per split, a
+    split only while the grid fits one round of the 256 CUs, and a workspace
+    that holds the split's partial sums."""
+    from w8a8_gemm_rl_amd import inputs as I
+
+    L = _L(B)
+    heights = {}
+    for t in range(B.num_tiles()):
+        m = re.search(r"_n(\d+)_m(\d+)_", B.tile_name(t))
+        heights[t] = (int(m.group(1)), int(m.group(2)))
+    shapes = set(I.LINEARS_7B.values()) | set(I.LINEARS_32B.values())
+    shapes |= {(512, 512), (37, 48), (300, 1040), (4104, 3600), (8, 16), (130, 27664)}
+    B.set_plan_override(-1)
+    for N, K in sorted(shapes):
+        nks = (K + 127) // 128
+        for M in (1, 7, 16, 32, 33, 64, 100, 256, 512, 1000, 4096):
+            for qt, code in (("int8", I8), ("fp8", 1)):
+                t, s, r = B.gemm_plan(M, N, K, qt)
+                assert (t, s, r) == B.gemm_plan(M, N, K, qt)
+                BN, BM = heights[t]
+                assert 8 <= r <= BN and r % 8 == 0, (M, N, K, qt, t, r)
+                assert 1 <= s <= nks, (M, N, K, qt, s)
+                blocks = -(-N // r) * -(-M // BM) * s
+                assert s == 1 or blocks <= 256, (M, N, K, qt, t, s, r, blocks)
+                ws = L.qr_workspace_size(b"qr_w8a8_gemm", M, N, K, code)
+                assert ws != ctypes.c_size_t(-1).value
+                if s > 1:
+                    assert ws >= s * M * N * 4, (M, N, K, qt, s, ws)

@@ -79,7 +79,10 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
     if (d.BM > 64 && (M > 1024 || d.BN > 128)) return d.BN;
     const int64_t base = ((N + d.BN - 1) / d.BN) * p.tiles_m * splits;
     const int64_t per = kCUs * ((base + kCUs - 1) / kCUs);  // blocks wanted
-    const int64_t want = 8 * ((N * p.tiles_m * splits + 8 * per - 1) / (8 * per));
+    // The fewest rows (a multiple of 8) whose tiles along N, rounded up,
+    // fit: at most per / (tiles_m * splits) of them.
+    const int64_t tn = per / (p.tiles_m * splits);
+    const int64_t want = 8 * ((N + 8 * tn - 1) / (8 * tn));
     return (want >= d.BN / 2 && want < d.BN) ? want : d.BN;
   };
   int64_t s = 1;
