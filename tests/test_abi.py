@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -190,10 +191,13 @@ def test_gemm_planner_invariants(B):
         heights[t] = (int(m.group(1)), int(m.group(2)))
     shapes = set(I.LINEARS_7B.values()) | set(I.LINEARS_32B.values())
     shapes |= {(512, 512), (37, 48), (300, 1040), (4104, 3600), (8, 16), (130, 27664)}
+    rng = np.random.default_rng(1)
+    shapes |= {(int(n), 16 * int(k)) for n, k in zip(rng.integers(8, 40000, 40),
+                                                     rng.integers(1, 2000, 40))}
     B.set_plan_override(-1)
     for N, K in sorted(shapes):
         nks = (K + 127) // 128
-        for M in (1, 7, 16, 32, 33, 64, 100, 256, 512, 1000, 4096):
+        for M in (1, 7, 16, 32, 33, 64, 100, 256, 384, 512, 768, 1000, 4096):
             for qt, code in (("int8", I8), ("fp8", 1)):
                 t, s, r = B.gemm_plan(M, N, K, qt)
                 assert (t, s, r) == B.gemm_plan(M, N, K, qt)
@@ -202,6 +206,9 @@ def test_gemm_planner_invariants(B):
                 assert 1 <= s <= nks, (M, N, K, qt, s)
                 blocks = -(-N // r) * -(-M // BM) * s
                 assert s == 1 or blocks <= 256, (M, N, K, qt, t, s, r, blocks)
+                # shrinking the rows never adds a round of blocks
+                full = -(-N // BN) * -(-M // BM) * s
+                assert -(-blocks // 256) <= -(-full // 256), (M, N, K, qt, t, s, r, blocks)
                 ws = L.qr_workspace_size(b"qr_w8a8_gemm", M, N, K, code)
                 assert ws != ctypes.c_size_t(-1).value
                 if s > 1:
