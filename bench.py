@@ -241,7 +241,7 @@ def committed_traffic(key, kind="gemm"):
 
 KERNEL_PATTERNS = {
     "mx": r"mx_dma_kernel",
-    "acr": r"acr_tis_kernel",
+    "acr": r"acr_(tis|sum)_kernel",  # one pass: the per-token kernel and the ordered sum
     "gemm": r"gemm_\w*kernel",  # the main GEMM kernels (any tile family), not the split-K reduction
     "refresh": r"weight_quant_kernel<[^>]*true>",  # the weight quantizer with flip counting
 }
@@ -671,7 +671,8 @@ def run_acr(args, dev):
         "roofline": {"bound": "hbm", "achieved": round(alg / (k_us * 1e-6) / 1e9, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(alg / (k_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "acr_tis_kernel + acr_sum_kernel",
+                     "traffic": committed_traffic(f"{args.workload}:acr:pass", "acr"),
+                     "kernel": "acr_tis_kernel + acr_sum_kernel",
                      "kernel_us": round(k_us, 2), "alg_bytes_per_launch": alg},
         "cpu_baseline": cpu,
         "mean_loss": float(sums[0] / max(sums[1], 1)), "clipped_frac": float(sums[2] / max(sums[1], 1)),
