@@ -43,12 +43,19 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
   } else if (M <= 128) {
     tile = 2;
   } else if (M <= 256) {
-    if (N >= 24576) tile = 5;
+    // Very wide layers: 128 x 256 tiles (every token in one block, so each
+    // weight byte is copied once) while they fit one round of the CUs, as
+    // for the 32B gate and up (27648 rows: 51 us against 76 us on 256 x 256
+    // tiles with split K); wider ones (the stacked 7B gate and up) 256 x 256.
+    if (N >= 24576) tile = (N + 127) / 128 <= kCUs ? 6 : 5;
     else if (N >= 8192) tile = 14;
     else if (nks >= 64) tile = 2;
-    else if (N >= 4096) tile = qt == kQInt8 ? 16 : 1;  // INT8: 80 x 64 tiles issue 20 copies per
-                                                     // K step where 128 x 64 ones issue 24
-                                                     // (7-8% faster on the 7B QKV)
+    else if (N >= 4096)
+      // INT8: 80 x 64 tiles issue 20 copies per K step where 128 x 64 ones
+      // issue 24 (7-8% faster on the 7B QKV), while their full-height grid
+      // fits one round; past it (the 32B stacked QKV, 7168 rows) the
+      // 128 x 64 tiles' single round wins (23.6 us against 36.3 us).
+      tile = qt == kQInt8 && ((N + 79) / 80) * ((M + 63) / 64) <= kCUs ? 16 : 1;
     else tile = qt == kQFp8 ? 8 : 0;  // FP8: 32x32 fragments 8% faster here
   } else if (M <= 1024) {
     if (N >= 16384) tile = 5;
