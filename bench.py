@@ -8,13 +8,21 @@ A "step" is one such layer pass over one batch; successive steps walk through
 distinct copies of the layer's weights (more bytes than the 256 MB Infinity
 Cache), like a decode pass walks a model's layers.
 
-The timed region is K steps between device synchronizations. Each step
-replays a HIP graph of the ops before the dominant GEMM, launches that GEMM
-directly between two stream events (its average duration feeds the roofline
-object), and replays a graph of the ops after it. Inputs are seeded synthetic
-tensors generated on the device. The roofline "traffic" (HBM bytes per
-launch) comes from the committed rocprofv3 counter summary in
+The timed region is K steps between device synchronizations. Each weight
+copy's whole step (quantizations and GEMMs) is captured as one HIP graph, and
+the K steps are K replays walking the copies (what a rollout engine that
+captures its decode step runs). The roofline object's kernel time comes from
+a second graph of 20 back-to-back launches of the dominant GEMM, replayed
+between events on its own stream, so no host launch gap is counted. Inputs
+are seeded synthetic tensors generated on the device. The roofline "traffic"
+(HBM bytes per launch) comes from the committed rocprofv3 counter summary in
 profiles/hbm_traffic.md and is null when the GEMM sources changed since.
+
+The default run adds, beside the 7B line: the peaks this GPU reaches (HBM
+read, dense INT8 / FP8 MFMA, the shader clock under MFMA load; every roofline
+object then also carries its fraction of the measured peak), the 32B-shaped
+decode layer at 512 tokens in INT8 and FP8, and the 32B prefill gate
+projection at 4096 tokens.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -281,18 +289,33 @@ def summarize_rocprof(paths, grid, kind="gemm"):
                       f"median {statistics.median(ds):.2f} us min {min(ds):.2f} us")
 
 
-def cpu_baseline(chain, shapes, M, qt, sigma, kind, s):
-    """Time the CPU oracle on one layer step of the same workload (host cores)."""
+def cpu_model():
+    """The host CPU's model name (first processor of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(chain, shapes, M, qt, sigma, kind, s, bytes_step, name):
+    """Time the CPU oracle on whole layer steps of the same workload on the
+    host's cores: about 10 s with every BLAS thread, then one step with one
+    thread."""
     import numpy as np
 
     import oracle as O
     from w8a8_gemm_rl_amd import inputs as I
 
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
 
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         threads = os.cpu_count()
     log("cpu baseline: preparing oracle weights ...")
     layers = []
@@ -313,7 +336,23 @@ def cpu_baseline(chain, shapes, M, qt, sigma, kind, s):
         dt = time.perf_counter() - t0
         if dt >= 10.0 or steps >= 30:
             break
-    return dt / steps, steps, threads
+    dt /= steps
+    one = None
+    if threadpool_limits is not None:
+        log("cpu baseline: one layer step on one thread ...")
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.decode_chain(x0, layers, qt)
+            one = time.perf_counter() - t0
+    return {"value": round(bytes_step / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{steps} {name} layer steps (M={M}, all {len(chain)} linears and their "
+                      f"per-token quantizations, exact accumulation) by the numpy oracle on "
+                      f"{threads} BLAS threads, {dt:.3f} s per step; then one step on 1 thread",
+            "seconds_per_step": round(dt, 4),
+            "one_thread": None if one is None else {"value": round(bytes_step / one / 1e9, 3),
+                                                   "unit": "GB/s", "seconds_per_step": round(one, 4)},
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def refresh_bytes(N, K):
@@ -689,6 +728,8 @@ def main():
                     choices=sorted(WORKLOADS) + sorted(REFRESH) + sorted(ACR) + sorted(MX))
     ap.add_argument("--m", type=int, default=None, help="override the token count M")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default workload only: skip the 32B decode / prefill lines and the measured peaks")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--summarize-rocprof", nargs="+", metavar="CSV",
                     help="print the figures used from rocprofv3 CSV files (with --grid) and exit")
@@ -748,6 +789,65 @@ def main():
     wl = dict(WORKLOADS[args.workload])
     if args.m is not None:
         wl["M"] = args.m
+    r = run_chain(args.workload, wl, dev, args.steps, args.warmup, args.eager)
+    M, qt, s = wl["M"], wl["qt"], 1.5
+    chain, shapes, sigma = chain_spec(wl["chain"])
+
+    extra = {}
+    if not args.no_extras and args.workload == "7b_decode_int8" and args.m is None:
+        # The 32B half of the metric (decode layer at 512 tokens, INT8 and
+        # FP8; the prefill gate projection at 4096 tokens) and the peaks the
+        # chip reaches, beside the headline 7B line.
+        extra["peaks_measured"] = measure_peaks(dev)
+        for name in ("32b_decode_int8", "32b_decode_fp8"):
+            x = run_chain(name, dict(WORKLOADS[name]), dev, 50, 5, False, breakdown=False)
+            extra[name] = {k: x[k] for k in ("layer_us", "tops", "value_gbs", "roofline", "config")}
+            add_measured_fraction(extra[name]["roofline"], extra["peaks_measured"])
+        extra["32b_prefill_gate_int8"] = prefill_gate(dev)
+        add_measured_fraction(extra["32b_prefill_gate_int8"]["roofline"], extra["peaks_measured"])
+        extra["gemm_source_sha16"] = kernel_source_sha256("gemm")[:16]
+        add_measured_fraction(r["roofline"], extra["peaks_measured"])
+
+    cpu = None
+    if any(L.get("prod") for L in chain):
+        log("bench: no CPU baseline for chains with producers (the oracle chain has none)")
+    elif not args.no_cpu_baseline:
+        cpu = cpu_baseline(chain, shapes, M, qt, sigma, wl["kind"], s, r["bytes_step"], args.workload)
+
+    out = {
+        "metric": METRIC,
+        "value": r["value_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["layer_us"] / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": qt,
+        "data": "synthetic",
+        "config": r["config"],
+        "layer_us": r["layer_us"],
+        "tops": r["tops"],
+        "alg_bytes_per_step": r["bytes_step"],
+        "roofline": r["roofline"],
+        "cpu_baseline": cpu,
+        "linears": r["linears"],
+    }
+    out.update(extra)
+    print(json.dumps(out), flush=True)
+
+
+def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
+    """Time one decoder layer's chain of quantized linears (the workload
+    `name`): whole-step HIP graphs over distinct weight sets, the dominant
+    GEMM alone in a graph of back-to-back launches, and (breakdown) eager
+    per-linear times."""
+    import torch
+
+    from w8a8_gemm_rl_amd import binding as B
+
     M, qt, s = wl["M"], wl["qt"], 1.5
     chain, shapes, sigma = chain_spec(wl["chain"])
     K0 = shapes[chain[0]["name"]][1]
@@ -763,6 +863,7 @@ def main():
     elif wl["kind"] == "heavy":
         x = x * torch.exp(torch.randn((1, K0), generator=g, device=dev))
     x0 = x.to(torch.bfloat16)
+    del x
     bufs = {}
     need = 0
     for L in chain:
@@ -773,7 +874,7 @@ def main():
         need = max(need, B.workspace_size("qr_w8a8_gemm", M, N, K, qt))
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
 
-    log(f"bench: {args.workload} M={M} qt={qt}: building {wl['sets']} weight sets ...")
+    log(f"bench: {name} M={M} qt={qt}: building {wl['sets']} weight sets ...")
     layers = [Layer(chain, shapes, M, qt, sigma, 1000 * (j + 1), dev, x0, bufs, ws, s,
                     fused=wl.get("fused", True)) for j in range(wl["sets"])]
     torch.cuda.synchronize()
@@ -795,14 +896,14 @@ def main():
     dom_bound = "hbm" if dom_intensity < MFMA8_PEAK_TOPS / HBM_PEAK_GBS * 1000 else "mfma"
 
     # ---- warmup (eager)
-    log(f"bench: warmup {args.warmup} steps")
-    for i in range(args.warmup):
+    log(f"bench: warmup {warmup} steps")
+    for i in range(warmup):
         layers[i % len(layers)].run()
     torch.cuda.synchronize()
 
-    K = args.steps
-    mode = "eager" if args.eager else "hip_graph"
-    if args.eager:
+    K = steps
+    mode = "eager" if eager else "hip_graph"
+    if eager:
         # Every op launched from the host; events around the dominant GEMM.
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(K)]
@@ -829,8 +930,8 @@ def main():
                     L.run()
             whole.append(gph)
         # The dominant GEMM alone: a graph of DOM_BATCH back-to-back launches
-        # over the weight sets, so events around its replays measure the
-        # kernels with no host launch gap in between.
+        # over the weight sets, replayed on stream `st` between events recorded
+        # on `st`, so they measure the kernels with no host launch gap.
         dom_graph = torch.cuda.CUDAGraph()
         dom_fns = [next(f for kind, n, f in L.ops() if kind == "gemm" and n == dom) for L in layers]
         with torch.cuda.stream(st):
@@ -853,102 +954,197 @@ def main():
         reps = max(3, min(20, K // DOM_BATCH))
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(reps)]
-        for a, b in evs:
-            a.record()
-            dom_graph.replay()
-            b.record()
+        with torch.cuda.stream(st):
+            for a, b in evs:
+                a.record(st)
+                dom_graph.replay()
+                b.record(st)
         torch.cuda.synchronize()
         dom_us = 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / (reps * DOM_BATCH)
         del whole, dom_graph
     sec_step = (t1 - t0) / K
 
     # ---- per-linear breakdown (eager, events around every GEMM; not timed)
-    per = {L["name"]: [] for L in chain}
-    reps = min(20, K)
-    for i in range(reps):
-        e = {L["name"]: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for L in chain}
-        layers[i % len(layers)].run(per_linear=e)
-        torch.cuda.synchronize()
-        for n, (a, b) in e.items():
-            per[n].append(a.elapsed_time(b) * 1000.0)
     linears = {}
-    for L in chain:
-        n = L["name"]
-        N_, K_ = shapes[n]
-        us = sorted(per[n])[len(per[n]) // 2]
-        # host-launched: at small M the host's own launch time between the
-        # events is counted too, so these are upper bounds on the kernels
-        linears[n] = dict(N=N_, K=K_, eager_us=round(us, 2),
-                          eager_gbs=round(gemm_bytes[n] / us / 1e3, 1),
-                          eager_tops=round(2 * M * N_ * K_ / us / 1e6, 1),
-                          plan=list(B.gemm_plan(M, N_, K_, qt)))
+    if breakdown:
+        per = {L["name"]: [] for L in chain}
+        reps = min(20, K)
+        for i in range(reps):
+            e = {L["name"]: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for L in chain}
+            layers[i % len(layers)].run(per_linear=e)
+            torch.cuda.synchronize()
+            for n, (a, b) in e.items():
+                per[n].append(a.elapsed_time(b) * 1000.0)
+        for L in chain:
+            n = L["name"]
+            N_, K_ = shapes[n]
+            us = sorted(per[n])[len(per[n]) // 2]
+            # host-launched: at small M the host's own launch time between the
+            # events is counted too, so these are upper bounds on the kernels
+            linears[n] = dict(N=N_, K=K_, eager_us=round(us, 2),
+                              eager_gbs=round(gemm_bytes[n] / us / 1e3, 1),
+                              eager_tops=round(2 * M * N_ * K_ / us / 1e6, 1),
+                              plan=list(B.gemm_plan(M, N_, K_, qt)))
 
     dom_plan = B.gemm_plan(M, Nd, Kd, qt)
-    traffic_key = (f"{args.workload}:{dom}:M{M}:N{Nd}:K{Kd}:tile{dom_plan[0]}:split{dom_plan[1]}"
+    traffic_key = (f"{name}:{dom}:M{M}:N{Nd}:K{Kd}:tile{dom_plan[0]}:split{dom_plan[1]}"
                    f":rows{dom_plan[2]}")
-    traffic = committed_traffic(traffic_key)
-    achieved = gemm_bytes[dom] / (dom_us * 1e-6) / 1e9 if dom_bound == "hbm" else dom_ops / (dom_us * 1e-6) / 1e12
-    peak = HBM_PEAK_GBS if dom_bound == "hbm" else MFMA8_PEAK_TOPS
-    roofline = {
-        "bound": dom_bound,
-        "achieved": round(achieved, 1),
-        "peak": peak,
-        "unit": "GB/s" if dom_bound == "hbm" else "TFLOP/s",
-        "frac": round(achieved / peak, 4),
-        "traffic": traffic,
+    roofline = roofline_object(dom_bound, gemm_bytes[dom], dom_ops, dom_us, qt)
+    roofline.update({
+        "traffic": committed_traffic(traffic_key),
         "traffic_key": traffic_key,
         "kernel": f"{dom} GEMM {Nd}x{Kd} M={M} ({B.tile_name(dom_plan[0])}, splitk {dom_plan[1]})",
-        "kernel_us": round(dom_us, 2),
-        "alg_bytes_per_launch": gemm_bytes[dom],
-        "alg_ops_per_launch": dom_ops,
+    })
+    config = {
+        "workload": f"{name}: one decoder layer's W8A8 linears, M={M} tokens, "
+                    + ", ".join(f"{L['name']} {shapes[L['name']][0]}x{shapes[L['name']][1]}"
+                                for L in chain)
+                    + f"; {len(quant_keys)} per-token quantizations + {len(chain)} GEMMs"
+                    + ("" if not any(L.get("prod") for L in chain) else
+                       (", producers (RMSNorm x2, SiLU x up) "
+                        + ("fused into the quantizers" if wl.get("fused", True)
+                           else "as separate torch ops"))),
+        "M": M, "qtype": qt, "uaq_s": s, "weight_sets": len(layers), "timing": mode,
+        "parallelism": "none (1 GPU)",
     }
-
-    cpu = None
-    if any(L.get("prod") for L in chain):
-        log("bench: no CPU baseline for chains with producers (the oracle chain has none)")
-    elif not args.no_cpu_baseline:
-        dt, nsteps, threads = cpu_baseline(chain, shapes, M, qt, sigma, wl["kind"], s)
-        cpu = {"value": round(bytes_step / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"{nsteps} {args.workload} layer steps (M={M}, all {len(chain)} linears and "
-                         f"their per-token quantizations, exact accumulation) by the numpy oracle, "
-                         f"{dt:.3f} s per step",
-               "seconds_per_step": round(dt, 4), "host_cpus": os.cpu_count()}
-
-    out = {
-        "metric": METRIC,
-        "value": round(bytes_step / sec_step / 1e9, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": args.warmup,
-        "ms_per_step": round(sec_step * 1e3, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": qt,
-        "data": "synthetic",
-        "config": {
-            "workload": f"{args.workload}: one decoder layer's W8A8 linears, M={M} tokens, "
-                        + ", ".join(f"{L['name']} {shapes[L['name']][0]}x{shapes[L['name']][1]}"
-                                    for L in chain)
-                        + f"; {len(quant_keys)} per-token quantizations + {len(chain)} GEMMs"
-                        + ("" if not any(L.get("prod") for L in chain) else
-                           (", producers (RMSNorm x2, SiLU x up) "
-                            + ("fused into the quantizers" if wl.get("fused", True)
-                               else "as separate torch ops"))),
-            "M": M, "qtype": qt, "uaq_s": s, "weight_sets": len(layers), "timing": mode,
-            "parallelism": "none (1 GPU)",
-        },
+    res = {
         "layer_us": round(sec_step * 1e6, 2),
+        "value_gbs": round(bytes_step / sec_step / 1e9, 1),
         "tops": round(ops_step / sec_step / 1e12, 1),
-        "alg_bytes_per_step": bytes_step,
+        "bytes_step": bytes_step,
         "roofline": roofline,
-        "cpu_baseline": cpu,
         "linears": linears,
+        "config": config,
     }
-    print(json.dumps(out), flush=True)
+    del layers, bufs, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def roofline_object(bound, alg_bytes, alg_ops, us, qt):
+    """Roofline of one kernel launch of `us` microseconds: algorithmic bytes
+    per second against HBM peak, or operations per second against the dense
+    8-bit MFMA peak (TOP/s for INT8, TFLOP/s for FP8)."""
+    if bound == "hbm":
+        achieved, peak, unit = alg_bytes / (us * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak = alg_ops / (us * 1e-6) / 1e12, MFMA8_PEAK_TOPS
+        unit = "TOP/s" if qt == "int8" else "TFLOP/s"
+    return {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "kernel_us": round(us, 2),
+            "alg_bytes_per_launch": alg_bytes, "alg_ops_per_launch": alg_ops}
+
+
+def add_measured_fraction(roof, peaks):
+    """Add the fraction against the peak measured on this GPU (same run)."""
+    if not peaks:
+        return
+    if roof["bound"] == "hbm":
+        p = peaks["hbm_read_gbs"]
+    else:
+        p = peaks["mfma_int8_tops"] if roof["unit"] == "TOP/s" else peaks["mfma_fp8_tflops"]
+    roof["measured_peak"] = p
+    roof["frac_of_measured_peak"] = round(roof["achieved"] / p, 4)
+
+
+def measure_peaks(dev):
+    """Peaks this GPU reaches (the library's measurement kernels): HBM read
+    rate over a 4 GiB buffer, dense INT8 / FP8 MFMA rate, and the shader clock
+    the matrix cores ran at (from the kernel's clock counters)."""
+    import statistics
+
+    import torch
+
+    from w8a8_gemm_rl_amd import binding as B
+
+    log("bench: measuring the HBM read and MFMA peaks")
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(2048, dtype=torch.int32, device=dev)
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return sorted(ts)[reps // 2]
+
+    t = timed(lambda: B.probe_read(buf, sink))
+    hbm = buf.numel() / t / 1e9
+    del buf
+    out = {"hbm_read_gbs": round(hbm, 1), "hbm_read_buffer_bytes": 4 << 30}
+    blocks, iters = 256, 4000  # one block of 8 waves per CU, all resident at once
+    for qt, key, ops_per in (("int8", "mfma_int8_tops", 65536), ("fp8", "mfma_fp8_tflops", 131072)):
+        res = {}
+        t = timed(lambda: res.update(r=B.probe_mfma(qt, blocks, iters, dev)))
+        _, ticks, khz = res["r"]
+        tk = ticks.view(-1, 4).cpu().tolist()
+        mhz = statistics.median((c1 - c0) / (w1 - w0) * khz / 1e3 for c0, c1, w0, w1 in tk if w1 > w0)
+        out[key] = round(blocks * 8 * iters * 8 * ops_per / t / 1e12, 1)
+        out["sclk_mhz_" + qt] = round(mhz, 0)
+    out["kernels"] = "read_probe_kernel (16-byte loads, 4 GiB once), mfma_probe_kernel (256 blocks x 8 waves, " \
+                     "8 independent 32x32 MFMAs per round, 4000 rounds)"
+    torch.cuda.empty_cache()
+    return out
+
+
+def prefill_gate(dev):
+    """The 32B prefill gate projection (27648x5120, INT8, 4096 tokens with
+    heavy-tailed channels): a graph of 20 launches over two weight copies."""
+    import torch
+
+    from w8a8_gemm_rl_amd import binding as B
+    from w8a8_gemm_rl_amd import inputs as I
+
+    M, (N, K) = 4096, I.LINEARS_32B["gate"]
+    qt = "int8"
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    x = torch.randn((M, K), generator=g, device=dev) * torch.exp(torch.randn((1, K), generator=g, device=dev))
+    xq, sx = B.quantize_act_per_token(x.to(torch.bfloat16), 1.5, qt)
+    del x
+    sets = []
+    for j in range(2):
+        W = torch.randn((N, K), generator=g, device=dev) * I.W_SIGMA_32B
+        sets.append(B.quantize_weights_uaq(W, 1.5, qt))
+        del W
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(max(B.workspace_size("qr_w8a8_gemm", M, N, K, qt), 256), dtype=torch.uint8,
+                     device=dev)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    gph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        B.w8a8_gemm(xq, sx, *sets[0], qt, Y=Y, ws=ws)
+        with torch.cuda.graph(gph, stream=st):
+            for i in range(DOM_BATCH):
+                B.w8a8_gemm(xq, sx, *sets[i % 2], qt, Y=Y, ws=ws)
+    torch.cuda.synchronize()
+    ts = []
+    with torch.cuda.stream(st):
+        gph.replay()
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            gph.replay()
+            b.record(st)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1000.0 / DOM_BATCH)
+    us = sorted(ts)[2]
+    plan = B.gemm_plan(M, N, K, qt)
+    roof = roofline_object("mfma", linear_bytes(M, N, K), 2 * M * N * K, us, qt)
+    roof["kernel"] = f"gate GEMM {N}x{K} M={M} ({B.tile_name(plan[0])}, splitk {plan[1]})"
+    del sets, Y, ws, xq, sx, gph
+    torch.cuda.empty_cache()
+    return {"us": round(us, 2), "tops": round(2 * M * N * K / us / 1e6, 1), "roofline": roof,
+            "config": "32B prefill gate projection, INT8, X[4096, 5120] (heavy-tailed channels) x "
+                      "W[27648, 5120], 2 weight copies, graph of 20 launches"}
 
 
 if __name__ == "__main__":

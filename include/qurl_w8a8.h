@@ -352,14 +352,41 @@ const char* qr_tile_name(int tile);
 int qr_num_tiles(void);
 
 /*
- * qr_set_plan_override -- tuning hook: force tile configuration `tile`,
- * `splitk` splits (0 = automatic) and `rows` weight rows per tile (0 = the
- * tile height; else a multiple of 8 no larger than it) for every later
- * qr_w8a8_gemm / qr_linear_fused / qr_workspace_size / qr_gemm_plan call in
- * the process (tile < 0 restores automatic planning). Not thread-safe;
- * meant for benchmarks and tests. Returns QR_OK or QR_ERR_INVALID_ARG.
+ * qr_set_plan_override -- tuning and test hook: force tile configuration
+ * `tile`, `splitk` splits (0 = automatic) and `rows` weight rows per tile
+ * (0 = the tile height; else a multiple of 8 no larger than it) for every
+ * later qr_w8a8_gemm / qr_linear_fused / qr_workspace_size / qr_gemm_plan
+ * call made by the calling thread (tile < 0 restores automatic planning).
+ * The override is thread-local: other threads keep their own plans. Set it
+ * before querying qr_workspace_size, and keep it until the GEMM call, since
+ * the workspace a plan needs depends on it. Meant for benchmarks and tests.
+ * Returns QR_OK or QR_ERR_INVALID_ARG.
  */
 int qr_set_plan_override(int tile, int splitk, int rows);
+
+/*
+ * Measurement helpers (not part of the linear): the peaks the chip reaches,
+ * against which the GEMMs' roofline fractions are also reported.
+ *
+ * qr_probe_read -- read `bytes` (a multiple of 16) of device memory at `buf`
+ *   (16-byte aligned) once with 16-byte loads; block b writes one XOR word to
+ *   sink[b]. sink holds at least sink_words >= 2048 uint32 (device memory).
+ *   bytes / kernel time is the memory read rate; use a buffer well past the
+ *   256 MB Infinity Cache to measure HBM.
+ * qr_probe_mfma -- `blocks` blocks of 8 waves; every wave runs `iters`
+ *   rounds of 8 independent dense MFMAs on register operands (qt = QR_INT8:
+ *   v_mfma_i32_32x32x32_i8, 65536 ops each; QR_FP8_E4M3FN:
+ *   v_mfma_scale_f32_32x32x64_f8f6f4, 131072 ops each) and writes one word
+ *   per wave to sink[8 b + w] (device, >= 8 * blocks uint32). Wave 0 of block
+ *   b writes its shader-clock counter and the constant-rate wall clock at
+ *   start and end to ticks[4 b + 0..3] (device, >= 4 * blocks uint64), and
+ *   *wall_khz (host) receives the wall clock's rate, so that
+ *   (t1 - t0) / (w1 - w0) * wall_khz is the shader clock in kHz.
+ *   blocks in [1, 65536], iters in [1, 2^24].
+ */
+int qr_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t sink_words, void* stream);
+int qr_probe_mfma(int qt, int blocks, int iters, uint32_t* sink, uint64_t* ticks, int* wall_khz,
+                  void* stream);
 
 /* Thread-local message describing the last non-QR_OK status ("" if none). */
 const char* qr_last_error(void);

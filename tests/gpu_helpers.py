@@ -60,3 +60,17 @@ def fp8_acc_bound(Xq, Wq):
     dw = np.abs(F.e4m3fn_decode(Wq))
     K = Xq.shape[1]
     return (2.0 ** -12 + max(K - 1, 1) * 2.0 ** -24) * (dx @ dw.T)
+
+
+def assert_bf16_close_fro(y_bits, ref_bits, rel, what=""):
+    """End-to-end form of the tolerance, for chains whose inputs already differ
+    upstream: ||y - ref||_F <= rel ||ref||_F only. Returns the relative
+    Frobenius error and the number of elements outside the elementwise
+    1e-2 bound, for the report."""
+    y = f32_of_bits(y_bits)
+    r = f32_of_bits(ref_bits)
+    nr = max(float(np.linalg.norm(r)), 1e-30)
+    e = float(np.linalg.norm(y - r)) / nr
+    assert e <= rel, (what, e)
+    rms = np.sqrt(np.mean(r * r)) if r.size else 0.0
+    return e, int(np.count_nonzero(np.abs(y - r) > 1e-2 * np.abs(r) + 1e-2 * rms))

@@ -1,8 +1,14 @@
 """HIP-graph capture of the decode chain: every replay must equal the eager result.
 
-The benchmark times graph replays, so the launch path (split-K counters reset
-by the kernels themselves, no memset nodes) must give identical outputs on
-every replay, with other eager work and synchronizations in between.
+The benchmark times graph replays, so the launch path (split-K partial sums
+written to the workspace with plain stores and added by a second kernel, no
+memset nodes) must give identical outputs on every replay, with other eager
+work and synchronizations in between.
+
+The binding's own workspace (used when a call passes none) is one buffer per
+device and stream: a graph captured with it must keep working after a later,
+larger call on the same stream grows it, and calls on two streams must not
+share one.
 """
 
 import numpy as np
@@ -58,3 +64,45 @@ def test_graph_replays_match_eager(qt):
         chain()  # eager calls between replays share the workspace
         torch.cuda.synchronize()
         assert float(junk) == float(junk)
+
+
+def test_binding_workspace_per_stream_and_kept_for_graphs():
+    qt = "int8"
+    M, N, K = 32, 2048, 4096  # split K: the call writes partial sums to the workspace
+    assert B.gemm_plan(M, N, K, qt)[1] > 1
+    X = to_dev_bf16(I.activations(M, K, seed=71, kind="outliers"))
+    Wq, sw = B.quantize_weights_uaq(to_dev_f32(I.weights(N, K, 0.02, seed=72)), 1.5, qt)
+    ref = B.linear_fused(X, 1.5, Wq, sw, qt)
+    torch.cuda.synchronize()
+
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    need = B.workspace_size("qr_linear_fused", M, N, K, qt)
+    with torch.cuda.stream(s1):
+        w1, _ = B.workspace(need, DEV)
+    with torch.cuda.stream(s2):
+        w2, _ = B.workspace(need, DEV)
+    assert w1.data_ptr() != w2.data_ptr()
+
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    s1.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        with torch.cuda.graph(g, stream=s1):
+            B.linear_fused(X, 1.5, Wq, sw, qt, Y=y)  # the binding's workspace of s1
+    torch.cuda.synchronize()
+    # A larger call on s1 outgrows that workspace; the old buffer must stay
+    # allocated for the graph, and new tensors must not land on it.
+    big_need = B.workspace_size("qr_linear_fused", 256, 4 * N, K, qt)
+    assert big_need > w1.numel()
+    with torch.cuda.stream(s1):
+        w1b, _ = B.workspace(big_need, DEV)
+    assert w1b.data_ptr() != w1.data_ptr()
+    fill = [torch.full((need // 2 + 1,), 7, dtype=torch.int16, device=DEV) for _ in range(4)]
+    for rep in range(3):
+        y.zero_()
+        with torch.cuda.stream(s1):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), f"replay {rep}"
+        for f in fill:
+            assert bool((f == 7).all()), f"replay {rep} wrote into a live tensor"

@@ -29,7 +29,7 @@ EXPORTS = [
     "qr_norm_quant", "qr_silu_mul_quant", "qr_acr_tis_loss", "qr_mx_quantize", "qr_mx_gemm",
     "qr_w8a8_gemm", "qr_linear_fused",
     "qr_workspace_size", "qr_gemm_plan", "qr_tile_name", "qr_num_tiles", "qr_set_plan_override",
-    "qr_last_error", "qr_version",
+    "qr_last_error", "qr_version", "qr_probe_read", "qr_probe_mfma",
 ]
 
 
@@ -62,6 +62,8 @@ _SIGS = {
     "qr_num_tiles": (_int, []),
     "qr_set_plan_override": (_int, [_int, _int, _int]),
     "qr_last_error": (ctypes.c_char_p, []),
+    "qr_probe_read": (_int, [_vp, _sz, _vp, _i64, _vp]),
+    "qr_probe_mfma": (_int, [_int, _int, _int, _vp, _vp, ctypes.POINTER(_int), _vp]),
     "qr_version": (ctypes.c_char_p, []),
 }
 
@@ -124,20 +126,28 @@ def code_dtype(qt):
 
 
 # ----------------------------------------------------------------------------
-# Workspace: one scratch buffer per device, grown on demand, shared by calls
-# made on that device (they are stream-ordered on the current stream).
+# Workspace: one scratch buffer per (device, stream), grown on demand. Calls on
+# one stream are ordered, so they may share it; calls on different streams may
+# run at the same time and get different buffers. A buffer that is outgrown is
+# kept alive (never freed): a HIP graph captured earlier may still write into
+# it on every replay, and the caching allocator must not hand its memory to
+# another tensor.
 # ----------------------------------------------------------------------------
 _ws = {}
+_ws_retired = []
 
 
 def workspace(nbytes, device):
-    dev = torch.device(device)
-    key = dev.index if dev.index is not None else torch.cuda.current_device()
-    buf = _ws.get(key)
     if nbytes == 0:
         return None, 0
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (idx, torch.cuda.current_stream(idx).cuda_stream)
+    buf = _ws.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        if buf is not None:
+            _ws_retired.append(buf)
+        buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=torch.device("cuda", idx))
         _ws[key] = buf
     return buf, buf.numel()
 
@@ -399,3 +409,35 @@ def linear_fused(X, act_mult, Wq, scale_w, qt, Y=None, ws=None):
                                    _qt(qt), _ptr(Y), ldy, _ptr(ws), wsb, _stream(X.device))
     _check("qr_linear_fused", st)
     return Y
+
+
+# ----------------------------------------------------------------------------
+# Measurement helpers (peaks the chip reaches; not part of the linear)
+# ----------------------------------------------------------------------------
+
+def probe_read(buf, sink=None):
+    """Enqueue one read of the whole byte buffer `buf` (a contiguous device
+    tensor whose size is a multiple of 16 bytes); returns the sink tensor."""
+    _need_cuda(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    if sink is None:
+        sink = torch.empty(2048, dtype=torch.int32, device=buf.device)
+    with torch.cuda.device(buf.device):
+        st = lib().qr_probe_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream(buf.device))
+    _check("qr_probe_read", st)
+    return sink
+
+
+def probe_mfma(qt, blocks, iters, device="cuda:0", sink=None, ticks=None):
+    """Enqueue the MFMA probe; returns (sink, ticks, wall clock rate in kHz)."""
+    dev = torch.device(device)
+    if sink is None:
+        sink = torch.empty(8 * blocks, dtype=torch.int32, device=dev)
+    if ticks is None:
+        ticks = torch.empty(4 * blocks, dtype=torch.int64, device=dev)
+    khz = ctypes.c_int(0)
+    with torch.cuda.device(dev):
+        st = lib().qr_probe_mfma(_qt(qt), blocks, iters, _ptr(sink), _ptr(ticks), ctypes.byref(khz),
+                                 _stream(dev))
+    _check("qr_probe_mfma", st)
+    return sink, ticks, khz.value

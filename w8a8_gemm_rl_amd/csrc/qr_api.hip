@@ -15,9 +15,12 @@
 namespace {
 
 thread_local std::string g_err;
-int g_force_tile = -1;
-int g_force_splitk = 0;
-int g_force_rows = 0;
+// Plan override of qr_set_plan_override (a tuning and test hook): per thread,
+// so a sweep on one thread never changes the plans, or the workspace sizes,
+// that calls on other threads see.
+thread_local int g_force_tile = -1;
+thread_local int g_force_splitk = 0;
+thread_local int g_force_rows = 0;
 
 constexpr int64_t kMaxKInt8 = 133144;  // K * 127^2 < 2^31
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
@@ -400,6 +403,38 @@ int qr_linear_fused(const void* X, int64_t ldx, float act_mult, const void* Wq, 
   st = hip_status(qr::launch_act_quant(X, M, K, ldx, act_mult, qt, xq, sx, hs), fn);
   if (st != QR_OK) return st;
   return run_gemm(fn, plan, xq, sx, Wq, scale_w, M, N, K, qt, QR_OUT_BF16, Y, ldy, gws, hs);
+}
+
+int qr_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t sink_words,
+                  void* stream) {
+  const char* fn = "qr_probe_read";
+  if (bytes % 16 != 0) return fail(QR_ERR_INVALID_ARG, "%s: bytes must be a multiple of 16", fn);
+  if (bytes > 0 && !buf) return fail(QR_ERR_INVALID_ARG, "%s: null buf", fn);
+  if (!aligned(buf, 16)) return fail(QR_ERR_UNSUPPORTED, "%s: buf must be 16-byte aligned", fn);
+  if (!sink || sink_words < (int64_t)qr::read_probe_blocks())
+    return fail(QR_ERR_INVALID_ARG, "%s: sink of %u words needed", fn, qr::read_probe_blocks());
+  (void)hipGetLastError();
+  return hip_status(qr::launch_read_probe(buf, (int64_t)(bytes / 16), sink,
+                                          static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int qr_probe_mfma(int qt, int blocks, int iters, uint32_t* sink, uint64_t* ticks, int* wall_khz,
+                  void* stream) {
+  const char* fn = "qr_probe_mfma";
+  if (!valid_qt(qt)) return fail(QR_ERR_INVALID_ARG, "%s: unknown qtype %d", fn, qt);
+  if (blocks < 1 || blocks > 65536 || iters < 1 || iters > (1 << 24))
+    return fail(QR_ERR_INVALID_ARG, "%s: blocks in [1, 65536] and iters in [1, 2^24]", fn);
+  if (!sink || !ticks || !wall_khz) return fail(QR_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (!aligned(ticks, 8)) return fail(QR_ERR_UNSUPPORTED, "%s: ticks must be 8-byte aligned", fn);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(wall_khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  (void)hipGetLastError();
+  return hip_status(qr::launch_mfma_probe(qt, blocks, iters, sink, ticks,
+                                          static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 }  // extern "C"

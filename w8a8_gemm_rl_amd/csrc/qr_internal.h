@@ -5,6 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "qr_device.h"
 #include "qr_gemm.h"
 
 namespace qr {
@@ -31,5 +32,10 @@ hipError_t launch_acr_tis(const float* logp, const float* lprox, const float* lb
                           float* loss, float* grad, double* sums, double* part, hipStream_t st);
 hipError_t launch_requant(const float* Wp, int64_t N, int64_t K, int64_t ldw, int qt, void* Wq,
                           float* scale_w, uint32_t* row_flips, hipStream_t st);
+
+unsigned read_probe_blocks();
+hipError_t launch_read_probe(const void* buf, int64_t n16, uint32_t* sink, hipStream_t st);
+hipError_t launch_mfma_probe(int qt, int blocks, int iters, uint32_t* sink, uint64_t* ticks,
+                             hipStream_t st);
 
 }  // namespace qr
