@@ -327,6 +327,27 @@ int qr_linear_fused(const void* X, int64_t ldx, float act_mult, const void* Wq, 
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qr_linear_fused_noalloc -- qr_linear_fused for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results, with the
+ * workspace (split-K partial sums, activation codes and scales) in a fixed
+ * 48 MiB device array owned by the library, one per GPU, held until the
+ * process ends. No call allocates or frees memory; the first call on a
+ * device looks up that device's array (hipGetSymbolAddress).
+ *   Arguments as qr_linear_fused, without the workspace.
+ *   Shapes whose qr_workspace_size("qr_linear_fused", ...) exceeds 48 MiB
+ *   return QR_ERR_WORKSPACE with nothing launched (e.g. up to 512 tokens for
+ *   the 7B- and 32B-shaped linears fit).
+ *   Every call on one GPU uses that GPU's one array, so calls that may run at
+ *   the same time on one GPU (different streams) race and must not be made;
+ *   calls ordered on one stream are safe. Nothing in the array needs to be
+ *   zero: each call writes what it later reads.
+ */
+int qr_linear_fused_noalloc(const void* X, int64_t ldx, float act_mult, const void* Wq,
+                            const float* scale_w, int64_t M, int64_t N, int64_t K, int qt,
+                            void* Y, int64_t ldy, void* stream);
+
+/*
  * qr_workspace_size -- bytes of workspace needed by `fn` ("qr_w8a8_gemm" or
  * "qr_linear_fused") for this shape; 0 if none. For "qr_acr_tis_loss" M is
  * the token count n (N, K and qt are ignored). Pure host function: it

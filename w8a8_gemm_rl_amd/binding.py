@@ -27,7 +27,7 @@ STATUS = {
 EXPORTS = [
     "qr_quantize_weights_uaq", "qr_requantize_weights", "qr_quantize_act_per_token",
     "qr_norm_quant", "qr_silu_mul_quant", "qr_acr_tis_loss", "qr_mx_quantize", "qr_mx_gemm",
-    "qr_w8a8_gemm", "qr_linear_fused",
+    "qr_w8a8_gemm", "qr_linear_fused", "qr_linear_fused_noalloc",
     "qr_workspace_size", "qr_gemm_plan", "qr_tile_name", "qr_num_tiles", "qr_set_plan_override",
     "qr_last_error", "qr_version", "qr_probe_read", "qr_probe_mfma",
 ]
@@ -55,6 +55,8 @@ _SIGS = {
     "qr_mx_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _vp]),
     "qr_w8a8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _sz, _vp]),
     "qr_linear_fused": (_int, [_vp, _i64, _f32, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _sz, _vp]),
+    "qr_linear_fused_noalloc": (_int, [_vp, _i64, _f32, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64,
+                                       _vp]),
     "qr_workspace_size": (_sz, [ctypes.c_char_p, _i64, _i64, _i64, _int]),
     "qr_gemm_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(_int), ctypes.POINTER(_int),
                             ctypes.POINTER(_int)]),
@@ -408,6 +410,26 @@ def linear_fused(X, act_mult, Wq, scale_w, qt, Y=None, ws=None):
         st = lib().qr_linear_fused(_ptr(X), ldx, float(act_mult), _ptr(Wq), _ptr(scale_w), M, N, K,
                                    _qt(qt), _ptr(Y), ldy, _ptr(ws), wsb, _stream(X.device))
     _check("qr_linear_fused", st)
+    return Y
+
+
+def linear_fused_noalloc(X, act_mult, Wq, scale_w, qt, Y=None):
+    """linear_fused with the library's fixed device scratch instead of a
+    workspace: the call allocates nothing (Y must be given to avoid torch's
+    own allocation)."""
+    _need_cuda(X, Wq, scale_w, Y)
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bfloat16")
+    M, K = X.shape
+    N = Wq.shape[0]
+    ldx = _rows(X, "X")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    ldy = _rows(Y, "Y")
+    with torch.cuda.device(X.device):
+        st = lib().qr_linear_fused_noalloc(_ptr(X), ldx, float(act_mult), _ptr(Wq), _ptr(scale_w),
+                                           M, N, K, _qt(qt), _ptr(Y), ldy, _stream(X.device))
+    _check("qr_linear_fused_noalloc", st)
     return Y
 
 

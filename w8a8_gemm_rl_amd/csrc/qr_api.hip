@@ -73,6 +73,22 @@ int check_shape(const char* fn, int64_t M, int64_t N, int64_t K, int qt) {
 
 }  // namespace
 
+namespace qr {
+
+int set_error(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_error(hipError_t e, const char* what) { return hip_status(e, what); }
+
+}  // namespace qr
+
 
 extern "C" {
 

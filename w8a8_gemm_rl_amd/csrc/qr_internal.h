@@ -33,6 +33,11 @@ hipError_t launch_acr_tis(const float* logp, const float* lprox, const float* lb
 hipError_t launch_requant(const float* Wp, int64_t N, int64_t K, int64_t ldw, int qt, void* Wq,
                           float* scale_w, uint32_t* row_flips, hipStream_t st);
 
+// Error reporting of the C ABI (qr_last_error): set the thread-local message
+// and return `code`; hip_error maps a HIP error to QR_ERR_HIP / QR_ERR_NO_DEVICE.
+int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int hip_error(hipError_t e, const char* what);
+
 unsigned read_probe_blocks();
 hipError_t launch_read_probe(const void* buf, int64_t n16, uint32_t* sink, hipStream_t st);
 hipError_t launch_mfma_probe(int qt, int blocks, int iters, uint32_t* sink, uint64_t* ticks,
