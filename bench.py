@@ -47,6 +47,11 @@ EPS = 1e-6  # RMSNorm epsilon of the producer workloads
 WORKLOADS = {
     "7b_decode_int8": dict(M=256, qt="int8", chain="7b", sets=4, kind="outliers"),
     "7b_decode_fp8": dict(M=256, qt="fp8", chain="7b", sets=4, kind="outliers"),
+    # the same layer with one launch per linear: qr_w8a8_gemm_quant adds split-K
+    # partial sums and quantizes the next linear's input inside the GEMM launch
+    # behind grid-wide barriers
+    "7b_decode_int8_one_launch": dict(M=256, qt="int8", chain="7b", sets=4, kind="outliers",
+                                      one_launch=True),
     "7b_decode_int8_gateup": dict(M=256, qt="int8", chain="7b_gateup", sets=4, kind="outliers"),
     # with the producers of the linears' inputs (two RMSNorms, SiLU x up), fused
     # into the quantizers or run as separate torch ops before them
@@ -123,10 +128,29 @@ def quant_bytes(M, K, prod=None):
     return 3 * M * K + 4 * M
 
 
-class Layer:
-    """One set of quantized weights for the chain, plus the ops of one step."""
+def chain_keys(chain):
+    """Input key of each linear (its source, column slice and producer) and,
+    for one launch per linear, the key each GEMM quantizes in its epilogue:
+    the first later linear that reads its output with no producer in between."""
+    key = {L["name"]: (L["src"], L["cols"], L.get("prod")) for L in chain}
+    epi = {}
+    for L in chain:
+        if L["src"] != "x0" and not L.get("prod") and L["src"] not in epi:
+            epi[L["src"]] = key[L["name"]]
+    return key, epi
 
-    def __init__(self, chain, shapes, M, qt, sigma, seed, dev, x0, bufs, ws, s, fused=True):
+
+class Layer:
+    """One set of quantized weights for the chain, plus the ops of one step.
+
+    one_launch: every GEMM is one qr_w8a8_gemm_quant launch that also
+    quantizes the next linear's input (and adds split-K partial sums) in its
+    epilogue; only the layer input (and inputs with a producer) keep a
+    quantizer launch. Otherwise: a quantizer before every distinct input and
+    qr_w8a8_gemm (with its split-K kernel)."""
+
+    def __init__(self, chain, shapes, M, qt, sigma, seed, dev, x0, bufs, ws, s, fused=True,
+                 one_launch=False, wsq=None):
         import torch
 
         from w8a8_gemm_rl_amd import binding as B
@@ -149,17 +173,25 @@ class Layer:
             del Wf
         self.x0, self.bufs, self.ws, self.s = x0, bufs, ws, s
         self.chain, self.M, self.fused = chain, M, fused
+        self.one_launch, self.wsq, self.shapes = one_launch, wsq, shapes
 
     def ops(self):
         """The step as a list of (kind, name, thunk): per-token quantizations
-        (one per distinct input) and GEMMs, in chain order."""
+        (one per distinct input not quantized by a GEMM epilogue) and GEMMs,
+        in chain order."""
         B, bufs = self.B, self.bufs
-        out, done = [], {}
+        key, epi = chain_keys(self.chain)
+        if not self.one_launch:
+            epi = {}
+        key_buf = {}
         for L in self.chain:
-            key = (L["src"], L["cols"], L.get("prod"))
-            if key not in done:
-                xq, sx = bufs["q_" + L["name"]]
-                done[key] = (xq, sx)
+            key_buf.setdefault(key[L["name"]], bufs["q_" + L["name"]])
+        by_epilogue = set(epi.values())
+        out, done = [], set()
+        for L in self.chain:
+            k = key[L["name"]]
+            if k not in done and k not in by_epilogue:
+                xq, sx = key_buf[k]
 
                 def q(L=L, xq=xq, sx=sx):
                     import torch.nn.functional as Fn
@@ -187,11 +219,24 @@ class Layer:
                         B.quantize_act_per_token(src, self.s, self.qt, Xq=xq, scale_x=sx)
 
                 out.append(("quant", L["name"], q))
-            xq, sx = done[key]
+            done.add(k)
+            xq, sx = key_buf[k]
             Wq, sw = self.W[L["name"]]
+            y = bufs["y_" + L["name"]]
+            if self.one_launch:
+                nk = epi.get(L["name"])
+                cols = None
+                xn = sn = None
+                if nk is not None:
+                    cols = nk[1] if nk[1] is not None else (0, self.shapes[L["name"]][0])
+                    xn, sn = key_buf[nk]
 
-            def gm(L=L, xq=xq, sx=sx, Wq=Wq, sw=sw):
-                B.w8a8_gemm(xq, sx, Wq, sw, self.qt, out="bf16", Y=bufs["y_" + L["name"]], ws=self.ws)
+                def gm(xq=xq, sx=sx, Wq=Wq, sw=sw, y=y, cols=cols, xn=xn, sn=sn):
+                    B.w8a8_gemm_quant(xq, sx, Wq, sw, self.qt, Y=y, q_cols=cols, q_act_mult=self.s,
+                                      Xq_next=xn, scale_x_next=sn, ws=self.wsq)
+            else:
+                def gm(xq=xq, sx=sx, Wq=Wq, sw=sw, y=y):
+                    B.w8a8_gemm(xq, sx, Wq, sw, self.qt, out="bf16", Y=y, ws=self.ws)
 
             out.append(("gemm", L["name"], gm))
         return out
@@ -865,18 +910,23 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
     x0 = x.to(torch.bfloat16)
     del x
     bufs = {}
-    need = 0
+    need = needq = 0
     for L in chain:
         N, K = shapes[L["name"]]
         bufs["y_" + L["name"]] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         bufs["q_" + L["name"]] = (torch.empty((M, K), dtype=B.code_dtype(qt), device=dev),
                                   torch.empty(M, dtype=torch.float32, device=dev))
         need = max(need, B.workspace_size("qr_w8a8_gemm", M, N, K, qt))
+        needq = max(needq, B.workspace_size("qr_w8a8_gemm_quant", M, N, K, qt))
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    # one launch per linear: its own workspace, zeroed once (barrier words)
+    wsq = torch.zeros(max(needq, 256), dtype=torch.uint8, device=dev)
+    one_launch = wl.get("one_launch", False)
 
     log(f"bench: {name} M={M} qt={qt}: building {wl['sets']} weight sets ...")
     layers = [Layer(chain, shapes, M, qt, sigma, 1000 * (j + 1), dev, x0, bufs, ws, s,
-                    fused=wl.get("fused", True)) for j in range(wl["sets"])]
+                    fused=wl.get("fused", True), one_launch=one_launch, wsq=wsq)
+              for j in range(wl["sets"])]
     torch.cuda.synchronize()
 
     # ---- per-step algorithmic work
@@ -889,6 +939,7 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
             quant_keys.add(k)
             qbytes += quant_bytes(M, shapes[L["name"]][1], L.get("prod"))
     bytes_step = sum(gemm_bytes.values()) + qbytes
+    n_epi = len(set(chain_keys(chain)[1].values())) if one_launch else 0
     dom = max(chain, key=lambda L: (gemm_bytes[L["name"]], -chain.index(L)))["name"]
     Nd, Kd = shapes[dom]
     dom_ops = 2 * M * Nd * Kd
@@ -1001,12 +1052,15 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
                     + ", ".join(f"{L['name']} {shapes[L['name']][0]}x{shapes[L['name']][1]}"
                                 for L in chain)
                     + f"; {len(quant_keys)} per-token quantizations + {len(chain)} GEMMs"
+                    + (f" in {len(chain) + len(quant_keys) - n_epi} launches ({n_epi} quantizations and "
+                       f"the split-K sums in the GEMM epilogues)" if one_launch else
+                       " as separate launches (quantizers, GEMMs, split-K sum kernels)")
                     + ("" if not any(L.get("prod") for L in chain) else
                        (", producers (RMSNorm x2, SiLU x up) "
                         + ("fused into the quantizers" if wl.get("fused", True)
                            else "as separate torch ops"))),
         "M": M, "qtype": qt, "uaq_s": s, "weight_sets": len(layers), "timing": mode,
-        "parallelism": "none (1 GPU)",
+        "launches": "one per linear" if one_launch else "separate", "parallelism": "none (1 GPU)",
     }
     res = {
         "layer_us": round(sec_step * 1e6, 2),

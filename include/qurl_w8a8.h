@@ -313,6 +313,48 @@ int qr_w8a8_gemm(const void* Xq, const float* scale_x, const void* Wq, const flo
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * qr_w8a8_gemm_quant -- one linear of a decode chain in one launch: the
+ * quantized product and its dequantization epilogue [Notes/System],
+ * [Notes/Training], and the token-wise quantization [Notes/Training] of a
+ * column range of its bf16 output, the next linear's input (the activation
+ * side of UAQ [Notes/UAQ] rides on q_act_mult as for
+ * qr_quantize_act_per_token).
+ *
+ *   Y         = qr_w8a8_gemm(..., QR_OUT_BF16)                  [M, ldy] bf16
+ *   Xq_next, scale_x_next
+ *             = qr_quantize_act_per_token(Y[:, q_col0 : q_col0 + q_cols],
+ *                                         q_act_mult)           [M, q_cols], [M]
+ *   bit for bit the results of those two calls. q_cols = 0 quantizes
+ *   nothing (Xq_next and scale_x_next are not used).
+ * Where the plan allows (all blocks of the grid resident on the GPU at once,
+ * M <= 4096, N, ldy multiples of 4, Y 16-byte aligned) a split-K sum and the
+ * quantization run inside the GEMM launch behind grid-wide barriers: no
+ * split-K kernel, no quantizer kernel. Otherwise the call launches the GEMM
+ * (and its split-K kernel) and the quantizer.
+ *
+ *   Xq, scale_x, Wq, scale_w, M, N, K, qt, Y, ldy   as qr_w8a8_gemm.
+ *   q_col0, q_cols  column range of Y to quantize: multiples of 16 (the
+ *             next linear's K), q_col0 + q_cols <= N; ldy % 8 == 0 when
+ *             q_cols > 0.
+ *   q_act_mult      finite, > 0 (the next linear's act_mult).
+ *   Xq_next   [M, q_cols] codes (written), 16-byte aligned.
+ *   scale_x_next    [M] fp32 (written).
+ *   workspace at least qr_workspace_size("qr_w8a8_gemm_quant", M, N, K, qt)
+ *             bytes, 256-byte aligned. Its first 64 KiB are barrier and
+ *             per-token maximum words: they must be zero before the first
+ *             call that uses this workspace, and every call leaves them
+ *             ready for the next one (zero the buffer once when it is
+ *             allocated; do not share it with calls of other entry points,
+ *             which use a workspace from its start). The rest holds split-K
+ *             partial sums. Calls that may run at the same time (different
+ *             streams) must not share it.
+ */
+int qr_w8a8_gemm_quant(const void* Xq, const float* scale_x, const void* Wq, const float* scale_w,
+                       int64_t M, int64_t N, int64_t K, int qt, void* Y, int64_t ldy, int64_t q_col0,
+                       int64_t q_cols, float q_act_mult, void* Xq_next, float* scale_x_next,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * qr_linear_fused -- the per-linear call of a rollout engine:
  *   qr_quantize_act_per_token followed by qr_w8a8_gemm(out = QR_OUT_BF16),
  *   with the activation codes and scales kept in the workspace.
@@ -348,8 +390,8 @@ int qr_linear_fused_noalloc(const void* X, int64_t ldx, float act_mult, const vo
                             void* Y, int64_t ldy, void* stream);
 
 /*
- * qr_workspace_size -- bytes of workspace needed by `fn` ("qr_w8a8_gemm" or
- * "qr_linear_fused") for this shape; 0 if none. For "qr_acr_tis_loss" M is
+ * qr_workspace_size -- bytes of workspace needed by `fn` ("qr_w8a8_gemm",
+ * "qr_w8a8_gemm_quant" or "qr_linear_fused") for this shape; 0 if none. For "qr_acr_tis_loss" M is
  * the token count n (N, K and qt are ignored). Pure host function: it
  * depends only on its arguments (and on qr_set_plan_override). Returns
  * (size_t)-1 for an unknown fn or invalid sizes.

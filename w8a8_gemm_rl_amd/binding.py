@@ -27,7 +27,7 @@ STATUS = {
 EXPORTS = [
     "qr_quantize_weights_uaq", "qr_requantize_weights", "qr_quantize_act_per_token",
     "qr_norm_quant", "qr_silu_mul_quant", "qr_acr_tis_loss", "qr_mx_quantize", "qr_mx_gemm",
-    "qr_w8a8_gemm", "qr_linear_fused", "qr_linear_fused_noalloc",
+    "qr_w8a8_gemm", "qr_w8a8_gemm_quant", "qr_linear_fused", "qr_linear_fused_noalloc",
     "qr_workspace_size", "qr_gemm_plan", "qr_tile_name", "qr_num_tiles", "qr_set_plan_override",
     "qr_last_error", "qr_version", "qr_probe_read", "qr_probe_mfma",
 ]
@@ -54,6 +54,8 @@ _SIGS = {
     "qr_mx_quantize": (_int, [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp]),
     "qr_mx_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _vp]),
     "qr_w8a8_gemm": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _sz, _vp]),
+    "qr_w8a8_gemm_quant": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _i64, _i64,
+                                  _f32, _vp, _vp, _vp, _sz, _vp]),
     "qr_linear_fused": (_int, [_vp, _i64, _f32, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _sz, _vp]),
     "qr_linear_fused_noalloc": (_int, [_vp, _i64, _f32, _vp, _vp, _i64, _i64, _i64, _int, _vp, _i64,
                                        _vp]),
@@ -388,6 +390,61 @@ def w8a8_gemm(Xq, scale_x, Wq, scale_w, qt, out="bf16", Y=None, ws=None):
                                 OUT[out], _ptr(Y), ldy, _ptr(ws), wsb, _stream(Xq.device))
     _check("qr_w8a8_gemm", st)
     return Y
+
+
+_wsq = {}
+
+
+def quant_workspace(nbytes, device):
+    """The binding's workspace for qr_w8a8_gemm_quant: one zeroed buffer per
+    (device, stream), separate from the other calls' (its header must stay
+    as the fused launches leave it); outgrown buffers are kept alive."""
+    if nbytes == 0:
+        return None, 0
+    dev = torch.device(device)
+    idx = dev.index if dev.index is not None else torch.cuda.current_device()
+    key = (idx, torch.cuda.current_stream(idx).cuda_stream)
+    buf = _wsq.get(key)
+    if buf is None or buf.numel() < nbytes:
+        if buf is not None:
+            _ws_retired.append(buf)
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=torch.device("cuda", idx))
+        _wsq[key] = buf
+    return buf, buf.numel()
+
+
+def w8a8_gemm_quant(Xq, scale_x, Wq, scale_w, qt, Y=None, q_cols=None, q_act_mult=1.0,
+                    Xq_next=None, scale_x_next=None, ws=None):
+    """Y = dequant(Xq @ Wq^T) in bf16, and (q_cols = (c0, c1)) the per-token
+    quantization of Y[:, c0:c1] with q_act_mult -> (Y, Xq_next, scale_x_next).
+    `ws`, if given, must be a workspace zeroed once when allocated and used
+    only by this call."""
+    _need_cuda(Xq, scale_x, Wq, scale_w, Y, Xq_next, scale_x_next)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    if Wq.shape[1] != K:
+        raise ValueError("Xq and Wq disagree on K")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=Xq.device)
+    ldy = _rows(Y, "Y")
+    c0, c1 = (0, 0) if q_cols is None else q_cols
+    if q_cols is not None:
+        if Xq_next is None:
+            Xq_next = torch.empty((M, c1 - c0), dtype=code_dtype(qt), device=Xq.device)
+        if scale_x_next is None:
+            scale_x_next = torch.empty(M, dtype=torch.float32, device=Xq.device)
+    need = workspace_size("qr_w8a8_gemm_quant", M, N, K, qt)
+    if ws is None:
+        ws, wsb = quant_workspace(need, Xq.device)
+    else:
+        wsb = ws.numel() * ws.element_size()
+    with torch.cuda.device(Xq.device):
+        st = lib().qr_w8a8_gemm_quant(_ptr(Xq), _ptr(scale_x), _ptr(Wq), _ptr(scale_w), M, N, K,
+                                      _qt(qt), _ptr(Y), ldy, c0, c1 - c0, float(q_act_mult),
+                                      _ptr(Xq_next), _ptr(scale_x_next), _ptr(ws), wsb,
+                                      _stream(Xq.device))
+    _check("qr_w8a8_gemm_quant", st)
+    return Y, Xq_next, scale_x_next
 
 
 def linear_fused(X, act_mult, Wq, scale_w, qt, Y=None, ws=None):

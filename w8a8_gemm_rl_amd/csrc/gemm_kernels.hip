@@ -91,6 +91,24 @@ struct Mfma<kQFp8, 32> {
 // swizzle; with stride 0 the bound check is offset < num_records.
 constexpr int kBufWord3 = 0x00020000;
 
+// Fused chain epilogue (one launch per linear of a decode chain): the
+// split-K sum and the per-token quantization of the output for the next
+// linear happen inside the GEMM launch, across blocks, behind grid-wide
+// barriers (all blocks of such a launch are resident at once; the host
+// checks). Fields are unused by plain launches.
+struct FuseParams {
+  uint32_t* bar;   // [0] arrivals, [1] generation (advances by 2 per launch), [2] timeout flag
+  uint32_t* pmax;  // [2][kFuseMaxM] per-token absmax bits; buffer (gen / 2) & 1 is this launch's
+  uint32_t* part;  // split-K partial sums [splitk][M][N]
+  uint8_t* xq2;    // [M][qcn] codes of Y[:, qc0 : qc0 + qcn]
+  float* sx2;      // [M] their per-token scales
+  int64_t qc0, qcn;
+  float am2;       // act_mult of the next linear
+  int ipw;         // split-K sum items (256 outputs of one token) per wave
+  uint16_t* y;     // bf16 output of a split launch (Y itself holds the partial sums there)
+  int64_t ldy;
+};
+
 struct KParams {
   const uint8_t* Xq;
   const float* sx;
@@ -104,6 +122,7 @@ struct KParams {
   int splitk;
   int tiles_n, tiles_m, nks;
   int rn;  // weight rows per tile: a multiple of 8, at most the tile's BN
+  FuseParams f;
 };
 
 // XOR swizzle of the 16-byte chunk index inside an LDS row. The LDS serves
@@ -317,6 +336,317 @@ __device__ __forceinline__ void store_tile_staged(
 }
 
 // ---------------------------------------------------------------------------
+// Fused chain epilogue.
+//
+// Barrier: bar[0] counts arriving blocks; the last one resets it to zero and
+// then publishes the next generation in bar[1], which the others wait for.
+// Generations advance by exactly 2 per launch (an intermediate barrier
+// publishes g0 + 1, the last g0 + 2), so (g0 / 2) & 1 alternates between
+// launches and selects this launch's half of the per-token absmax buffer;
+// the launch clears the other half for the next one. Both words and both
+// halves start at zero (the caller zeroes the workspace header once) and
+// every completed launch leaves them so.
+//
+// The blocks of one launch run on different XCDs, whose L2 caches are not
+// kept coherent with each other for ordinary stores. Every word one block
+// writes and another reads inside the launch (barrier words, per-token
+// maxima, split-K partial sums) is therefore stored, loaded or updated with
+// device-scope atomic operations, which the hardware performs at the
+// device's point of coherence; a wave waits for its own such operations
+// (vmcnt 0) before its block arrives. No cache-wide write-back or
+// invalidate is issued (one per wave cost about 0.2 us each, serialized per
+// XCD). Ordinary stores (bf16 outputs, codes, the next launch's cleared
+// half) are only read by later launches.
+// The wait is bounded: a block that waits for more than about 0.3 s sets
+// bar[2] and goes on (results are then wrong but the kernel ends).
+// ---------------------------------------------------------------------------
+constexpr int kSpinLimit = 1 << 20;
+
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_own_memory_ops() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Read by every wave (one load each, no LDS: some tiles use all of it). It
+// cannot change before this block has arrived at the first barrier.
+__device__ __forceinline__ uint32_t fuse_generation(uint32_t* bar) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)ld_dev(&bar[1]));
+}
+
+__device__ __forceinline__ void grid_barrier(uint32_t* bar, uint32_t target) {
+  wait_own_memory_ops();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&bar[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 == gridDim.x) {
+      st_dev(&bar[0], 0u);
+      wait_own_memory_ops();  // the reset lands before any block can arrive again
+      st_dev(&bar[1], target);
+    } else {
+      int spins = 0;
+      while (ld_dev(&bar[1]) != target) {
+        if (++spins > kSpinLimit) {
+          __hip_atomic_fetch_or(&bar[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Split-K partial sums of the fused path, with device-scope stores (another
+// block adds them after the barrier). N % 4 == 0 there, so every group of
+// four outputs is 16 contiguous, 16-byte aligned bytes.
+template <int QT, int T, int BN, int BM, int WN, int WM, typename acc_t, int FN, int FM>
+__device__ __forceinline__ void store_partials_dev(const KParams& p, const acc_t (&acc)[FN][FM],
+                                                   int tn, int tm, int z, int wn, int wm,
+                                                   int lane) {
+  constexpr int NG = Mfma<QT, T>::NACC / 4;
+  const int64_t N = p.N, M = p.M;
+  uint32_t* part = p.f.part + (int64_t)z * M * N;
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const int nl = epi_nloc<T, BN, WN>(wn, i, g, lane);
+        const int64_t n0 = (int64_t)tn * p.rn + nl;
+        const int64_t m = epi_row<T, BN, BM, WN, WM>(p, tm, wm, j, lane);
+        if (m >= M || n0 >= N || nl >= p.rn) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (QT == kQInt8) w[e] = (uint32_t)acc[i][j][4 * g + e];
+          else w[e] = __float_as_uint(acc[i][j][4 * g + e]);
+        }
+        uint64_t* y = reinterpret_cast<uint64_t*>(part + m * N + n0);
+        st_dev64(y, (uint64_t)w[0] | ((uint64_t)w[1] << 32));
+        st_dev64(y + 1, (uint64_t)w[2] | ((uint64_t)w[3] << 32));
+      }
+}
+
+__device__ __forceinline__ uint32_t* pmax_half(const FuseParams& f, uint32_t g0, int which) {
+  return f.pmax + (int64_t)(((g0 >> 1) + which) & 1) * qr::kFuseMaxM;
+}
+
+// Clear the other half of the absmax buffer for the next launch.
+__device__ __forceinline__ void clear_next_pmax(const FuseParams& f, uint32_t g0) {
+  uint32_t* nx = pmax_half(f, g0, 1);
+  const int nt = blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * nt + threadIdx.x; i < qr::kFuseMaxM;
+       i += (int64_t)gridDim.x * nt)
+    st_dev(&nx[i], 0u);
+}
+
+// |bf16| of the two halves of a packed word, as fp32
+__device__ __forceinline__ float absmax2(uint32_t w) {
+  return fmaxf(fabsf(bf16_lo(w)), fabsf(bf16_hi(w)));
+}
+
+// Codes of four bf16 outputs (packed in two words) with step t; zero step:
+// zero codes (an all-zero quantized row), as the per-token quantizer.
+template <int QT>
+__device__ __forceinline__ uint32_t codes4_of(uint32_t w0, uint32_t w1, float t) {
+  if (t == 0.0f) return 0u;
+  return quant_codes4<QT>(bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1), t);
+}
+
+// No split: the outputs are still in the accumulators. Per-token absmax of
+// the quantized columns (lanes, then the waves that share the tokens through
+// LDS, then one atomic max per token and block), the bf16 stores, the
+// barrier, then the codes from the same bf16 values.
+template <int QT, int T, int BN, int BM, int WN, int WM, int LDT, int CH, typename acc_t, int FN,
+          int FM>
+__device__ __forceinline__ void fused_direct_tail(const KParams& p, const acc_t (&acc)[FN][FM],
+                                                  const EpiScales<FN, FM, Mfma<QT, T>::NACC / 4>& sc,
+                                                  uint8_t* smem, uint32_t g0, int tn, int tm, int wn,
+                                                  int wm, int lane, int tid) {
+  constexpr int NG = Mfma<QT, T>::NACC / 4;
+  constexpr int WTM = BM / WM;
+  const FuseParams& f = p.f;
+  const int64_t N = p.N, M = p.M;
+  const int64_t q0 = f.qc0, q1 = f.qc0 + f.qcn;
+  auto nloc = [&](int i, int g) -> int { return epi_nloc<T, BN, WN>(wn, i, g, lane); };
+  auto inq = [&](int i, int g) -> bool {
+    const int64_t n0 = (int64_t)tn * p.rn + nloc(i, g);
+    return nloc(i, g) < p.rn && n0 < N && n0 >= q0 && n0 < q1;
+  };
+  auto ybits = [&](int i, int j, int g, int e) -> uint32_t {
+    return epi_bf16((float)acc[i][j][4 * g + e], sc.sx[j], sc.sw[i][g][e]);
+  };
+  // ---- per-token absmax of this block's quantized columns
+  float tmx[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+        if (inq(i, g)) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v = fmaxf(v, fabsf(__uint_as_float(ybits(i, j, g, e) << 16)));
+        }
+    // lanes holding the same token: l % T
+#pragma unroll
+    for (int o = T; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    tmx[j] = v;
+  }
+  uint32_t* red = reinterpret_cast<uint32_t*>(smem);  // [BM] token maxima (bits)
+  __syncthreads();  // every wave is past its last read of the operand ring
+  for (int t = tid; t < BM; t += 64 * WN * WM) red[t] = 0u;
+  __syncthreads();
+  if (lane < T) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) atomicMax(&red[wm * WTM + j * T + lane], __float_as_uint(tmx[j]));
+  }
+  __syncthreads();
+  const int64_t bn0 = (int64_t)tn * p.rn;
+  const int64_t bn1 = bn0 + p.rn < N ? bn0 + p.rn : N;
+  const bool any_q = bn0 < q1 && bn1 > q0;  // this block owns quantized columns
+  uint32_t* pm = pmax_half(f, g0, 0);
+  if (any_q) {
+    for (int t = tid; t < BM; t += 64 * WN * WM) {
+      const int64_t m = (int64_t)tm * BM + t;
+      if (m < M) atomicMax(&pm[m], red[t]);
+    }
+  }
+  // ---- bf16 outputs
+  if (CH >= WTM && (p.ldy & 7) == 0)
+    store_tile_staged<QT, T, BN, BM, WN, WM, LDT, (CH >= WTM ? CH : WTM)>(p, acc, sc, smem, tn, tm,
+                                                                           wn, wm, lane, tid);
+  else
+    store_tile<QT, T, BN, BM, WN, WM>(p, acc, sc, tn, tm, 0, wn, wm, lane);
+  clear_next_pmax(f, g0);
+  grid_barrier(f.bar, g0 + 2);
+  if (!any_q) return;
+  // ---- codes of the quantized columns, from the same bf16 values
+  const float Q = qmax<QT>();
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int64_t m = epi_row<T, BN, BM, WN, WM>(p, tm, wm, j, lane);
+    if (m >= M) continue;
+    const float t = __uint_as_float(ld_dev(&pm[m])) / Q;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (!inq(i, g)) continue;
+        const int64_t n0 = bn0 + nloc(i, g);
+        const uint32_t w0 = ybits(i, j, g, 0) | (ybits(i, j, g, 1) << 16);
+        const uint32_t w1 = ybits(i, j, g, 2) | (ybits(i, j, g, 3) << 16);
+        *reinterpret_cast<uint32_t*>(f.xq2 + m * f.qcn + (n0 - q0)) = codes4_of<QT>(w0, w1, t);
+      }
+  }
+  // the scales, by the block that owns the first quantized column
+  if (bn0 <= q0 && q0 < bn1) {
+    for (int t = tid; t < BM; t += 64 * WN * WM) {
+      const int64_t m = (int64_t)tm * BM + t;
+      if (m < M) f.sx2[m] = (__uint_as_float(ld_dev(&pm[m])) / Q) * f.am2;
+    }
+  }
+}
+
+// Split K: the partial sums are in the workspace. After the first barrier
+// every wave adds up to f.ipw items of 256 outputs of one token (in split
+// order, as the separate reduction kernel does), stores their bf16 values,
+// and keeps them in registers for the codes; per-token absmax by one atomic
+// max per item; second barrier; codes.
+template <int QT, int NW>
+__device__ __forceinline__ void fused_splitk_tail(const KParams& p, uint32_t g0, int wid, int lane) {
+  constexpr int kItems = kFuseItems;
+  const FuseParams& f = p.f;
+  const int64_t N = p.N, M = p.M;
+  const int S = p.splitk;
+  const bool quant = f.qcn > 0;
+  const int64_t q0 = f.qc0, q1 = f.qc0 + f.qcn;
+  grid_barrier(f.bar, quant ? g0 + 1 : g0 + 2);
+  const int64_t nseg = (N + 255) / 256;
+  const int64_t items = M * nseg;
+  const int64_t tw = (int64_t)gridDim.x * NW;
+  const int64_t gw = (int64_t)blockIdx.x * NW + wid;
+  uint32_t* pm = pmax_half(f, g0, 0);
+  uint32_t keep[kItems][2];
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    keep[r][0] = keep[r][1] = 0u;
+    const int64_t it = gw + r * tw;
+    if (r >= f.ipw || it >= items) continue;
+    const int64_t m = it / nseg;
+    const int64_t n0 = (it - m * nseg) * 256 + 4 * lane;
+    float amax = 0.0f;
+    if (n0 < N) {
+      const uint32_t* src = f.part + m * N + n0;
+      int32_t si[4] = {0, 0, 0, 0};
+      float sf[4] = {0.f, 0.f, 0.f, 0.f};
+      uint4 w[8];
+#pragma unroll
+      for (int zz = 0; zz < 8; ++zz)
+        if (zz < S) {
+          const uint64_t* q = reinterpret_cast<const uint64_t*>(src + (int64_t)zz * M * N);
+          const uint64_t lo = ld_dev64(q), hi = ld_dev64(q + 1);
+          w[zz] = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+        }
+#pragma unroll
+      for (int zz = 0; zz < 8; ++zz) {
+        if (zz < S) {
+          const uint32_t u[4] = {w[zz].x, w[zz].y, w[zz].z, w[zz].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (QT == kQInt8) si[e] += (int32_t)u[e];
+            else sf[e] += __uint_as_float(u[e]);
+          }
+        }
+      }
+      const float sxm = p.sx[m];
+      uint32_t bb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = (QT == kQInt8) ? (float)si[e] : sf[e];
+        bb[e] = epi_bf16(a, sxm, p.sw[n0 + e]);
+      }
+      keep[r][0] = bb[0] | (bb[1] << 16);
+      keep[r][1] = bb[2] | (bb[3] << 16);
+      *reinterpret_cast<uint2*>(f.y + m * f.ldy + n0) = make_uint2(keep[r][0], keep[r][1]);
+      if (quant && n0 >= q0 && n0 < q1) amax = fmaxf(absmax2(keep[r][0]), absmax2(keep[r][1]));
+    }
+    if (quant) {
+      amax = wave_max(amax);
+      if (lane == 0) atomicMax(&pm[m], __float_as_uint(amax));
+    }
+  }
+  clear_next_pmax(f, g0);
+  if (!quant) return;
+  grid_barrier(f.bar, g0 + 2);
+  const float Q = qmax<QT>();
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int64_t it = gw + r * tw;
+    if (r >= f.ipw || it >= items) continue;
+    const int64_t m = it / nseg;
+    const int64_t n0 = (it - m * nseg) * 256 + 4 * lane;
+    if (n0 >= N || n0 < q0 || n0 >= q1) continue;
+    const float t = __uint_as_float(ld_dev(&pm[m])) / Q;
+    *reinterpret_cast<uint32_t*>(f.xq2 + m * f.qcn + (n0 - q0)) = codes4_of<QT>(keep[r][0], keep[r][1], t);
+    if (n0 == q0) f.sx2[m] = t * f.am2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // LDS-DMA variant. Operand tiles move from global memory straight into LDS
 // with buffer_load_dwordx4 ... lds: one wave instruction writes 64 x 16
 // bytes to LDS at M0 + offset + 16 * lane, where the 12-bit instruction
@@ -396,7 +726,7 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   }
 }
 
-template <int QT, int T, int BN, int BM, int WN, int WM, int S, bool IP>
+template <int QT, int T, int BN, int BM, int WN, int WM, int S, bool IP, bool FUSE>
 __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams p) {
   using MF = Mfma<QT, T>;
   using acc_t = typename MF::acc_t;
@@ -621,6 +951,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
   constexpr bool kEarlyScales = FN * FM * MF::NACC < 128;
   EpiScales<FN, FM, MF::NACC / 4> sc;
   if constexpr (kEarlyScales) load_scales<QT, T, BN, BM, WN, WM>(p, tn, tm, wn, wm, lane, sc);
+  uint32_t g0 = 0;  // fused launches: barrier generation at launch start
+  if constexpr (FUSE) g0 = fuse_generation(p.f.bar);
 
   const int nk = ks1 - ks0;
 #pragma unroll
@@ -638,14 +970,25 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
 
   if constexpr (!kEarlyScales) load_scales<QT, T, BN, BM, WN, WM>(p, tn, tm, wn, wm, lane, sc);
 
+  constexpr int LDT = BN + 4;  // staged row stride in bf16 (8 bytes of padding)
+  constexpr int CHF = (S * STAGE) / (LDT * 2);      // tokens that fit the ring
+  constexpr int CH0 = CHF >= BM ? BM : CHF / WTM * WTM;  // chunk: whole wave tiles
+  if constexpr (FUSE) {
+    if (p.splitk > 1) {
+      store_partials_dev<QT, T, BN, BM, WN, WM>(p, acc, tn, tm, z, wn, wm, lane);
+      fused_splitk_tail<QT, NW>(p, g0, wid, lane);
+    } else {
+      fused_direct_tail<QT, T, BN, BM, WN, WM, LDT, CH0>(p, acc, sc, smem, g0, tn, tm, wn, wm,
+                                                          lane, tid);
+    }
+    return;
+  }
+
   // bf16 outputs go through LDS (the ring is free once every wave is past
   // its last K step), so each lane stores 16 contiguous bytes of a token's
   // row: the MFMA layout would make every store instruction write 8 bytes
   // into each of 32 rows. Split partial sums, raw accumulators and row
   // strides that are not a multiple of 8 take the direct path.
-  constexpr int LDT = BN + 4;  // staged row stride in bf16 (8 bytes of padding)
-  constexpr int CHF = (S * STAGE) / (LDT * 2);      // tokens that fit the ring
-  constexpr int CH0 = CHF >= BM ? BM : CHF / WTM * WTM;  // chunk: whole wave tiles
   if constexpr (CH0 >= WTM) {
     if (p.splitk == 1 && !p.out_raw && (p.ldy & 7) == 0) {
       store_tile_staged<QT, T, BN, BM, WN, WM, LDT, CH0>(p, acc, sc, smem, tn, tm, wn, wm, lane,
@@ -875,34 +1218,35 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
 // same with MFMA operands double-buffered and interleaved with the MFMAs
 // (scheduling groups), 2 the direct register-path kernel; S is the LDS ring
 // depth (the prefetch depth in K steps for KIND 2), T the MFMA edge, BN x BM
-// the macro tile over N and M, WN x WM the waves along N and M. Every K step
-// covers 128 bytes of K.
+// the macro tile over N and M, WN x WM the waves along N and M, FU 1 when the
+// tile also has a fused chain-epilogue instantiation (the tiles the planner
+// picks up to 1024 tokens). Every K step covers 128 bytes of K.
 // ---------------------------------------------------------------------------
-#define QR_TILES(X)                                                       \
-  X(0, 4, 16, 128, 32, 8, 1)  /*  0: M <= 32, weight streaming        */ \
-  X(0, 4, 32, 128, 64, 4, 2)  /*  1: M <= 64; narrow 256-token layers */ \
-  X(0, 4, 32, 128, 128, 2, 4) /*  2: M <= 128; long-K 256-token ones  */ \
-  X(0, 3, 32, 192, 128, 2, 2) /*  3: 4-wave version of tile 14        */ \
-  X(0, 3, 32, 256, 128, 4, 2) /*  4: long-K / narrow large-M layers   */ \
-  X(0, 2, 32, 256, 256, 2, 4) /*  5: wide large-M layers              */ \
-  X(0, 3, 32, 128, 256, 2, 4) /*  6: 256-token alternative            */ \
-  X(0, 3, 32, 96, 256, 1, 4)  /*  7: 256-token alternative, 96 rows   */ \
-  X(0, 4, 32, 128, 32, 4, 1)  /*  8: M <= 32 alternative, 4 waves     */ \
-  X(0, 4, 16, 64, 16, 4, 1)   /*  9: M <= 16 alternative, narrow      */ \
-  X(1, 3, 32, 192, 128, 2, 2) /* 10: interleaved variant of tile 3    */ \
-  X(1, 4, 16, 128, 32, 8, 1)  /* 11: interleaved variant of tile 0    */ \
-  X(2, 4, 16, 128, 16, 8, 1)  /* 12: direct, M <= 16                  */ \
-  X(2, 2, 16, 128, 32, 4, 1)  /* 13: direct, M <= 32                  */ \
-  X(0, 4, 32, 192, 128, 2, 4) /* 14: wide 256-token layers, 8 waves   */ \
-  X(1, 4, 32, 192, 128, 2, 4) /* 15: interleaved variant of tile 14   */ \
-  X(0, 4, 16, 80, 64, 5, 1)   /* 16: 256-token INT8 QKV, 5 waves      */
+#define QR_TILES(X)                                                          \
+  X(0, 4, 16, 128, 32, 8, 1, 1)  /*  0: M <= 32, weight streaming        */ \
+  X(0, 4, 32, 128, 64, 4, 2, 1)  /*  1: M <= 64; narrow 256-token layers */ \
+  X(0, 4, 32, 128, 128, 2, 4, 1) /*  2: M <= 128; long-K 256-token ones  */ \
+  X(0, 3, 32, 192, 128, 2, 2, 0) /*  3: 4-wave version of tile 14        */ \
+  X(0, 3, 32, 256, 128, 4, 2, 1) /*  4: long-K / narrow large-M layers   */ \
+  X(0, 2, 32, 256, 256, 2, 4, 0) /*  5: wide large-M layers              */ \
+  X(0, 3, 32, 128, 256, 2, 4, 1) /*  6: 256-token alternative            */ \
+  X(0, 3, 32, 96, 256, 1, 4, 0)  /*  7: 256-token alternative, 96 rows   */ \
+  X(0, 4, 32, 128, 32, 4, 1, 1)  /*  8: M <= 32 alternative, 4 waves     */ \
+  X(0, 4, 16, 64, 16, 4, 1, 1)   /*  9: M <= 16 alternative, narrow      */ \
+  X(1, 3, 32, 192, 128, 2, 2, 0) /* 10: interleaved variant of tile 3    */ \
+  X(1, 4, 16, 128, 32, 8, 1, 0)  /* 11: interleaved variant of tile 0    */ \
+  X(2, 4, 16, 128, 16, 8, 1, 0)  /* 12: direct, M <= 16                  */ \
+  X(2, 2, 16, 128, 32, 4, 1, 0)  /* 13: direct, M <= 32                  */ \
+  X(0, 4, 32, 192, 128, 2, 4, 1) /* 14: wide 256-token layers, 8 waves   */ \
+  X(1, 4, 32, 192, 128, 2, 4, 0) /* 15: interleaved variant of tile 14   */ \
+  X(0, 4, 16, 80, 64, 5, 1, 1)   /* 16: 256-token INT8 QKV, 5 waves      */
 
 #define QR_STR(x) #x
-#define QR_DESC(KIND, S, T, BN, BM, WN, WM)                                        \
+#define QR_DESC(KIND, S, T, BN, BM, WN, WM, FU)                                    \
   {KIND == 2   ? "dir" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN                \
    : KIND == 1 ? "dmaip" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM      \
                : "dma" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM,       \
-   T, BN, BM, 128, 64 * WN * WM, S},
+   T, BN, BM, 128, 64 * WN * WM, S, FU},
 const TileDesc kTiles[] = {QR_TILES(QR_DESC)};
 #undef QR_DESC
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
@@ -913,9 +1257,29 @@ hipError_t launch_one(const KParams& kp, unsigned grid, hipStream_t st) {
     hipLaunchKernelGGL((gemm_direct_kernel<QT, BN, BM, WN, S>), dim3(grid), dim3(64 * WN), 0, st,
                        kp);
   else
-    hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, KIND == 1>), dim3(grid),
+    hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, KIND == 1, false>), dim3(grid),
                        dim3(64 * WN * WM), 0, st, kp);
   return hipGetLastError();
+}
+
+// Fused-epilogue kernel of a tile: its function (for the residency check) or
+// its launch.
+template <int QT, int KIND, int S, int T, int BN, int BM, int WN, int WM, int FU>
+const void* fused_fn() {
+  if constexpr (FU == 1 && KIND == 0)
+    return reinterpret_cast<const void*>(&gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, false, true>);
+  else
+    return nullptr;
+}
+template <int QT, int KIND, int S, int T, int BN, int BM, int WN, int WM, int FU>
+hipError_t launch_fused_one(const KParams& kp, unsigned grid, hipStream_t st) {
+  if constexpr (FU == 1 && KIND == 0) {
+    hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, false, true>), dim3(grid),
+                       dim3(64 * WN * WM), 0, st, kp);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -938,7 +1302,7 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   const unsigned grid = (unsigned)(plan.tiles_n * plan.tiles_m * plan.splitk);
   hipError_t e = hipErrorInvalidValue;
   int idx = 0;
-#define QR_CASE(KIND, S, T, BN, BM, WN, WM)                                        \
+#define QR_CASE(KIND, S, T, BN, BM, WN, WM, FU)                                    \
   if (plan.tile == idx) {                                                           \
     e = qt == kQInt8 ? launch_one<kQInt8, KIND, S, T, BN, BM, WN, WM>(kp, grid, st) \
                      : launch_one<kQFp8, KIND, S, T, BN, BM, WN, WM>(kp, grid, st); \
@@ -971,6 +1335,90 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   if (qt == kQInt8) by_splits(std::integral_constant<int, kQInt8>{});
   else by_splits(std::integral_constant<int, kQFp8>{});
   return hipGetLastError();
+}
+
+namespace {
+
+// Items of 256 outputs of one token per wave of a split plan's fused sum.
+int64_t fused_items_per_wave(const GemmPlan& plan, int64_t M, int64_t N) {
+  const int64_t waves = plan.tiles_n * plan.tiles_m * plan.splitk * (tile_desc(plan.tile).NT / 64);
+  const int64_t items = M * ((N + 255) / 256);
+  return (items + waves - 1) / waves;
+}
+
+// Blocks of the fused kernel of (tile, qt) one CU holds at once (0 if it
+// has none); queried once per device and cached.
+int fused_blocks_per_cu(int tile, int qt, int dev) {
+  constexpr int kDevs = 16;
+  static int cache[kDevs][2][32];  // 0: not queried yet; else 1 + blocks
+  if (dev < 0 || dev >= kDevs || tile < 0 || tile >= 32) return 0;
+  int& c = cache[dev][qt == kQInt8 ? 0 : 1][tile];
+  if (c == 0) {
+    const void* fn = nullptr;
+    int idx = 0;
+#define QR_FN(KIND, S, T, BN, BM, WN, WM, FU)                                          \
+  if (tile == idx)                                                                    \
+    fn = qt == kQInt8 ? fused_fn<kQInt8, KIND, S, T, BN, BM, WN, WM, FU>()            \
+                      : fused_fn<kQFp8, KIND, S, T, BN, BM, WN, WM, FU>();            \
+  ++idx;
+    QR_TILES(QR_FN)
+#undef QR_FN
+    int nb = 0;
+    if (fn && hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, tile_desc(tile).NT, 0) !=
+                  hipSuccess)
+      nb = 0;
+    c = 1 + nb;
+  }
+  return c - 1;
+}
+
+}  // namespace
+
+bool fused_ok(const GemmPlan& plan, int qt, int64_t M, int64_t N) {
+  if (plan.tile < 0 || plan.tile >= kNumTiles || !kTiles[plan.tile].FU) return false;
+  if (M > kFuseMaxM || M <= 0 || N <= 0) return false;
+  if (plan.splitk > 1 && fused_items_per_wave(plan, M, N) > kFuseItems) return false;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;
+  const int64_t grid = plan.tiles_n * plan.tiles_m * plan.splitk;
+  return grid <= (int64_t)cus * fused_blocks_per_cu(plan.tile, qt, dev);
+}
+
+hipError_t launch_gemm_fused(const GemmPlan& plan, int qt, const GemmArgs& a, const FuseArgs& fa,
+                             hipStream_t st) {
+  KParams kp;
+  kp.Xq = a.Xq; kp.sx = a.sx; kp.Wq = a.Wq; kp.sw = a.sw;
+  kp.M = a.M; kp.N = a.N; kp.K = a.K;
+  kp.splitk = plan.splitk;
+  kp.tiles_n = (int)plan.tiles_n; kp.tiles_m = (int)plan.tiles_m; kp.nks = (int)plan.nks;
+  kp.rn = plan.rows;
+  uint32_t* hdr = static_cast<uint32_t*>(fa.header);
+  kp.f.bar = hdr;
+  kp.f.pmax = hdr + 64;  // 256 bytes in
+  kp.f.part = static_cast<uint32_t*>(fa.part);
+  kp.f.xq2 = fa.xq2; kp.f.sx2 = fa.sx2;
+  kp.f.qc0 = fa.qc0; kp.f.qcn = fa.qcn; kp.f.am2 = fa.am2;
+  kp.f.ipw = plan.splitk > 1 ? (int)fused_items_per_wave(plan, a.M, a.N) : 0;
+  kp.f.y = static_cast<uint16_t*>(a.Y); kp.f.ldy = a.ldy;
+  if (plan.splitk > 1) {
+    kp.Y = fa.part; kp.ldy = a.N; kp.out_raw = 1; kp.vec = (a.N % 4) == 0;
+  } else {
+    kp.Y = a.Y; kp.ldy = a.ldy; kp.out_raw = 0; kp.vec = (a.ldy % 4) == 0;
+  }
+  const unsigned grid = (unsigned)(plan.tiles_n * plan.tiles_m * plan.splitk);
+  hipError_t e = hipErrorInvalidValue;
+  int idx = 0;
+#define QR_FCASE(KIND, S, T, BN, BM, WN, WM, FU)                                              \
+  if (plan.tile == idx) {                                                                      \
+    e = qt == kQInt8 ? launch_fused_one<kQInt8, KIND, S, T, BN, BM, WN, WM, FU>(kp, grid, st)  \
+                     : launch_fused_one<kQFp8, KIND, S, T, BN, BM, WN, WM, FU>(kp, grid, st); \
+  }                                                                                            \
+  ++idx;
+  QR_TILES(QR_FCASE)
+#undef QR_FCASE
+  return e;
 }
 
 }  // namespace qr

@@ -139,6 +139,8 @@ size_t qr_workspace_size(const char* fn, int64_t M, int64_t N, int64_t K, int qt
   const qr::GemmPlan p = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk, g_force_rows);
   const size_t gemm = (M == 0 || N == 0) ? 0 : p.ws_bytes();
   if (std::strcmp(fn, "qr_w8a8_gemm") == 0) return gemm;
+  if (std::strcmp(fn, "qr_w8a8_gemm_quant") == 0)
+    return (M == 0 || N == 0) ? 0 : qr::kFuseHeaderBytes + p.part_bytes;
   if (std::strcmp(fn, "qr_linear_fused") == 0) {
     if (M == 0 || N == 0) return 0;
     return p.part_bytes + align256((size_t)M * (size_t)K) + align256((size_t)M * 4);
@@ -385,6 +387,70 @@ int qr_w8a8_gemm(const void* Xq, const float* scale_x, const void* Wq, const flo
   (void)hipGetLastError();
   return run_gemm(fn, plan, Xq, scale_x, Wq, scale_w, M, N, K, qt, out, Y, ldy, workspace,
                   static_cast<hipStream_t>(stream));
+}
+
+int qr_w8a8_gemm_quant(const void* Xq, const float* scale_x, const void* Wq, const float* scale_w,
+                       int64_t M, int64_t N, int64_t K, int qt, void* Y, int64_t ldy, int64_t q_col0,
+                       int64_t q_cols, float q_act_mult, void* Xq_next, float* scale_x_next,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "qr_w8a8_gemm_quant";
+  int st = check_shape(fn, M, N, K, qt);
+  if (st != QR_OK) return st;
+  st = check_gemm_io(fn, M, N, K, QR_OUT_BF16, true, scale_x, Wq, scale_w, Y, ldy);
+  if (st != QR_OK) return st;
+  if (M > 0 && N > 0 && K > 0 && !Xq) return fail(QR_ERR_INVALID_ARG, "%s: null Xq", fn);
+  if (!aligned(Xq, 16)) return fail(QR_ERR_UNSUPPORTED, "%s: misaligned Xq", fn);
+  if (N * K >= kMaxCodeBytes || M * K >= kMaxCodeBytes)
+    return fail(QR_ERR_UNSUPPORTED, "%s: a code matrix of 2^31 - 2^16 bytes or more", fn);
+  if (q_col0 < 0 || q_cols < 0 || q_col0 + q_cols > N)
+    return fail(QR_ERR_INVALID_ARG, "%s: quantized columns [%lld, %lld) outside [0, N=%lld)", fn,
+                (long long)q_col0, (long long)(q_col0 + q_cols), (long long)N);
+  if (q_cols > 0) {
+    if (q_col0 % 16 != 0 || q_cols % 16 != 0)
+      return fail(QR_ERR_UNSUPPORTED, "%s: q_col0 and q_cols must be multiples of 16", fn);
+    if (!std::isfinite(q_act_mult) || !(q_act_mult > 0.0f))
+      return fail(QR_ERR_INVALID_ARG, "%s: q_act_mult must be finite and > 0", fn);
+    if (M > 0 && (!Xq_next || !scale_x_next))
+      return fail(QR_ERR_INVALID_ARG, "%s: null Xq_next or scale_x_next", fn);
+    if (!aligned(Xq_next, 16) || !aligned(scale_x_next, 4))
+      return fail(QR_ERR_UNSUPPORTED, "%s: misaligned Xq_next (16 bytes) or scale_x_next", fn);
+    if (ldy % 8 != 0) return fail(QR_ERR_UNSUPPORTED, "%s: ldy must be a multiple of 8", fn);
+  }
+  if (M == 0 || N == 0) return ok();
+  const qr::GemmPlan plan = qr::make_plan(M, N, K, qt, g_force_tile, g_force_splitk, g_force_rows);
+  st = check_ws(fn, workspace, workspace_bytes, qr::kFuseHeaderBytes + plan.part_bytes);
+  if (st != QR_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  qr::GemmArgs a;
+  a.Xq = static_cast<const uint8_t*>(Xq);
+  a.sx = scale_x;
+  a.Wq = static_cast<const uint8_t*>(Wq);
+  a.sw = scale_w;
+  a.M = M; a.N = N; a.K = K;
+  a.Y = Y; a.ldy = ldy;
+  a.out_raw = 0;
+  a.part = plan.splitk > 1 ? ws + qr::kFuseHeaderBytes : nullptr;
+  (void)hipGetLastError();
+  const bool want = plan.splitk > 1 || q_cols > 0;
+  if (want && N % 4 == 0 && ldy % 4 == 0 && aligned(Y, 16) && qr::fused_ok(plan, qt, M, N)) {
+    qr::FuseArgs fa;
+    fa.header = ws;
+    fa.part = a.part;
+    fa.xq2 = static_cast<uint8_t*>(Xq_next);
+    fa.sx2 = scale_x_next;
+    fa.qc0 = q_col0;
+    fa.qcn = q_cols;
+    fa.am2 = q_act_mult;
+    return hip_status(qr::launch_gemm_fused(plan, qt, a, fa, hs), fn);
+  }
+  // Not fusable here: the GEMM (with its split-K kernel), then the
+  // per-token quantizer on the column range; the same results.
+  st = hip_status(qr::launch_gemm(plan, qt, a, hs), fn);
+  if (st != QR_OK || q_cols == 0) return st;
+  return hip_status(qr::launch_act_quant(static_cast<const uint16_t*>(Y) + q_col0, M, q_cols, ldy,
+                                         q_act_mult, qt, Xq_next, scale_x_next, hs),
+                    fn);
 }
 
 int qr_linear_fused(const void* X, int64_t ldx, float act_mult, const void* Wq, const float* scale_w,

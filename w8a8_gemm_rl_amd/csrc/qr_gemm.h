@@ -16,6 +16,7 @@ struct TileDesc {
   int BK;  // bytes of K per pipeline stage
   int NT;  // threads per block
   int S;   // LDS-DMA ring slots (prefetch depth in K steps for the direct kernel)
+  int FU;  // 1: has a fused chain-epilogue instantiation
 };
 
 int num_tiles();
@@ -48,5 +49,33 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStream_t st);
+
+// Fused chain epilogue: the split-K sum and the per-token quantization of
+// Y[:, qc0 : qc0 + qcn] for the next linear inside the GEMM launch.
+// Workspace: a header of kFuseHeaderBytes (barrier words at offset 0, the
+// per-token absmax buffer [2][kFuseMaxM] at offset 256; zero before the first
+// launch that uses it, left so by every launch), then the partial sums.
+constexpr size_t kFuseHeaderBytes = (size_t)64 << 10;
+constexpr int64_t kFuseMaxM = 4096;
+constexpr int kFuseItems = 4;  // split-K sum items of 256 outputs per wave, at most
+
+struct FuseArgs {
+  void* header;
+  void* part;
+  uint8_t* xq2;  // [M][qcn]
+  float* sx2;    // [M]
+  int64_t qc0, qcn;
+  float am2;
+};
+
+// Whether `plan` can run fused for this shape: the tile has a fused
+// instantiation, every block of the grid can be resident at once on this
+// device, M <= kFuseMaxM, and a split plan's sum fits kFuseItems items per
+// wave. The shape's other conditions (N, ldy, qc0, qcn multiples of 4) are
+// the caller's.
+bool fused_ok(const GemmPlan& plan, int qt, int64_t M, int64_t N);
+
+hipError_t launch_gemm_fused(const GemmPlan& plan, int qt, const GemmArgs& a, const FuseArgs& fa,
+                             hipStream_t st);
 
 }  // namespace qr
