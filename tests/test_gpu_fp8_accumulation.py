@@ -31,7 +31,7 @@ from gpu_helpers import fp8_acc_bound, to_dev_codes, to_dev_f32
 
 pytestmark = pytest.mark.gpu
 
-NUM_TILES = 17
+NUM_TILES = 10
 C448, CMIN, CONE = 0x7E, 0x01, 0x38  # E4M3FN codes of 448, 2^-9 and 1.0
 
 
@@ -81,7 +81,7 @@ def test_in_group_sum_drops_low_order_products(tile):
     print(f"tile {B.tile_name(tile)}: device sum {np.unique(got).tolist()}, exact {exact[0, 0]}")
 
 
-@pytest.mark.parametrize("tile", [0, 9, 14])
+@pytest.mark.parametrize("tile", [0, 7, 8])
 def test_sums_across_groups_are_exact(tile):
     M, N, K = 40, 72, 256
     xq, wq = _operands(M, N, K, small_at=128)

@@ -27,7 +27,7 @@ from gpu_helpers import DEV, bf16_np, codes_np, to_dev_bf16, to_dev_f32
 pytestmark = pytest.mark.gpu
 
 QTS = ["int8", "fp8"]
-FUSED_TILES = [0, 1, 2, 4, 6, 8, 9, 14, 16]  # tiles with a fused instantiation
+FUSED_TILES = [0, 1, 2, 3, 5, 6, 7, 8, 9]  # tiles with a fused instantiation
 
 
 @pytest.fixture(autouse=True)

@@ -726,26 +726,29 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   }
 }
 
-template <int QT, int T, int BN, int BM, int WN, int WM, int S, bool IP, bool FUSE>
+template <int QT, int T, int BN, int BM, int WN, int WM, int S, int BK, bool FUSE>
 __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams p) {
   using MF = Mfma<QT, T>;
   using acc_t = typename MF::acc_t;
   using op_t = typename MF::op_t;
-  constexpr int BK = 128;
+  static_assert(BK == 128 || BK == 64, "K step of 64 or 128 bytes");
+  constexpr int RB = 1024 / BK;  // rows per 1 KB copy
+  constexpr int CPR = BK / 16;   // 16-byte chunks per row
   constexpr int NW = WN * WM;
   constexpr int WTN = BN / WN, WTM = BM / WM;
   constexpr int FN = WTN / T, FM = WTM / T;
   constexpr int KI = MF::KI, LB = MF::LB;
   constexpr int NKK = BK / KI;
-  // 1 KB row blocks (8 rows of 128 bytes) per stage; the token part is
+  static_assert(NKK >= 1, "an MFMA's K fits the step");
+  // 1 KB row blocks (RB rows of BK bytes) per stage; the token part is
   // padded so every wave issues the same number of copies.
-  constexpr int IA = BN / 8;
-  constexpr int IB0 = BM / 8;
+  constexpr int IA = BN / RB;
+  constexpr int IB0 = BM / RB;
   constexpr int IB = IB0 + (NW - IB0 % NW) % NW;
   constexpr int NA = IA / NW, NB = IB / NW, NI = NA + NB;
   constexpr int GA = (NA + 3) / 4, GB = (NB + 3) / 4, NG = GA + GB;  // M0 groups
   constexpr int STAGE = (IA + IB) * 1024;
-  static_assert(BN % 8 == 0 && BM % 8 == 0 && IA % NW == 0, "row blocks per wave");
+  static_assert(BN % RB == 0 && BM % RB == 0 && IA % NW == 0, "row blocks per wave");
   static_assert(WTN % T == 0 && WTM % T == 0, "wave tile");
   static_assert(S >= 2 && S <= 8 && (S - 2) * NI <= 63, "ring depth");
   static_assert(S * STAGE <= 160 * 1024, "LDS");
@@ -768,8 +771,8 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
     for (int j = 0; j < FM; ++j) acc[i][j] = acc_t{};
 
   // ---- copy addressing. Wave wid moves weight row blocks wid*NA + i and
-  // token row blocks wid*NB + i. Lane l covers row 8*rb + l/8 of the block,
-  // physical chunk l%8. Rows past the tile (rn), past N or M, or in the
+  // token row blocks wid*NB + i. Lane l covers row RB*rb + l/CPR of the
+  // block, physical chunk l%CPR. Rows past the tile (rn), past N or M, or in the
   // padded token rows point at offset 2^31 (beyond any code matrix, which is
   // kept below 2^31 - 2^16 bytes so the bias below stays out of range) and
   // read as zero. Offsets are biased by -1 KB * (i % 4), the instruction
@@ -779,14 +782,14 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
       __builtin_amdgcn_make_buffer_rsrc((void*)p.Wq, (short)0, (int)(uint32_t)(N * K), kBufWord3);
   const __amdgpu_buffer_rsrc_t rsx =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.Xq, (short)0, (int)(uint32_t)(M * K), kBufWord3);
-  const int lrow = lane >> 3, pch = lane & 7;
+  const int lrow = lane / CPR, pch = lane % CPR;
   uint32_t oa[NA], ob[NB];
   bool ka[NA], kb[NB];  // copy i holds real K bytes on the ragged last step
   const bool ktail = (K % BK) != 0;
   const int krem = (int)(K % BK);
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int r = (wid * NA + i) * 8 + lrow;
+    const int r = (wid * NA + i) * RB + lrow;
     const int c = pch ^ swz<BK>(r);
     const int64_t row = (int64_t)tn * p.rn + r;
     const uint32_t bias = 1024u * (uint32_t)(i % 4);
@@ -795,7 +798,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int r = (wid * NB + i) * 8 + lrow;
+    const int r = (wid * NB + i) * RB + lrow;
     const int c = pch ^ swz<BK>(r);
     const int64_t row = (int64_t)tm * BM + r;
     const uint32_t bias = 1024u * (uint32_t)(i % 4);
@@ -895,51 +898,6 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
     }
   };
 
-  op_t na[FN], nb[FM];  // operands of the next sub-step (IP)
-  auto load_ops = [&](int slot, int kk) {
-    const uint8_t* A = smem + slot * STAGE + rbaseA;
-    const uint8_t* B = smem + slot * STAGE + rbaseB;
-#pragma unroll
-    for (int i = 0; i < FN; ++i) na[i] = lds_op(A + i * T * BK, kk);
-#pragma unroll
-    for (int j = 0; j < FM; ++j) nb[j] = lds_op(B + j * T * BK, kk);
-  };
-
-  // IP: operands double-buffered in registers within a K step, and the
-  // LDS reads of sub-step kk + 1 interleaved one by one with the MFMAs of
-  // sub-step kk (scheduling groups), so the reads' latency hides behind the
-  // matrix work.
-  auto compute_ip = [&](int slot, bool do_issue, int islot, int iks) {
-    constexpr int NM = FN * FM, NR = (FN + FM) * (LB / 16);
-    load_ops(slot, 0);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      op_t a[FN], bb[FM];
-#pragma unroll
-      for (int i = 0; i < FN; ++i) a[i] = na[i];
-#pragma unroll
-      for (int j = 0; j < FM; ++j) bb[j] = nb[j];
-      if (do_issue) {
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-          if (g * NKK / NG == kk) issue_group(g, islot, iks);
-      }
-      if (kk + 1 < NKK) load_ops(slot, kk + 1);
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = MF::run(a[i], bb[j], acc[i][j]);
-      if (kk + 1 < NKK) {
-#pragma unroll
-        for (int q = 0; q < NM; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-        }
-        if (NR > NM) __builtin_amdgcn_sched_group_barrier(0x100, NR > NM ? NR - NM : 0, 0);
-      }
-    }
-  };
-
   // ---- main loop. K step ks0 + it lives in slot it % S. At the top of step
   // it the copies of steps up to it + S - 2 have been issued; this wave
   // waits for its copies of step it, the barrier makes every wave's copies
@@ -962,8 +920,7 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
   for (int it = 0; it < nk; ++it) {
     wait_stages<NI, S - 2>(nk - 1 - it);
     __syncthreads();
-    if constexpr (IP) compute_ip(cs, it + S - 1 < nk, is, ks0 + it + S - 1);
-    else compute(cs, it + S - 1 < nk, is, ks0 + it + S - 1);
+    compute(cs, it + S - 1 < nk, is, ks0 + it + S - 1);
     cs = cs + 1 == S ? 0 : cs + 1;
     is = is + 1 == S ? 0 : is + 1;
   }
@@ -997,139 +954,6 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
     }
   }
   store_tile<QT, T, BN, BM, WN, WM>(p, acc, sc, tn, tm, z, wn, wm, lane);
-}
-
-// ---------------------------------------------------------------------------
-// Direct (LDS-free) variant for small token counts, where the product is a
-// weight stream. Every wave owns 16 * FN weight rows and all BM tokens of
-// the tile and loads its MFMA operands straight from global memory into
-// registers, D K steps ahead (a register ring, unrolled so stage indices
-// are compile-time constants). There is no LDS and no barrier, so waves
-// never wait for each other and the hardware interleaves many of them per
-// SIMD. Lane l of a 16x16 fragment holds row l % 16 and the 32 bytes
-// [32 (l / 16), 32 (l / 16) + 32) of each 128-byte K step: the first 16
-// feed the INT8 MFMA of half-step 0 and the next 16 that of half-step 1
-// (the FP8 MFMA takes all 32 at once). A and B use the same K placement.
-// ---------------------------------------------------------------------------
-template <int QT, int BN, int BM, int WPB, int D>
-__global__ __launch_bounds__(64 * WPB, 1) void gemm_direct_kernel(const KParams p) {
-  constexpr int T = 16;
-  using MF = Mfma<QT, T>;
-  using acc_t = typename MF::acc_t;
-  constexpr int FN = BN / (16 * WPB), FM = BM / 16;
-  static_assert(FN * 16 * WPB == BN && FM * 16 == BM && FN >= 1 && FM >= 1, "direct tile");
-  static_assert(D >= 1 && D <= 8, "prefetch depth");
-
-  int tn, tm, z, ks0, ks1;
-  block_tile(p, tn, tm, z, ks0, ks1);
-  const int lane = threadIdx.x & 63;
-  const int wn = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t N = p.N, M = p.M, K = p.K;
-  constexpr uint32_t kOOB = 0x80000000u;
-  const int limA = (int)((N - (int64_t)tn * p.rn) < p.rn ? (N - (int64_t)tn * p.rn) : p.rn);
-  const int r0 = wn * 16 * FN;  // first local row of this wave
-  if (r0 >= limA) return;       // no valid row: nothing to load or store
-
-  const __amdgpu_buffer_rsrc_t rsw =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.Wq, (short)0, (int)(uint32_t)(N * K), kBufWord3);
-  const __amdgpu_buffer_rsrc_t rsx =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.Xq, (short)0, (int)(uint32_t)(M * K), kBufWord3);
-  const int lrow = lane & 15, g = lane >> 4;
-  uint32_t oa[FN], ob[FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i) {
-    const int r = r0 + i * 16 + lrow;
-    const int64_t row = (int64_t)tn * p.rn + r;
-    oa[i] = (r < limA) ? (uint32_t)(row * K + g * 32) : kOOB;
-  }
-#pragma unroll
-  for (int j = 0; j < FM; ++j) {
-    const int64_t row = (int64_t)tm * BM + j * 16 + lrow;
-    ob[j] = row < M ? (uint32_t)(row * K + g * 32) : kOOB;
-  }
-  const bool ktail = (K % 128) != 0;
-  const int krem = (int)(K % 128);
-  // In the ragged last step, 16-byte half h of this lane is valid when
-  // 32 g + 16 h < krem.
-  const bool h0 = g * 32 < krem, h1 = g * 32 + 16 < krem;
-
-  acc_t acc[FN][FM];
-#pragma unroll
-  for (int i = 0; i < FN; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) acc[i][j] = acc_t{};
-
-  uint4 ra[D][FN][2], rb[D][FM][2];
-  auto ld = [&](__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) -> uint4 {
-    const v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0);
-    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
-  };
-  auto load = [&](uint4 (&a)[FN][2], uint4 (&b)[FM][2], int ks) {
-    const int soff = ks * 128;
-    if (!ktail || ks + 1 < p.nks) {
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        a[i][0] = ld(rsw, oa[i], soff);
-        a[i][1] = ld(rsw, oa[i] + 16, soff);
-      }
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        b[j][0] = ld(rsx, ob[j], soff);
-        b[j][1] = ld(rsx, ob[j] + 16, soff);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
-        a[i][0] = ld(rsw, h0 ? oa[i] : kOOB, soff);
-        a[i][1] = ld(rsw, h1 ? oa[i] + 16 : kOOB, soff);
-      }
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        b[j][0] = ld(rsx, h0 ? ob[j] : kOOB, soff);
-        b[j][1] = ld(rsx, h1 ? ob[j] + 16 : kOOB, soff);
-      }
-    }
-  };
-  auto op16 = [](const uint4& u) -> v4i { return v4i{(int)u.x, (int)u.y, (int)u.z, (int)u.w}; };
-  auto compute = [&](const uint4 (&a)[FN][2], const uint4 (&b)[FM][2]) {
-    if constexpr (QT == kQInt8) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int i = 0; i < FN; ++i)
-#pragma unroll
-          for (int j = 0; j < FM; ++j) acc[i][j] = MF::run(op16(a[i][h]), op16(b[j][h]), acc[i][j]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          const v8i av{(int)a[i][0].x, (int)a[i][0].y, (int)a[i][0].z, (int)a[i][0].w,
-                       (int)a[i][1].x, (int)a[i][1].y, (int)a[i][1].z, (int)a[i][1].w};
-          const v8i bv{(int)b[j][0].x, (int)b[j][0].y, (int)b[j][0].z, (int)b[j][0].w,
-                       (int)b[j][1].x, (int)b[j][1].y, (int)b[j][1].z, (int)b[j][1].w};
-          acc[i][j] = MF::run(av, bv, acc[i][j]);
-        }
-    }
-  };
-
-  EpiScales<FN, FM, MF::NACC / 4> sc;
-  load_scales<QT, T, BN, BM, WPB, 1>(p, tn, tm, wn, 0, lane, sc);
-
-  const int nk = ks1 - ks0;
-#pragma unroll
-  for (int s = 0; s < D; ++s)
-    if (s < nk) load(ra[s], rb[s], ks0 + s);
-  for (int it = 0; it < nk; it += D) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      if (it + s < nk) {
-        compute(ra[s], rb[s]);
-        if (it + s + D < nk) load(ra[s], rb[s], ks0 + it + s + D);
-      }
-    }
-  }
-  store_tile<QT, T, BN, BM, WPB, 1>(p, acc, sc, tn, tm, z, wn, 0, lane);
 }
 
 // Split-K second pass: Y[m, n] = epilogue(sum_{z = 0..S-1} part[z][m][n]),
@@ -1214,67 +1038,56 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
 
 // ---------------------------------------------------------------------------
 // Tile table. Order matters: the planner and the tuning hook refer to tiles
-// by index. (KIND, S, T, BN, BM, WN, WM): KIND 0 is the LDS-DMA kernel, 1 the
-// same with MFMA operands double-buffered and interleaved with the MFMAs
-// (scheduling groups), 2 the direct register-path kernel; S is the LDS ring
-// depth (the prefetch depth in K steps for KIND 2), T the MFMA edge, BN x BM
-// the macro tile over N and M, WN x WM the waves along N and M, FU 1 when the
-// tile also has a fused chain-epilogue instantiation (the tiles the planner
-// picks up to 1024 tokens). Every K step covers 128 bytes of K.
+// by index. (S, T, BN, BM, WN, WM, BK, FU): S is the LDS ring depth, T the
+// MFMA edge, BN x BM the macro tile over N and M, WN x WM the waves along N
+// and M, BK the bytes of K per step, FU 1 when the tile also has a fused
+// chain-epilogue instantiation (the tiles the planner picks up to 1024
+// tokens). The kernel also takes 64-byte K steps (twice the ring slots in
+// the same LDS); measured on the 32B-shaped GEMMs at 512 and 4096 tokens,
+// 256 x 256 and 256 x 128 tiles with 64-byte steps and rings of 4-6 were
+// 2-15% slower than their 128-byte versions, so no tile uses them.
 // ---------------------------------------------------------------------------
-#define QR_TILES(X)                                                          \
-  X(0, 4, 16, 128, 32, 8, 1, 1)  /*  0: M <= 32, weight streaming        */ \
-  X(0, 4, 32, 128, 64, 4, 2, 1)  /*  1: M <= 64; narrow 256-token layers */ \
-  X(0, 4, 32, 128, 128, 2, 4, 1) /*  2: M <= 128; long-K 256-token ones  */ \
-  X(0, 3, 32, 192, 128, 2, 2, 0) /*  3: 4-wave version of tile 14        */ \
-  X(0, 3, 32, 256, 128, 4, 2, 1) /*  4: long-K / narrow large-M layers   */ \
-  X(0, 2, 32, 256, 256, 2, 4, 0) /*  5: wide large-M layers              */ \
-  X(0, 3, 32, 128, 256, 2, 4, 1) /*  6: 256-token alternative            */ \
-  X(0, 3, 32, 96, 256, 1, 4, 0)  /*  7: 256-token alternative, 96 rows   */ \
-  X(0, 4, 32, 128, 32, 4, 1, 1)  /*  8: M <= 32 alternative, 4 waves     */ \
-  X(0, 4, 16, 64, 16, 4, 1, 1)   /*  9: M <= 16 alternative, narrow      */ \
-  X(1, 3, 32, 192, 128, 2, 2, 0) /* 10: interleaved variant of tile 3    */ \
-  X(1, 4, 16, 128, 32, 8, 1, 0)  /* 11: interleaved variant of tile 0    */ \
-  X(2, 4, 16, 128, 16, 8, 1, 0)  /* 12: direct, M <= 16                  */ \
-  X(2, 2, 16, 128, 32, 4, 1, 0)  /* 13: direct, M <= 32                  */ \
-  X(0, 4, 32, 192, 128, 2, 4, 1) /* 14: wide 256-token layers, 8 waves   */ \
-  X(1, 4, 32, 192, 128, 2, 4, 0) /* 15: interleaved variant of tile 14   */ \
-  X(0, 4, 16, 80, 64, 5, 1, 1)   /* 16: 256-token INT8 QKV, 5 waves      */
+#define QR_TILES(X)                                                             \
+  X(4, 16, 128, 32, 8, 1, 128, 1)  /*  0: M <= 32, weight streaming        */ \
+  X(4, 32, 128, 64, 4, 2, 128, 1)  /*  1: M <= 64; narrow 256-token layers */ \
+  X(4, 32, 128, 128, 2, 4, 128, 1) /*  2: M <= 128; long-K 256-token ones  */ \
+  X(3, 32, 256, 128, 4, 2, 128, 1) /*  3: long-K / narrow large-M layers   */ \
+  X(2, 32, 256, 256, 2, 4, 128, 0) /*  4: wide large-M layers              */ \
+  X(3, 32, 128, 256, 2, 4, 128, 1) /*  5: 256-token very wide layers       */ \
+  X(4, 32, 128, 32, 4, 1, 128, 1)  /*  6: M <= 32 narrow layers, 4 waves   */ \
+  X(4, 16, 64, 16, 4, 1, 128, 1)   /*  7: M <= 16 narrow layers            */ \
+  X(4, 32, 192, 128, 2, 4, 128, 1) /*  8: wide 256-token layers, 8 waves   */ \
+  X(4, 16, 80, 64, 5, 1, 128, 1)   /*  9: 256-token INT8 QKV, 5 waves      */
 
 #define QR_STR(x) #x
-#define QR_DESC(KIND, S, T, BN, BM, WN, WM, FU)                                    \
-  {KIND == 2   ? "dir" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN                \
-   : KIND == 1 ? "dmaip" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM      \
-               : "dma" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM,       \
-   T, BN, BM, 128, 64 * WN * WM, S, FU},
+#define QR_DESC(S, T, BN, BM, WN, WM, BK, FU)                                          \
+  {BK == 64 ? "dma" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM "_k64"         \
+            : "dma" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM,               \
+   T, BN, BM, BK, 64 * WN * WM, S, FU},
 const TileDesc kTiles[] = {QR_TILES(QR_DESC)};
 #undef QR_DESC
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-template <int QT, int KIND, int S, int T, int BN, int BM, int WN, int WM>
+template <int QT, int S, int T, int BN, int BM, int WN, int WM, int BK>
 hipError_t launch_one(const KParams& kp, unsigned grid, hipStream_t st) {
-  if constexpr (KIND == 2)
-    hipLaunchKernelGGL((gemm_direct_kernel<QT, BN, BM, WN, S>), dim3(grid), dim3(64 * WN), 0, st,
-                       kp);
-  else
-    hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, KIND == 1, false>), dim3(grid),
-                       dim3(64 * WN * WM), 0, st, kp);
+  hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, BK, false>), dim3(grid),
+                     dim3(64 * WN * WM), 0, st, kp);
   return hipGetLastError();
 }
 
 // Fused-epilogue kernel of a tile: its function (for the residency check) or
 // its launch.
-template <int QT, int KIND, int S, int T, int BN, int BM, int WN, int WM, int FU>
+template <int QT, int S, int T, int BN, int BM, int WN, int WM, int BK, int FU>
 const void* fused_fn() {
-  if constexpr (FU == 1 && KIND == 0)
-    return reinterpret_cast<const void*>(&gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, false, true>);
+  if constexpr (FU == 1)
+    return reinterpret_cast<const void*>(&gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, BK, true>);
   else
     return nullptr;
 }
-template <int QT, int KIND, int S, int T, int BN, int BM, int WN, int WM, int FU>
+template <int QT, int S, int T, int BN, int BM, int WN, int WM, int BK, int FU>
 hipError_t launch_fused_one(const KParams& kp, unsigned grid, hipStream_t st) {
-  if constexpr (FU == 1 && KIND == 0) {
-    hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, false, true>), dim3(grid),
+  if constexpr (FU == 1) {
+    hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, BK, true>), dim3(grid),
                        dim3(64 * WN * WM), 0, st, kp);
     return hipGetLastError();
   } else {
@@ -1302,10 +1115,10 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   const unsigned grid = (unsigned)(plan.tiles_n * plan.tiles_m * plan.splitk);
   hipError_t e = hipErrorInvalidValue;
   int idx = 0;
-#define QR_CASE(KIND, S, T, BN, BM, WN, WM, FU)                                    \
+#define QR_CASE(S, T, BN, BM, WN, WM, BK, FU)                                      \
   if (plan.tile == idx) {                                                           \
-    e = qt == kQInt8 ? launch_one<kQInt8, KIND, S, T, BN, BM, WN, WM>(kp, grid, st) \
-                     : launch_one<kQFp8, KIND, S, T, BN, BM, WN, WM>(kp, grid, st); \
+    e = qt == kQInt8 ? launch_one<kQInt8, S, T, BN, BM, WN, WM, BK>(kp, grid, st)   \
+                     : launch_one<kQFp8, S, T, BN, BM, WN, WM, BK>(kp, grid, st);   \
   }                                                                                 \
   ++idx;
   QR_TILES(QR_CASE)
@@ -1356,10 +1169,10 @@ int fused_blocks_per_cu(int tile, int qt, int dev) {
   if (c == 0) {
     const void* fn = nullptr;
     int idx = 0;
-#define QR_FN(KIND, S, T, BN, BM, WN, WM, FU)                                          \
+#define QR_FN(S, T, BN, BM, WN, WM, BK, FU)                                            \
   if (tile == idx)                                                                    \
-    fn = qt == kQInt8 ? fused_fn<kQInt8, KIND, S, T, BN, BM, WN, WM, FU>()            \
-                      : fused_fn<kQFp8, KIND, S, T, BN, BM, WN, WM, FU>();            \
+    fn = qt == kQInt8 ? fused_fn<kQInt8, S, T, BN, BM, WN, WM, BK, FU>()              \
+                      : fused_fn<kQFp8, S, T, BN, BM, WN, WM, BK, FU>();              \
   ++idx;
     QR_TILES(QR_FN)
 #undef QR_FN
@@ -1410,10 +1223,10 @@ hipError_t launch_gemm_fused(const GemmPlan& plan, int qt, const GemmArgs& a, co
   const unsigned grid = (unsigned)(plan.tiles_n * plan.tiles_m * plan.splitk);
   hipError_t e = hipErrorInvalidValue;
   int idx = 0;
-#define QR_FCASE(KIND, S, T, BN, BM, WN, WM, FU)                                              \
+#define QR_FCASE(S, T, BN, BM, WN, WM, BK, FU)                                                \
   if (plan.tile == idx) {                                                                      \
-    e = qt == kQInt8 ? launch_fused_one<kQInt8, KIND, S, T, BN, BM, WN, WM, FU>(kp, grid, st)  \
-                     : launch_fused_one<kQFp8, KIND, S, T, BN, BM, WN, WM, FU>(kp, grid, st); \
+    e = qt == kQInt8 ? launch_fused_one<kQInt8, S, T, BN, BM, WN, WM, BK, FU>(kp, grid, st)    \
+                     : launch_fused_one<kQFp8, S, T, BN, BM, WN, WM, BK, FU>(kp, grid, st);    \
   }                                                                                            \
   ++idx;
   QR_TILES(QR_FCASE)

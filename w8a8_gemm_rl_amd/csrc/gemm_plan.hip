@@ -37,7 +37,7 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
   } else if (M <= 32) {
     // weight streaming; narrow layers (split K below) on 64 x 16 tiles up to
     // 16 tokens and 4-wave 128 x 32 tiles of 32 x 32 fragments up to 32
-    tile = N >= 8192 ? 0 : (M <= 16 ? 9 : 8);
+    tile = N >= 8192 ? 0 : (M <= 16 ? 7 : 6);
   } else if (M <= 64) {
     tile = 1;
   } else if (M <= 128) {
@@ -47,22 +47,22 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
     // weight byte is copied once) while they fit one round of the CUs, as
     // for the 32B gate and up (27648 rows: 51 us against 76 us on 256 x 256
     // tiles with split K); wider ones (the stacked 7B gate and up) 256 x 256.
-    if (N >= 24576) tile = (N + 127) / 128 <= kCUs ? 6 : 5;
-    else if (N >= 8192) tile = 14;
+    if (N >= 24576) tile = (N + 127) / 128 <= kCUs ? 5 : 4;
+    else if (N >= 8192) tile = 8;
     else if (nks >= 64) tile = 2;
     else if (N >= 4096)
       // INT8: 80 x 64 tiles issue 20 copies per K step where 128 x 64 ones
       // issue 24 (7-8% faster on the 7B QKV), while their full-height grid
       // fits one round; past it (the 32B stacked QKV, 7168 rows) the
       // 128 x 64 tiles' single round wins (23.6 us against 36.3 us).
-      tile = qt == kQInt8 && ((N + 79) / 80) * ((M + 63) / 64) <= kCUs ? 16 : 1;
-    else tile = qt == kQFp8 ? 8 : 0;  // FP8: 32x32 fragments 8% faster here
+      tile = qt == kQInt8 && ((N + 79) / 80) * ((M + 63) / 64) <= kCUs ? 9 : 1;
+    else tile = qt == kQFp8 ? 6 : 0;  // FP8: 32x32 fragments 8% faster here
   } else if (M <= 1024) {
-    if (N >= 16384) tile = 5;
-    else if (N <= 2048) tile = 9;
-    else tile = nks >= 64 ? 4 : 2;
+    if (N >= 16384) tile = 4;
+    else if (N <= 2048) tile = 7;
+    else tile = nks >= 64 ? 3 : 2;
   } else {
-    tile = N >= 7168 ? 5 : 4;
+    tile = N >= 7168 ? 4 : 3;
   }
   const TileDesc& d = tile_desc(tile);
   p.tile = tile;
