@@ -1142,7 +1142,7 @@ def measure_peaks(dev):
         mhz = statistics.median((c1 - c0) / (w1 - w0) * khz / 1e3 for c0, c1, w0, w1 in tk if w1 > w0)
         out[key] = round(blocks * 8 * iters * 8 * ops_per / t / 1e12, 1)
         out["sclk_mhz_" + qt] = round(mhz, 0)
-    out["kernels"] = "read_probe_kernel (16-byte loads, 4 GiB once), mfma_probe_kernel (256 blocks x 8 waves, " \
+    out["kernels"] = "read_probe_kernel (16-byte non-temporal loads, 4 GiB once), mfma_probe_kernel (256 blocks x 8 waves, " \
                      "8 independent 32x32 MFMAs per round, 4000 rounds)"
     torch.cuda.empty_cache()
     return out

@@ -432,8 +432,9 @@ int qr_set_plan_override(int tile, int splitk, int rows);
  * against which the GEMMs' roofline fractions are also reported.
  *
  * qr_probe_read -- read `bytes` (a multiple of 16) of device memory at `buf`
- *   (16-byte aligned) once with 16-byte loads; block b writes one XOR word to
- *   sink[b]. sink holds at least sink_words >= 2048 uint32 (device memory).
+ *   (16-byte aligned) once with 16-byte non-temporal loads; block b writes
+ *   one XOR word to sink[b]. sink holds at least sink_words >= 1024 uint32
+ *   (device memory).
  *   bytes / kernel time is the memory read rate; use a buffer well past the
  *   256 MB Infinity Cache to measure HBM.
  * qr_probe_mfma -- `blocks` blocks of 8 waves; every wave runs `iters`

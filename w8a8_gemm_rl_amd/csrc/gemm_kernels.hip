@@ -661,45 +661,64 @@ __device__ __forceinline__ void fused_splitk_tail(const KParams& p, uint32_t g0,
 // swizzle is applied on the global side: the lane that owns physical chunk
 // c of LDS row r fetches logical chunk c ^ swz(r).
 // ---------------------------------------------------------------------------
-template <int CNT>
+// NT: the non-temporal hint on the copies (data streamed once).
+template <int CNT, bool NT>
 __device__ __forceinline__ void dma_group(uint32_t lds_addr, const uint32_t* vo,
                                           __amdgpu_buffer_rsrc_t r, int soff) {
   static_assert(CNT >= 1 && CNT <= 4, "one M0 covers at most 4 KB of offsets");
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-  if constexpr (CNT == 1)
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds"
-        :
-        : "s"(lds_addr), "v"(vo[0]), "s"(r), "s"(soff)
-        : "memory", "m0");
-  else if constexpr (CNT == 2)
+  if constexpr (CNT == 1 && !NT)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 : : "s"(lds_addr), "v"(vo[0]), "s"(r), "s"(soff) : "memory", "m0");
+  else if constexpr (CNT == 1)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+                 : : "s"(lds_addr), "v"(vo[0]), "s"(r), "s"(soff) : "memory", "m0");
+  else if constexpr (CNT == 2 && !NT)
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "buffer_load_dwordx4 %1, %3, %4 offen lds\n\t"
         "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 lds"
-        :
-        : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "s"(r), "s"(soff)
-        : "memory", "m0");
-  else if constexpr (CNT == 3)
+        : : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "s"(r), "s"(soff) : "memory", "m0");
+  else if constexpr (CNT == 2)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %3, %4 offen nt lds\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen offset:1024 nt lds"
+        : : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "s"(r), "s"(soff) : "memory", "m0");
+  else if constexpr (CNT == 3 && !NT)
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "buffer_load_dwordx4 %1, %4, %5 offen lds\n\t"
         "buffer_load_dwordx4 %2, %4, %5 offen offset:1024 lds\n\t"
         "buffer_load_dwordx4 %3, %4, %5 offen offset:2048 lds"
-        :
-        : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "s"(r), "s"(soff)
+        : : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "s"(r), "s"(soff)
         : "memory", "m0");
-  else
+  else if constexpr (CNT == 3)
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %4, %5 offen nt lds\n\t"
+        "buffer_load_dwordx4 %2, %4, %5 offen offset:1024 nt lds\n\t"
+        "buffer_load_dwordx4 %3, %4, %5 offen offset:2048 nt lds"
+        : : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "s"(r), "s"(soff)
+        : "memory", "m0");
+  else if constexpr (!NT)
     asm volatile(
         "s_mov_b32 m0, %0\n\t"
         "buffer_load_dwordx4 %1, %5, %6 offen lds\n\t"
         "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 lds\n\t"
         "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 lds\n\t"
         "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 lds"
-        :
-        : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(r), "s"(soff)
+        : : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(r), "s"(soff)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %5, %6 offen nt lds\n\t"
+        "buffer_load_dwordx4 %2, %5, %6 offen offset:1024 nt lds\n\t"
+        "buffer_load_dwordx4 %3, %5, %6 offen offset:2048 nt lds\n\t"
+        "buffer_load_dwordx4 %4, %5, %6 offen offset:3072 nt lds"
+        : : "s"(lds_addr), "v"(vo[0]), "v"(vo[1]), "v"(vo[2]), "v"(vo[3]), "s"(r), "s"(soff)
         : "memory", "m0");
 #pragma clang diagnostic pop
 }
@@ -726,7 +745,7 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   }
 }
 
-template <int QT, int T, int BN, int BM, int WN, int WM, int S, int BK, bool FUSE>
+template <int QT, int T, int BN, int BM, int WN, int WM, int S, int BK, bool NTW, bool FUSE>
 __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams p) {
   using MF = Mfma<QT, T>;
   using acc_t = typename MF::acc_t;
@@ -834,10 +853,12 @@ __global__ __launch_bounds__(64 * WN * WM, 1) void gemm_dma_kernel(const KParams
 #pragma unroll
         for (int e = 0; e < C; ++e) {
           const uint32_t u = vo[e] + 1024u * (uint32_t)e;
-          dma_group<1>(base + 1024u * (uint32_t)e, &u, isA ? rsw : rsx, soff);
+          if (isA) dma_group<1, NTW>(base + 1024u * (uint32_t)e, &u, rsw, soff);
+          else dma_group<1, false>(base + 1024u * (uint32_t)e, &u, rsx, soff);
         }
       } else {
-        dma_group<C>(base, vo, isA ? rsw : rsx, soff);
+        if (isA) dma_group<C, NTW>(base, vo, rsw, soff);
+        else dma_group<C, false>(base, vo, rsx, soff);
       }
     };
     const int cnt = isA ? (NA - i0 < 4 ? NA - i0 : 4) : (NB - i0 < 4 ? NB - i0 : 4);
@@ -1042,25 +1063,29 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
 // MFMA edge, BN x BM the macro tile over N and M, WN x WM the waves along N
 // and M, BK the bytes of K per step, FU 1 when the tile also has a fused
 // chain-epilogue instantiation (the tiles the planner picks up to 1024
-// tokens). The kernel also takes 64-byte K steps (twice the ring slots in
+// tokens), NT 1 when the weight copies carry the non-temporal hint: weight
+// bytes are streamed once (measured 3-6% faster at 1, 32 and 512 tokens);
+// the 192 x 128 tile reads each weight tile twice (two token tiles, one
+// after the other on the same XCD) and the hint made it 5% slower, so its
+// second read would not hit in L2. The kernel also takes 64-byte K steps (twice the ring slots in
 // the same LDS); measured on the 32B-shaped GEMMs at 512 and 4096 tokens,
 // 256 x 256 and 256 x 128 tiles with 64-byte steps and rings of 4-6 were
 // 2-15% slower than their 128-byte versions, so no tile uses them.
 // ---------------------------------------------------------------------------
-#define QR_TILES(X)                                                             \
-  X(4, 16, 128, 32, 8, 1, 128, 1)  /*  0: M <= 32, weight streaming        */ \
-  X(4, 32, 128, 64, 4, 2, 128, 1)  /*  1: M <= 64; narrow 256-token layers */ \
-  X(4, 32, 128, 128, 2, 4, 128, 1) /*  2: M <= 128; long-K 256-token ones  */ \
-  X(3, 32, 256, 128, 4, 2, 128, 1) /*  3: long-K / narrow large-M layers   */ \
-  X(2, 32, 256, 256, 2, 4, 128, 0) /*  4: wide large-M layers              */ \
-  X(3, 32, 128, 256, 2, 4, 128, 1) /*  5: 256-token very wide layers       */ \
-  X(4, 32, 128, 32, 4, 1, 128, 1)  /*  6: M <= 32 narrow layers, 4 waves   */ \
-  X(4, 16, 64, 16, 4, 1, 128, 1)   /*  7: M <= 16 narrow layers            */ \
-  X(4, 32, 192, 128, 2, 4, 128, 1) /*  8: wide 256-token layers, 8 waves   */ \
-  X(4, 16, 80, 64, 5, 1, 128, 1)   /*  9: 256-token INT8 QKV, 5 waves      */
+#define QR_TILES(X)                                                                \
+  X(4, 16, 128, 32, 8, 1, 128, 1, 1)  /*  0: M <= 32, weight streaming        */ \
+  X(4, 32, 128, 64, 4, 2, 128, 1, 1)  /*  1: M <= 64; narrow 256-token layers */ \
+  X(4, 32, 128, 128, 2, 4, 128, 1, 1) /*  2: M <= 128; long-K 256-token ones  */ \
+  X(3, 32, 256, 128, 4, 2, 128, 1, 1) /*  3: long-K / narrow large-M layers   */ \
+  X(2, 32, 256, 256, 2, 4, 128, 0, 1) /*  4: wide large-M layers              */ \
+  X(3, 32, 128, 256, 2, 4, 128, 1, 1) /*  5: 256-token very wide layers       */ \
+  X(4, 32, 128, 32, 4, 1, 128, 1, 1)  /*  6: M <= 32 narrow layers, 4 waves   */ \
+  X(6, 16, 64, 16, 4, 1, 128, 1, 1)   /*  7: M <= 16 narrow layers            */ \
+  X(4, 32, 192, 128, 2, 4, 128, 1, 0) /*  8: wide 256-token layers, 8 waves   */ \
+  X(4, 16, 80, 64, 5, 1, 128, 1, 1)   /*  9: 256-token INT8 QKV, 5 waves      */
 
 #define QR_STR(x) #x
-#define QR_DESC(S, T, BN, BM, WN, WM, BK, FU)                                          \
+#define QR_DESC(S, T, BN, BM, WN, WM, BK, FU, NT)                                          \
   {BK == 64 ? "dma" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM "_k64"         \
             : "dma" QR_STR(S) "_t" #T "_n" #BN "_m" #BM "_w" #WN "x" #WM,               \
    T, BN, BM, BK, 64 * WN * WM, S, FU},
@@ -1068,26 +1093,27 @@ const TileDesc kTiles[] = {QR_TILES(QR_DESC)};
 #undef QR_DESC
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 
-template <int QT, int S, int T, int BN, int BM, int WN, int WM, int BK>
+template <int QT, int S, int T, int BN, int BM, int WN, int WM, int BK, int NT>
 hipError_t launch_one(const KParams& kp, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, BK, false>), dim3(grid),
+  hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, BK, NT == 1, false>), dim3(grid),
                      dim3(64 * WN * WM), 0, st, kp);
   return hipGetLastError();
 }
 
 // Fused-epilogue kernel of a tile: its function (for the residency check) or
 // its launch.
-template <int QT, int S, int T, int BN, int BM, int WN, int WM, int BK, int FU>
+template <int QT, int S, int T, int BN, int BM, int WN, int WM, int BK, int FU, int NT>
 const void* fused_fn() {
   if constexpr (FU == 1)
-    return reinterpret_cast<const void*>(&gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, BK, true>);
+    return reinterpret_cast<const void*>(
+        &gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, BK, NT == 1, true>);
   else
     return nullptr;
 }
-template <int QT, int S, int T, int BN, int BM, int WN, int WM, int BK, int FU>
+template <int QT, int S, int T, int BN, int BM, int WN, int WM, int BK, int FU, int NT>
 hipError_t launch_fused_one(const KParams& kp, unsigned grid, hipStream_t st) {
   if constexpr (FU == 1) {
-    hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, BK, true>), dim3(grid),
+    hipLaunchKernelGGL((gemm_dma_kernel<QT, T, BN, BM, WN, WM, S, BK, NT == 1, true>), dim3(grid),
                        dim3(64 * WN * WM), 0, st, kp);
     return hipGetLastError();
   } else {
@@ -1115,10 +1141,10 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   const unsigned grid = (unsigned)(plan.tiles_n * plan.tiles_m * plan.splitk);
   hipError_t e = hipErrorInvalidValue;
   int idx = 0;
-#define QR_CASE(S, T, BN, BM, WN, WM, BK, FU)                                      \
+#define QR_CASE(S, T, BN, BM, WN, WM, BK, FU, NT)                                  \
   if (plan.tile == idx) {                                                           \
-    e = qt == kQInt8 ? launch_one<kQInt8, S, T, BN, BM, WN, WM, BK>(kp, grid, st)   \
-                     : launch_one<kQFp8, S, T, BN, BM, WN, WM, BK>(kp, grid, st);   \
+    e = qt == kQInt8 ? launch_one<kQInt8, S, T, BN, BM, WN, WM, BK, NT>(kp, grid, st) \
+                     : launch_one<kQFp8, S, T, BN, BM, WN, WM, BK, NT>(kp, grid, st); \
   }                                                                                 \
   ++idx;
   QR_TILES(QR_CASE)
@@ -1169,10 +1195,10 @@ int fused_blocks_per_cu(int tile, int qt, int dev) {
   if (c == 0) {
     const void* fn = nullptr;
     int idx = 0;
-#define QR_FN(S, T, BN, BM, WN, WM, BK, FU)                                            \
+#define QR_FN(S, T, BN, BM, WN, WM, BK, FU, NT)                                        \
   if (tile == idx)                                                                    \
-    fn = qt == kQInt8 ? fused_fn<kQInt8, S, T, BN, BM, WN, WM, BK, FU>()              \
-                      : fused_fn<kQFp8, S, T, BN, BM, WN, WM, BK, FU>();              \
+    fn = qt == kQInt8 ? fused_fn<kQInt8, S, T, BN, BM, WN, WM, BK, FU, NT>()          \
+                      : fused_fn<kQFp8, S, T, BN, BM, WN, WM, BK, FU, NT>();          \
   ++idx;
     QR_TILES(QR_FN)
 #undef QR_FN
@@ -1223,10 +1249,10 @@ hipError_t launch_gemm_fused(const GemmPlan& plan, int qt, const GemmArgs& a, co
   const unsigned grid = (unsigned)(plan.tiles_n * plan.tiles_m * plan.splitk);
   hipError_t e = hipErrorInvalidValue;
   int idx = 0;
-#define QR_FCASE(S, T, BN, BM, WN, WM, BK, FU)                                                \
+#define QR_FCASE(S, T, BN, BM, WN, WM, BK, FU, NT)                                            \
   if (plan.tile == idx) {                                                                      \
-    e = qt == kQInt8 ? launch_fused_one<kQInt8, S, T, BN, BM, WN, WM, BK, FU>(kp, grid, st)    \
-                     : launch_fused_one<kQFp8, S, T, BN, BM, WN, WM, BK, FU>(kp, grid, st);    \
+    e = qt == kQInt8 ? launch_fused_one<kQInt8, S, T, BN, BM, WN, WM, BK, FU, NT>(kp, grid, st) \
+                     : launch_fused_one<kQFp8, S, T, BN, BM, WN, WM, BK, FU, NT>(kp, grid, st); \
   }                                                                                            \
   ++idx;
   QR_TILES(QR_FCASE)

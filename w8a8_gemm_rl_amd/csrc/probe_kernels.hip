@@ -2,8 +2,8 @@
 // GEMMs' roofline fractions can be given against measured peaks as well as
 // the datasheet ones.
 //
-//  * read_probe_kernel streams a buffer once with 16-byte loads (four in
-//    flight per thread per round) and keeps one XOR word per block, so the
+//  * read_probe_kernel streams a buffer once with 16-byte non-temporal loads
+//    (eight in flight per thread) and keeps one XOR word per block, so the
 //    loads cannot be removed. Bytes / time = the HBM read rate (for a buffer
 //    well past the 256 MB Infinity Cache).
 //  * mfma_probe_kernel runs rounds of eight independent dense 8-bit MFMAs
@@ -21,24 +21,35 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+// Block b reads its own contiguous 1/grid of the buffer; every thread keeps
+// eight 16-byte non-temporal loads in flight (a wave reads 1 KB contiguous
+// per load). Measured on MI355X over 4 GiB: 7.0 TB/s, against 6.1-6.3 TB/s
+// with plain loads and 5.7 TB/s with a grid-strided loop of four.
 __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src, int64_t n16,
                                                          uint32_t* __restrict__ sink) {
-  __shared__ uint32_t red[256];
-  const int64_t stride = (int64_t)gridDim.x * 256;
+  typedef unsigned v4u __attribute__((ext_vector_type(4)));
+  constexpr int U = 8, NT = 256;
+  __shared__ uint32_t red[NT];
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t b0 = (int64_t)blockIdx.x * per;
+  const int64_t b1 = b0 + per < n16 ? b0 + per : n16;
   uint32_t x = 0;
-  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^
-         d.w;
+  int64_t i = b0 + threadIdx.x;
+  for (; i + (U - 1) * NT < b1; i += U * NT) {
+    v4u r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      r[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(&src[i + u * NT]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= r[u].x ^ r[u].y ^ r[u].z ^ r[u].w;
   }
-  for (; i < n16; i += stride) {
+  for (; i < b1; i += NT) {
     const uint4 a = src[i];
     x ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   red[threadIdx.x] = x;
   __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
+  for (int o = NT / 2; o > 0; o >>= 1) {
     if ((int)threadIdx.x < o) red[threadIdx.x] ^= red[threadIdx.x + o];
     __syncthreads();
   }
@@ -102,7 +113,7 @@ __global__ __launch_bounds__(512) void mfma_probe_kernel(int iters, uint32_t* __
 
 }  // namespace
 
-unsigned read_probe_blocks() { return 256 * 8; }
+unsigned read_probe_blocks() { return 1024; }
 
 hipError_t launch_read_probe(const void* buf, int64_t n16, uint32_t* sink, hipStream_t st) {
   hipLaunchKernelGGL(read_probe_kernel, dim3(read_probe_blocks()), dim3(256), 0, st,
