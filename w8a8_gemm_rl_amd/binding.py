@@ -14,7 +14,9 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqurl_w8a8.so")
+# The in-tree build; QR_LIB_PATH names another build of the same library to
+# load instead (the CPU tests use it for the host-sanitizer build).
+LIB_PATH = os.environ.get("QR_LIB_PATH") or os.path.join(_HERE, "libqurl_w8a8.so")
 
 QT = {"int8": 0, "fp8": 1}
 OUT = {"bf16": 0, "raw": 1}

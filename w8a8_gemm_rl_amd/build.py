@@ -112,6 +112,49 @@ def build(verbose=True, jobs=None):
     return LIB
 
 
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build of the whole
+# library (argument validation, planning, error reporting, the launchers'
+# host code); device code is compiled as usual. For CPU tests only: it lives
+# in _build/sanitize/, never next to the package, and needs the sanitizer
+# runtime preloaded into the process that loads it.
+SAN_DIR = os.path.join(BUILD, "sanitize")
+SAN_LIB = os.path.join(SAN_DIR, "libqurl_w8a8_san.so")
+SAN_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=undefined",
+                  "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+CLANGXX = os.environ.get("CLANGXX", "/opt/rocm/llvm/bin/clang++")
+
+
+def sanitizer_runtime():
+    """Path of clang's shared AddressSanitizer runtime (to preload)."""
+    out = subprocess.run([CLANGXX, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         stdout=subprocess.PIPE, text=True).stdout.strip()
+    if not os.path.isabs(out) or not os.path.exists(out):
+        raise RuntimeError("clang's shared AddressSanitizer runtime was not found")
+    return out
+
+
+def build_sanitized(jobs=None):
+    os.makedirs(SAN_DIR, exist_ok=True)
+    objs = [os.path.join(SAN_DIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+
+    def compile_one(i):
+        src = os.path.join(CSRC, SOURCES[i])
+        return _run([HIPCC, *CFLAGS, *EXTRA.get(SOURCES[i], []), *SAN_HOST_FLAGS, "-c", src, "-o",
+                     objs[i]])
+
+    jobs = jobs or min(len(SOURCES), 8)
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(compile_one, range(len(SOURCES))))
+    # the link is a host link of HIP objects (each embeds its device code)
+    _run([CLANGXX, "-shared", "-fPIC", "-shared-libasan", "-fsanitize=address,undefined", *objs,
+          "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", SAN_LIB])
+    return SAN_LIB
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) > 1 and sys.argv[1] == "sanitize":
+        print(build_sanitized())
+    else:
+        build(verbose=True)
     sys.exit(0)
