@@ -320,7 +320,8 @@ def summarize_rocprof(paths, grid, kind="gemm"):
                 if int(r["Grid_Size"]) == grid and is_kernel(r["Kernel_Name"], kind):
                     by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
             for c, v in by.items():
-                print(f"{path}: {c} per dispatch (grid {grid}): mean {statistics.mean(v):.1f} KiB, "
+                unit = " KiB" if c in ("FETCH_SIZE", "WRITE_SIZE") else ""
+                print(f"{path}: {c} per dispatch (grid {grid}): mean {statistics.mean(v):.1f}{unit}, "
                       f"n={len(v)}")
             if not by:
                 for r in rows:
