@@ -118,6 +118,33 @@ def linear_bytes(M, N, K):
     return N * K + M * K + 4 * (M + N) + 2 * M * N
 
 
+def fused_linear_bytes(M, N, K):
+    """Algorithmic bytes of one linear that quantizes its bf16 input itself:
+    weight codes, bf16 input, weight scales, bf16 out."""
+    return N * K + 2 * M * K + 4 * N + 2 * M * N
+
+
+SMALL_M_MK = 8192  # qr_linear_fused runs as one launch (input quantized in the kernel) up to M K
+
+
+def small_m_linears(chain, shapes, M, one_launch):
+    """Linears that run as one qr_linear_fused launch: up to M K = 8192, no
+    producer before them (the library's own choice for qr_linear_fused)."""
+    if one_launch:
+        return set()
+    return {L["name"] for L in chain
+            if not L.get("prod") and M <= 4 and M * shapes[L["name"]][1] <= SMALL_M_MK}
+
+
+def small_m_rf(N):
+    """Block height (16-row fragments) the library picks for the one-launch
+    path: the fewest, 1-5, that keep the grid within 256 blocks."""
+    for rf in range(1, 5):
+        if -(-N // (16 * rf)) <= 256:
+            return rf
+    return 5
+
+
 def quant_bytes(M, K, prod=None):
     """Algorithmic bytes of one input quantization: bf16 rows in, codes and
     scales out; a fused norm also reads its gain, SiLU x up two inputs."""
@@ -150,7 +177,7 @@ class Layer:
     qr_w8a8_gemm (with its split-K kernel)."""
 
     def __init__(self, chain, shapes, M, qt, sigma, seed, dev, x0, bufs, ws, s, fused=True,
-                 one_launch=False, wsq=None):
+                 one_launch=False, wsq=None, small=()):
         import torch
 
         from w8a8_gemm_rl_amd import binding as B
@@ -174,6 +201,7 @@ class Layer:
         self.x0, self.bufs, self.ws, self.s = x0, bufs, ws, s
         self.chain, self.M, self.fused = chain, M, fused
         self.one_launch, self.wsq, self.shapes = one_launch, wsq, shapes
+        self.small = set(small)  # linears run as one qr_linear_fused launch
 
     def ops(self):
         """The step as a list of (kind, name, thunk): per-token quantizations
@@ -187,10 +215,24 @@ class Layer:
         for L in self.chain:
             key_buf.setdefault(key[L["name"]], bufs["q_" + L["name"]])
         by_epilogue = set(epi.values())
+        # inputs whose every reader quantizes them itself need no quantizer
+        needed = {key[L["name"]] for L in self.chain if L["name"] not in self.small}
         out, done = [], set()
         for L in self.chain:
             k = key[L["name"]]
-            if k not in done and k not in by_epilogue:
+            if L["name"] in self.small:
+                src = self.x0 if L["src"] == "x0" else bufs["y_" + L["src"]]
+                if L["cols"] is not None:
+                    src = src[:, L["cols"][0]:L["cols"][1]]
+                Wq, sw = self.W[L["name"]]
+                y = bufs["y_" + L["name"]]
+
+                def fl(src=src, Wq=Wq, sw=sw, y=y):
+                    B.linear_fused(src, self.s, Wq, sw, self.qt, Y=y, ws=self.ws)
+
+                out.append(("gemm", L["name"], fl))
+                continue
+            if k not in done and k not in by_epilogue and k in needed:
                 xq, sx = key_buf[k]
 
                 def q(L=L, xq=xq, sx=sx):
@@ -917,24 +959,29 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
         bufs["y_" + L["name"]] = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         bufs["q_" + L["name"]] = (torch.empty((M, K), dtype=B.code_dtype(qt), device=dev),
                                   torch.empty(M, dtype=torch.float32, device=dev))
-        need = max(need, B.workspace_size("qr_w8a8_gemm", M, N, K, qt))
+        need = max(need, B.workspace_size("qr_w8a8_gemm", M, N, K, qt),
+                   B.workspace_size("qr_linear_fused", M, N, K, qt))
         needq = max(needq, B.workspace_size("qr_w8a8_gemm_quant", M, N, K, qt))
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
     # one launch per linear: its own workspace, zeroed once (barrier words)
     wsq = torch.zeros(max(needq, 256), dtype=torch.uint8, device=dev)
     one_launch = wl.get("one_launch", False)
 
+    small = small_m_linears(chain, shapes, M, one_launch)
     log(f"bench: {name} M={M} qt={qt}: building {wl['sets']} weight sets ...")
     layers = [Layer(chain, shapes, M, qt, sigma, 1000 * (j + 1), dev, x0, bufs, ws, s,
-                    fused=wl.get("fused", True), one_launch=one_launch, wsq=wsq)
+                    fused=wl.get("fused", True), one_launch=one_launch, wsq=wsq, small=small)
               for j in range(wl["sets"])]
     torch.cuda.synchronize()
 
     # ---- per-step algorithmic work
-    gemm_bytes = {L["name"]: linear_bytes(M, *shapes[L["name"]]) for L in chain}
+    gemm_bytes = {L["name"]: (fused_linear_bytes if L["name"] in small else linear_bytes)(
+        M, *shapes[L["name"]]) for L in chain}
     ops_step = sum(2 * M * shapes[L["name"]][0] * shapes[L["name"]][1] for L in chain)
     quant_keys, qbytes = set(), 0
     for L in chain:
+        if L["name"] in small:
+            continue
         k = (L["src"], L["cols"], L.get("prod"))
         if k not in quant_keys:
             quant_keys.add(k)
@@ -1037,25 +1084,36 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
             linears[n] = dict(N=N_, K=K_, eager_us=round(us, 2),
                               eager_gbs=round(gemm_bytes[n] / us / 1e3, 1),
                               eager_tops=round(2 * M * N_ * K_ / us / 1e6, 1),
-                              plan=list(B.gemm_plan(M, N_, K_, qt)))
+                              plan=(["small_m", 16 * small_m_rf(N_)] if n in small
+                                    else list(B.gemm_plan(M, N_, K_, qt))))
 
     dom_plan = B.gemm_plan(M, Nd, Kd, qt)
-    traffic_key = (f"{name}:{dom}:M{M}:N{Nd}:K{Kd}:tile{dom_plan[0]}:split{dom_plan[1]}"
-                   f":rows{dom_plan[2]}")
+    if dom in small:
+        rf = small_m_rf(Nd)
+        traffic_key = f"{name}:{dom}:M{M}:N{Nd}:K{Kd}:small_m:rows{16 * rf}"
+        kernel = (f"{dom} linear {Nd}x{Kd} M={M} (small_m_linear_kernel: input quantized in the "
+                  f"kernel, {16 * rf}-row blocks, K split over the waves)")
+    else:
+        traffic_key = (f"{name}:{dom}:M{M}:N{Nd}:K{Kd}:tile{dom_plan[0]}:split{dom_plan[1]}"
+                       f":rows{dom_plan[2]}")
+        kernel = f"{dom} GEMM {Nd}x{Kd} M={M} ({B.tile_name(dom_plan[0])}, splitk {dom_plan[1]})"
     roofline = roofline_object(dom_bound, gemm_bytes[dom], dom_ops, dom_us, qt)
     roofline.update({
         "traffic": committed_traffic(traffic_key),
         "traffic_key": traffic_key,
-        "kernel": f"{dom} GEMM {Nd}x{Kd} M={M} ({B.tile_name(dom_plan[0])}, splitk {dom_plan[1]})",
+        "kernel": kernel,
     })
     config = {
         "workload": f"{name}: one decoder layer's W8A8 linears, M={M} tokens, "
                     + ", ".join(f"{L['name']} {shapes[L['name']][0]}x{shapes[L['name']][1]}"
                                 for L in chain)
-                    + f"; {len(quant_keys)} per-token quantizations + {len(chain)} GEMMs"
+                    + f"; {len(quant_keys) + len(small)} per-token quantizations + {len(chain)} GEMMs"
                     + (f" in {len(chain) + len(quant_keys) - n_epi} launches ({n_epi} quantizations and "
                        f"the split-K sums in the GEMM epilogues)" if one_launch else
-                       " as separate launches (quantizers, GEMMs, split-K sum kernels)")
+                       " as separate launches (quantizers, GEMMs, split-K sum kernels)"
+                       + ("" if not small else
+                          f"; {', '.join(L['name'] for L in chain if L['name'] in small)} each as one "
+                          f"launch that quantizes its own input"))
                     + ("" if not any(L.get("prod") for L in chain) else
                        (", producers (RMSNorm x2, SiLU x up) "
                         + ("fused into the quantizers" if wl.get("fused", True)

@@ -363,6 +363,16 @@ int qr_w8a8_gemm_quant(const void* Xq, const float* scale_x, const void* Wq, con
  *   workspace    at least qr_workspace_size("qr_linear_fused", M, N, K, qt)
  *                bytes (never 0 when M, N > 0), 256-byte aligned scratch:
  *                split-K partial sums, then the activation codes and scales.
+ *
+ *   Decode steps of a few tokens (M x K <= 8192, e.g. 1 or 2 tokens of a
+ *   3584-wide input; with qr_set_small_m_override up to M <= 4 and
+ *   M x K <= 20480) run as one launch whose blocks quantize X themselves
+ *   into on-chip memory and split K among their waves: the workspace is
+ *   then not touched (it is still required), no codes are written to
+ *   memory, and the result is the same (INT8: the same bits; FP8: the fp32
+ *   sums of the waves' partial accumulators are added in a fixed order, so
+ *   the bf16 output may differ from the two-call path within the FP8
+ *   accumulation bound). qr_set_small_m_override selects or disables it.
  */
 int qr_linear_fused(const void* X, int64_t ldx, float act_mult, const void* Wq, const float* scale_w,
                     int64_t M, int64_t N, int64_t K, int qt, void* Y, int64_t ldy,
@@ -426,6 +436,17 @@ int qr_num_tiles(void);
  * Returns QR_OK or QR_ERR_INVALID_ARG.
  */
 int qr_set_plan_override(int tile, int splitk, int rows);
+
+/*
+ * qr_set_small_m_override -- tuning and test hook for the one-launch
+ * decode path of qr_linear_fused (and qr_linear_fused_noalloc): rf = 0
+ * takes it where it is the faster path (M x K <= 8192), rf = -1 never,
+ * rf = 1..5 wherever it can run (M <= 4, M x K <= 20480) with blocks of
+ * 16 * rf output channels. A qr_set_plan_override tile also disables the
+ * path. Thread-local like qr_set_plan_override; meant for benchmarks and
+ * tests. Returns QR_OK or QR_ERR_INVALID_ARG.
+ */
+int qr_set_small_m_override(int rf);
 
 /*
  * Measurement helpers (not part of the linear): the peaks the chip reaches,

@@ -159,6 +159,15 @@ def test_workspace_size_and_plan_are_pure(B):
     B.set_plan_override(-1)
 
 
+def test_small_m_override_validation(B):
+    for rf in [-1, 0, 1, 5]:
+        B.set_small_m_override(rf)
+    for bad in [-2, 6, 99]:
+        with pytest.raises(B.QRError):
+            B.set_small_m_override(bad)
+    B.set_small_m_override(0)
+
+
 def test_build_rejects_register_spills():
     # The build reads the compiler's per-kernel resource report and fails on
     # any kernel that keeps registers in scratch memory.

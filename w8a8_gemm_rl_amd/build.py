@@ -27,7 +27,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqurl_w8a8.so")
 SOURCES = ["quant_kernels.hip", "producer_kernels.hip", "gemm_kernels.hip", "gemm_plan.hip",
-           "acr_kernels.hip", "mx_kernels.hip", "probe_kernels.hip", "qr_api.hip",
+           "acr_kernels.hip", "mx_kernels.hip", "probe_kernels.hip", "small_m_kernels.hip", "qr_api.hip",
            "qr_noalloc.hip"]
 # Per-source flags: the fused producers fix the order of their fp32 roundings,
 # so no multiply-add may be contracted there.

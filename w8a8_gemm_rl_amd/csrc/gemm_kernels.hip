@@ -13,12 +13,12 @@
 //    v_mfma_scale_f32_{16x16x128,32x32x64}_f8f6f4 with unit block scales
 //    (E8M0 127 = 2^0), accumulating in fp32.
 //  * A block owns a BN x BM macro tile (of which the first `rn` weight rows
-//    are its own) and a contiguous range of K. Two kernel families move the
-//    operands: LDS-DMA (global -> LDS with buffer_load ... lds into an S-slot
-//    ring, optionally with the MFMA operands double-buffered in registers)
-//    and direct (global -> MFMA registers, no LDS) for small token counts.
-//    16-byte LDS chunks are XOR-swizzled by row so the 16-byte fragment
-//    reads of the MFMA operands are free of bank conflicts.
+//    are its own) and a contiguous range of K. The operands move global ->
+//    LDS with buffer_load ... lds into an S-slot ring (LDS-DMA). 16-byte LDS
+//    chunks are XOR-swizzled by row so the 16-byte fragment reads of the
+//    MFMA operands are free of bank conflicts. (Linears of one or two tokens
+//    whose input has no producer run instead on the one-launch kernel in
+//    small_m_kernels.hip.)
 //  * Each lane feeds the MFMA a contiguous 16- or 32-byte run of K for its row.
 //    The K order inside one instruction is the same for A and B, so any lane
 //    placement of K gives the same dot product.
@@ -136,12 +136,6 @@ __device__ __forceinline__ int swz(int row) {
   else return (row >> 2) & 3;
 }
 
-// fl32(acc) * sx * sw -> bf16 bits
-__device__ __forceinline__ uint32_t epi_bf16(float a, float sx, float sw) {
-  const float t = a * sx;
-  const float y = t * sw;
-  return f32_to_bf16_rne(y);
-}
 
 // Logical tile of this block. Blocks are dealt to the 8 XCDs round-robin,
 // so block b is renumbered to make runs of consecutive logical tiles (the K

@@ -21,6 +21,7 @@ thread_local std::string g_err;
 thread_local int g_force_tile = -1;
 thread_local int g_force_splitk = 0;
 thread_local int g_force_rows = 0;
+thread_local int g_small_m = 0;  // small-token path: 0 automatic, -1 off, 1..5 rows / 16
 
 constexpr int64_t kMaxKInt8 = 133144;  // K * 127^2 < 2^31
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
@@ -114,6 +115,14 @@ int qr_set_plan_override(int tile, int splitk, int rows) {
   g_force_tile = tile < 0 ? -1 : tile;
   g_force_splitk = tile < 0 ? 0 : splitk;
   g_force_rows = tile < 0 ? 0 : rows;
+  return ok();
+}
+
+int qr_set_small_m_override(int rf) {
+  if (rf < -1 || rf > qr::kSmallMaxRF)
+    return fail(QR_ERR_INVALID_ARG, "qr_set_small_m_override: rf %d must be in [-1, %d]", rf,
+                qr::kSmallMaxRF);
+  g_small_m = rf;
   return ok();
 }
 
@@ -476,6 +485,14 @@ int qr_linear_fused(const void* X, int64_t ldx, float act_mult, const void* Wq, 
   const size_t head = plan.part_bytes;
   st = check_ws(fn, workspace, workspace_bytes, head + xq_bytes + sx_bytes);
   if (st != QR_OK) return st;
+  if (g_force_tile < 0 && (g_small_m > 0 ? qr::small_m_ok(M, N, K, ldx)
+                                          : g_small_m == 0 && qr::small_m_auto(M, N, K, ldx))) {
+    (void)hipGetLastError();
+    return hip_status(qr::launch_small_m_linear(X, ldx, act_mult, Wq, scale_w, M, N, K, qt, Y, ldy,
+                                                qr::small_m_rf(N, g_small_m),
+                                                static_cast<hipStream_t>(stream)),
+                      fn);
+  }
   char* ws = static_cast<char*>(workspace);
   void* gws = ws;
   void* xq = ws + head;

@@ -31,6 +31,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// The GEMM epilogue: fl32(acc) * sx * sw -> bf16 bits (two roundings to fp32,
+// one to bf16; no fused multiply-add).
+__device__ __forceinline__ uint32_t epi_bf16(float a, float sx, float sw) {
+  const float t = a * sx;
+  const float y = t * sw;
+  return f32_to_bf16_rne(y);
+}
+
 // Four codes from fp32 values and the row's step t (t > 0), packed
 // little-endian (a -> byte 0). Each value is first divided by t with IEEE
 // division (correctly rounded).
@@ -57,6 +65,22 @@ __device__ __forceinline__ uint32_t quant_codes4(float a, float b, float c, floa
     w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
     return (uint32_t)w;
   }
+}
+
+// Absmax of eight bf16 values (one 16-byte chunk of a row).
+__device__ __forceinline__ float absmax8_bf16(const uint4 v) {
+  float m = fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x)));
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))));
+  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
+  return m;
+}
+
+// Eight codes of one 16-byte bf16 chunk with step t > 0.
+template <int QT>
+__device__ __forceinline__ uint2 codes8_bf16(const uint4 v, float t) {
+  return make_uint2(quant_codes4<QT>(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y), t),
+                    quant_codes4<QT>(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w), t));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -17,20 +17,6 @@
 namespace qr {
 namespace {
 
-__device__ __forceinline__ float absmax8_bf16(const uint4 v) {
-  float m = fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x)));
-  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y))));
-  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))));
-  m = fmaxf(m, fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w))));
-  return m;
-}
-
-template <int QT>
-__device__ __forceinline__ uint2 codes8_bf16(const uint4 v, float t) {
-  return make_uint2(quant_codes4<QT>(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y), t),
-                    quant_codes4<QT>(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w), t));
-}
-
 // Threads per block: 256 (four rows of one wave each) when TPR == 64, else
 // one row per block of TPR threads (256, 512 or 1024).
 constexpr int block_threads(int tpr) { return tpr < 256 ? 256 : tpr; }
