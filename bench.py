@@ -299,6 +299,7 @@ KERNEL_SOURCES = {
     "acr": ("acr_kernels.hip",),
     "gemm": ("gemm_kernels.hip", "gemm_plan.hip", "qr_gemm.h", "qr_device.h"),
     "refresh": ("quant_kernels.hip", "qr_device.h"),
+    "small": ("small_m_kernels.hip", "qr_device.h", "qr_internal.h"),
 }
 
 
@@ -339,6 +340,7 @@ KERNEL_PATTERNS = {
     "acr": r"acr_(tis|sum)_kernel",  # one pass: the per-token kernel and the ordered sum
     "gemm": r"gemm_\w*kernel",  # the main GEMM kernels (any tile family), not the split-K reduction
     "refresh": r"weight_quant_kernel<[^>]*true>",  # the weight quantizer with flip counting
+    "small": r"small_m_linear_kernel",  # the one-launch linear of one or two tokens
 }
 
 
@@ -1099,7 +1101,7 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
         kernel = f"{dom} GEMM {Nd}x{Kd} M={M} ({B.tile_name(dom_plan[0])}, splitk {dom_plan[1]})"
     roofline = roofline_object(dom_bound, gemm_bytes[dom], dom_ops, dom_us, qt)
     roofline.update({
-        "traffic": committed_traffic(traffic_key),
+        "traffic": committed_traffic(traffic_key, "small" if dom in small else "gemm"),
         "traffic_key": traffic_key,
         "kernel": kernel,
     })
