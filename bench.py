@@ -821,6 +821,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="default workload only: skip the 32B decode / prefill lines and the measured peaks")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
+    ap.add_argument("--no-small-m", action="store_true",
+                    help="run every linear as quantizer + GEMM launches, also at 1-2 tokens")
     ap.add_argument("--summarize-rocprof", nargs="+", metavar="CSV",
                     help="print the figures used from rocprofv3 CSV files (with --grid) and exit")
     ap.add_argument("--grid", type=int, default=0, help="grid size (threads) of the dispatches to summarize")
@@ -879,6 +881,8 @@ def main():
     wl = dict(WORKLOADS[args.workload])
     if args.m is not None:
         wl["M"] = args.m
+    if args.no_small_m:
+        wl["no_small_m"] = True
     r = run_chain(args.workload, wl, dev, args.steps, args.warmup, args.eager)
     M, qt, s = wl["M"], wl["qt"], 1.5
     chain, shapes, sigma = chain_spec(wl["chain"])
@@ -969,7 +973,7 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
     wsq = torch.zeros(max(needq, 256), dtype=torch.uint8, device=dev)
     one_launch = wl.get("one_launch", False)
 
-    small = small_m_linears(chain, shapes, M, one_launch)
+    small = set() if wl.get("no_small_m") else small_m_linears(chain, shapes, M, one_launch)
     log(f"bench: {name} M={M} qt={qt}: building {wl['sets']} weight sets ...")
     layers = [Layer(chain, shapes, M, qt, sigma, 1000 * (j + 1), dev, x0, bufs, ws, s,
                     fused=wl.get("fused", True), one_launch=one_launch, wsq=wsq, small=small)
