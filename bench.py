@@ -17,6 +17,10 @@ between events on its own stream, so no host launch gap is counted. Inputs
 are seeded synthetic tensors generated on the device. The roofline "traffic"
 (HBM bytes per launch) comes from the committed rocprofv3 counter summary in
 profiles/hbm_traffic.md and is null when the GEMM sources changed since.
+Where the dominant GEMM runs on a tiling the copy-stream probe replays (192x128
+or 256x256 tiles without split K), "copy_stream_us" is that probe's time over
+the same weights and codes, timed the same way: the GEMM's operand copies,
+LDS ring, waits and barriers without the matrix work.
 
 The default run adds, beside the 7B line: the peaks this GPU reaches (HBM
 read, dense INT8 / FP8 MFMA, the shader clock under MFMA load; every roofline
@@ -297,7 +301,7 @@ class Layer:
 KERNEL_SOURCES = {
     "mx": ("mx_kernels.hip", "qr_device.h"),
     "acr": ("acr_kernels.hip",),
-    "gemm": ("gemm_kernels.hip", "gemm_plan.hip", "qr_gemm.h", "qr_device.h"),
+    "gemm": ("gemm_kernels.hip", "gemm_plan.hip", "qr_gemm.h", "qr_device.h", "qr_copy.h"),
     "refresh": ("quant_kernels.hip", "qr_device.h"),
     "small": ("small_m_kernels.hip", "qr_device.h", "qr_internal.h"),
 }
@@ -1008,6 +1012,7 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
 
     K = steps
     mode = "eager" if eager else "hip_graph"
+    copy_us = None
     if eager:
         # Every op launched from the host; events around the dominant GEMM.
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -1066,6 +1071,8 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
                 b.record(st)
         torch.cuda.synchronize()
         dom_us = 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / (reps * DOM_BATCH)
+        copy_us = copy_stream_us(B, layers, bufs, chain, dom, M, Nd, Kd, qt, small, one_launch,
+                                 st, reps)
         del whole, dom_graph
     sec_step = (t1 - t0) / K
 
@@ -1109,6 +1116,11 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
         "traffic_key": traffic_key,
         "kernel": kernel,
     })
+    if copy_us:
+        # the same tiling's operand copies, ring, waits and barriers without
+        # the matrix work: the kernel's time against its copy pipeline's
+        roofline["copy_stream_us"] = round(copy_us, 2)
+        roofline["copy_stream_over_kernel"] = round(copy_us / dom_us, 4)
     config = {
         "workload": f"{name}: one decoder layer's W8A8 linears, M={M} tokens, "
                     + ", ".join(f"{L['name']} {shapes[L['name']][0]}x{shapes[L['name']][1]}"
@@ -1139,6 +1151,39 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
     del layers, bufs, ws
     torch.cuda.empty_cache()
     return res
+
+
+def copy_stream_us(B, layers, bufs, chain, dom, M, N, K, qt, small, one_launch, st, reps):
+    """Mean time of qr_probe_copy_stream over the dominant GEMM's tiling (its
+    plan's tile and rows, the same weight sets and input codes), timed like
+    the GEMM: a graph of DOM_BATCH launches replayed between events on `st`.
+    None where the probe does not replay the plan (other tiles, split K)."""
+    import torch
+
+    tile, split, rows = B.gemm_plan(M, N, K, qt)
+    if dom in small or one_launch or split != 1 or tile not in (4, 8) or K % 128:
+        return None
+    key = chain_keys(chain)[0]
+    xq = next(bufs["q_" + L["name"]][0] for L in chain if key[L["name"]] == key[dom])
+    bm = 256 if tile == 4 else 128
+    sink = torch.empty(-(-N // rows) * -(-M // bm), dtype=torch.int32, device=xq.device)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(graph, stream=st):
+            for j in range(DOM_BATCH):
+                B.probe_copy_stream(tile, layers[j % len(layers)].W[dom][0], xq, rows, sink=sink)
+    graph.replay()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    with torch.cuda.stream(st):
+        for a, b in evs:
+            a.record(st)
+            graph.replay()
+            b.record(st)
+    torch.cuda.synchronize()
+    del graph
+    return 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / (reps * DOM_BATCH)
 
 
 def roofline_object(bound, alg_bytes, alg_ops, us, qt):
@@ -1259,6 +1304,29 @@ def prefill_gate(dev):
     plan = B.gemm_plan(M, N, K, qt)
     roof = roofline_object("mfma", linear_bytes(M, N, K), 2 * M * N * K, us, qt)
     roof["kernel"] = f"gate GEMM {N}x{K} M={M} ({B.tile_name(plan[0])}, splitk {plan[1]})"
+    if plan[1] == 1 and plan[0] in (4, 8):
+        # the tiling's operand copies alone (qr_probe_copy_stream), timed alike
+        bm = 256 if plan[0] == 4 else 128
+        sink = torch.empty(-(-N // plan[2]) * -(-M // bm), dtype=torch.int32, device=dev)
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(st):
+            with torch.cuda.graph(cg, stream=st):
+                for i in range(DOM_BATCH):
+                    B.probe_copy_stream(plan[0], sets[i % 2][0], xq, plan[2], sink=sink)
+        torch.cuda.synchronize()
+        cts = []
+        with torch.cuda.stream(st):
+            cg.replay()
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                cg.replay()
+                b.record(st)
+                b.synchronize()
+                cts.append(a.elapsed_time(b) * 1000.0 / DOM_BATCH)
+        del cg
+        roof["copy_stream_us"] = round(sorted(cts)[2], 2)
+        roof["copy_stream_over_kernel"] = round(sorted(cts)[2] / us, 4)
     del sets, Y, ws, xq, sx, gph
     torch.cuda.empty_cache()
     return {"us": round(us, 2), "tops": round(2 * M * N * K / us / 1e6, 1), "roofline": roof,

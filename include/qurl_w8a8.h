@@ -468,8 +468,25 @@ int qr_set_small_m_override(int rf);
  *   *wall_khz (host) receives the wall clock's rate, so that
  *   (t1 - t0) / (w1 - w0) * wall_khz is the shader clock in kHz.
  *   blocks in [1, 65536], iters in [1, 2^24].
+ * qr_probe_copy_stream -- the operand copies of one LDS-DMA GEMM tiling with
+ *   no matrix work: the blocks, copies, LDS ring, waits and per-step
+ *   barriers that qr_w8a8_gemm runs for tile `tile` (4: 256x256 tiles,
+ *   2-slot ring, non-temporal weight copies; 8: 192x128 tiles, 4-slot ring)
+ *   with `rows` weight rows per tile (a multiple of 8 up to the tile height,
+ *   as qr_gemm_plan reports it) over the code matrices Wq [N][K] and
+ *   Xq [M][K] (row-major, device, K a multiple of 128), without split K.
+ *   Its time is what that tiling's copy pipeline alone takes. Block b
+ *   (tile n = b / tiles_m, token tile m = b % tiles_m, tiles_m = ceil(M /
+ *   tile width)) writes to sink[b] the XOR of the four 32-bit words at
+ *   Wq[n * rows][K - 128 .. K - 113] and Xq[m * width][K - 128 .. K - 113]
+ *   as they arrived in LDS, so the copies can be checked. sink: device,
+ *   >= ceil(N / rows) * tiles_m words. QR_ERR_INVALID_ARG for another tile,
+ *   bad sizes or a short sink; QR_ERR_UNSUPPORTED for a code matrix of
+ *   2^31 - 2^16 bytes or more.
  */
 int qr_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t sink_words, void* stream);
+int qr_probe_copy_stream(int tile, const void* Wq, int64_t N, const void* Xq, int64_t M, int64_t K,
+                         int rows, uint32_t* sink, int64_t sink_words, void* stream);
 int qr_probe_mfma(int qt, int blocks, int iters, uint32_t* sink, uint64_t* ticks, int* wall_khz,
                   void* stream);
 

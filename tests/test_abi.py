@@ -222,3 +222,36 @@ def test_gemm_planner_invariants(B):
                 assert ws != ctypes.c_size_t(-1).value
                 if s > 1:
                     assert ws >= s * M * N * 4, (M, N, K, qt, s, ws)
+
+
+def test_probe_validation(B):
+    L = _L(B)
+    fake = ctypes.c_void_p(256)
+    INV, UNS = -1, -2
+    # the read probe: sizes in whole 16-byte words, a sink of 1024 words
+    assert L.qr_probe_read(fake, 24, fake, 1024, NULL) == INV
+    assert L.qr_probe_read(fake, 32, fake, 1023, NULL) == INV
+    assert L.qr_probe_read(fake, 32, NULL, 1024, NULL) == INV
+    # the MFMA probe: qtype, block and round counts, pointers
+    khz = ctypes.c_int(0)
+    assert L.qr_probe_mfma(7, 256, 10, fake, fake, ctypes.byref(khz), NULL) == INV
+    assert L.qr_probe_mfma(I8, 0, 10, fake, fake, ctypes.byref(khz), NULL) == INV
+    assert L.qr_probe_mfma(I8, 256, 0, fake, fake, ctypes.byref(khz), NULL) == INV
+    assert L.qr_probe_mfma(I8, 256, 10, fake, NULL, ctypes.byref(khz), NULL) == INV
+    # the copy-stream probe: only tiles 4 and 8, K a multiple of 128, rows a
+    # multiple of 8 up to the tile height, a sink word per block
+    cs = L.qr_probe_copy_stream
+    assert cs(2, fake, 18944, fake, 256, 3584, 192, fake, 1 << 20, NULL) == INV
+    assert cs(8, fake, 18944, fake, 256, 3600, 192, fake, 1 << 20, NULL) == INV
+    assert cs(8, fake, 18944, fake, 256, 0, 192, fake, 1 << 20, NULL) == INV
+    assert cs(8, fake, 0, fake, 256, 3584, 192, fake, 1 << 20, NULL) == INV
+    assert cs(8, fake, 18944, fake, 0, 3584, 192, fake, 1 << 20, NULL) == INV
+    for rows in (0, 12, 200):
+        assert cs(8, fake, 18944, fake, 256, 3584, rows, fake, 1 << 20, NULL) == INV
+    assert cs(4, fake, 27648, fake, 512, 5120, 264, fake, 1 << 20, NULL) == INV
+    assert cs(8, NULL, 18944, fake, 256, 3584, 192, fake, 1 << 20, NULL) == INV
+    assert cs(8, fake, 18944, fake, 256, 3584, 192, NULL, 1 << 20, NULL) == INV
+    # 99 weight tiles x 2 token tiles = 198 blocks
+    assert cs(8, fake, 18944, fake, 256, 3584, 192, fake, 197, NULL) == INV
+    assert "198" in L.qr_last_error().decode()
+    assert cs(8, fake, 1 << 20, fake, 256, 1 << 11, 192, fake, 1 << 30, NULL) == UNS

@@ -32,6 +32,7 @@ EXPORTS = [
     "qr_w8a8_gemm", "qr_w8a8_gemm_quant", "qr_linear_fused", "qr_linear_fused_noalloc",
     "qr_workspace_size", "qr_gemm_plan", "qr_tile_name", "qr_num_tiles", "qr_set_plan_override",
     "qr_set_small_m_override", "qr_last_error", "qr_version", "qr_probe_read", "qr_probe_mfma",
+    "qr_probe_copy_stream",
 ]
 
 
@@ -71,6 +72,7 @@ _SIGS = {
     "qr_last_error": (ctypes.c_char_p, []),
     "qr_probe_read": (_int, [_vp, _sz, _vp, _i64, _vp]),
     "qr_probe_mfma": (_int, [_int, _int, _int, _vp, _vp, ctypes.POINTER(_int), _vp]),
+    "qr_probe_copy_stream": (_int, [_int, _vp, _i64, _vp, _i64, _i64, _int, _vp, _i64, _vp]),
     "qr_version": (ctypes.c_char_p, []),
 }
 
@@ -513,6 +515,27 @@ def probe_read(buf, sink=None):
     with torch.cuda.device(buf.device):
         st = lib().qr_probe_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream(buf.device))
     _check("qr_probe_read", st)
+    return sink
+
+
+def probe_copy_stream(tile, Wq, Xq, rows, sink=None):
+    """Enqueue the operand copies GEMM tile `tile` (4 or 8) makes over the
+    code matrices Wq [N, K] and Xq [M, K] with `rows` weight rows per tile,
+    without the matrix work; returns the sink tensor (one word per block)."""
+    _need_cuda(Wq, Xq, sink)
+    if Wq.dim() != 2 or Xq.dim() != 2 or Wq.shape[1] != Xq.shape[1]:
+        raise ValueError("Wq [N, K] and Xq [M, K] with the same K expected")
+    if not (Wq.is_contiguous() and Xq.is_contiguous()) or Wq.element_size() != 1 or Xq.element_size() != 1:
+        raise ValueError("contiguous 8-bit code matrices expected")
+    (N, K), M = Wq.shape, Xq.shape[0]
+    bm = {4: 256, 8: 128}.get(tile, 1)
+    grid = -(-N // max(rows, 1)) * -(-M // bm)
+    if sink is None:
+        sink = torch.empty(max(grid, 1), dtype=torch.int32, device=Wq.device)
+    with torch.cuda.device(Wq.device):
+        st = lib().qr_probe_copy_stream(tile, _ptr(Wq), N, _ptr(Xq), M, K, rows, _ptr(sink), sink.numel(),
+                                        _stream(Wq.device))
+    _check("qr_probe_copy_stream", st)
     return sink
 
 

@@ -6,11 +6,16 @@
 //    (eight in flight per thread) and keeps one XOR word per block, so the
 //    loads cannot be removed. Bytes / time = the HBM read rate (for a buffer
 //    well past the 256 MB Infinity Cache).
+//  * copy_stream_probe_kernel replays the operand copies of one LDS-DMA GEMM
+//    tiling (the same blocks, copies, ring, waits and barriers) with no
+//    fragment reads and no MFMAs: the time the copy pipeline alone needs
+//    for that tiling, against which the GEMM's own time can be read.
 //  * mfma_probe_kernel runs rounds of eight independent dense 8-bit MFMAs
 //    (INT8 32x32x32 or FP8 32x32x64, the shapes the GEMMs use) per wave on
 //    register operands. Wave 0 of each block reads the shader-clock counter
 //    and the constant-rate wall clock at its start and end, so the host can
 //    tell the shader clock the matrix cores ran at.
+#include "qr_copy.h"
 #include "qr_internal.h"
 
 namespace qr {
@@ -111,9 +116,114 @@ __global__ __launch_bounds__(512) void mfma_probe_kernel(int iters, uint32_t* __
   }
 }
 
+// Block b (dealt to the XCDs round-robin and ordered token tile fastest, as
+// the GEMM deals its blocks) copies weight rows [tn * rows, tn * rows + rows)
+// and token rows [tm * BM, tm * BM + BM) over K in 128-byte steps into an
+// S-slot LDS ring: wave w copies weight row blocks (1 KB = 8 rows) w * NA ..
+// w * NA + NA - 1 and token row blocks w * NB .. w * NB + NB - 1 of every
+// step, the lane owning physical chunk c of row r fetching logical chunk
+// c ^ ((r >> 1) & 7); rows outside the tile or the matrix read as zero. Each
+// wave waits for its own copies of a step, all meet at one barrier per step,
+// and the copies of step it + S - 1 are issued after it. Thread 0 then writes
+// sink[b] = XOR of the first 16 bytes of the block's first weight row and of
+// its first token row in the last K step, as they arrived in LDS.
+template <int BN, int BM, int NW, int S, bool NTW>
+__global__ __launch_bounds__(64 * NW, 1) void copy_stream_probe_kernel(
+    const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, int64_t N, int64_t M, int64_t K,
+    int rows, int tiles_m, uint32_t* __restrict__ sink) {
+  constexpr int BK = 128, RB = 8, CPR = 8;
+  constexpr int IA = BN / RB, IB = BM / RB;
+  static_assert(IA % NW == 0 && IB % NW == 0, "row blocks per wave");
+  constexpr int NA = IA / NW, NB = IB / NW, NI = NA + NB;
+  static_assert(NA >= 1 && NA <= 4 && NB >= 1 && NB <= 4, "one M0 group per operand");
+  constexpr int STAGE = (IA + IB) * 1024;
+  static_assert(S >= 2 && S * STAGE <= 160 * 1024 && (S - 2) * NI <= 63, "ring");
+  constexpr uint32_t kOOB = 0x80000000u;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+
+  const int G = gridDim.x, G8 = G & ~7;
+  int b = blockIdx.x;
+  if (b < G8) b = (b & 7) * (G8 >> 3) + (b >> 3);
+  const int tm = b % tiles_m, tn = b / tiles_m;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rsw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)(uint32_t)(N * K), kBufWord3);
+  const __amdgpu_buffer_rsrc_t rsx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)(uint32_t)(M * K), kBufWord3);
+  const int lrow = lane / CPR, pch = lane % CPR;
+  uint32_t oa[NA], ob[NB];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int r = (wid * NA + i) * RB + lrow;
+    const int c = pch ^ ((r >> 1) & 7);
+    const int64_t row = (int64_t)tn * rows + r;
+    oa[i] = ((r < rows && row < N) ? (uint32_t)(row * K + c * 16) : kOOB) - 1024u * (uint32_t)i;
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int r = (wid * NB + i) * RB + lrow;
+    const int c = pch ^ ((r >> 1) & 7);
+    const int64_t row = (int64_t)tm * BM + r;
+    ob[i] = ((row < M) ? (uint32_t)(row * K + c * 16) : kOOB) - 1024u * (uint32_t)i;
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
+  const uint32_t la0 = lds0 + (uint32_t)(wid * NA) * 1024u;
+  const uint32_t lb0 = lds0 + (uint32_t)(IA + wid * NB) * 1024u;
+  auto issue = [&](int slot, int ks) {
+    const int soff = ks * BK;
+    dma_group<NA, NTW>(la0 + (uint32_t)(slot * STAGE), oa, rsw, soff);
+    dma_group<NB, false>(lb0 + (uint32_t)(slot * STAGE), ob, rsx, soff);
+  };
+  const int nk = (int)(K / BK);
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s);
+  int is = S - 1;
+  for (int it = 0; it < nk; ++it) {
+    wait_stages<NI, S - 2>(nk - 1 - it);
+    __syncthreads();
+    if (it + S - 1 < nk) issue(is, it + S - 1);
+    is = is + 1 == S ? 0 : is + 1;
+  }
+  wait_vm<0>();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int last = (nk - 1) % S;
+    const uint32_t* wa = reinterpret_cast<const uint32_t*>(smem + last * STAGE);
+    const uint32_t* xa = reinterpret_cast<const uint32_t*>(smem + last * STAGE + IA * 1024);
+    sink[b] = wa[0] ^ wa[1] ^ wa[2] ^ wa[3] ^ xa[0] ^ xa[1] ^ xa[2] ^ xa[3];
+  }
+}
+
 }  // namespace
 
 unsigned read_probe_blocks() { return 1024; }
+
+// Geometry of the GEMM tilings the copy-stream probe replays (tile index of
+// the GEMM planner; the same ring depth, waves and hint on the weights).
+bool copy_stream_probe_tile(int tile, int& bn, int& bm) {
+  if (tile == 4) { bn = 256; bm = 256; return true; }
+  if (tile == 8) { bn = 192; bm = 128; return true; }
+  return false;
+}
+
+hipError_t launch_copy_stream_probe(int tile, const void* W, const void* X, int64_t N, int64_t M,
+                                    int64_t K, int rows, uint32_t* sink, hipStream_t st) {
+  int bn = 0, bm = 0;
+  if (!copy_stream_probe_tile(tile, bn, bm)) return hipErrorInvalidValue;
+  const int64_t tiles_m = (M + bm - 1) / bm, tiles_n = (N + rows - 1) / rows;
+  const dim3 grid((unsigned)(tiles_n * tiles_m));
+  const uint8_t* w = static_cast<const uint8_t*>(W);
+  const uint8_t* x = static_cast<const uint8_t*>(X);
+  if (tile == 4)
+    hipLaunchKernelGGL((copy_stream_probe_kernel<256, 256, 8, 2, true>), grid, dim3(512), 0, st, w,
+                       x, N, M, K, rows, (int)tiles_m, sink);
+  else
+    hipLaunchKernelGGL((copy_stream_probe_kernel<192, 128, 8, 4, false>), grid, dim3(512), 0, st, w,
+                       x, N, M, K, rows, (int)tiles_m, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_read_probe(const void* buf, int64_t n16, uint32_t* sink, hipStream_t st) {
   hipLaunchKernelGGL(read_probe_kernel, dim3(read_probe_blocks()), dim3(256), 0, st,
