@@ -41,6 +41,7 @@
 namespace qr {
 namespace {
 
+typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -316,9 +317,13 @@ __device__ __forceinline__ void store_tile_staged(
       const uint16_t* src = so + ml * LDT + nl;
       uint16_t* dst = Y + (int64_t)(c0 + ml) * p.ldy + nl;
       if (nl + 8 <= own) {
+        // Non-temporal: the tile's outputs leave in one burst at the end of
+        // the kernel and are read by another launch, usually from another
+        // XCD's L2; streaming them out drains the burst sooner.
         const uint2 lo = *reinterpret_cast<const uint2*>(src);
         const uint2 hi = *reinterpret_cast<const uint2*>(src + 4);
-        *reinterpret_cast<uint4*>(dst) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        const v4u_t v = {lo.x, lo.y, hi.x, hi.y};
+        __builtin_nontemporal_store(v, reinterpret_cast<v4u_t*>(dst));
       } else {
         for (int e = 0; nl + e < own; ++e) dst[e] = src[e];
       }
