@@ -106,14 +106,15 @@ def _check_fp8(y_bits, X_bits, Wq, sw, what):
 SHAPES = [(3584, 3584), (4608, 3584), (18944, 3584), (3584, 18944), (200, 1040), (37, 16)]
 
 
-@pytest.mark.parametrize("mode", ["auto", "forced"])
-@pytest.mark.parametrize("qt", QTS)
-@pytest.mark.parametrize("N,K", SHAPES)
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+# forced cases only where the kernel can run (the others are the auto cases'
+# fallback to the general path)
+CASES = [(mode, qt, N, K, M) for mode in ("auto", "forced") for qt in QTS for N, K in SHAPES
+         for M in (1, 2, 3, 4) if mode == "auto" or can_run(M, K)]
+
+
+@pytest.mark.parametrize("mode,qt,N,K,M", CASES)
 def test_linear_fused_small_m_vs_oracle(mode, qt, N, K, M):
     if mode == "forced":
-        if not can_run(M, K):
-            pytest.skip("outside the kernel's limits (covered by the auto case)")
         B.set_small_m_override(rf_for(N))
     X_bits = I.activations(M, K, seed=I.matrix_seed(6, M * 7 + K % 97), kind="outliers")
     y, untouched, Wq, sw = _run(X_bits, N, K, qt, seed=N + K)
