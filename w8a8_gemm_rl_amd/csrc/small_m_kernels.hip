@@ -12,18 +12,19 @@
 // weights: a separate quantizer launch for its input, and, on narrow layers,
 // split K with a second kernel that adds the partial sums. Here
 //  * one block owns 16 * RF output channels and the whole K. In every block
-//    wave 0 quantizes the M token rows into an LDS panel [M][KP] (absmax
-//    over K, then the codes, with the arithmetic of the per-token quantizer
-//    kernel: the same helpers, so the codes and scales are the same bits)
-//    while waves 1-7 start streaming weights; the rows are a few to tens of
-//    KB and come from L2 after the first block;
-//  * waves 1-7 split K instead of the blocks: wave w takes the 128-byte K
-//    chunks c = w - 1, w + 6, ...; each lane loads 16-byte pieces of whole
-//    128-byte weight lines into registers, PD chunks ahead, which a per-wave
-//    LDS stage turns into the MFMA A operand (no barrier in the loop), and
-//    reads the matching bytes of its token's codes from the panel (the B
-//    operand; lanes of tokens >= M feed zeros). A and B use the same K order
-//    inside an instruction, so the dot product is the plain one;
+//    waves 0..QW-1 (QW = 1 to 4, one per 4096 input elements) quantize the
+//    M token rows into an LDS panel [M][KP] (absmax over K, then the codes,
+//    with the arithmetic of the per-token quantizer kernel: the same
+//    helpers, so the codes and scales are the same bits) while the other
+//    NSW = 8 - QW waves start streaming weights; the rows are a few to tens
+//    of KB and come from L2 after the first block;
+//  * the streaming waves split K instead of the blocks: wave w takes the
+//    128-byte K chunks c = w - QW, w - QW + NSW, ...; each lane loads 16-byte
+//    pieces of whole 128-byte weight lines into registers, PD chunks ahead,
+//    which a per-wave LDS stage turns into the MFMA A operand (no barrier in
+//    the loop), and reads the matching bytes of its token's codes from the
+//    panel (the B operand; lanes of tokens >= M feed zeros). A and B use the
+//    same K order inside an instruction, so the dot product is the plain one;
 //  * the waves' partial sums meet in LDS and are added in wave order (FP8
 //    sums are deterministic), then the GEMM epilogue
 //    y = bf16_rne(fl32(fl32(fl32(acc) * sx[m]) * sw[n])) with
