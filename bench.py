@@ -838,6 +838,10 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times (for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
+    ap.add_argument("--copy-stream-variants", action="store_true",
+                    help="only time the copy-stream probe's variants (row strides padded by a line, "
+                         "weights as K panels, no barrier per K step) beside the GEMM on the 7B and "
+                         "32B gate shapes, print one JSON line and exit")
     args = ap.parse_args()
 
     if args.summarize_rocprof:
@@ -872,6 +876,9 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}))
         return
     B.lib()
+    if args.copy_stream_variants:
+        print(json.dumps(copy_stream_variants(dev)))
+        return
     if args.workload in REFRESH:
         run_refresh(args, dev)
         return
@@ -1184,6 +1191,81 @@ def copy_stream_us(B, layers, bufs, chain, dom, M, N, K, qt, small, one_launch, 
     torch.cuda.synchronize()
     del graph
     return 1000.0 * sum(a.elapsed_time(b) for a, b in evs) / (reps * DOM_BATCH)
+
+
+def copy_stream_variants(dev, rounds=7):
+    """The copy-stream probe's variants on the 7B gate at 256 tokens (tile 8,
+    K = 3584) and the 32B gate at 512 tokens (tile 4, K = 5120), INT8, each a
+    graph of DOM_BATCH launches walking enough weight copies to exceed the
+    256 MB Infinity Cache, replayed round-robin with the GEMM itself on the
+    same codes: row-major codes as the GEMM reads them, row strides padded
+    by one 128-byte line (weights and tokens), the weights read as K panels,
+    and no barrier per K step (alone and with panels). Median per-launch us."""
+    import statistics
+
+    import torch
+
+    from w8a8_gemm_rl_amd import binding as B
+
+    out = []
+    for name, M, N, K in (("7b_gate_m256", 256, 18944, 3584), ("32b_gate_m512", 512, 27648, 5120)):
+        tile, split, rows = B.gemm_plan(M, N, K, "int8")
+        if split != 1 or tile not in (4, 8):
+            continue
+        ncopy = max(2, int(600e6 // (N * K)) + 1)
+        g = torch.Generator(device=dev)
+        g.manual_seed(N + K)
+        W = [torch.randint(-127, 128, (N, K), dtype=torch.int8, device=dev, generator=g) for _ in range(ncopy)]
+        Wp = [torch.randint(-127, 128, (N, K + 128), dtype=torch.int8, device=dev, generator=g)[:, :K]
+              for _ in range(ncopy)]
+        X = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+        Xp = torch.randint(-127, 128, (M, K + 128), dtype=torch.int8, device=dev, generator=g)[:, :K]
+        sx = torch.rand(M, device=dev) * 1e-3
+        sw = torch.rand(N, device=dev) * 1e-3
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.zeros(max(B.workspace_size("qr_w8a8_gemm", M, N, K, "int8"), 256), dtype=torch.uint8,
+                         device=dev)
+        bm = 256 if tile == 4 else 128
+        sink = torch.empty(-(-N // rows) * -(-M // bm), dtype=torch.int32, device=dev)
+        cases = {
+            "gemm": lambda j: B.w8a8_gemm(X, sx, W[j], sw, "int8", Y=Y, ws=ws),
+            "copies": lambda j: B.probe_copy_stream(tile, W[j], X, rows, sink=sink),
+            "copies_padded_rows": lambda j: B.probe_copy_stream(tile, Wp[j], Xp, rows, sink=sink),
+            "copies_k_panels": lambda j: B.probe_copy_stream(tile, W[j], X, rows, sink=sink, panel=True),
+            "copies_no_barrier": lambda j: B.probe_copy_stream(tile, W[j], X, rows, sink=sink, barrier=False),
+            "copies_k_panels_no_barrier": lambda j: B.probe_copy_stream(tile, W[j], X, rows, sink=sink,
+                                                                        panel=True, barrier=False),
+        }
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        graphs = {}
+        with torch.cuda.stream(st):
+            for key, fn in cases.items():
+                fn(0)
+                gph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gph, stream=st):
+                    for j in range(DOM_BATCH):
+                        fn(j % ncopy)
+                graphs[key] = gph
+        torch.cuda.synchronize()
+        ts = {key: [] for key in graphs}
+        with torch.cuda.stream(st):
+            for gph in graphs.values():
+                gph.replay()
+            for _ in range(rounds):
+                for key, gph in graphs.items():
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(st)
+                    gph.replay()
+                    b.record(st)
+                    b.synchronize()
+                    ts[key].append(a.elapsed_time(b) * 1000.0 / DOM_BATCH)
+        out.append({"shape": name, "M": M, "N": N, "K": K, "tile": B.tile_name(tile), "rows": rows,
+                    "weight_copies": ncopy,
+                    "us": {key: round(statistics.median(v), 2) for key, v in ts.items()}})
+        del graphs, W, Wp, X, Xp, Y, ws
+        torch.cuda.empty_cache()
+    return {"copy_stream_variants": out, "gemm_source_sha16": kernel_source_sha256()[:16]}
 
 
 def roofline_object(bound, alg_bytes, alg_ops, us, qt):

@@ -473,20 +473,28 @@ int qr_set_small_m_override(int rf);
  *   barriers that qr_w8a8_gemm runs for tile `tile` (4: 256x256 tiles,
  *   2-slot ring, non-temporal weight copies; 8: 192x128 tiles, 4-slot ring)
  *   with `rows` weight rows per tile (a multiple of 8 up to the tile height,
- *   as qr_gemm_plan reports it) over the code matrices Wq [N][K] and
- *   Xq [M][K] (row-major, device, K a multiple of 128), without split K.
- *   Its time is what that tiling's copy pipeline alone takes. Block b
- *   (tile n = b / tiles_m, token tile m = b % tiles_m, tiles_m = ceil(M /
- *   tile width)) writes to sink[b] the XOR of the four 32-bit words at
- *   Wq[n * rows][K - 128 .. K - 113] and Xq[m * width][K - 128 .. K - 113]
- *   as they arrived in LDS, so the copies can be checked. sink: device,
+ *   as qr_gemm_plan reports it), without split K, over the codes Wq (N rows)
+ *   and Xq (M rows) of K bytes each (device, K a multiple of 128). Its time
+ *   is what that tiling's copy pipeline alone takes. Row r of Xq starts at
+ *   byte r * ldx, row r of Wq at r * ldw (ldw, ldx >= K, multiples of 16; the
+ *   GEMM's layout is ldw = ldx = K). Variants, by `flags`:
+ *   QR_PROBE_PANEL reads Wq as K panels, the 128 bytes of K step k of row r
+ *   at byte (k * N + r) * 128 (ldw ignored), so that each step of a tile is
+ *   one contiguous block; QR_PROBE_NO_BARRIER drops the barrier per K step
+ *   (each wave waits only for its own copies). Block b (tile n = b / tiles_m,
+ *   token tile m = b % tiles_m, tiles_m = ceil(M / tile width)) writes to
+ *   sink[b] the XOR of the four 32-bit words of the first 16 bytes of K step
+ *   K / 128 - 1 of weight row n * rows and of token row m * width, as they
+ *   arrived in LDS, so the copies can be checked. sink: device,
  *   >= ceil(N / rows) * tiles_m words. QR_ERR_INVALID_ARG for another tile,
- *   bad sizes or a short sink; QR_ERR_UNSUPPORTED for a code matrix of
- *   2^31 - 2^16 bytes or more.
+ *   unknown flags, bad sizes or strides or a short sink;
+ *   QR_ERR_UNSUPPORTED for a code buffer of 2^31 - 2^16 bytes or more.
  */
 int qr_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t sink_words, void* stream);
-int qr_probe_copy_stream(int tile, const void* Wq, int64_t N, const void* Xq, int64_t M, int64_t K,
-                         int rows, uint32_t* sink, int64_t sink_words, void* stream);
+enum { QR_PROBE_PANEL = 1, QR_PROBE_NO_BARRIER = 2 };
+int qr_probe_copy_stream(int tile, const void* Wq, int64_t N, int64_t ldw, const void* Xq, int64_t M,
+                         int64_t ldx, int64_t K, int rows, int flags, uint32_t* sink, int64_t sink_words,
+                         void* stream);
 int qr_probe_mfma(int qt, int blocks, int iters, uint32_t* sink, uint64_t* ticks, int* wall_khz,
                   void* stream);
 

@@ -239,19 +239,27 @@ def test_probe_validation(B):
     assert L.qr_probe_mfma(I8, 256, 0, fake, fake, ctypes.byref(khz), NULL) == INV
     assert L.qr_probe_mfma(I8, 256, 10, fake, NULL, ctypes.byref(khz), NULL) == INV
     # the copy-stream probe: only tiles 4 and 8, K a multiple of 128, rows a
-    # multiple of 8 up to the tile height, a sink word per block
+    # multiple of 8 up to the tile height, strides >= K in 16-byte units, known
+    # flags, a sink word per block
     cs = L.qr_probe_copy_stream
-    assert cs(2, fake, 18944, fake, 256, 3584, 192, fake, 1 << 20, NULL) == INV
-    assert cs(8, fake, 18944, fake, 256, 3600, 192, fake, 1 << 20, NULL) == INV
-    assert cs(8, fake, 18944, fake, 256, 0, 192, fake, 1 << 20, NULL) == INV
-    assert cs(8, fake, 0, fake, 256, 3584, 192, fake, 1 << 20, NULL) == INV
-    assert cs(8, fake, 18944, fake, 0, 3584, 192, fake, 1 << 20, NULL) == INV
+
+    def call(tile=8, N=18944, ldw=3584, M=256, ldx=3584, K=3584, rows=192, flags=0, sink=fake,
+             words=1 << 20, W=fake, X=fake):
+        return cs(tile, W, N, ldw, X, M, ldx, K, rows, flags, sink, words, NULL)
+
+    assert call(tile=2) == INV
+    assert call(K=3600, ldw=3600, ldx=3600) == INV
+    assert call(K=0) == INV
+    assert call(N=0) == INV and call(M=0) == INV
     for rows in (0, 12, 200):
-        assert cs(8, fake, 18944, fake, 256, 3584, rows, fake, 1 << 20, NULL) == INV
-    assert cs(4, fake, 27648, fake, 512, 5120, 264, fake, 1 << 20, NULL) == INV
-    assert cs(8, NULL, 18944, fake, 256, 3584, 192, fake, 1 << 20, NULL) == INV
-    assert cs(8, fake, 18944, fake, 256, 3584, 192, NULL, 1 << 20, NULL) == INV
+        assert call(rows=rows) == INV
+    assert call(tile=4, N=27648, M=512, K=5120, ldw=5120, ldx=5120, rows=264) == INV
+    assert call(flags=4) == INV and call(flags=-1) == INV
+    assert call(ldw=3520) == INV and call(ldx=3590) == INV
+    assert call(W=NULL) == INV and call(sink=NULL) == INV
     # 99 weight tiles x 2 token tiles = 198 blocks
-    assert cs(8, fake, 18944, fake, 256, 3584, 192, fake, 197, NULL) == INV
+    assert call(words=197) == INV
     assert "198" in L.qr_last_error().decode()
-    assert cs(8, fake, 1 << 20, fake, 256, 1 << 11, 192, fake, 1 << 30, NULL) == UNS
+    assert call(N=1 << 20, K=1 << 11, ldw=1 << 11, ldx=1 << 11, words=1 << 30) == UNS
+    # the panel variant sizes the weights as N x K, whatever ldw says
+    assert call(N=(1 << 20) - 64, K=1 << 11, ldw=1 << 12, ldx=1 << 11, words=1 << 30) == UNS

@@ -32,29 +32,48 @@ def test_read_probe_reads_every_word():
     assert got == _xor_words(buf.cpu().numpy())
 
 
-@pytest.mark.parametrize("tile,N,M,K,rows", [
-    (8, 3600, 200, 1024, 192),    # ragged weight and token tiles, 8 K steps (ring of 4)
-    (8, 18944, 256, 3584, 192),   # the 7B gate projection at 256 tokens
-    (8, 1000, 130, 384, 96),      # shrunk tiles, 3 K steps
-    (4, 1000, 300, 640, 248),     # ring of 2, 5 K steps
-    (4, 27648, 512, 5120, 256),   # the 32B gate projection at 512 tokens
+@pytest.mark.parametrize("tile,N,M,K,rows,pad,panel,barrier", [
+    (8, 3600, 200, 1024, 192, 0, False, True),    # ragged weight and token tiles, 8 K steps (ring of 4)
+    (8, 18944, 256, 3584, 192, 0, False, True),   # the 7B gate projection at 256 tokens
+    (8, 1000, 130, 384, 96, 0, False, True),      # shrunk tiles, 3 K steps
+    (4, 1000, 300, 640, 248, 0, False, True),     # ring of 2, 5 K steps
+    (4, 27648, 512, 5120, 256, 0, False, True),   # the 32B gate projection at 512 tokens
+    (8, 3600, 200, 1024, 192, 128, False, True),  # rows padded by one 128-byte line
+    (4, 1000, 300, 640, 248, 48, False, True),    # rows padded by 48 bytes
+    (8, 3600, 200, 1024, 192, 0, True, True),     # weights read as K panels
+    (4, 1000, 300, 640, 248, 0, True, True),
+    (8, 3600, 200, 1024, 192, 0, False, False),   # no barrier per K step
+    (4, 1000, 300, 640, 248, 128, True, False),
 ])
-def test_copy_stream_probe_copies_the_tiles(tile, N, M, K, rows):
+def test_copy_stream_probe_copies_the_tiles(tile, N, M, K, rows, pad, panel, barrier):
     g = torch.Generator(device=DEV)
-    g.manual_seed(N + M + K)
-    Wq = torch.randint(-128, 128, (N, K), dtype=torch.int8, device=DEV, generator=g)
-    Xq = torch.randint(-128, 128, (M, K), dtype=torch.int8, device=DEV, generator=g)
+    g.manual_seed(N + M + K + pad)
+    Wbuf = torch.randint(-128, 128, (N, K + pad), dtype=torch.int8, device=DEV, generator=g)
+    Xbuf = torch.randint(-128, 128, (M, K + pad), dtype=torch.int8, device=DEV, generator=g)
+    Wq, Xq = Wbuf[:, :K], Xbuf[:, :K]
+    if panel:
+        Wq = Wq.contiguous()
     bm = {4: 256, 8: 128}[tile]
     tiles_m, tiles_n = -(-M // bm), -(-N // rows)
     sink = torch.full((tiles_n * tiles_m + 5,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
-    B.probe_copy_stream(tile, Wq, Xq, rows, sink=sink)
+    B.probe_copy_stream(tile, Wq, Xq, rows, sink=sink, panel=panel, barrier=barrier)
     torch.cuda.synchronize()
     s = sink.cpu().numpy().view(np.uint32)
-    w = Wq.cpu().numpy().view(np.uint8)
     x = Xq.cpu().numpy().view(np.uint8)
+    if panel:
+        flat = Wq.cpu().numpy().view(np.uint8).reshape(-1)
+        last = (K // 128 - 1) * N * 128  # byte offset of the last K panel
+
+        def wfirst(r):
+            return flat[last + r * 128:last + r * 128 + 16]
+    else:
+        w = Wq.cpu().numpy().view(np.uint8)
+
+        def wfirst(r):
+            return w[r, K - 128:K - 112]
     for b in range(tiles_n * tiles_m):
         n, m = b // tiles_m, b % tiles_m
-        want = _xor_words(w[n * rows, K - 128:K - 112]) ^ _xor_words(x[m * bm, K - 128:K - 112])
+        want = _xor_words(wfirst(n * rows)) ^ _xor_words(x[m * bm, K - 128:K - 112])
         assert int(s[b]) == want, (b, n, m)
     assert (s[tiles_n * tiles_m:] == 0x5A5A5A5A).all()
 

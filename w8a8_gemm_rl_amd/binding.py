@@ -72,7 +72,7 @@ _SIGS = {
     "qr_last_error": (ctypes.c_char_p, []),
     "qr_probe_read": (_int, [_vp, _sz, _vp, _i64, _vp]),
     "qr_probe_mfma": (_int, [_int, _int, _int, _vp, _vp, ctypes.POINTER(_int), _vp]),
-    "qr_probe_copy_stream": (_int, [_int, _vp, _i64, _vp, _i64, _i64, _int, _vp, _i64, _vp]),
+    "qr_probe_copy_stream": (_int, [_int, _vp, _i64, _i64, _vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp]),
     "qr_version": (ctypes.c_char_p, []),
 }
 
@@ -518,23 +518,33 @@ def probe_read(buf, sink=None):
     return sink
 
 
-def probe_copy_stream(tile, Wq, Xq, rows, sink=None):
+PROBE_PANEL, PROBE_NO_BARRIER = 1, 2
+
+
+def probe_copy_stream(tile, Wq, Xq, rows, sink=None, panel=False, barrier=True):
     """Enqueue the operand copies GEMM tile `tile` (4 or 8) makes over the
-    code matrices Wq [N, K] and Xq [M, K] with `rows` weight rows per tile,
-    without the matrix work; returns the sink tensor (one word per block)."""
+    8-bit code matrices Wq [N, K] and Xq [M, K] (rows contiguous; their row
+    strides are passed on) with `rows` weight rows per tile, without the
+    matrix work; panel reads Wq's bytes as K panels instead (Wq contiguous),
+    barrier=False drops the barrier per K step. Returns the sink tensor (one
+    word per block)."""
     _need_cuda(Wq, Xq, sink)
     if Wq.dim() != 2 or Xq.dim() != 2 or Wq.shape[1] != Xq.shape[1]:
         raise ValueError("Wq [N, K] and Xq [M, K] with the same K expected")
-    if not (Wq.is_contiguous() and Xq.is_contiguous()) or Wq.element_size() != 1 or Xq.element_size() != 1:
-        raise ValueError("contiguous 8-bit code matrices expected")
+    if Wq.element_size() != 1 or Xq.element_size() != 1:
+        raise ValueError("8-bit code matrices expected")
+    if panel and not Wq.is_contiguous():
+        raise ValueError("panel reads need a contiguous Wq")
     (N, K), M = Wq.shape, Xq.shape[0]
+    ldw, ldx = _rows(Wq, "Wq"), _rows(Xq, "Xq")
     bm = {4: 256, 8: 128}.get(tile, 1)
     grid = -(-N // max(rows, 1)) * -(-M // bm)
     if sink is None:
         sink = torch.empty(max(grid, 1), dtype=torch.int32, device=Wq.device)
+    flags = (PROBE_PANEL if panel else 0) | (0 if barrier else PROBE_NO_BARRIER)
     with torch.cuda.device(Wq.device):
-        st = lib().qr_probe_copy_stream(tile, _ptr(Wq), N, _ptr(Xq), M, K, rows, _ptr(sink), sink.numel(),
-                                        _stream(Wq.device))
+        st = lib().qr_probe_copy_stream(tile, _ptr(Wq), N, ldw, _ptr(Xq), M, ldx, K, rows, flags,
+                                        _ptr(sink), sink.numel(), _stream(Wq.device))
     _check("qr_probe_copy_stream", st)
     return sink
 

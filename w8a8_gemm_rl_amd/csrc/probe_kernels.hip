@@ -9,7 +9,9 @@
 //  * copy_stream_probe_kernel replays the operand copies of one LDS-DMA GEMM
 //    tiling (the same blocks, copies, ring, waits and barriers) with no
 //    fragment reads and no MFMAs: the time the copy pipeline alone needs
-//    for that tiling, against which the GEMM's own time can be read.
+//    for that tiling, against which the GEMM's own time can be read. Its
+//    variants (padded row strides, weights stored as K panels, no barrier
+//    per K step) measure what each of those would change in the copies.
 //  * mfma_probe_kernel runs rounds of eight independent dense 8-bit MFMAs
 //    (INT8 32x32x32 or FP8 32x32x64, the shapes the GEMMs use) per wave on
 //    register operands. Wave 0 of each block reads the shader-clock counter
@@ -123,14 +125,19 @@ __global__ __launch_bounds__(512) void mfma_probe_kernel(int iters, uint32_t* __
 // w * NA + NA - 1 and token row blocks w * NB .. w * NB + NB - 1 of every
 // step, the lane owning physical chunk c of row r fetching logical chunk
 // c ^ ((r >> 1) & 7); rows outside the tile or the matrix read as zero. Each
-// wave waits for its own copies of a step, all meet at one barrier per step,
-// and the copies of step it + S - 1 are issued after it. Thread 0 then writes
-// sink[b] = XOR of the first 16 bytes of the block's first weight row and of
-// its first token row in the last K step, as they arrived in LDS.
-template <int BN, int BM, int NW, int S, bool NTW>
+// wave waits for its own copies of a step, all meet at one barrier per step
+// (SYNC; without it every wave runs ahead on its own waits alone), and the
+// copies of step it + S - 1 are issued after it. Row r of the weights starts
+// at byte r * ldw, K step k at k * 128 within it; PANEL instead reads the
+// weights as K panels, K step k of row r at byte (k * N + r) * 128, so one
+// step of a tile is one contiguous block. Token row r starts at r * ldx.
+// Thread 0 then writes sink[b] = XOR of the first 16 bytes of the block's
+// first weight row and of its first token row in the last K step, as they
+// arrived in LDS.
+template <int BN, int BM, int NW, int S, bool NTW, bool PANEL, bool SYNC>
 __global__ __launch_bounds__(64 * NW, 1) void copy_stream_probe_kernel(
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, int64_t N, int64_t M, int64_t K,
-    int rows, int tiles_m, uint32_t* __restrict__ sink) {
+    int64_t ldw, int64_t ldx, int rows, int tiles_m, uint32_t* __restrict__ sink) {
   constexpr int BK = 128, RB = 8, CPR = 8;
   constexpr int IA = BN / RB, IB = BM / RB;
   static_assert(IA % NW == 0 && IB % NW == 0, "row blocks per wave");
@@ -147,10 +154,12 @@ __global__ __launch_bounds__(64 * NW, 1) void copy_stream_probe_kernel(
   const int tm = b % tiles_m, tn = b / tiles_m;
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int nk = (int)(K / BK);
+  const int64_t wbytes = PANEL ? (int64_t)nk * N * BK : N * ldw;
   const __amdgpu_buffer_rsrc_t rsw =
-      __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)(uint32_t)(N * K), kBufWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)(uint32_t)wbytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t rsx =
-      __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)(uint32_t)(M * K), kBufWord3);
+      __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)(uint32_t)(M * ldx), kBufWord3);
   const int lrow = lane / CPR, pch = lane % CPR;
   uint32_t oa[NA], ob[NB];
 #pragma unroll
@@ -158,31 +167,32 @@ __global__ __launch_bounds__(64 * NW, 1) void copy_stream_probe_kernel(
     const int r = (wid * NA + i) * RB + lrow;
     const int c = pch ^ ((r >> 1) & 7);
     const int64_t row = (int64_t)tn * rows + r;
-    oa[i] = ((r < rows && row < N) ? (uint32_t)(row * K + c * 16) : kOOB) - 1024u * (uint32_t)i;
+    oa[i] = ((r < rows && row < N) ? (uint32_t)(row * (PANEL ? (int64_t)BK : ldw) + c * 16) : kOOB) -
+            1024u * (uint32_t)i;
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int r = (wid * NB + i) * RB + lrow;
     const int c = pch ^ ((r >> 1) & 7);
     const int64_t row = (int64_t)tm * BM + r;
-    ob[i] = ((row < M) ? (uint32_t)(row * K + c * 16) : kOOB) - 1024u * (uint32_t)i;
+    ob[i] = ((row < M) ? (uint32_t)(row * ldx + c * 16) : kOOB) - 1024u * (uint32_t)i;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;
   const uint32_t la0 = lds0 + (uint32_t)(wid * NA) * 1024u;
   const uint32_t lb0 = lds0 + (uint32_t)(IA + wid * NB) * 1024u;
   auto issue = [&](int slot, int ks) {
     const int soff = ks * BK;
-    dma_group<NA, NTW>(la0 + (uint32_t)(slot * STAGE), oa, rsw, soff);
+    const int soffw = PANEL ? (int)((int64_t)ks * N * BK) : soff;
+    dma_group<NA, NTW>(la0 + (uint32_t)(slot * STAGE), oa, rsw, soffw);
     dma_group<NB, false>(lb0 + (uint32_t)(slot * STAGE), ob, rsx, soff);
   };
-  const int nk = (int)(K / BK);
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < nk) issue(s, s);
   int is = S - 1;
   for (int it = 0; it < nk; ++it) {
     wait_stages<NI, S - 2>(nk - 1 - it);
-    __syncthreads();
+    if constexpr (SYNC) __syncthreads();
     if (it + S - 1 < nk) issue(is, it + S - 1);
     is = is + 1 == S ? 0 : is + 1;
   }
@@ -194,6 +204,26 @@ __global__ __launch_bounds__(64 * NW, 1) void copy_stream_probe_kernel(
     const uint32_t* xa = reinterpret_cast<const uint32_t*>(smem + last * STAGE + IA * 1024);
     sink[b] = wa[0] ^ wa[1] ^ wa[2] ^ wa[3] ^ xa[0] ^ xa[1] ^ xa[2] ^ xa[3];
   }
+}
+
+template <int BN, int BM, int S, bool NTW>
+hipError_t launch_copy_stream(dim3 grid, int flags, const uint8_t* w, const uint8_t* x, int64_t N,
+                              int64_t M, int64_t K, int64_t ldw, int64_t ldx, int rows, int tiles_m,
+                              uint32_t* sink, hipStream_t st) {
+  const bool panel = (flags & 1) != 0, sync = (flags & 2) == 0;
+  if (panel && sync)
+    hipLaunchKernelGGL((copy_stream_probe_kernel<BN, BM, 8, S, NTW, true, true>), grid, dim3(512), 0,
+                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, sink);
+  else if (panel)
+    hipLaunchKernelGGL((copy_stream_probe_kernel<BN, BM, 8, S, NTW, true, false>), grid, dim3(512), 0,
+                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, sink);
+  else if (sync)
+    hipLaunchKernelGGL((copy_stream_probe_kernel<BN, BM, 8, S, NTW, false, true>), grid, dim3(512), 0,
+                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, sink);
+  else
+    hipLaunchKernelGGL((copy_stream_probe_kernel<BN, BM, 8, S, NTW, false, false>), grid, dim3(512), 0,
+                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, sink);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -209,7 +239,8 @@ bool copy_stream_probe_tile(int tile, int& bn, int& bm) {
 }
 
 hipError_t launch_copy_stream_probe(int tile, const void* W, const void* X, int64_t N, int64_t M,
-                                    int64_t K, int rows, uint32_t* sink, hipStream_t st) {
+                                    int64_t K, int64_t ldw, int64_t ldx, int rows, int flags,
+                                    uint32_t* sink, hipStream_t st) {
   int bn = 0, bm = 0;
   if (!copy_stream_probe_tile(tile, bn, bm)) return hipErrorInvalidValue;
   const int64_t tiles_m = (M + bm - 1) / bm, tiles_n = (N + rows - 1) / rows;
@@ -217,12 +248,10 @@ hipError_t launch_copy_stream_probe(int tile, const void* W, const void* X, int6
   const uint8_t* w = static_cast<const uint8_t*>(W);
   const uint8_t* x = static_cast<const uint8_t*>(X);
   if (tile == 4)
-    hipLaunchKernelGGL((copy_stream_probe_kernel<256, 256, 8, 2, true>), grid, dim3(512), 0, st, w,
-                       x, N, M, K, rows, (int)tiles_m, sink);
-  else
-    hipLaunchKernelGGL((copy_stream_probe_kernel<192, 128, 8, 4, false>), grid, dim3(512), 0, st, w,
-                       x, N, M, K, rows, (int)tiles_m, sink);
-  return hipGetLastError();
+    return launch_copy_stream<256, 256, 2, true>(grid, flags, w, x, N, M, K, ldw, ldx, rows,
+                                                 (int)tiles_m, sink, st);
+  return launch_copy_stream<192, 128, 4, false>(grid, flags, w, x, N, M, K, ldw, ldx, rows,
+                                                (int)tiles_m, sink, st);
 }
 
 hipError_t launch_read_probe(const void* buf, int64_t n16, uint32_t* sink, hipStream_t st) {

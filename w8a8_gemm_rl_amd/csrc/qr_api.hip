@@ -518,8 +518,9 @@ int qr_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t sink_wo
                     fn);
 }
 
-int qr_probe_copy_stream(int tile, const void* Wq, int64_t N, const void* Xq, int64_t M, int64_t K,
-                         int rows, uint32_t* sink, int64_t sink_words, void* stream) {
+int qr_probe_copy_stream(int tile, const void* Wq, int64_t N, int64_t ldw, const void* Xq, int64_t M,
+                         int64_t ldx, int64_t K, int rows, int flags, uint32_t* sink, int64_t sink_words,
+                         void* stream) {
   const char* fn = "qr_probe_copy_stream";
   int bn = 0, bm = 0;
   if (!qr::copy_stream_probe_tile(tile, bn, bm))
@@ -528,15 +529,20 @@ int qr_probe_copy_stream(int tile, const void* Wq, int64_t N, const void* Xq, in
     return fail(QR_ERR_INVALID_ARG, "%s: N, M >= 1 and K a positive multiple of 128 needed", fn);
   if (rows < 8 || rows > bn || rows % 8 != 0)
     return fail(QR_ERR_INVALID_ARG, "%s: rows must be a multiple of 8 in [8, %d]", fn, bn);
+  if (flags < 0 || flags > (QR_PROBE_PANEL | QR_PROBE_NO_BARRIER))
+    return fail(QR_ERR_INVALID_ARG, "%s: unknown flags %d", fn, flags);
+  if (ldw < K || ldx < K || ldw % 16 != 0 || ldx % 16 != 0)
+    return fail(QR_ERR_INVALID_ARG, "%s: ldw and ldx must be >= K and multiples of 16", fn);
   if (!Wq || !Xq || !sink) return fail(QR_ERR_INVALID_ARG, "%s: null pointer", fn);
-  if (N * K >= kMaxCodeBytes || M * K >= kMaxCodeBytes)
+  const int64_t wbytes = (flags & QR_PROBE_PANEL) ? N * K : N * ldw;
+  if (wbytes >= kMaxCodeBytes || M * ldx >= kMaxCodeBytes)
     return fail(QR_ERR_UNSUPPORTED, "%s: a code matrix of 2^31 - 2^16 bytes or more", fn);
   const int64_t grid = ((N + rows - 1) / rows) * ((M + bm - 1) / bm);
   if (grid > INT32_MAX) return fail(QR_ERR_UNSUPPORTED, "%s: grid too large", fn);
   if (sink_words < grid)
     return fail(QR_ERR_INVALID_ARG, "%s: sink of %lld words needed", fn, (long long)grid);
   (void)hipGetLastError();
-  return hip_status(qr::launch_copy_stream_probe(tile, Wq, Xq, N, M, K, rows, sink,
+  return hip_status(qr::launch_copy_stream_probe(tile, Wq, Xq, N, M, K, ldw, ldx, rows, flags, sink,
                                                  static_cast<hipStream_t>(stream)),
                     fn);
 }

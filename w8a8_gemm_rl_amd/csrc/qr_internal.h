@@ -60,7 +60,8 @@ unsigned read_probe_blocks();
 hipError_t launch_read_probe(const void* buf, int64_t n16, uint32_t* sink, hipStream_t st);
 bool copy_stream_probe_tile(int tile, int& bn, int& bm);
 hipError_t launch_copy_stream_probe(int tile, const void* W, const void* X, int64_t N, int64_t M,
-                                    int64_t K, int rows, uint32_t* sink, hipStream_t st);
+                                    int64_t K, int64_t ldw, int64_t ldx, int rows, int flags,
+                                    uint32_t* sink, hipStream_t st);
 hipError_t launch_mfma_probe(int qt, int blocks, int iters, uint32_t* sink, uint64_t* ticks,
                              hipStream_t st);
 
