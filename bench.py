@@ -303,7 +303,7 @@ KERNEL_SOURCES = {
     "acr": ("acr_kernels.hip",),
     "gemm": ("gemm_kernels.hip", "gemm_plan.hip", "qr_gemm.h", "qr_device.h", "qr_copy.h"),
     "refresh": ("quant_kernels.hip", "qr_device.h"),
-    "small": ("small_m_kernels.hip", "qr_device.h", "qr_internal.h"),
+    "small": ("small_m_kernels.hip", "qr_device.h", "qr_small_m.h"),
 }
 
 

@@ -7,6 +7,7 @@
 
 #include "qr_device.h"
 #include "qr_gemm.h"
+#include "qr_small_m.h"
 
 namespace qr {
 
@@ -32,24 +33,6 @@ hipError_t launch_acr_tis(const float* logp, const float* lprox, const float* lb
                           float* loss, float* grad, double* sums, double* part, hipStream_t st);
 hipError_t launch_requant(const float* Wp, int64_t N, int64_t K, int64_t ldw, int qt, void* Wq,
                           float* scale_w, uint32_t* row_flips, hipStream_t st);
-
-// The small-token linear (quantization of the bf16 input, product and
-// epilogue in one launch) for M <= kSmallMaxM token rows, M K <= kSmallMaxMK;
-// it holds the bf16 rows and their codes ([M][K rounded up to 128]) in LDS.
-constexpr int kSmallMaxM = 4;
-constexpr int kSmallMaxRF = 5;
-constexpr int64_t kSmallMaxMK = 20480;  // M K: bf16 rows and codes fit the LDS beside the stage
-// LDS bytes of the bf16 token rows, rounded up to whole 1 KB LDS-DMA copies.
-__host__ __device__ inline size_t small_m_rows_bytes(int64_t M, int64_t K) {
-  return (size_t)(((M * K * 2 + 1023) / 1024) * 1024);
-}
-size_t small_m_lds_bytes(int64_t M, int64_t K, int rf);
-bool small_m_ok(int64_t M, int64_t N, int64_t K, int64_t ldx);    // the kernel can run it
-bool small_m_auto(int64_t M, int64_t N, int64_t K, int64_t ldx);  // and it is the faster path
-int small_m_rf(int64_t N, int force_rf);
-hipError_t launch_small_m_linear(const void* X, int64_t ldx, float act_mult, const void* Wq,
-                                 const float* scale_w, int64_t M, int64_t N, int64_t K, int qt,
-                                 void* Y, int64_t ldy, int rf, hipStream_t st);
 
 // Error reporting of the C ABI (qr_last_error): set the thread-local message
 // and return `code`; hip_error maps a HIP error to QR_ERR_HIP / QR_ERR_NO_DEVICE.

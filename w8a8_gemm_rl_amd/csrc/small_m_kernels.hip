@@ -33,7 +33,7 @@
 #include <type_traits>
 
 #include "qr_device.h"
-#include "qr_internal.h"
+#include "qr_small_m.h"
 
 namespace qr {
 namespace {
