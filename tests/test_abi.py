@@ -261,5 +261,7 @@ def test_probe_validation(B):
     assert call(words=197) == INV
     assert "198" in L.qr_last_error().decode()
     assert call(N=1 << 20, K=1 << 11, ldw=1 << 11, ldx=1 << 11, words=1 << 30) == UNS
-    # the panel variant sizes the weights as N x K, whatever ldw says
+    # the panel variant sizes the weights as N x K and ignores ldw
     assert call(N=(1 << 20) - 64, K=1 << 11, ldw=1 << 12, ldx=1 << 11, words=1 << 30) == UNS
+    assert call(flags=1, ldw=0, sink=NULL) == INV  # (stops at the null sink, past the stride check)
+    assert "null" in L.qr_last_error().decode()

@@ -531,6 +531,7 @@ int qr_probe_copy_stream(int tile, const void* Wq, int64_t N, int64_t ldw, const
     return fail(QR_ERR_INVALID_ARG, "%s: rows must be a multiple of 8 in [8, %d]", fn, bn);
   if (flags < 0 || flags > (QR_PROBE_PANEL | QR_PROBE_NO_BARRIER))
     return fail(QR_ERR_INVALID_ARG, "%s: unknown flags %d", fn, flags);
+  if (flags & QR_PROBE_PANEL) ldw = K;  // panels have no row stride
   if (ldw < K || ldx < K || ldw % 16 != 0 || ldx % 16 != 0)
     return fail(QR_ERR_INVALID_ARG, "%s: ldw and ldx must be >= K and multiples of 16", fn);
   if (!Wq || !Xq || !sink) return fail(QR_ERR_INVALID_ARG, "%s: null pointer", fn);
