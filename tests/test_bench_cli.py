@@ -1,0 +1,86 @@
+"""CPU checks of bench.py's measurement plumbing (no GPU is used).
+
+The JSON line's roofline "traffic" comes from profiles/hbm_traffic.md, keyed
+by kernel and by the hash of the kernel's sources; the rocprofv3 summaries
+come from bench.py --summarize-rocprof. These tests pin that plumbing: the
+multi-GPU refusal, the source hashes, the traffic rows' arithmetic, the
+lookup's refusal of rows taken on other sources, and the summarizer.
+"""
+
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+@pytest.mark.parametrize("kind", sorted(bench.KERNEL_SOURCES))
+def test_source_hashes(kind):
+    h = bench.kernel_source_sha256(kind)
+    assert re.fullmatch(r"[0-9a-f]{64}", h)
+    assert h == bench.kernel_source_sha256(kind)  # stable
+
+
+def _traffic_rows():
+    rows = []
+    with open(bench.TRAFFIC_FILE) as f:
+        for line in f:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) == 6 and re.fullmatch(r"[0-9a-f]{16}", cells[1]):
+                rows.append(cells)
+    return rows
+
+
+def test_traffic_rows_are_fetch_times_two_plus_write():
+    rows = _traffic_rows()
+    assert len(rows) >= 3
+    for key, sha, traffic, fetch, write, alg in rows:
+        if not fetch or not write:
+            continue
+        want = (float(fetch) * 2.0 + float(write)) * 1024.0
+        assert abs(int(traffic) - want) <= 1024 * 0.2, (key, traffic, want)
+        assert int(traffic) >= int(alg) * 0.99, (key, "traffic below the algorithmic bytes")
+
+
+def test_traffic_lookup_checks_the_source_hash(tmp_path, monkeypatch):
+    sha = bench.kernel_source_sha256("gemm")[:16]
+    f = tmp_path / "traffic.md"
+    f.write_text("| key | sha | traffic | f | w | alg |\n|---|---|---|---|---|---|\n"
+                 f"| k:current | {sha} | 123 | 1 | 1 | 100 |\n"
+                 "| k:stale | 0123456789abcdef | 456 | 1 | 1 | 100 |\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.committed_traffic("k:current") == 123
+    assert bench.committed_traffic("k:stale") is None
+    assert bench.committed_traffic("k:missing") is None
+
+
+def test_summarize_rocprof_counters_and_trace(tmp_path, capsys):
+    pmc = tmp_path / "pmc.csv"
+    pmc.write_text("Kernel_Name,Grid_Size,Counter_Name,Counter_Value\n"
+                   "void qr::gemm_dma_kernel<0>(x),1024,FETCH_SIZE,100\n"
+                   "void qr::gemm_dma_kernel<0>(x),1024,FETCH_SIZE,300\n"
+                   "void qr::gemm_dma_kernel<0>(x),2048,FETCH_SIZE,999\n"
+                   "void qr::act_quant_kernel<0>(x),1024,FETCH_SIZE,777\n")
+    trace = tmp_path / "trace.csv"
+    trace.write_text("Kernel_Name,Grid_Size_X,Start_Timestamp,End_Timestamp\n"
+                     "void qr::gemm_dma_kernel<0>(x),1024,1000,11000\n"
+                     "void qr::gemm_dma_kernel<0>(x),1024,20000,50000\n"
+                     "void qr::copy_stream_probe_kernel<1>(x),1024,0,5000\n")
+    bench.summarize_rocprof([str(pmc), str(trace)], 1024, "gemm")
+    out = capsys.readouterr().out
+    assert "FETCH_SIZE per dispatch (grid 1024): mean 200.0 KiB, n=2" in out
+    assert "n=2 mean 20.00 us" in out
