@@ -51,9 +51,9 @@ EPS = 1e-6  # RMSNorm epsilon of the producer workloads
 WORKLOADS = {
     "7b_decode_int8": dict(M=256, qt="int8", chain="7b", sets=4, kind="outliers"),
     "7b_decode_fp8": dict(M=256, qt="fp8", chain="7b", sets=4, kind="outliers"),
-    # the same layer with one launch per linear: qr_w8a8_gemm_quant adds split-K
-    # partial sums and quantizes the next linear's input inside the GEMM launch
-    # behind grid-wide barriers
+    # the same layer with one launch per linear: qr_w8a8_gemm_quant (fuse
+    # override 1) adds split-K partial sums and quantizes the next linear's
+    # input inside the GEMM launch behind grid-wide barriers
     "7b_decode_int8_one_launch": dict(M=256, qt="int8", chain="7b", sets=4, kind="outliers",
                                       one_launch=True),
     "7b_decode_int8_gateup": dict(M=256, qt="int8", chain="7b_gateup", sets=4, kind="outliers"),
@@ -140,6 +140,25 @@ def small_m_linears(chain, shapes, M, one_launch):
             if not L.get("prod") and M <= 4 and M * shapes[L["name"]][1] <= SMALL_M_MK}
 
 
+def sum_quant_linears(B, chain, shapes, M, qt, small, one_launch):
+    """Linears run as qr_w8a8_gemm_quant's separate launches: the GEMM writes
+    split-K partial sums and one kernel adds them and quantizes the next
+    linear's input (its output read next with no producer in between, by a
+    linear that does not quantize its own input; a plan that splits K; N a
+    multiple of 8 up to 16384). Their readers need no quantizer launch."""
+    if one_launch:
+        return set()
+    key, epi = chain_keys(chain)
+    needed = {key[L["name"]] for L in chain if L["name"] not in small}
+    out = set()
+    for name, k in epi.items():
+        N, K = shapes[name]
+        if (name not in small and k in needed and N % 8 == 0 and N <= 16384
+                and B.gemm_plan(M, N, K, qt)[1] > 1):
+            out.add(name)
+    return out
+
+
 def small_m_rf(N):
     """Block height (16-row fragments) the library picks for the one-launch
     path: the fewest, 1-5, that keep the grid within 256 blocks."""
@@ -181,7 +200,7 @@ class Layer:
     qr_w8a8_gemm (with its split-K kernel)."""
 
     def __init__(self, chain, shapes, M, qt, sigma, seed, dev, x0, bufs, ws, s, fused=True,
-                 one_launch=False, wsq=None, small=()):
+                 one_launch=False, wsq=None, small=(), sum_quant=()):
         import torch
 
         from w8a8_gemm_rl_amd import binding as B
@@ -206,6 +225,8 @@ class Layer:
         self.chain, self.M, self.fused = chain, M, fused
         self.one_launch, self.wsq, self.shapes = one_launch, wsq, shapes
         self.small = set(small)  # linears run as one qr_linear_fused launch
+        # linears whose split-K sum also quantizes the next input (separate launches)
+        self.sum_quant = set(sum_quant)
 
     def ops(self):
         """The step as a list of (kind, name, thunk): per-token quantizations
@@ -214,7 +235,7 @@ class Layer:
         B, bufs = self.B, self.bufs
         key, epi = chain_keys(self.chain)
         if not self.one_launch:
-            epi = {}
+            epi = {k: v for k, v in epi.items() if k in self.sum_quant}
         key_buf = {}
         for L in self.chain:
             key_buf.setdefault(key[L["name"]], bufs["q_" + L["name"]])
@@ -269,7 +290,7 @@ class Layer:
             xq, sx = key_buf[k]
             Wq, sw = self.W[L["name"]]
             y = bufs["y_" + L["name"]]
-            if self.one_launch:
+            if self.one_launch or L["name"] in self.sum_quant:
                 nk = epi.get(L["name"])
                 cols = None
                 xn = sn = None
@@ -827,6 +848,9 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of a graph")
     ap.add_argument("--no-small-m", action="store_true",
                     help="run every linear as quantizer + GEMM launches, also at 1-2 tokens")
+    ap.add_argument("--no-sum-quant", action="store_true",
+                    help="keep a quantizer launch after every split-K sum (instead of the sum "
+                         "kernel that also quantizes the next linear's input)")
     ap.add_argument("--summarize-rocprof", nargs="+", metavar="CSV",
                     help="print the figures used from rocprofv3 CSV files (with --grid) and exit")
     ap.add_argument("--grid", type=int, default=0, help="grid size (threads) of the dispatches to summarize")
@@ -894,6 +918,8 @@ def main():
         wl["M"] = args.m
     if args.no_small_m:
         wl["no_small_m"] = True
+    if args.no_sum_quant:
+        wl["no_sum_quant"] = True
     r = run_chain(args.workload, wl, dev, args.steps, args.warmup, args.eager)
     M, qt, s = wl["M"], wl["qt"], 1.5
     chain, shapes, sigma = chain_spec(wl["chain"])
@@ -985,11 +1011,32 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
     one_launch = wl.get("one_launch", False)
 
     small = set() if wl.get("no_small_m") else small_m_linears(chain, shapes, M, one_launch)
+    sum_quant = (set() if wl.get("no_sum_quant") else
+                 sum_quant_linears(B, chain, shapes, M, qt, small, one_launch))
     log(f"bench: {name} M={M} qt={qt}: building {wl['sets']} weight sets ...")
     layers = [Layer(chain, shapes, M, qt, sigma, 1000 * (j + 1), dev, x0, bufs, ws, s,
-                    fused=wl.get("fused", True), one_launch=one_launch, wsq=wsq, small=small)
+                    fused=wl.get("fused", True), one_launch=one_launch, wsq=wsq, small=small,
+                    sum_quant=sum_quant)
               for j in range(wl["sets"])]
     torch.cuda.synchronize()
+    # qr_w8a8_gemm_quant's one-launch path for the one-launch workload (the
+    # mode is read when each call is made, so also while graphs are captured)
+    B.set_fuse_override(1 if one_launch else 0)
+    try:
+        res = _time_chain(name, wl, layers, bufs, ws, chain, shapes, M, qt, s, small, sum_quant,
+                          one_launch, steps, warmup, eager, breakdown)
+    finally:
+        B.set_fuse_override(0)
+    del layers, bufs, ws, wsq
+    torch.cuda.empty_cache()
+    return res
+
+
+def _time_chain(name, wl, layers, bufs, ws, chain, shapes, M, qt, s, small, sum_quant, one_launch,
+                steps, warmup, eager, breakdown):
+    import torch
+
+    from w8a8_gemm_rl_amd import binding as B
 
     # ---- per-step algorithmic work
     gemm_bytes = {L["name"]: (fused_linear_bytes if L["name"] in small else linear_bytes)(
@@ -1005,6 +1052,7 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
             qbytes += quant_bytes(M, shapes[L["name"]][1], L.get("prod"))
     bytes_step = sum(gemm_bytes.values()) + qbytes
     n_epi = len(set(chain_keys(chain)[1].values())) if one_launch else 0
+    n_sq = len(sum_quant)
     dom = max(chain, key=lambda L: (gemm_bytes[L["name"]], -chain.index(L)))["name"]
     Nd, Kd = shapes[dom]
     dom_ops = 2 * M * Nd * Kd
@@ -1136,6 +1184,9 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
                     + (f" in {len(chain) + len(quant_keys) - n_epi} launches ({n_epi} quantizations and "
                        f"the split-K sums in the GEMM epilogues)" if one_launch else
                        " as separate launches (quantizers, GEMMs, split-K sum kernels)"
+                       + ("" if not n_sq else
+                          f"; the split-K sums of {', '.join(L['name'] for L in chain if L['name'] in sum_quant)} "
+                          f"also quantize the next linear's input ({n_sq} quantizer launches fewer)")
                        + ("" if not small else
                           f"; {', '.join(L['name'] for L in chain if L['name'] in small)} each as one "
                           f"launch that quantizes its own input"))
@@ -1155,8 +1206,6 @@ def run_chain(name, wl, dev, steps, warmup, eager, breakdown=True):
         "linears": linears,
         "config": config,
     }
-    del layers, bufs, ws
-    torch.cuda.empty_cache()
     return res
 
 

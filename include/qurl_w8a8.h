@@ -326,11 +326,16 @@ int qr_w8a8_gemm(const void* Xq, const float* scale_x, const void* Wq, const flo
  *                                         q_act_mult)           [M, q_cols], [M]
  *   bit for bit the results of those two calls. q_cols = 0 quantizes
  *   nothing (Xq_next and scale_x_next are not used).
- * Where the plan allows (all blocks of the grid resident on the GPU at once,
- * M <= 4096, N, ldy multiples of 4, Y 16-byte aligned) a split-K sum and the
- * quantization run inside the GEMM launch behind grid-wide barriers: no
- * split-K kernel, no quantizer kernel. Otherwise the call launches the GEMM
- * (and its split-K kernel) and the quantizer.
+ * By default the call launches the GEMM and then, for a plan that splits K
+ * (qr_gemm_plan) with q_cols > 0 and N a multiple of 8 up to 16384, one
+ * kernel that adds the partial sums, applies the epilogue and quantizes the
+ * column range; otherwise the GEMM (and its split-K kernel) and the
+ * quantizer. With qr_set_fuse_override(1), where the plan allows (all
+ * blocks of the grid resident on the GPU at once, M <= 4096, N, ldy
+ * multiples of 4, Y 16-byte aligned) the split-K sum and the quantization
+ * run inside the GEMM launch behind grid-wide barriers instead (one launch;
+ * measured slower than the separate launches on the 7B- and 32B-shaped
+ * linears, so it is not the default).
  *
  *   Xq, scale_x, Wq, scale_w, M, N, K, qt, Y, ldy   as qr_w8a8_gemm.
  *   q_col0, q_cols  column range of Y to quantize: multiples of 16 (the
@@ -447,6 +452,15 @@ int qr_set_plan_override(int tile, int splitk, int rows);
  * tests. Returns QR_OK or QR_ERR_INVALID_ARG.
  */
 int qr_set_small_m_override(int rf);
+
+/*
+ * qr_set_fuse_override -- tuning and test hook for qr_w8a8_gemm_quant:
+ * mode 0 (the default) runs its separate launches, mode 1 its one-launch
+ * grid-barrier path wherever the plan allows. The results are the same.
+ * Thread-local like qr_set_plan_override; meant for benchmarks and tests.
+ * Returns QR_OK or QR_ERR_INVALID_ARG for another mode.
+ */
+int qr_set_fuse_override(int mode);
 
 /*
  * Measurement helpers (not part of the linear): the peaks the chip reaches,

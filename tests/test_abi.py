@@ -168,6 +168,15 @@ def test_small_m_override_validation(B):
     B.set_small_m_override(0)
 
 
+def test_fuse_override_validation(B):
+    for mode in [1, 0]:
+        B.set_fuse_override(mode)
+    for bad in [-1, 2, 99]:
+        with pytest.raises(B.QRError):
+            B.set_fuse_override(bad)
+    B.set_fuse_override(0)
+
+
 def test_build_rejects_register_spills():
     # The build reads the compiler's per-kernel resource report and fails on
     # any kernel that keeps registers in scratch memory.

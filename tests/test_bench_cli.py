@@ -84,3 +84,20 @@ def test_summarize_rocprof_counters_and_trace(tmp_path, capsys):
     out = capsys.readouterr().out
     assert "FETCH_SIZE per dispatch (grid 1024): mean 200.0 KiB, n=2" in out
     assert "n=2 mean 20.00 us" in out
+
+
+@pytest.mark.parametrize("M,expect", [(1, set()), (32, {"qkv", "o"}), (256, set())])
+def test_sum_quant_selection_7b(M, expect):
+    # Linears whose split-K sum also quantizes the next input: the 7B layer's
+    # QKV and O split K at 32 tokens and feed quantized inputs; at one token
+    # their readers quantize their own inputs, at 256 tokens they do not split.
+    from w8a8_gemm_rl_amd import binding as B
+
+    chain, shapes, _ = bench.chain_spec("7b")
+    small = bench.small_m_linears(chain, shapes, M, False)
+    got = bench.sum_quant_linears(B, chain, shapes, M, "int8", small, False)
+    assert got == expect
+    for name in got:
+        N, K = shapes[name]
+        assert B.gemm_plan(M, N, K, "int8")[1] > 1
+    assert bench.sum_quant_linears(B, chain, shapes, M, "int8", small, True) == set()

@@ -1,17 +1,19 @@
-"""One launch per linear: qr_w8a8_gemm_quant against the separate calls and the oracle.
+"""qr_w8a8_gemm_quant against the separate calls and the oracle.
 
 qr_w8a8_gemm_quant computes a linear's bf16 output and the token-wise
 quantization of a column range of it (the next linear's input; paper notes,
-"Loss / training strategy": token-wise activations, INT8 or FP8), with the
-split-K sum and the quantization inside the GEMM launch where the plan allows.
-Its results must equal those of qr_w8a8_gemm followed by
+"Loss / training strategy": token-wise activations, INT8 or FP8). By default
+(fuse override 0) a plan that splits K runs the GEMM and one kernel that adds
+the partial sums and quantizes; with qr_set_fuse_override(1) the split-K sum
+and the quantization run inside the GEMM launch where the plan allows. Either
+way its results must equal those of qr_w8a8_gemm followed by
 qr_quantize_act_per_token bit for bit, INT8 and FP8 (the same accumulators
 and the same arithmetic), and the INT8 chain built from it must equal the
 oracle chain bit for bit.
 
 The workspace header's generation word advances by 2 per fused launch and
 the arrival counter and timeout flag stay zero: the tests read them to know
-that the fused path ran and that no barrier wait timed out.
+whether the fused path ran and that no barrier wait timed out.
 """
 
 import numpy as np
@@ -33,9 +35,16 @@ FUSED_TILES = [0, 1, 2, 3, 5, 6, 7, 8, 9]  # tiles with a fused instantiation
 @pytest.fixture(autouse=True)
 def _reset_plan():
     B.set_plan_override(-1)
+    B.set_fuse_override(0)
     yield
     B.set_plan_override(-1)
+    B.set_fuse_override(0)
     torch.cuda.synchronize()
+
+
+@pytest.fixture
+def one_launch():
+    B.set_fuse_override(1)
 
 
 def _ws(M, N, K, qt):
@@ -48,31 +57,43 @@ def _hdr(ws):
     return int(h[0]), int(h[1]), int(h[2])
 
 
-def _operands(M, N, K, qt, seed):
+def _operands(M, N, K, qt, seed, zero_rows=()):
     X = to_dev_bf16(I.activations(M, K, seed=seed, kind="outliers"))
+    for r in zero_rows:  # all-zero tokens: zero output rows, zero scales and codes
+        X[r] = 0
     Wq, sw = B.quantize_weights_uaq(to_dev_f32(I.weights(N, K, 0.02, seed=seed + 1)), 1.5, qt)
     Xq, sx = B.quantize_act_per_token(X, 1.5, qt)
     return Xq, sx, Wq, sw
 
 
-def _compare(M, N, K, qt, cols, seed, expect_fused, ws=None, reps=2):
-    Xq, sx, Wq, sw = _operands(M, N, K, qt, seed)
-    # separate calls
-    Yr = B.w8a8_gemm(Xq, sx, Wq, sw, qt)
+def _compare(M, N, K, qt, cols, seed, expect_fused, ws=None, reps=2, zero_rows=(), pad=0):
+    Xq, sx, Wq, sw = _operands(M, N, K, qt, seed, zero_rows)
+    # separate calls (into a buffer of the same row stride)
+    Yr = B.w8a8_gemm(Xq, sx, Wq, sw, qt,
+                     Y=torch.empty((M, N + pad), dtype=torch.bfloat16, device=DEV)[:, :N])
     c0, c1 = cols if cols else (0, 0)
     if cols:
         Xr, sr = B.quantize_act_per_token(Yr[:, c0:c1], 1.25, qt)
     ws = _ws(M, N, K, qt) if ws is None else ws
     _, g_before, _ = _hdr(ws)
     for rep in range(reps):  # the header must be ready again after every launch
-        Y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=DEV)
-        Y, Xn, sn = B.w8a8_gemm_quant(Xq, sx, Wq, sw, qt, Y=Y, q_cols=cols, q_act_mult=1.25, ws=ws)
+        # pad > 0: Y is a column slice of a wider buffer (ldy = N + pad), whose
+        # padding must stay untouched
+        Yb = torch.full((M, N + pad), 7.0, dtype=torch.bfloat16, device=DEV)
+        Y, Xn, sn = B.w8a8_gemm_quant(Xq, sx, Wq, sw, qt, Y=Yb[:, :N], q_cols=cols,
+                                      q_act_mult=1.25, ws=ws)
         torch.cuda.synchronize()
         what = (qt, M, N, K, cols, B.gemm_plan(M, N, K, qt), rep)
         assert torch.equal(Y.view(torch.int16), Yr.view(torch.int16)), what
+        if pad:
+            assert bool((Yb[:, N:] == 7.0).all()), what
         if cols:
             assert torch.equal(Xn.view(torch.uint8), Xr.view(torch.uint8)), what
             assert torch.equal(sn, sr), what
+        for r in zero_rows:
+            assert not bool(Y[r].any()), what
+            if cols:
+                assert float(sn[r]) == 0.0 and not bool(Xn[r].view(torch.uint8).any()), what
     arrivals, g_after, timeout = _hdr(ws)
     assert arrivals == 0 and timeout == 0, (arrivals, timeout)
     assert g_after - g_before == (2 * reps if expect_fused else 0), (g_before, g_after, what)
@@ -82,7 +103,7 @@ def _compare(M, N, K, qt, cols, seed, expect_fused, ws=None, reps=2):
 @pytest.mark.parametrize("name,cols", [("qkv", (0, 3584)), ("o", None), ("o", (0, 3584)),
                                        ("gate", None), ("up", (0, 18944)), ("down", None)])
 @pytest.mark.parametrize("M", [1, 32, 256])
-def test_7b_linears_fused_equal_separate_calls(qt, name, cols, M):
+def test_7b_linears_fused_equal_separate_calls(qt, name, cols, M, one_launch):
     N, K = I.LINEARS_7B[name]
     plan = B.gemm_plan(M, N, K, qt)
     fused = plan[1] > 1 or cols is not None
@@ -92,7 +113,7 @@ def test_7b_linears_fused_equal_separate_calls(qt, name, cols, M):
 @pytest.mark.parametrize("qt", QTS)
 @pytest.mark.parametrize("tile", FUSED_TILES)
 @pytest.mark.parametrize("splitk", [1, 3])
-def test_every_fused_tile_ragged(qt, tile, splitk):
+def test_every_fused_tile_ragged(qt, tile, splitk, one_launch):
     # ragged M, N a multiple of 8 but not of the tile, a 16-byte last K
     # step; quantized columns in the middle of N
     M, N, K = 70, 296, 1040
@@ -101,14 +122,14 @@ def test_every_fused_tile_ragged(qt, tile, splitk):
 
 
 @pytest.mark.parametrize("qt", QTS)
-def test_unfusable_shapes_fall_back(qt):
+def test_unfusable_shapes_fall_back(qt, one_launch):
     # more tokens than the fused launch's absmax buffer holds: the separate
     # kernels run, with the same results
     _compare(4160, 256, 256, qt, (0, 256), seed=5, expect_fused=False)
 
 
 @pytest.mark.parametrize("M", [1, 32, 256])
-def test_7b_int8_chain_fused_equals_oracle(M):
+def test_7b_int8_chain_fused_equals_oracle(M, one_launch):
     """The 7B-shaped INT8 layer with one launch per linear (after the layer
     input's quantizer): every output equals the oracle chain bit for bit."""
     qt = "int8"
@@ -142,7 +163,7 @@ def test_7b_int8_chain_fused_equals_oracle(M):
 
 
 @pytest.mark.parametrize("qt", QTS)
-def test_fused_chain_graph_replays(qt):
+def test_fused_chain_graph_replays(qt, one_launch):
     """A chain of fused launches captured in a HIP graph: every replay equals
     the eager result (the header is carried from launch to launch)."""
     M = 32
@@ -187,6 +208,117 @@ def test_fused_chain_graph_replays(qt):
         assert float(junk) == float(junk)
     arrivals, _, timeout = _hdr(ws)
     assert arrivals == 0 and timeout == 0
+
+
+# ---- the default: separate launches (GEMM, then the split-K sum that also
+# quantizes, or the GEMM's own split-K kernel and the quantizer)
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("name,cols", [("qkv", (0, 3584)), ("o", None), ("o", (0, 3584)),
+                                       ("gate", None), ("up", (0, 18944)), ("down", None)])
+@pytest.mark.parametrize("M", [1, 32, 256])
+def test_7b_linears_separate_launches_equal_separate_calls(qt, name, cols, M):
+    N, K = I.LINEARS_7B[name]
+    _compare(M, N, K, qt, cols, seed=M + N + 7, expect_fused=False)
+
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("splitk", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("tile", [2, 6])
+def test_split_sum_quant_every_split(qt, splitk, tile):
+    # ragged M, N a multiple of 8 but not of the tile, a 16-byte last K step,
+    # all-zero token rows; column ranges at the start, in the middle, one
+    # 16-column group, and the widest multiple of 16
+    M, N, K = 70, 296, 2064
+    B.set_plan_override(tile, splitk)
+    assert B.gemm_plan(M, N, K, qt)[1] == splitk
+    ws = _ws(M, N, K, qt)
+    for i, cols in enumerate([(0, 288), (32, 272), (16, 32), (272, 288), None]):
+        _compare(M, N, K, qt, cols, seed=17 * splitk + tile + i, expect_fused=False, ws=ws,
+                 reps=1, zero_rows=(0, 33, 69))
+
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("M,N,K,splitk,cols", [
+    (20, 4608, 512, 2, (0, 3584)),      # 4 groups of 8 per thread (N <= 8192)
+    (20, 9216, 512, 3, (1024, 9216)),   # 8 groups (N <= 16384)
+    (9, 16384, 256, 2, (0, 16384)),     # the widest N it takes
+    (33, 8, 512, 4, (0, 0)),            # one group of 8 columns, nothing quantized
+    (3, 16, 1024, 8, (0, 16)),
+])
+def test_split_sum_quant_widths(qt, M, N, K, splitk, cols):
+    B.set_plan_override(6, splitk)
+    _compare(M, N, K, qt, cols if cols[1] else None, seed=N + splitk, expect_fused=False,
+             zero_rows=(M - 1,), pad=8)
+
+
+@pytest.mark.parametrize("qt", QTS)
+@pytest.mark.parametrize("M,N,K,splitk,cols", [
+    (20, 16392, 256, 2, (0, 16384)),    # wider than the sum-and-quantize kernel takes
+    (20, 300, 512, 3, (16, 288)),       # N not a multiple of 8
+])
+def test_split_sum_quant_falls_back(qt, M, N, K, splitk, cols):
+    # the GEMM's split-K kernel and the quantizer run instead: same results
+    B.set_plan_override(6, splitk)
+    _compare(M, N, K, qt, cols, seed=N, expect_fused=False, pad=8 + (-N) % 8)  # ldy % 8 == 0
+
+
+@pytest.mark.parametrize("qt", QTS)
+def test_split_sum_quant_chain_graph_replays(qt):
+    """A chain of separate-launch calls with split plans captured in a HIP
+    graph: every replay equals the eager result."""
+    M = 32
+    shapes = [(1024, 2048), (2048, 1024), (768, 2048)]
+    B.set_plan_override(6, 4)
+    X = to_dev_bf16(I.activations(M, 2048, seed=91, kind="outliers"))
+    Ws = [B.quantize_weights_uaq(to_dev_f32(I.weights(N, K, 0.02, seed=92 + i)), 1.5, qt)
+          for i, (N, K) in enumerate(shapes)]
+    ws = torch.zeros(max(B.workspace_size("qr_w8a8_gemm_quant", M, N, K, qt) for N, K in shapes),
+                     dtype=torch.uint8, device=DEV)
+    xq0, sx0 = B.quantize_act_per_token(X, 1.5, qt)
+    ys = [torch.empty((M, N), dtype=torch.bfloat16, device=DEV) for N, _ in shapes]
+    qs = [(torch.empty((M, N), dtype=B.code_dtype(qt), device=DEV),
+           torch.empty(M, dtype=torch.float32, device=DEV)) for N, _ in shapes[:2]]
+
+    def chain():
+        B.w8a8_gemm_quant(xq0, sx0, *Ws[0], qt, Y=ys[0], q_cols=(0, 1024), q_act_mult=1.5,
+                          Xq_next=qs[0][0], scale_x_next=qs[0][1], ws=ws)
+        B.w8a8_gemm_quant(*qs[0], *Ws[1], qt, Y=ys[1], q_cols=(0, 2048), q_act_mult=1.5,
+                          Xq_next=qs[1][0], scale_x_next=qs[1][1], ws=ws)
+        B.w8a8_gemm_quant(*qs[1], *Ws[2], qt, Y=ys[2], ws=ws)
+
+    # the separate calls as the reference
+    ref = []
+    xq, sx = xq0, sx0
+    for i, (N, K) in enumerate(shapes):
+        y = B.w8a8_gemm(xq, sx, *Ws[i], qt)
+        ref.append(y)
+        if i < 2:
+            xq, sx = B.quantize_act_per_token(y, 1.5, qt)
+    chain()
+    torch.cuda.synchronize()
+    for t, r in zip(ys, ref):
+        assert torch.equal(t.view(torch.int16), r.view(torch.int16))
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            chain()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in ys:
+            t.zero_()
+        junk = torch.randn(1000, device=DEV).sum()
+        g.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(ys, ref):
+            assert torch.equal(t.view(torch.int16), r.view(torch.int16)), f"replay {rep}"
+        chain()
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+    _, gen, _ = _hdr(ws)
+    assert gen == 0  # no fused launch ran
 
 
 def test_rejects_bad_column_ranges():

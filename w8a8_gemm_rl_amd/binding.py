@@ -31,7 +31,7 @@ EXPORTS = [
     "qr_norm_quant", "qr_silu_mul_quant", "qr_acr_tis_loss", "qr_mx_quantize", "qr_mx_gemm",
     "qr_w8a8_gemm", "qr_w8a8_gemm_quant", "qr_linear_fused", "qr_linear_fused_noalloc",
     "qr_workspace_size", "qr_gemm_plan", "qr_tile_name", "qr_num_tiles", "qr_set_plan_override",
-    "qr_set_small_m_override", "qr_last_error", "qr_version", "qr_probe_read", "qr_probe_mfma",
+    "qr_set_small_m_override", "qr_set_fuse_override", "qr_last_error", "qr_version", "qr_probe_read", "qr_probe_mfma",
     "qr_probe_copy_stream",
 ]
 
@@ -69,6 +69,7 @@ _SIGS = {
     "qr_num_tiles": (_int, []),
     "qr_set_plan_override": (_int, [_int, _int, _int]),
     "qr_set_small_m_override": (_int, [_int]),
+    "qr_set_fuse_override": (_int, [_int]),
     "qr_last_error": (ctypes.c_char_p, []),
     "qr_probe_read": (_int, [_vp, _sz, _vp, _i64, _vp]),
     "qr_probe_mfma": (_int, [_int, _int, _int, _vp, _vp, ctypes.POINTER(_int), _vp]),
@@ -186,6 +187,12 @@ def set_small_m_override(rf=0):
     """One-launch decode path of linear_fused at 1-4 tokens: 0 automatic,
     -1 off, 1..5 blocks of 16 * rf output channels (calling thread only)."""
     _check("qr_set_small_m_override", lib().qr_set_small_m_override(rf))
+
+
+def set_fuse_override(mode=0):
+    """w8a8_gemm_quant: 0 separate launches (default), 1 the one-launch
+    grid-barrier path where the plan allows (calling thread only)."""
+    _check("qr_set_fuse_override", lib().qr_set_fuse_override(mode))
 
 
 def gemm_plan(M, N, K, qt):

@@ -964,6 +964,82 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
   }
 }
 
+// Split-K sum that also quantizes the next linear's input: one block per
+// token row m. Each thread owns groups of 8 consecutive outputs (16 bytes of
+// bf16), n = 8 (t + 256 i): it adds the S partial sums of the group in split
+// order (as splitk_reduce_kernel does), applies the bf16 epilogue, stores the
+// group to Y and keeps it in registers; then the row's absmax over the
+// quantized columns [q0, q0 + qn) and their codes follow the per-token
+// quantizer's arithmetic on those same bf16 values (absmax8_bf16,
+// t = absmax / Q, codes8_bf16, scale t * act_mult), so Y, the codes and the
+// scale equal the reduction kernel followed by the quantizer bit for bit.
+// Requires N % 8 == 0, ldy % 8 == 0, q0 and qn multiples of 8, and
+// N <= 2048 G.
+template <int QT, int SC, int G>
+__global__ __launch_bounds__(256) void splitk_reduce_quant_kernel(
+    const uint32_t* __restrict__ part, int64_t M, int64_t N, const float* __restrict__ sx,
+    const float* __restrict__ sw, uint16_t* __restrict__ Y, int64_t ldy, int64_t q0, int64_t qn,
+    float act_mult, uint8_t* __restrict__ Xq, float* __restrict__ scale_x) {
+  static_assert(SC >= 2 && SC <= 8, "splits");
+  __shared__ float red[4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t m = blockIdx.x;
+  const int64_t ng = N >> 3;
+  const float sxm = sx[m];
+  uint4 v[G];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int64_t g = t + 256 * (int64_t)i;
+    v[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (g >= ng) continue;
+    const int64_t n0 = 8 * g;
+    uint32_t w[SC][8];
+#pragma unroll
+    for (int z = 0; z < SC; ++z) {
+      const uint4* src = reinterpret_cast<const uint4*>(part + (int64_t)z * M * N + m * N + n0);
+      const uint4 a = src[0], b = src[1];
+      w[z][0] = a.x; w[z][1] = a.y; w[z][2] = a.z; w[z][3] = a.w;
+      w[z][4] = b.x; w[z][5] = b.y; w[z][6] = b.z; w[z][7] = b.w;
+    }
+    uint32_t bb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float acc;
+      if constexpr (QT == kQInt8) {
+        int32_t si = 0;
+#pragma unroll
+        for (int z = 0; z < SC; ++z) si += (int32_t)w[z][e];
+        acc = (float)si;
+      } else {
+        float sf = 0.0f;
+#pragma unroll
+        for (int z = 0; z < SC; ++z) sf += __uint_as_float(w[z][e]);
+        acc = sf;
+      }
+      bb[e] = epi_bf16(acc, sxm, sw[n0 + e]);
+    }
+    v[i] = make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16),
+                      bb[6] | (bb[7] << 16));
+    *reinterpret_cast<uint4*>(Y + m * ldy + n0) = v[i];
+    if (n0 >= q0 && n0 < q0 + qn) amax = fmaxf(amax, absmax8_bf16(v[i]));
+  }
+  if (qn == 0) return;
+  amax = wave_max(amax);
+  if (lane == 0) red[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float tq = amax / qmax<QT>();
+  if (t == 0) scale_x[m] = tq * act_mult;
+  uint2* qrow = reinterpret_cast<uint2*>(Xq + m * qn);
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int64_t n0 = 8 * (t + 256 * (int64_t)i);
+    if (n0 >= N || n0 < q0 || n0 >= q0 + qn) continue;
+    qrow[(n0 - q0) >> 3] = tq == 0.0f ? make_uint2(0u, 0u) : codes8_bf16<QT>(v[i], tq);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tile table. Order matters: the planner and the tuning hook refer to tiles
 // by index. (S, T, BN, BM, WN, WM, BK, FU): S is the LDS ring depth, T the
@@ -1033,7 +1109,7 @@ hipError_t launch_fused_one(const KParams& kp, unsigned grid, hipStream_t st) {
 int num_tiles() { return kNumTiles; }
 const TileDesc& tile_desc(int tile) { return kTiles[tile]; }
 
-hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStream_t st) {
+hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStream_t st, bool sum_splits) {
   KParams kp;
   kp.Xq = a.Xq; kp.sx = a.sx; kp.Wq = a.Wq; kp.sw = a.sw;
   kp.M = a.M; kp.N = a.N; kp.K = a.K;
@@ -1056,7 +1132,7 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   ++idx;
   QR_TILES(QR_CASE)
 #undef QR_CASE
-  if (e != hipSuccess || plan.splitk <= 1) return e;
+  if (e != hipSuccess || plan.splitk <= 1 || !sum_splits) return e;
   const int64_t work = a.M * ((a.N + 3) / 4);
   const unsigned rgrid = (unsigned)((work + 255) / 256);
   const int vec = (a.ldy % 4) == 0;
@@ -1080,6 +1156,43 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   };
   if (qt == kQInt8) by_splits(std::integral_constant<int, kQInt8>{});
   else by_splits(std::integral_constant<int, kQFp8>{});
+  return hipGetLastError();
+}
+
+bool splitk_reduce_quant_ok(int64_t N, int splitk) {
+  return splitk >= 2 && splitk <= 8 && N % 8 == 0 && N <= 8 * 2048;
+}
+
+hipError_t launch_splitk_reduce_quant(int splitk, int qt, const void* part, int64_t M, int64_t N,
+                                      const float* sx, const float* sw, void* Y, int64_t ldy,
+                                      int64_t q0, int64_t qn, float act_mult, void* Xq,
+                                      float* scale_x, hipStream_t st) {
+  if (!splitk_reduce_quant_ok(N, splitk) || M <= 0) return hipErrorInvalidValue;
+  const int G = N <= 2 * 2048 ? 2 : N <= 4 * 2048 ? 4 : 8;
+  auto go = [&](auto qt_c, auto sc_c, auto g_c) {
+    constexpr int Q = decltype(qt_c)::value, SC = decltype(sc_c)::value, GG = decltype(g_c)::value;
+    hipLaunchKernelGGL((splitk_reduce_quant_kernel<Q, SC, GG>), dim3((unsigned)M), dim3(256), 0, st,
+                       static_cast<const uint32_t*>(part), M, N, sx, sw, static_cast<uint16_t*>(Y),
+                       ldy, q0, qn, act_mult, static_cast<uint8_t*>(Xq), scale_x);
+  };
+  auto by_g = [&](auto qt_c, auto sc_c) {
+    if (G == 2) go(qt_c, sc_c, std::integral_constant<int, 2>{});
+    else if (G == 4) go(qt_c, sc_c, std::integral_constant<int, 4>{});
+    else go(qt_c, sc_c, std::integral_constant<int, 8>{});
+  };
+  auto by_s = [&](auto qt_c) {
+    switch (splitk) {
+      case 2: by_g(qt_c, std::integral_constant<int, 2>{}); break;
+      case 3: by_g(qt_c, std::integral_constant<int, 3>{}); break;
+      case 4: by_g(qt_c, std::integral_constant<int, 4>{}); break;
+      case 5: by_g(qt_c, std::integral_constant<int, 5>{}); break;
+      case 6: by_g(qt_c, std::integral_constant<int, 6>{}); break;
+      case 7: by_g(qt_c, std::integral_constant<int, 7>{}); break;
+      default: by_g(qt_c, std::integral_constant<int, 8>{}); break;
+    }
+  };
+  if (qt == kQInt8) by_s(std::integral_constant<int, kQInt8>{});
+  else by_s(std::integral_constant<int, kQFp8>{});
   return hipGetLastError();
 }
 

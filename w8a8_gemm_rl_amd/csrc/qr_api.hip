@@ -22,6 +22,7 @@ thread_local int g_force_tile = -1;
 thread_local int g_force_splitk = 0;
 thread_local int g_force_rows = 0;
 thread_local int g_small_m = 0;  // small-token path: 0 automatic, -1 off, 1..5 rows / 16
+thread_local int g_fuse = 0;     // qr_w8a8_gemm_quant: 0 separate launches, 1 one launch
 
 constexpr int64_t kMaxKInt8 = 133144;  // K * 127^2 < 2^31
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
@@ -115,6 +116,13 @@ int qr_set_plan_override(int tile, int splitk, int rows) {
   g_force_tile = tile < 0 ? -1 : tile;
   g_force_splitk = tile < 0 ? 0 : splitk;
   g_force_rows = tile < 0 ? 0 : rows;
+  return ok();
+}
+
+int qr_set_fuse_override(int mode) {
+  if (mode != 0 && mode != 1)
+    return fail(QR_ERR_INVALID_ARG, "qr_set_fuse_override: mode %d must be 0 or 1", mode);
+  g_fuse = mode;
   return ok();
 }
 
@@ -442,7 +450,8 @@ int qr_w8a8_gemm_quant(const void* Xq, const float* scale_x, const void* Wq, con
   a.part = plan.splitk > 1 ? ws + qr::kFuseHeaderBytes : nullptr;
   (void)hipGetLastError();
   const bool want = plan.splitk > 1 || q_cols > 0;
-  if (want && N % 4 == 0 && ldy % 4 == 0 && aligned(Y, 16) && qr::fused_ok(plan, qt, M, N)) {
+  if (g_fuse == 1 && want && N % 4 == 0 && ldy % 4 == 0 && aligned(Y, 16) &&
+      qr::fused_ok(plan, qt, M, N)) {
     qr::FuseArgs fa;
     fa.header = ws;
     fa.part = a.part;
@@ -453,8 +462,19 @@ int qr_w8a8_gemm_quant(const void* Xq, const float* scale_x, const void* Wq, con
     fa.am2 = q_act_mult;
     return hip_status(qr::launch_gemm_fused(plan, qt, a, fa, hs), fn);
   }
-  // Not fusable here: the GEMM (with its split-K kernel), then the
-  // per-token quantizer on the column range; the same results.
+  // Separate launches. A split plan whose output is quantized: the GEMM
+  // writes its partial sums and one kernel adds them, applies the epilogue
+  // and quantizes the column range. Otherwise the GEMM (with its split-K
+  // kernel), then the per-token quantizer. The same results either way.
+  if (plan.splitk > 1 && q_cols > 0 && qr::splitk_reduce_quant_ok(N, plan.splitk) &&
+      aligned(Y, 16)) {
+    st = hip_status(qr::launch_gemm(plan, qt, a, hs, false), fn);
+    if (st != QR_OK) return st;
+    return hip_status(qr::launch_splitk_reduce_quant(plan.splitk, qt, a.part, M, N, scale_x,
+                                                     scale_w, Y, ldy, q_col0, q_cols, q_act_mult,
+                                                     Xq_next, scale_x_next, hs),
+                      fn);
+  }
   st = hip_status(qr::launch_gemm(plan, qt, a, hs), fn);
   if (st != QR_OK || q_cols == 0) return st;
   return hip_status(qr::launch_act_quant(static_cast<const uint16_t*>(Y) + q_col0, M, q_cols, ldy,

@@ -48,7 +48,21 @@ struct GemmArgs {
   void* part;  // split-K partial sums (workspace)
 };
 
-hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStream_t st);
+// With sum_splits = false a split plan only writes its partial sums to a.part.
+hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStream_t st,
+                       bool sum_splits = true);
+
+// The split-K sum of a.part ([splitk][M][N]) with the bf16 epilogue into Y,
+// and the per-token quantization of Y's columns [q0, q0 + qn) into Xq
+// ([M][qn]) and scale_x, in one launch (one block per token row); the same
+// bits as the split-K sum kernel followed by the per-token quantizer. For
+// 2-8 splits, N a multiple of 8 up to 16384 (splitk_reduce_quant_ok), ldy,
+// q0 and qn multiples of 8.
+bool splitk_reduce_quant_ok(int64_t N, int splitk);
+hipError_t launch_splitk_reduce_quant(int splitk, int qt, const void* part, int64_t M, int64_t N,
+                                      const float* sx, const float* sw, void* Y, int64_t ldy,
+                                      int64_t q0, int64_t qn, float act_mult, void* Xq,
+                                      float* scale_x, hipStream_t st);
 
 // Fused chain epilogue: the split-K sum and the per-token quantization of
 // Y[:, qc0 : qc0 + qcn] for the next linear inside the GEMM launch.
