@@ -866,6 +866,9 @@ def main():
                     help="only time the copy-stream probe's variants (row strides padded by a line, "
                          "weights as K panels, no barrier per K step) beside the GEMM on the 7B and "
                          "32B gate shapes, print one JSON line and exit")
+    ap.add_argument("--gemm-bound-sweeps", action="store_true",
+                    help="only time the 7B gate GEMM at 256 tokens and its copy stream over fewer "
+                         "blocks and fewer owned rows per tile, print one JSON line and exit")
     args = ap.parse_args()
 
     if args.summarize_rocprof:
@@ -902,6 +905,9 @@ def main():
     B.lib()
     if args.copy_stream_variants:
         print(json.dumps(copy_stream_variants(dev)))
+        return
+    if args.gemm_bound_sweeps:
+        print(json.dumps(gemm_bound_sweeps(dev)))
         return
     if args.workload in REFRESH:
         run_refresh(args, dev)
@@ -1315,6 +1321,96 @@ def copy_stream_variants(dev, rounds=7):
         del graphs, W, Wp, X, Xp, Y, ws
         torch.cuda.empty_cache()
     return {"copy_stream_variants": out, "gemm_source_sha16": kernel_source_sha256()[:16]}
+
+
+def gemm_bound_sweeps(dev, rounds=7):
+    """What bounds the 7B gate GEMM at 256 tokens (INT8, 192 x 128 tiles,
+    K = 3584): the GEMM and its copy stream alone (qr_probe_copy_stream)
+    timed (1) at a fixed 192 weight rows per block while the number of
+    blocks, 2 per weight tile, shrinks from the gate's 198 to 24 (N cut to
+    fewer rows), and (2) on the gate's 18944 rows with 192 down to 152 rows
+    owned per tile (198 to 250 blocks; the copies of the rows a tile does not
+    own still issue and read zeros). Every case is a graph of launches
+    walking 720 MB of weight codes (past the 256 MB Infinity Cache), replayed
+    round-robin with the others; median per-launch us."""
+    import statistics
+
+    import torch
+
+    from w8a8_gemm_rl_amd import binding as B
+
+    M, K, NFULL, TILE, BN = 256, 3584, 18944, 8, 192
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    total = (720 << 20) // K
+    Wall = torch.randint(-127, 128, (total, K), dtype=torch.int8, device=dev, generator=g)
+    X = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev, generator=g)
+    sx = torch.rand(M, device=dev) * 1e-3
+    sw = torch.rand(NFULL, device=dev) * 1e-3
+    Y = torch.empty((M, NFULL), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(256, dtype=torch.uint8, device=dev)
+    sink = torch.empty(2 * -(-NFULL // 152), dtype=torch.int32, device=dev)
+    cases = {}  # key -> (N, rows, gemm?)
+    for tiles in (99, 74, 50, 25, 12):
+        N = min(tiles * BN, NFULL)
+        cases[f"blocks{2 * tiles}_gemm"] = (N, BN, True)
+        cases[f"blocks{2 * tiles}_copies"] = (N, BN, False)
+    for rows in (176, 160, 152):
+        cases[f"rows{rows}_gemm"] = (NFULL, rows, True)
+        cases[f"rows{rows}_copies"] = (NFULL, rows, False)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    graphs = {}
+    try:
+        with torch.cuda.stream(st):
+            for key, (N, rows, gemm) in cases.items():
+                sets = total // N
+                launches = max(DOM_BATCH, sets)
+
+                def fn(j, N=N, rows=rows, gemm=gemm, sets=sets):
+                    Wj = Wall[(j % sets) * N:(j % sets + 1) * N]
+                    if gemm:
+                        B.w8a8_gemm(X, sx, Wj, sw[:N], "int8", Y=Y[:, :N], ws=ws)
+                    else:
+                        B.probe_copy_stream(TILE, Wj, X, rows, sink=sink)
+
+                B.set_plan_override(TILE, 1, rows)
+                assert B.gemm_plan(M, N, K, "int8") == (TILE, 1, rows)
+                fn(0)
+                gph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gph, stream=st):
+                    for j in range(launches):
+                        fn(j)
+                graphs[key] = (gph, launches)
+    finally:
+        B.set_plan_override(-1)
+    torch.cuda.synchronize()
+    ts = {key: [] for key in graphs}
+    with torch.cuda.stream(st):
+        for gph, _ in graphs.values():
+            gph.replay()
+        for _ in range(rounds):
+            for key, (gph, launches) in graphs.items():
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(st)
+                gph.replay()
+                b.record(st)
+                b.synchronize()
+                ts[key].append(a.elapsed_time(b) * 1000.0 / launches)
+    us = {key: round(statistics.median(v), 2) for key, v in ts.items()}
+    blocks = [{"blocks": 2 * t, "rows": BN, "gemm_us": us[f"blocks{2 * t}_gemm"],
+               "copies_us": us[f"blocks{2 * t}_copies"],
+               "copy_bytes_per_block": (BN + 128) * K} for t in (99, 74, 50, 25, 12)]
+    rows = [{"rows": BN, "blocks": 198, "gemm_us": us["blocks198_gemm"],
+             "copies_us": us["blocks198_copies"], "copy_bytes_per_block": (BN + 128) * K}]
+    rows += [{"rows": r, "blocks": 2 * -(-NFULL // r), "gemm_us": us[f"rows{r}_gemm"],
+              "copies_us": us[f"rows{r}_copies"], "copy_bytes_per_block": (r + 128) * K}
+             for r in (176, 160, 152)]
+    del graphs, Wall
+    torch.cuda.empty_cache()
+    return {"gemm_bound_sweeps": {"shape": "7b_gate_m256 (M=256, N=18944, K=3584, INT8)",
+                                  "tile": B.tile_name(TILE), "by_blocks": blocks, "by_rows": rows},
+            "gemm_source_sha16": kernel_source_sha256()[:16]}
 
 
 def roofline_object(bound, alg_bytes, alg_ops, us, qt):
