@@ -1255,7 +1255,9 @@ def copy_stream_variants(dev, rounds=7):
     256 MB Infinity Cache, replayed round-robin with the GEMM itself on the
     same codes: row-major codes as the GEMM reads them, row strides padded
     by one 128-byte line (weights and tokens), the weights read as K panels,
-    and no barrier per K step (alone and with panels). Median per-launch us."""
+    no barrier per K step (alone and with panels), and every K step
+    re-reading the first step's bytes (the operands resident in L2: the copy
+    pipeline's rate when no miss reaches HBM). Median per-launch us."""
     import statistics
 
     import torch
@@ -1290,6 +1292,8 @@ def copy_stream_variants(dev, rounds=7):
             "copies_no_barrier": lambda j: B.probe_copy_stream(tile, W[j], X, rows, sink=sink, barrier=False),
             "copies_k_panels_no_barrier": lambda j: B.probe_copy_stream(tile, W[j], X, rows, sink=sink,
                                                                         panel=True, barrier=False),
+            "copies_l2_resident": lambda j: B.probe_copy_stream(tile, W[j], X, rows, sink=sink,
+                                                                resident=True),
         }
         st = torch.cuda.Stream()
         st.wait_stream(torch.cuda.current_stream())

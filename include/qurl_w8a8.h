@@ -495,17 +495,21 @@ int qr_set_fuse_override(int mode);
  *   QR_PROBE_PANEL reads Wq as K panels, the 128 bytes of K step k of row r
  *   at byte (k * N + r) * 128 (ldw ignored), so that each step of a tile is
  *   one contiguous block; QR_PROBE_NO_BARRIER drops the barrier per K step
- *   (each wave waits only for its own copies). Block b (tile n = b / tiles_m,
- *   token tile m = b % tiles_m, tiles_m = ceil(M / tile width)) writes to
- *   sink[b] the XOR of the four 32-bit words of the first 16 bytes of K step
- *   K / 128 - 1 of weight row n * rows and of token row m * width, as they
- *   arrived in LDS, so the copies can be checked. sink: device,
+ *   (each wave waits only for its own copies); QR_PROBE_RESIDENT copies the
+ *   bytes of K step 0 at every step (the same copies, waits and barriers,
+ *   the operands resident in L2 after the first step), the copy pipeline's
+ *   rate when no miss reaches HBM. Flags combine. Block b (tile
+ *   n = b / tiles_m, token tile m = b % tiles_m, tiles_m = ceil(M / tile
+ *   width)) writes to sink[b] the XOR of the four 32-bit words of the first
+ *   16 bytes of the last K step copied (K / 128 - 1; 0 with
+ *   QR_PROBE_RESIDENT) of weight row n * rows and of token row m * width, as
+ *   they arrived in LDS, so the copies can be checked. sink: device,
  *   >= ceil(N / rows) * tiles_m words. QR_ERR_INVALID_ARG for another tile,
  *   unknown flags, bad sizes or strides or a short sink;
  *   QR_ERR_UNSUPPORTED for a code buffer of 2^31 - 2^16 bytes or more.
  */
 int qr_probe_read(const void* buf, size_t bytes, uint32_t* sink, int64_t sink_words, void* stream);
-enum { QR_PROBE_PANEL = 1, QR_PROBE_NO_BARRIER = 2 };
+enum { QR_PROBE_PANEL = 1, QR_PROBE_NO_BARRIER = 2, QR_PROBE_RESIDENT = 4 };
 int qr_probe_copy_stream(int tile, const void* Wq, int64_t N, int64_t ldw, const void* Xq, int64_t M,
                          int64_t ldx, int64_t K, int rows, int flags, uint32_t* sink, int64_t sink_words,
                          void* stream);

@@ -263,7 +263,7 @@ def test_probe_validation(B):
     for rows in (0, 12, 200):
         assert call(rows=rows) == INV
     assert call(tile=4, N=27648, M=512, K=5120, ldw=5120, ldx=5120, rows=264) == INV
-    assert call(flags=4) == INV and call(flags=-1) == INV
+    assert call(flags=8) == INV and call(flags=-1) == INV
     assert call(ldw=3520) == INV and call(ldx=3590) == INV
     assert call(W=NULL) == INV and call(sink=NULL) == INV
     # 99 weight tiles x 2 token tiles = 198 blocks

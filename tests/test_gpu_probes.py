@@ -45,7 +45,8 @@ def test_read_probe_reads_every_word():
     (8, 3600, 200, 1024, 192, 0, False, False),   # no barrier per K step
     (4, 1000, 300, 640, 248, 128, True, False),
 ])
-def test_copy_stream_probe_copies_the_tiles(tile, N, M, K, rows, pad, panel, barrier):
+@pytest.mark.parametrize("resident", [False, True])  # every K step re-reads step 0's bytes
+def test_copy_stream_probe_copies_the_tiles(tile, N, M, K, rows, pad, panel, barrier, resident):
     g = torch.Generator(device=DEV)
     g.manual_seed(N + M + K + pad)
     Wbuf = torch.randint(-128, 128, (N, K + pad), dtype=torch.int8, device=DEV, generator=g)
@@ -56,13 +57,15 @@ def test_copy_stream_probe_copies_the_tiles(tile, N, M, K, rows, pad, panel, bar
     bm = {4: 256, 8: 128}[tile]
     tiles_m, tiles_n = -(-M // bm), -(-N // rows)
     sink = torch.full((tiles_n * tiles_m + 5,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
-    B.probe_copy_stream(tile, Wq, Xq, rows, sink=sink, panel=panel, barrier=barrier)
+    B.probe_copy_stream(tile, Wq, Xq, rows, sink=sink, panel=panel, barrier=barrier,
+                        resident=resident)
     torch.cuda.synchronize()
     s = sink.cpu().numpy().view(np.uint32)
     x = Xq.cpu().numpy().view(np.uint8)
+    k0 = 0 if resident else K - 128  # byte offset of the last K step copied
     if panel:
         flat = Wq.cpu().numpy().view(np.uint8).reshape(-1)
-        last = (K // 128 - 1) * N * 128  # byte offset of the last K panel
+        last = (k0 // 128) * N * 128  # byte offset of that K panel
 
         def wfirst(r):
             return flat[last + r * 128:last + r * 128 + 16]
@@ -70,10 +73,10 @@ def test_copy_stream_probe_copies_the_tiles(tile, N, M, K, rows, pad, panel, bar
         w = Wq.cpu().numpy().view(np.uint8)
 
         def wfirst(r):
-            return w[r, K - 128:K - 112]
+            return w[r, k0:k0 + 16]
     for b in range(tiles_n * tiles_m):
         n, m = b // tiles_m, b % tiles_m
-        want = _xor_words(wfirst(n * rows)) ^ _xor_words(x[m * bm, K - 128:K - 112])
+        want = _xor_words(wfirst(n * rows)) ^ _xor_words(x[m * bm, k0:k0 + 16])
         assert int(s[b]) == want, (b, n, m)
     assert (s[tiles_n * tiles_m:] == 0x5A5A5A5A).all()
 

@@ -525,16 +525,17 @@ def probe_read(buf, sink=None):
     return sink
 
 
-PROBE_PANEL, PROBE_NO_BARRIER = 1, 2
+PROBE_PANEL, PROBE_NO_BARRIER, PROBE_RESIDENT = 1, 2, 4
 
 
-def probe_copy_stream(tile, Wq, Xq, rows, sink=None, panel=False, barrier=True):
+def probe_copy_stream(tile, Wq, Xq, rows, sink=None, panel=False, barrier=True, resident=False):
     """Enqueue the operand copies GEMM tile `tile` (4 or 8) makes over the
     8-bit code matrices Wq [N, K] and Xq [M, K] (rows contiguous; their row
     strides are passed on) with `rows` weight rows per tile, without the
     matrix work; panel reads Wq's bytes as K panels instead (Wq contiguous),
-    barrier=False drops the barrier per K step. Returns the sink tensor (one
-    word per block)."""
+    barrier=False drops the barrier per K step, resident=True copies K step
+    0's bytes at every step (operands resident in L2). Returns the sink
+    tensor (one word per block)."""
     _need_cuda(Wq, Xq, sink)
     if Wq.dim() != 2 or Xq.dim() != 2 or Wq.shape[1] != Xq.shape[1]:
         raise ValueError("Wq [N, K] and Xq [M, K] with the same K expected")
@@ -548,7 +549,8 @@ def probe_copy_stream(tile, Wq, Xq, rows, sink=None, panel=False, barrier=True):
     grid = -(-N // max(rows, 1)) * -(-M // bm)
     if sink is None:
         sink = torch.empty(max(grid, 1), dtype=torch.int32, device=Wq.device)
-    flags = (PROBE_PANEL if panel else 0) | (0 if barrier else PROBE_NO_BARRIER)
+    flags = ((PROBE_PANEL if panel else 0) | (0 if barrier else PROBE_NO_BARRIER)
+             | (PROBE_RESIDENT if resident else 0))
     with torch.cuda.device(Wq.device):
         st = lib().qr_probe_copy_stream(tile, _ptr(Wq), N, ldw, _ptr(Xq), M, ldx, K, rows, flags,
                                         _ptr(sink), sink.numel(), _stream(Wq.device))

@@ -128,16 +128,17 @@ __global__ __launch_bounds__(512) void mfma_probe_kernel(int iters, uint32_t* __
 // wave waits for its own copies of a step, all meet at one barrier per step
 // (SYNC; without it every wave runs ahead on its own waits alone), and the
 // copies of step it + S - 1 are issued after it. Row r of the weights starts
-// at byte r * ldw, K step k at k * 128 within it; PANEL instead reads the
-// weights as K panels, K step k of row r at byte (k * N + r) * 128, so one
-// step of a tile is one contiguous block. Token row r starts at r * ldx.
-// Thread 0 then writes sink[b] = XOR of the first 16 bytes of the block's
-// first weight row and of its first token row in the last K step, as they
-// arrived in LDS.
+// at byte r * ldw, K step k at k * kb within it (kb = 128; kb = 0 re-reads
+// the first step's bytes at every step, so after the first step the operands
+// come from L2); PANEL instead reads the weights as K panels, K step k of
+// row r at byte (k * N + r) * 128 (k * kb / 128 panels in), so one step of a
+// tile is one contiguous block. Token row r starts at r * ldx. Thread 0 then
+// writes sink[b] = XOR of the first 16 bytes of the block's first weight row
+// and of its first token row in the last K step, as they arrived in LDS.
 template <int BN, int BM, int NW, int S, bool NTW, bool PANEL, bool SYNC>
 __global__ __launch_bounds__(64 * NW, 1) void copy_stream_probe_kernel(
     const uint8_t* __restrict__ W, const uint8_t* __restrict__ X, int64_t N, int64_t M, int64_t K,
-    int64_t ldw, int64_t ldx, int rows, int tiles_m, uint32_t* __restrict__ sink) {
+    int64_t ldw, int64_t ldx, int rows, int tiles_m, int kb, uint32_t* __restrict__ sink) {
   constexpr int BK = 128, RB = 8, CPR = 8;
   constexpr int IA = BN / RB, IB = BM / RB;
   static_assert(IA % NW == 0 && IB % NW == 0, "row blocks per wave");
@@ -181,8 +182,8 @@ __global__ __launch_bounds__(64 * NW, 1) void copy_stream_probe_kernel(
   const uint32_t la0 = lds0 + (uint32_t)(wid * NA) * 1024u;
   const uint32_t lb0 = lds0 + (uint32_t)(IA + wid * NB) * 1024u;
   auto issue = [&](int slot, int ks) {
-    const int soff = ks * BK;
-    const int soffw = PANEL ? (int)((int64_t)ks * N * BK) : soff;
+    const int soff = ks * kb;
+    const int soffw = PANEL ? (int)((int64_t)ks * N * kb) : soff;
     dma_group<NA, NTW>(la0 + (uint32_t)(slot * STAGE), oa, rsw, soffw);
     dma_group<NB, false>(lb0 + (uint32_t)(slot * STAGE), ob, rsx, soff);
   };
@@ -211,18 +212,19 @@ hipError_t launch_copy_stream(dim3 grid, int flags, const uint8_t* w, const uint
                               int64_t M, int64_t K, int64_t ldw, int64_t ldx, int rows, int tiles_m,
                               uint32_t* sink, hipStream_t st) {
   const bool panel = (flags & 1) != 0, sync = (flags & 2) == 0;
+  const int kb = (flags & 4) ? 0 : 128;
   if (panel && sync)
     hipLaunchKernelGGL((copy_stream_probe_kernel<BN, BM, 8, S, NTW, true, true>), grid, dim3(512), 0,
-                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, sink);
+                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, kb, sink);
   else if (panel)
     hipLaunchKernelGGL((copy_stream_probe_kernel<BN, BM, 8, S, NTW, true, false>), grid, dim3(512), 0,
-                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, sink);
+                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, kb, sink);
   else if (sync)
     hipLaunchKernelGGL((copy_stream_probe_kernel<BN, BM, 8, S, NTW, false, true>), grid, dim3(512), 0,
-                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, sink);
+                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, kb, sink);
   else
     hipLaunchKernelGGL((copy_stream_probe_kernel<BN, BM, 8, S, NTW, false, false>), grid, dim3(512), 0,
-                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, sink);
+                       st, w, x, N, M, K, ldw, ldx, rows, tiles_m, kb, sink);
   return hipGetLastError();
 }
 

@@ -549,7 +549,7 @@ int qr_probe_copy_stream(int tile, const void* Wq, int64_t N, int64_t ldw, const
     return fail(QR_ERR_INVALID_ARG, "%s: N, M >= 1 and K a positive multiple of 128 needed", fn);
   if (rows < 8 || rows > bn || rows % 8 != 0)
     return fail(QR_ERR_INVALID_ARG, "%s: rows must be a multiple of 8 in [8, %d]", fn, bn);
-  if (flags < 0 || flags > (QR_PROBE_PANEL | QR_PROBE_NO_BARRIER))
+  if (flags < 0 || flags > (QR_PROBE_PANEL | QR_PROBE_NO_BARRIER | QR_PROBE_RESIDENT))
     return fail(QR_ERR_INVALID_ARG, "%s: unknown flags %d", fn, flags);
   if (flags & QR_PROBE_PANEL) ldw = K;  // panels have no row stride
   if (ldw < K || ldx < K || ldw % 16 != 0 || ldx % 16 != 0)
