@@ -128,10 +128,15 @@ def test_unfusable_shapes_fall_back(qt, one_launch):
     _compare(4160, 256, 256, qt, (0, 256), seed=5, expect_fused=False)
 
 
+@pytest.mark.parametrize("fuse", [0, 1])
 @pytest.mark.parametrize("M", [1, 32, 256])
-def test_7b_int8_chain_fused_equals_oracle(M, one_launch):
-    """The 7B-shaped INT8 layer with one launch per linear (after the layer
-    input's quantizer): every output equals the oracle chain bit for bit."""
+def test_7b_int8_chain_fused_equals_oracle(M, fuse):
+    """The 7B-shaped INT8 layer built from qr_w8a8_gemm_quant (after the
+    layer input's quantizer), with its separate launches (fuse 0: at 32
+    tokens the QKV and O split-K sums also quantize the next input) and with
+    one launch per linear (fuse 1): every output equals the oracle chain bit
+    for bit."""
+    B.set_fuse_override(fuse)
     qt = "int8"
     x0 = I.activations(M, 3584, seed=I.matrix_seed(2, 70 + M), kind="outliers")
     layers, dev = [], {}
