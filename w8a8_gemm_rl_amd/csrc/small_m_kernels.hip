@@ -47,6 +47,7 @@ constexpr int kNW = 8;                      // waves per block
 constexpr int kSmallMaxQW = 4;              // waves that quantize the token rows, at most
 constexpr int kBufWord3 = 0x00020000;       // raw buffer resource, 32-bit format, no swizzle
 constexpr uint32_t kOOB = 0x80000000u;      // a buffer offset past every code matrix: reads 0
+constexpr int kWeightNT = 2;                // cache policy of the weight loads: non-temporal
 
 struct SmallParams {
   const uint16_t* X;
@@ -66,7 +67,9 @@ struct SmallParams {
 // lines instead of 8). The rows reach the MFMA layout through a per-wave
 // LDS stage. Chunks past the wave's last one (c >= nch) are issued as
 // out-of-range loads (zeros, no memory traffic), so every step issues the
-// same number of loads and the compiler's counted waits stay exact.
+// same number of loads and the compiler's counted waits stay exact. Every
+// weight line is read once, so the loads carry the non-temporal hint
+// (measured 4-7% faster on the 7B-shaped linears at one and two tokens).
 template <int RF>
 __device__ __forceinline__ void load_chunk(v4u (&w)[RF][2], __amdgpu_buffer_rsrc_t rw,
                                            const uint32_t (&rowoff)[RF][2], int pl, int K, int c) {
@@ -76,7 +79,7 @@ __device__ __forceinline__ void load_chunk(v4u (&w)[RF][2], __amdgpu_buffer_rsrc
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t o = k0 < K ? rowoff[f][h] + (uint32_t)k0 : kOOB;
-      w[f][h] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)o, 0, 0));
+      w[f][h] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)o, 0, kWeightNT));
     }
 }
 
