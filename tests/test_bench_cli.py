@@ -101,3 +101,17 @@ def test_sum_quant_selection_7b(M, expect):
         N, K = shapes[name]
         assert B.gemm_plan(M, N, K, "int8")[1] > 1
     assert bench.sum_quant_linears(B, chain, shapes, M, "int8", small, True) == set()
+
+
+@pytest.mark.parametrize("chain_name,M,expect", [
+    ("32b", 32, {"q", "o"}),        # q feeds o's input, o feeds gate / up; both split K
+    ("32b", 512, set()),            # unsplit plans at 512 tokens
+    ("32b_qkv", 64, {"qkv", "o"}),  # stacked q, k, v: its q slice feeds o
+    ("7b_producers", 32, {"qkv"}),  # o's output feeds a norm, not a quantizer
+])
+def test_sum_quant_selection_other_chains(chain_name, M, expect):
+    from w8a8_gemm_rl_amd import binding as B
+
+    chain, shapes, _ = bench.chain_spec(chain_name)
+    small = bench.small_m_linears(chain, shapes, M, False)
+    assert bench.sum_quant_linears(B, chain, shapes, M, "int8", small, False) == expect
