@@ -964,6 +964,48 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const uint32_t* __re
   }
 }
 
+// Split-K sum with the bf16 epilogue, eight consecutive outputs of one token
+// per thread (N % 8 == 0, ldy % 8 == 0, Y 16-byte aligned): the same sums in
+// split order and the same epilogue as splitk_reduce_kernel, one 16-byte store.
+template <int QT, int SC>
+__global__ __launch_bounds__(256) void splitk_reduce8_kernel(
+    const uint32_t* __restrict__ part, int64_t M, int64_t N, const float* __restrict__ sx,
+    const float* __restrict__ sw, uint16_t* __restrict__ Y, int64_t ldy) {
+  const int64_t ng = N >> 3;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * ng) return;
+  const int64_t m = idx / ng, n0 = (idx % ng) * 8;
+  uint32_t w[SC][8];
+#pragma unroll
+  for (int z = 0; z < SC; ++z) {
+    const uint4* src = reinterpret_cast<const uint4*>(part + (int64_t)z * M * N + m * N + n0);
+    const uint4 a = src[0], b = src[1];
+    w[z][0] = a.x; w[z][1] = a.y; w[z][2] = a.z; w[z][3] = a.w;
+    w[z][4] = b.x; w[z][5] = b.y; w[z][6] = b.z; w[z][7] = b.w;
+  }
+  const float sxm = sx[m];
+  uint32_t bb[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float acc;
+    if constexpr (QT == kQInt8) {
+      int32_t si = 0;
+#pragma unroll
+      for (int z = 0; z < SC; ++z) si += (int32_t)w[z][e];
+      acc = (float)si;
+    } else {
+      float sf = 0.0f;
+#pragma unroll
+      for (int z = 0; z < SC; ++z) sf += __uint_as_float(w[z][e]);
+      acc = sf;
+    }
+    bb[e] = epi_bf16(acc, sxm, sw[n0 + e]);
+  }
+  *reinterpret_cast<uint4*>(Y + m * ldy + n0) =
+      make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16),
+                 bb[6] | (bb[7] << 16));
+}
+
 // Split-K sum that also quantizes the next linear's input: one block per
 // token row m. Each thread owns groups of 8 consecutive outputs (16 bytes of
 // bf16), n = 8 (t + 256 i): it adds the S partial sums of the group in split
@@ -1136,8 +1178,22 @@ hipError_t launch_gemm(const GemmPlan& plan, int qt, const GemmArgs& a, hipStrea
   const int64_t work = a.M * ((a.N + 3) / 4);
   const unsigned rgrid = (unsigned)((work + 255) / 256);
   const int vec = (a.ldy % 4) == 0;
+  // bf16 outputs with N and ldy multiples of 8 and Y 16-byte aligned: eight
+  // outputs per thread and one 16-byte store (measured 1-4 us faster on the
+  // 256- and 512-token down projections, the same bits); otherwise four.
+  const bool by8 = !a.out_raw && a.N % 8 == 0 && a.ldy % 8 == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.Y) & 15) == 0;
+  const unsigned rgrid8 = (unsigned)((a.M * (a.N / 8) + 255) / 256);
   auto reduce = [&](auto qt_c, auto sc_c) {
     constexpr int Q = decltype(qt_c)::value, SC = decltype(sc_c)::value;
+    if constexpr (SC >= 2) {
+      if (by8) {
+        hipLaunchKernelGGL((splitk_reduce8_kernel<Q, SC>), dim3(rgrid8), dim3(256), 0, st,
+                           static_cast<const uint32_t*>(a.part), a.M, a.N, a.sx, a.sw,
+                           static_cast<uint16_t*>(a.Y), a.ldy);
+        return;
+      }
+    }
     hipLaunchKernelGGL((splitk_reduce_kernel<Q, SC>), dim3(rgrid), dim3(256), 0, st,
                        static_cast<const uint32_t*>(a.part), plan.splitk, a.M, a.N, a.sx, a.sw,
                        a.Y, a.ldy, a.out_raw, vec);
