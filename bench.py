@@ -17,8 +17,8 @@ between events on its own stream, so no host launch gap is counted. Inputs
 are seeded synthetic tensors generated on the device. The roofline "traffic"
 (HBM bytes per launch) comes from the committed rocprofv3 counter summary in
 profiles/hbm_traffic.md and is null when the GEMM sources changed since.
-Where the dominant GEMM runs on a tiling the copy-stream probe replays (192x128
-or 256x256 tiles without split K), "copy_stream_us" is that probe's time over
+Where the dominant GEMM runs on a tiling the copy-stream probe replays (192x128,
+192x256 or 256x256 tiles without split K), "copy_stream_us" is that probe's time over
 the same weights and codes, timed the same way: the GEMM's operand copies,
 LDS ring, waits and barriers without the matrix work.
 
@@ -49,14 +49,17 @@ DOM_BATCH = 20  # dominant-GEMM launches per timing graph
 EPS = 1e-6  # RMSNorm epsilon of the producer workloads
 
 WORKLOADS = {
-    "7b_decode_int8": dict(M=256, qt="int8", chain="7b", sets=4, kind="outliers"),
-    "7b_decode_fp8": dict(M=256, qt="fp8", chain="7b", sets=4, kind="outliers"),
+    # gate and up run as one GEMM over the stacked [W_gate; W_up] (as rollout
+    # engines merge them; the same outputs bit for bit), QKV fused likewise
+    "7b_decode_int8": dict(M=256, qt="int8", chain="7b_gateup", sets=4, kind="outliers"),
+    "7b_decode_fp8": dict(M=256, qt="fp8", chain="7b_gateup", sets=4, kind="outliers"),
     # the same layer with one launch per linear: qr_w8a8_gemm_quant (fuse
     # override 1) adds split-K partial sums and quantizes the next linear's
     # input inside the GEMM launch behind grid-wide barriers
     "7b_decode_int8_one_launch": dict(M=256, qt="int8", chain="7b", sets=4, kind="outliers",
                                       one_launch=True),
-    "7b_decode_int8_gateup": dict(M=256, qt="int8", chain="7b_gateup", sets=4, kind="outliers"),
+    # gate and up as two GEMMs of 18944 rows each
+    "7b_decode_int8_separate": dict(M=256, qt="int8", chain="7b", sets=4, kind="outliers"),
     # with the producers of the linears' inputs (two RMSNorms, SiLU x up), fused
     # into the quantizers or run as separate torch ops before them
     "7b_decode_int8_fused": dict(M=256, qt="int8", chain="7b_producers", sets=4, kind="outliers",
@@ -1223,11 +1226,11 @@ def copy_stream_us(B, layers, bufs, chain, dom, M, N, K, qt, small, one_launch, 
     import torch
 
     tile, split, rows = B.gemm_plan(M, N, K, qt)
-    if dom in small or one_launch or split != 1 or tile not in (4, 8) or K % 128:
+    if dom in small or one_launch or split != 1 or tile not in (4, 8, 10) or K % 128:
         return None
     key = chain_keys(chain)[0]
     xq = next(bufs["q_" + L["name"]][0] for L in chain if key[L["name"]] == key[dom])
-    bm = 256 if tile == 4 else 128
+    bm = 128 if tile == 8 else 256
     sink = torch.empty(-(-N // rows) * -(-M // bm), dtype=torch.int32, device=xq.device)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(st):

@@ -485,8 +485,8 @@ int qr_set_fuse_override(int mode);
  * qr_probe_copy_stream -- the operand copies of one LDS-DMA GEMM tiling with
  *   no matrix work: the blocks, copies, LDS ring, waits and per-step
  *   barriers that qr_w8a8_gemm runs for tile `tile` (4: 256x256 tiles,
- *   2-slot ring, non-temporal weight copies; 8: 192x128 tiles, 4-slot ring)
- *   with `rows` weight rows per tile (a multiple of 8 up to the tile height,
+ *   2-slot ring, non-temporal weight copies; 8: 192x128 tiles, 4-slot ring;
+ *   10: 192x256 tiles, 2-slot ring, non-temporal weight copies) with `rows` weight rows per tile (a multiple of 8 up to the tile height,
  *   as qr_gemm_plan reports it), without split K, over the codes Wq (N rows)
  *   and Xq (M rows) of K bytes each (device, K a multiple of 128). Its time
  *   is what that tiling's copy pipeline alone takes. Row r of Xq starts at

@@ -165,6 +165,20 @@ def test_7b_decode_chain_fp8(M):
     _fp8_chain(I.CHAIN_7B, I.LINEARS_7B, ref, dev, x0, np.arange(M), 256)
 
 
+def test_7b_decode_chain_fp8_gate_up_stacked_m256():
+    # gate and up as one GEMM over [W_gate; W_up] (37888 rows, the benchmark's
+    # default layer), 256 tokens, sampled tokens checked
+    M = 256
+    ref, dev = _layer("7b", 3, I.CHAIN_7B, I.LINEARS_7B, I.W_SIGMA_7B, "fp8")
+    ref = dict(ref, gateup={k: np.concatenate([ref["gate"][k], ref["up"][k]])
+                            for k in ("Wq", "scale_w")})
+    dev = dict(dev, gateup=(torch.cat([dev["gate"][0], dev["up"][0]]),
+                            torch.cat([dev["gate"][1], dev["up"][1]])))
+    assert B.gemm_plan(M, *I.LINEARS_7B["gateup"], "fp8")[0] == 10  # 192x256 tiles
+    x0 = I.activations(M, 3584, seed=I.matrix_seed(3, 62), kind="outliers")
+    _fp8_chain(I.CHAIN_7B_GATEUP, I.LINEARS_7B, ref, dev, x0, _sample(M, 48, seed=6), 256)
+
+
 def test_32b_decode_chain_fp8_m512_sampled_tokens():
     M = 512
     ref, dev = _layer("32b", 5, I.CHAIN_32B, I.LINEARS_32B, I.W_SIGMA_32B, "fp8")

@@ -38,6 +38,8 @@ def test_read_probe_reads_every_word():
     (8, 1000, 130, 384, 96, 0, False, True),      # shrunk tiles, 3 K steps
     (4, 1000, 300, 640, 248, 0, False, True),     # ring of 2, 5 K steps
     (4, 27648, 512, 5120, 256, 0, False, True),   # the 32B gate projection at 512 tokens
+    (10, 1000, 300, 640, 184, 0, False, True),    # 192x256 tiles, ring of 2, ragged tokens
+    (10, 37888, 256, 3584, 192, 0, False, True),  # the stacked 7B gate and up at 256 tokens
     (8, 3600, 200, 1024, 192, 128, False, True),  # rows padded by one 128-byte line
     (4, 1000, 300, 640, 248, 48, False, True),    # rows padded by 48 bytes
     (8, 3600, 200, 1024, 192, 0, True, True),     # weights read as K panels
@@ -54,7 +56,7 @@ def test_copy_stream_probe_copies_the_tiles(tile, N, M, K, rows, pad, panel, bar
     Wq, Xq = Wbuf[:, :K], Xbuf[:, :K]
     if panel:
         Wq = Wq.contiguous()
-    bm = {4: 256, 8: 128}[tile]
+    bm = {4: 256, 8: 128, 10: 256}[tile]
     tiles_m, tiles_n = -(-M // bm), -(-N // rows)
     sink = torch.full((tiles_n * tiles_m + 5,), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
     B.probe_copy_stream(tile, Wq, Xq, rows, sink=sink, panel=panel, barrier=barrier,

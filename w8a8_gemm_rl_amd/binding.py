@@ -529,7 +529,7 @@ PROBE_PANEL, PROBE_NO_BARRIER, PROBE_RESIDENT = 1, 2, 4
 
 
 def probe_copy_stream(tile, Wq, Xq, rows, sink=None, panel=False, barrier=True, resident=False):
-    """Enqueue the operand copies GEMM tile `tile` (4 or 8) makes over the
+    """Enqueue the operand copies GEMM tile `tile` (4, 8 or 10) makes over the
     8-bit code matrices Wq [N, K] and Xq [M, K] (rows contiguous; their row
     strides are passed on) with `rows` weight rows per tile, without the
     matrix work; panel reads Wq's bytes as K panels instead (Wq contiguous),
@@ -545,7 +545,7 @@ def probe_copy_stream(tile, Wq, Xq, rows, sink=None, panel=False, barrier=True, 
         raise ValueError("panel reads need a contiguous Wq")
     (N, K), M = Wq.shape, Xq.shape[0]
     ldw, ldx = _rows(Wq, "Wq"), _rows(Xq, "Xq")
-    bm = {4: 256, 8: 128}.get(tile, 1)
+    bm = {4: 256, 8: 128, 10: 256}.get(tile, 1)
     grid = -(-N // max(rows, 1)) * -(-M // bm)
     if sink is None:
         sink = torch.empty(max(grid, 1), dtype=torch.int32, device=Wq.device)

@@ -1107,7 +1107,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_quant_kernel(
   X(4, 32, 128, 32, 4, 1, 128, 1, 1)  /*  6: M <= 32 narrow layers, 4 waves   */ \
   X(6, 16, 64, 16, 4, 1, 128, 1, 1)   /*  7: M <= 16 narrow layers            */ \
   X(4, 32, 192, 128, 2, 4, 128, 1, 0) /*  8: wide 256-token layers, 8 waves   */ \
-  X(4, 16, 80, 64, 5, 1, 128, 1, 1)   /*  9: 256-token INT8 QKV, 5 waves      */
+  X(4, 16, 80, 64, 5, 1, 128, 1, 1)   /*  9: 256-token INT8 QKV, 5 waves      */ \
+  X(2, 32, 192, 256, 2, 4, 128, 0, 1) /* 10: 256-token stacked gate + up      */
 
 #define QR_STR(x) #x
 #define QR_DESC(S, T, BN, BM, WN, WM, BK, FU, NT)                                          \

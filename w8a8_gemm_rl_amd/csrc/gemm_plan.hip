@@ -46,8 +46,12 @@ GemmPlan make_plan(int64_t M, int64_t N, int64_t K, int qt, int force_tile, int 
     // Very wide layers: 128 x 256 tiles (every token in one block, so each
     // weight byte is copied once) while they fit one round of the CUs, as
     // for the 32B gate and up (27648 rows: 51 us against 76 us on 256 x 256
-    // tiles with split K); wider ones (the stacked 7B gate and up) 256 x 256.
-    if (N >= 24576) tile = (N + 127) / 128 <= kCUs ? 5 : 4;
+    // tiles with split K); wider ones, such as the stacked 7B gate and up
+    // (37888 rows), 192 x 256 while those fit one round (INT8 45.0 us against
+    // 54.3 on 256 x 256 tiles and 57.9 for gate and up as two GEMMs on
+    // 192 x 128 tiles; FP8 49.3, 55.6 and 58.8), 256 x 256 beyond.
+    if (N >= 24576)
+      tile = (N + 127) / 128 <= kCUs ? 5 : ((N + 191) / 192 <= kCUs ? 10 : 4);
     else if (N >= 8192) tile = 8;
     else if (nks >= 64) tile = 2;
     else if (N >= 4096)

@@ -237,6 +237,7 @@ unsigned read_probe_blocks() { return 1024; }
 bool copy_stream_probe_tile(int tile, int& bn, int& bm) {
   if (tile == 4) { bn = 256; bm = 256; return true; }
   if (tile == 8) { bn = 192; bm = 128; return true; }
+  if (tile == 10) { bn = 192; bm = 256; return true; }
   return false;
 }
 
@@ -251,6 +252,9 @@ hipError_t launch_copy_stream_probe(int tile, const void* W, const void* X, int6
   const uint8_t* x = static_cast<const uint8_t*>(X);
   if (tile == 4)
     return launch_copy_stream<256, 256, 2, true>(grid, flags, w, x, N, M, K, ldw, ldx, rows,
+                                                 (int)tiles_m, sink, st);
+  if (tile == 10)
+    return launch_copy_stream<192, 256, 2, true>(grid, flags, w, x, N, M, K, ldw, ldx, rows,
                                                  (int)tiles_m, sink, st);
   return launch_copy_stream<192, 128, 4, false>(grid, flags, w, x, N, M, K, ldw, ldx, rows,
                                                 (int)tiles_m, sink, st);

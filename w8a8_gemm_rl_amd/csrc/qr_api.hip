@@ -544,7 +544,7 @@ int qr_probe_copy_stream(int tile, const void* Wq, int64_t N, int64_t ldw, const
   const char* fn = "qr_probe_copy_stream";
   int bn = 0, bm = 0;
   if (!qr::copy_stream_probe_tile(tile, bn, bm))
-    return fail(QR_ERR_INVALID_ARG, "%s: tile %d is not replayed (4 and 8 are)", fn, tile);
+    return fail(QR_ERR_INVALID_ARG, "%s: tile %d is not replayed (4, 8 and 10 are)", fn, tile);
   if (N < 1 || M < 1 || K < 128 || K % 128 != 0)
     return fail(QR_ERR_INVALID_ARG, "%s: N, M >= 1 and K a positive multiple of 128 needed", fn);
   if (rows < 8 || rows > bn || rows % 8 != 0)
