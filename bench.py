@@ -1,9 +1,10 @@
 """Benchmark of the W8A8 rollout linear on one MI355X.
 
 Default workload: one 7B-shaped decoder layer's quantized linears at decode
-size, INT8, M = 256 tokens: QKV 4608x3584, O 3584x3584, gate and up
-18944x3584, down 3584x18944 (N x K), with per-token activation quantization in
-front of each (gate and up share one): 4 quantizations + 5 GEMMs per step.
+size, INT8, M = 256 tokens: QKV 4608x3584, O 3584x3584, gate and up stacked
+into one 37888x3584 GEMM (the same outputs as two 18944-row GEMMs, bit for
+bit), down 3584x18944 (N x K), with per-token activation quantization in front
+of each: 4 quantizations + 4 GEMMs per step.
 A "step" is one such layer pass over one batch; successive steps walk through
 distinct copies of the layer's weights (more bytes than the 256 MB Infinity
 Cache), like a decode pass walks a model's layers.
