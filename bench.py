@@ -67,12 +67,13 @@ WORKLOADS = {
                                  fused=True),
     "7b_decode_int8_unfused": dict(M=256, qt="int8", chain="7b_producers", sets=4,
                                    kind="outliers", fused=False),
-    "32b_decode_int8": dict(M=512, qt="int8", chain="32b", sets=2, kind="normal"),
-    "32b_decode_fp8": dict(M=512, qt="fp8", chain="32b", sets=2, kind="normal"),
     # q, k and v stacked into one 7168-row projection (the merged QKV rollout
     # engines run; the 7B layer's QKV is merged the same way)
-    "32b_decode_int8_qkv": dict(M=512, qt="int8", chain="32b_qkv", sets=2, kind="normal"),
-    "32b_decode_fp8_qkv": dict(M=512, qt="fp8", chain="32b_qkv", sets=2, kind="normal"),
+    "32b_decode_int8": dict(M=512, qt="int8", chain="32b_qkv", sets=2, kind="normal"),
+    "32b_decode_fp8": dict(M=512, qt="fp8", chain="32b_qkv", sets=2, kind="normal"),
+    # q, k and v as three GEMMs
+    "32b_decode_int8_separate": dict(M=512, qt="int8", chain="32b", sets=2, kind="normal"),
+    "32b_decode_fp8_separate": dict(M=512, qt="fp8", chain="32b", sets=2, kind="normal"),
     "32b_prefill_int8": dict(M=4096, qt="int8", chain="32b_prefill", sets=2, kind="heavy"),
     # one small linear (X[16, 512] x W[512, 512], INT8): launch-bound, timed for
     # its latency, with no roofline claim behind its fraction
