@@ -274,3 +274,19 @@ def test_probe_validation(B):
     assert call(N=(1 << 20) - 64, K=1 << 11, ldw=1 << 12, ldx=1 << 11, words=1 << 30) == UNS
     assert call(flags=1, ldw=0, sink=NULL) == INV  # (stops at the null sink, past the stride check)
     assert "null" in L.qr_last_error().decode()
+
+
+@pytest.mark.parametrize("qt", ["int8", "fp8"])
+def test_plan_very_wide_256_token_layers(B, qt):
+    # 256 tokens on very wide layers: 128x256 tiles while they fit one round
+    # of the 256 CUs (the 32B gate, 27648 rows), 192x256 tiles while those do
+    # (the stacked 7B gate and up, 37888 rows: 198 blocks), 256x256 beyond
+    # (the stacked 32B gate and up, 55296 rows)
+    names = {t: B.tile_name(t) for t in range(B.num_tiles())}
+    t, s, r = B.gemm_plan(256, 27648, 5120, qt)
+    assert "_n128_m256_" in names[t] and s == 1
+    assert B.gemm_plan(256, 37888, 3584, qt) == (10, 1, 192)
+    assert "_n192_m256_" in names[10]
+    t, s, r = B.gemm_plan(256, 55296, 5120, qt)
+    assert "_n256_m256_" in names[t]
+    assert B.gemm_plan(128, 37888, 3584, qt)[0] != 10  # one token tile of 128 fits
